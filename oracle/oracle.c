@@ -1,0 +1,305 @@
+/*
+ * oracle.c -- the plain, slow CPU reference for the fused memory-bound chains.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The product path (the HIP library libmbp.so and its
+ * Python binding) never includes, links, imports or calls anything in oracle/.
+ * Only the tests, the smoke check and the bench's cpu_baseline leg use it.  It
+ * shares no header, helper, table or constant with the HIP sources.
+ *
+ * Form.  Every function runs the UNFUSED op sequence literally: one loop per op,
+ * in the order the pages write the ops, with every intermediate materialised as
+ * a full array.  Inputs are the stored binary32 / bfloat16 values widened
+ * exactly to binary64.  Built with -O2 -fno-fast-math -ffp-contract=off, so no
+ * multiply-add is contracted and nothing is reassociated.
+ *
+ * Modes.
+ *   ORACLE_EXACT (0): every intermediate is binary64; constants are the decimal
+ *     literals parsed to binary64.  This is the reference the fused kernels are
+ *     gated against.
+ *   ORACLE_SEQ (1): emulates one-op-per-launch execution.  After each op the
+ *     value is rounded to the unfused variant's storage type (binary32 for the
+ *     fp32 chains; bfloat16 for bf16 I/O, reached as binary32 then bfloat16,
+ *     because such a kernel computes in fp32 and stores bf16).  Row statistics
+ *     are stored as binary32.  Constants are rounded to binary32 first, as an
+ *     fp32 kernel multiplying by a Python float does.  For + - * / sqrt on
+ *     binary32 operands, computing in binary64 and rounding once to binary32 is
+ *     the correctly rounded binary32 result (53 >= 2*24 + 2; S. A. Figueroa,
+ *     "When is double rounding innocuous?", SIGNUM Newsletter 1995), so SEQ is
+ *     bit-exact for element-wise ops.  Reductions depend on summation order;
+ *     SEQ sums in binary64, so for them it is a tolerance reference only.
+ *   ORACLE_SEQ3 (2): residual add + LayerNorm + GeLU as three eager launches
+ *     (add, a LayerNorm kernel, gelu), each stored in the I/O type.
+ *
+ * All outputs are written as binary64 (the stored value, widened, in SEQ modes).
+ * Return value: 0 on success, negative on a bad argument or allocation failure.
+ *
+ * Sources (the four pages on operator fusion):
+ *   [P1] PyTorch operator-fusion practice post, 0539edu.com/news/5489619
+ *        section 1.1 (the add/relu/mul/add step table), section 3.1 (baseline
+ *        chain, randn inputs, scale 0.5).
+ *   [P2] "算子融合与 Kernel 优化：从 CUDA Graph 到 FlashAttention 的极致性能"
+ *        (plumephp.com), section 2.3 (residual + LayerNorm + GeLU kernel).
+ *   [P3] "4、算子融合（Kernel Fusion）" (5688vip.com course chapter), section 4.3
+ *        (LayerNorm definition and its five unfused kernels).
+ *   [P4] "TorchInductor Pipeline 与算子融合" (blog.kkkzoz.top), the 10-op model at
+ *        the top of the post, section 6.4 (mean = row sum, then divide), section
+ *        02 Table 2 (the ten eager kernels).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_EXACT = 0, ORACLE_SEQ = 1, ORACLE_SEQ3 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_ACT_NONE = 0, ORACLE_ACT_GELU_TANH = 1 };
+
+/* ---- storage formats ------------------------------------------------------ */
+
+/* bfloat16 is the upper half of a binary32 bit pattern. */
+static double bf16_bits_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* binary32 -> bfloat16, round to nearest even on the dropped 16 bits; a NaN
+ * stays a (quiet) NaN. */
+static uint16_t float_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+/* round a binary64 value to binary32 (x86-64 SSE conversion, round-to-nearest-even) */
+static double r32(double v) { return (double)(float)v; }
+
+/* round to bfloat16 the way a kernel that computes in fp32 and stores bf16 does */
+static double rbf16(double v) { return bf16_bits_to_double(float_to_bf16_rne((float)v)); }
+
+/* round to the storage type of the I/O (SEQ modes) */
+static double rstore(int dtype, double v) { return dtype == ORACLE_BF16 ? rbf16(v) : r32(v); }
+
+static double load_elem(int dtype, const void* p, int64_t i) {
+  if (dtype == ORACLE_BF16) return bf16_bits_to_double(((const uint16_t*)p)[i]);
+  return (double)((const float*)p)[i];
+}
+
+static double* alloc_d(int64_t n) { return (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double)); }
+
+/* ---- tanh-approximated GeLU ----------------------------------------------
+ * [P2] section 2.3: g(u) = 0.5 u (1 + tanh(0.7978845608 (u + 0.044715 u^3))),
+ * constants exactly as the page writes them. */
+static double gelu_tanh(double u) {
+  double u3 = u * u * u;
+  double inner = u + 0.044715 * u3;
+  double z = 0.7978845608 * inner;
+  return 0.5 * u * (1.0 + tanh(z));
+}
+
+void oracle_gelu_tanh(const double* u, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = gelu_tanh(u[i]);
+}
+
+/* bfloat16 encode/decode, exported so that the tests can pin them against an
+ * independent library conversion. */
+void oracle_to_bf16(const float* in, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = float_to_bf16_rne(in[i]);
+}
+
+/* ---- (a) pointwise chain --------------------------------------------------
+ * [P1] section 1.1 and 3.1: y = relu(x + b1) * scale + b2, run as four eager
+ * ops: t = x + b1; r = relu(t); u = r * scale; y = u + b2.  b1 and b2 are full
+ * tensors of x's shape (randn_like).  relu keeps NaN (eager semantics: t < 0
+ * selects 0, everything else passes through). */
+int oracle_pointwise_chain(const float* x, const float* b1, const float* b2, int64_t n,
+                           double scale, int mode, double* y) {
+  if (n < 0) return -1;
+  if (mode != ORACLE_EXACT && mode != ORACLE_SEQ) return -2;
+  if (n == 0) return 0;
+  if (!x || !b1 || !b2 || !y) return -1;
+  const int seq = (mode == ORACLE_SEQ);
+  const double s = seq ? r32(scale) : scale;
+  double* t = alloc_d(n);
+  double* r = alloc_d(n);
+  double* u = alloc_d(n);
+  if (!t || !r || !u) { free(t); free(r); free(u); return -3; }
+
+  for (int64_t i = 0; i < n; ++i) {           /* op 1: add */
+    t[i] = (double)x[i] + (double)b1[i];
+    if (seq) t[i] = r32(t[i]);
+  }
+  for (int64_t i = 0; i < n; ++i)             /* op 2: relu */
+    r[i] = (t[i] < 0.0) ? 0.0 : t[i];
+  for (int64_t i = 0; i < n; ++i) {           /* op 3: mul by the scalar */
+    u[i] = r[i] * s;
+    if (seq) u[i] = r32(u[i]);
+  }
+  for (int64_t i = 0; i < n; ++i) {           /* op 4: add */
+    y[i] = u[i] + (double)b2[i];
+    if (seq) y[i] = r32(y[i]);
+  }
+  free(t); free(r); free(u);
+  return 0;
+}
+
+/* ---- (b1) the 10-op graph: prologue, row mean, epilogue --------------------
+ * [P4] the model at the top of the post, x [rows, cols], bias/gamma/beta [cols]
+ * broadcast over rows (section 1.1: stride 0 along the row dimension):
+ *   t = x * alpha + bias        (two ops: mul, add)        alpha = 1.1
+ *   a = relu(t)
+ *   p = a * a ; q = a * c ; s = p + q                      c = 0.1
+ *   m = s.mean(dim=1)           (section 6.4: a row SUM, then divide by cols)
+ *   y = (s - m) * gamma + beta  (three ops: sub, mul, add)
+ * Ten eager kernels in all (section 02, Table 2). */
+int oracle_row_mean_epilogue(const float* x, const float* bias, const float* gamma,
+                             const float* beta, int64_t rows, int64_t cols, double alpha,
+                             double c, int mode, double* y) {
+  if (rows < 0 || cols <= 0) return -1;
+  if (mode != ORACLE_EXACT && mode != ORACLE_SEQ) return -2;
+  if (rows == 0) return 0;
+  if (!x || !bias || !gamma || !beta || !y) return -1;
+  const int seq = (mode == ORACLE_SEQ);
+  const double al = seq ? r32(alpha) : alpha;
+  const double cc = seq ? r32(c) : c;
+  const int64_t n = rows * cols;
+  double* t1 = alloc_d(n);
+  double* t = alloc_d(n);
+  double* a = alloc_d(n);
+  double* p = alloc_d(n);
+  double* q = alloc_d(n);
+  double* s = alloc_d(n);
+  double* m = alloc_d(rows);
+  double* d = alloc_d(n);
+  double* e = alloc_d(n);
+  int rc = 0;
+  if (!t1 || !t || !a || !p || !q || !s || !m || !d || !e) { rc = -3; goto done; }
+#define RS(v) (seq ? r32(v) : (v))
+  for (int64_t i = 0; i < rows; ++i)          /* op 1: mul by alpha */
+    for (int64_t j = 0; j < cols; ++j) t1[i * cols + j] = RS((double)x[i * cols + j] * al);
+  for (int64_t i = 0; i < rows; ++i)          /* op 2: add bias[j] */
+    for (int64_t j = 0; j < cols; ++j) t[i * cols + j] = RS(t1[i * cols + j] + (double)bias[j]);
+  for (int64_t k = 0; k < n; ++k)             /* op 3: relu */
+    a[k] = (t[k] < 0.0) ? 0.0 : t[k];
+  for (int64_t k = 0; k < n; ++k)             /* op 4: a * a */
+    p[k] = RS(a[k] * a[k]);
+  for (int64_t k = 0; k < n; ++k)             /* op 5: a * c */
+    q[k] = RS(a[k] * cc);
+  for (int64_t k = 0; k < n; ++k)             /* op 6: p + q */
+    s[k] = RS(p[k] + q[k]);
+  for (int64_t i = 0; i < rows; ++i) {        /* op 7: row mean = row sum / cols */
+    double acc = 0.0;
+    for (int64_t j = 0; j < cols; ++j) acc += s[i * cols + j];
+    m[i] = RS(acc / (double)cols);
+  }
+  for (int64_t i = 0; i < rows; ++i)          /* op 8: s - m (m broadcast over the row) */
+    for (int64_t j = 0; j < cols; ++j) d[i * cols + j] = RS(s[i * cols + j] - m[i]);
+  for (int64_t i = 0; i < rows; ++i)          /* op 9: * gamma[j] */
+    for (int64_t j = 0; j < cols; ++j) e[i * cols + j] = RS(d[i * cols + j] * (double)gamma[j]);
+  for (int64_t i = 0; i < rows; ++i)          /* op 10: + beta[j] */
+    for (int64_t j = 0; j < cols; ++j) y[i * cols + j] = RS(e[i * cols + j] + (double)beta[j]);
+#undef RS
+done:
+  free(t1); free(t); free(a); free(p); free(q); free(s); free(m); free(d); free(e);
+  return rc;
+}
+
+/* ---- (b2) residual add + LayerNorm + tanh-GeLU -----------------------------
+ * [P3] section 4.3: mean = mean(x); var = var(x); y = (x - mean)/sqrt(var + eps)
+ * * gamma + beta, as five unfused kernels (mean, var, subtract, divide,
+ * multiply-add).  The variance is the biased one (divide by cols), computed
+ * about the finished mean (the chapter's second pass).  [P2] section 2.3 puts a
+ * residual add in front (v = x + residual) and the tanh-GeLU behind:
+ * out = gelu(LN(x + residual) * gamma + beta).  residual == NULL skips the add;
+ * act == ORACLE_ACT_NONE skips the GeLU (plain LayerNorm).
+ * dtype ORACLE_F32: x, residual, gamma, beta are binary32; ORACLE_BF16: all four
+ * are bfloat16 bit patterns (uint16). */
+int oracle_add_layernorm_gelu(int dtype, const void* x, const void* residual, const void* gamma,
+                              const void* beta, int64_t rows, int64_t cols, double eps, int act,
+                              int mode, double* y) {
+  if (rows < 0 || cols <= 0) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -2;
+  if (act != ORACLE_ACT_NONE && act != ORACLE_ACT_GELU_TANH) return -2;
+  if (mode != ORACLE_EXACT && mode != ORACLE_SEQ && mode != ORACLE_SEQ3) return -2;
+  if (rows == 0) return 0;
+  if (!x || !gamma || !beta || !y) return -1;
+  const int seq = (mode == ORACLE_SEQ);
+  const int seq3 = (mode == ORACLE_SEQ3);
+  const int64_t n = rows * cols;
+  double* v = alloc_d(n);
+  double* mean = alloc_d(rows);
+  double* var = alloc_d(rows);
+  double* cen = alloc_d(n);
+  double* nrm = alloc_d(n);
+  double* u = alloc_d(n);
+  if (!v || !mean || !var || !cen || !nrm || !u) {
+    free(v); free(mean); free(var); free(cen); free(nrm); free(u);
+    return -3;
+  }
+  const double eps_used = seq ? r32(eps) : eps;
+
+  /* op 0 (only with a residual): v = x + residual */
+  for (int64_t k = 0; k < n; ++k) {
+    double xv = load_elem(dtype, x, k);
+    if (residual) {
+      xv = xv + load_elem(dtype, residual, k);
+      if (seq || seq3) xv = rstore(dtype, xv);
+    }
+    v[k] = xv;
+  }
+  /* op 1: mean over the row */
+  for (int64_t i = 0; i < rows; ++i) {
+    double acc = 0.0;
+    for (int64_t j = 0; j < cols; ++j) acc += v[i * cols + j];
+    mean[i] = acc / (double)cols;
+    if (seq) mean[i] = r32(mean[i]);
+  }
+  /* op 2: biased variance about that mean */
+  for (int64_t i = 0; i < rows; ++i) {
+    double acc = 0.0;
+    for (int64_t j = 0; j < cols; ++j) {
+      double dlt = v[i * cols + j] - mean[i];
+      acc += dlt * dlt;
+    }
+    var[i] = acc / (double)cols;
+    if (seq) var[i] = r32(var[i]);
+  }
+  /* op 3: subtract the mean */
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t j = 0; j < cols; ++j) {
+      double cv = v[i * cols + j] - mean[i];
+      cen[i * cols + j] = seq ? rstore(dtype, cv) : cv;
+    }
+  /* op 4: divide by sqrt(var + eps) (eps inside the root) */
+  for (int64_t i = 0; i < rows; ++i) {
+    double sd = seq ? r32(sqrt(r32(var[i] + eps_used))) : sqrt(var[i] + eps_used);
+    for (int64_t j = 0; j < cols; ++j) {
+      double nv = cen[i * cols + j] / sd;
+      nrm[i * cols + j] = seq ? rstore(dtype, nv) : nv;
+    }
+  }
+  /* op 5: multiply-add with gamma[j], beta[j] */
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t j = 0; j < cols; ++j) {
+      double g = load_elem(dtype, gamma, j), b = load_elem(dtype, beta, j);
+      double uv;
+      if (seq) uv = rstore(dtype, r32(r32(nrm[i * cols + j] * g) + b));
+      else uv = nrm[i * cols + j] * g + b;
+      if (seq3) uv = rstore(dtype, uv);
+      u[i * cols + j] = uv;
+    }
+  /* op 6 (only with act): tanh-GeLU */
+  for (int64_t k = 0; k < n; ++k) {
+    double o = u[k];
+    if (act == ORACLE_ACT_GELU_TANH) {
+      o = gelu_tanh(o);
+      if (seq || seq3) o = rstore(dtype, o);
+    }
+    y[k] = o;
+  }
+  free(v); free(mean); free(var); free(cen); free(nrm); free(u);
+  return 0;
+}

@@ -1,0 +1,397 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each ``pin_*`` takes a loaded oracle library (``oracle.load()`` or a mutant
+build) and raises ``AssertionError`` when the oracle disagrees with:
+
+* the hand-derived worked examples under ``tests/golden/`` (each cites the page
+  and section whose definition it works through);
+* exact rational arithmetic (``fractions.Fraction``) or 40-digit ``mpmath`` on
+  tiny inputs (brute force);
+* closed forms and invariants that the definitions fix;
+* independent library code (numpy float64 / float32, torch CPU float64
+  ``layer_norm`` and tanh-``gelu``, torch's bfloat16 conversion).
+
+The same functions run in ``test_oracle_pins.py`` (must pass) and in
+``test_oracle_mutants.py`` (a planted mistake in the oracle must make at least
+one of them fail).
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import mpmath
+import numpy as np
+
+import oracle
+from golden_io import read
+
+RNG_SEED = 20241202
+
+
+def _rng(k=0):
+    return np.random.default_rng([RNG_SEED, k])
+
+
+def _close(a, b, rtol, atol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    bad = ~(np.abs(a - b) <= atol + rtol * np.abs(b))
+    bad |= np.isnan(a) != np.isnan(b)
+    assert not bad.any(), f"{what}: {int(bad.sum())} mismatches, first {a[bad][:3]} vs {b[bad][:3]}"
+
+
+# ----------------------------------------------------------------- chain
+
+def pin_chain_worked(lib):
+    g = read("chain_worked.txt")
+    x, b1, b2 = (np.array(g[k], np.float32) for k in ("x", "b1", "b2"))
+    y = oracle.pointwise_chain(x, b1, b2, g["scale"], lib=lib)
+    assert np.array_equal(y, np.array(g["y"])), f"chain worked example: {y}"
+
+
+def pin_chain_bruteforce(lib):
+    r = _rng(1)
+    x, b1, b2 = (r.standard_normal(32).astype(np.float32) for _ in range(3))
+    scale = Fraction(1, 2)
+    exact = []
+    for i in range(32):
+        t = Fraction(float(x[i])) + Fraction(float(b1[i]))
+        t = t if t > 0 else Fraction(0)
+        exact.append(float(t * scale + Fraction(float(b2[i]))))
+    y = oracle.pointwise_chain(x, b1, b2, 0.5, lib=lib)
+    _close(y, exact, 1e-15, 1e-300, "chain vs exact rationals")
+    ys = oracle.pointwise_chain(x, b1, b2, 0.5, mode=oracle.SEQ, lib=lib)
+    _close(ys, exact, 2.0 ** -22, 2.0 ** -40, "chain seq vs exact rationals")
+
+
+def pin_chain_invariants(lib):
+    r = _rng(2)
+    n = 4096
+    x, b1, b2 = (r.standard_normal(n).astype(np.float32) for _ in range(3))
+    y = oracle.pointwise_chain(x, b1, b2, 0.5, lib=lib)
+    b2d = b2.astype(np.float64)
+    assert (y >= b2d).all(), "relu(.)*scale + b2 must be >= b2 for scale > 0"
+    dead = (x.astype(np.float64) + b1.astype(np.float64)) <= 0
+    assert dead.any() and np.array_equal(y[dead], b2d[dead]), "y == b2 exactly where x + b1 <= 0"
+    y1 = oracle.pointwise_chain(x, b1, np.zeros(n, np.float32), 1.0, lib=lib)
+    relu = np.maximum(x.astype(np.float64) + b1.astype(np.float64), 0.0)
+    assert np.array_equal(y1, relu), "scale 1, b2 0 reduces to relu(x + b1)"
+    # NaN propagates through relu (eager semantics)
+    xn = x.copy()
+    xn[7] = np.nan
+    yn = oracle.pointwise_chain(xn, b1, b2, 0.5, lib=lib)
+    assert np.isnan(yn[7]) and not np.isnan(np.delete(yn, 7)).any()
+
+
+def pin_chain_numpy(lib):
+    r = _rng(3)
+    x, b1, b2 = (r.standard_normal(10007).astype(np.float32) for _ in range(3))
+    ref = np.maximum(x.astype(np.float64) + b1, 0.0) * 0.5 + b2.astype(np.float64)
+    _close(oracle.pointwise_chain(x, b1, b2, 0.5, lib=lib), ref, 1e-15, 0.0, "chain vs numpy f64")
+    # SEQ mode is one correctly rounded fp32 op at a time: numpy float32 does exactly that
+    t = x + b1
+    u = np.where(t < 0, np.float32(0), t) * np.float32(0.5)
+    ref32 = (u + b2).astype(np.float64)
+    ys = oracle.pointwise_chain(x, b1, b2, 0.5, mode=oracle.SEQ, lib=lib)
+    assert np.array_equal(ys, ref32), "chain SEQ must equal numpy float32 op by op"
+    # a non-dyadic scale: rounding t before the multiply now matters
+    u = np.where(t < 0, np.float32(0), t) * np.float32(0.3)
+    ys = oracle.pointwise_chain(x, b1, b2, 0.3, mode=oracle.SEQ, lib=lib)
+    assert np.array_equal(ys, (u + b2).astype(np.float64)), "chain SEQ, scale 0.3"
+
+
+# ----------------------------------------------------------------- 10-op graph
+
+def pin_tenop_worked(lib):
+    g = read("tenop_worked.txt")
+    x = np.array([g["x"]], np.float32)
+    y = oracle.row_mean_epilogue(x, *(np.array(g[k], np.float32) for k in ("bias", "gamma", "beta")),
+                                 alpha=g["alpha"], c=g["c"], lib=lib)
+    _close(y[0], g["y"], 1e-13, 1e-13, "10-op worked example")
+
+
+def _tenop_exact(x, bias, gamma, beta, alpha, c):
+    rows, cols = x.shape
+    al, cc = Fraction(alpha), Fraction(c)
+    s = [[None] * cols for _ in range(rows)]
+    for i in range(rows):
+        for j in range(cols):
+            t = Fraction(float(x[i, j])) * al + Fraction(float(bias[j]))
+            a = t if t > 0 else Fraction(0)
+            s[i][j] = a * a + a * cc
+    y = np.empty((rows, cols))
+    for i in range(rows):
+        m = sum(s[i]) / cols
+        for j in range(cols):
+            y[i, j] = float((s[i][j] - m) * Fraction(float(gamma[j])) + Fraction(float(beta[j])))
+    return y
+
+
+def pin_tenop_bruteforce(lib):
+    r = _rng(4)
+    x = r.standard_normal((4, 8)).astype(np.float32)
+    bias, gamma, beta = (r.standard_normal(8).astype(np.float32) for _ in range(3))
+    ref = _tenop_exact(x, bias, gamma, beta, "1.1", "0.1")
+    y = oracle.row_mean_epilogue(x, bias, gamma, beta, 1.1, 0.1, lib=lib)
+    _close(y, ref, 1e-12, 1e-12, "10-op vs exact rationals (decimal 1.1, 0.1)")
+    # a wide, non-square case against numpy float64 (rows and cols differ, so a
+    # swapped axis or a bias indexed by row cannot pass)
+    x = r.standard_normal((5, 37)).astype(np.float32)
+    bias, gamma, beta = (r.standard_normal(37).astype(np.float32) for _ in range(3))
+    a = np.maximum(x.astype(np.float64) * 1.1 + bias, 0.0)
+    s = a * a + a * 0.1
+    ref = (s - s.mean(axis=1, keepdims=True)) * gamma.astype(np.float64) + beta
+    _close(oracle.row_mean_epilogue(x, bias, gamma, beta, lib=lib), ref, 1e-12, 1e-12, "10-op vs numpy f64")
+
+
+def pin_tenop_invariants(lib):
+    r = _rng(5)
+    rows, cols = 6, 40
+    x = r.standard_normal((rows, cols)).astype(np.float32)
+    bias, beta = (r.standard_normal(cols).astype(np.float32) for _ in range(2))
+    k = np.float32(1.75)
+    y = oracle.row_mean_epilogue(x, bias, np.full(cols, k, np.float32), beta, lib=lib)
+    # constant gamma: every row of y has mean(beta) as its mean
+    _close(y.mean(axis=1), np.full(rows, beta.astype(np.float64).mean()), 0, 1e-12, "row mean = mean(beta)")
+    y = oracle.row_mean_epilogue(x, bias, np.ones(cols, np.float32), np.zeros(cols, np.float32), lib=lib)
+    _close(y.mean(axis=1), np.zeros(rows), 0, 1e-12, "gamma 1, beta 0: row mean 0")
+    # every t <= 0: s = 0, m = 0, so y == beta exactly
+    xn = -np.abs(x) - 1
+    y = oracle.row_mean_epilogue(xn, -np.abs(bias), r.standard_normal(cols).astype(np.float32), beta, lib=lib)
+    assert np.array_equal(y, np.broadcast_to(beta.astype(np.float64), y.shape)), "all-dead rows give beta"
+    # s >= 0, so y - beta has the sign pattern of (s - m) * gamma; with gamma = 1
+    # the row minimum sits at the smallest s, which is >= 0 - m
+    y = oracle.row_mean_epilogue(x, bias, np.ones(cols, np.float32), np.zeros(cols, np.float32), lib=lib)
+    a = np.maximum(x.astype(np.float64) * 1.1 + bias, 0)
+    m = (a * a + 0.1 * a).mean(axis=1)
+    assert (y.min(axis=1) >= -m - 1e-12).all(), "s >= 0 bounds y below by -m"
+
+
+def pin_tenop_seq(lib):
+    # rows of 8 values of moderate size: the row sums of the fp32 s values are
+    # exact in binary64, so the SEQ mean is RN32 of the exact mean, and every
+    # other op is one correctly rounded fp32 op (numpy float32)
+    r = _rng(6)
+    x = r.standard_normal((16, 8)).astype(np.float32)
+    bias, gamma, beta = (r.standard_normal(8).astype(np.float32) for _ in range(3))
+    t = x * np.float32(1.1) + bias
+    a = np.where(t < 0, np.float32(0), t)
+    s = a * a + a * np.float32(0.1)
+    m = np.array([np.float32(math.fsum(map(float, row)) / 8) for row in s], np.float32)[:, None]
+    ref = ((s - m) * gamma + beta).astype(np.float64)
+    y = oracle.row_mean_epilogue(x, bias, gamma, beta, mode=oracle.SEQ, lib=lib)
+    assert np.array_equal(y, ref), "10-op SEQ must equal numpy float32 op by op"
+
+
+# ----------------------------------------------------------------- LayerNorm (+ residual, GeLU)
+
+def _ln_mp(v, gamma, beta, eps, act):
+    """40-digit mpmath LayerNorm (+ tanh-GeLU) of one row of exact inputs."""
+    mpmath.mp.dps = 40
+    vv = [mpmath.mpf(float(t)) for t in v]
+    n = len(vv)
+    mu = mpmath.fsum(vv) / n
+    var = mpmath.fsum([(t - mu) ** 2 for t in vv]) / n
+    sd = mpmath.sqrt(var + mpmath.mpf(eps))
+    out = []
+    for j, t in enumerate(vv):
+        u = (t - mu) / sd * mpmath.mpf(float(gamma[j])) + mpmath.mpf(float(beta[j]))
+        if act:
+            z = mpmath.mpf("0.7978845608") * (u + mpmath.mpf("0.044715") * u ** 3)
+            u = mpmath.mpf("0.5") * u * (1 + mpmath.tanh(z))
+        out.append(float(u))
+    return out
+
+
+def pin_ln_worked(lib):
+    g = read("layernorm_worked.txt")
+    y = oracle.add_layernorm_gelu(np.array([g["x"]], np.float32), None,
+                                  np.array(g["gamma"], np.float32), np.array(g["beta"], np.float32),
+                                  eps=g["eps"], act=oracle.ACT_NONE, lib=lib)
+    _close(y[0], g["y"], 1e-15, 0, "LayerNorm worked example")
+    mpmath.mp.dps = 30
+    inv = float(1 / mpmath.sqrt(mpmath.mpf("1.00001")))
+    _close(np.abs(y[0]), np.full(8, inv), 1e-15, 0, "1/sqrt(1 + eps)")
+
+
+def pin_ln_closed_forms(lib):
+    r = _rng(7)
+    # two-valued row a, b alternating: +-(|a - b|/2) / sqrt(((a - b)/2)^2 + eps)
+    a, b = 1.25, -3.5
+    x = np.array([[a, b] * 6], np.float32)
+    y = oracle.add_layernorm_gelu(x, None, np.ones(12, np.float32), np.zeros(12, np.float32),
+                                  eps=1e-5, act=oracle.ACT_NONE, lib=lib)
+    h = abs(a - b) / 2
+    mag = h / math.sqrt(h * h + 1e-5)
+    _close(y[0], np.array([mag, -mag] * 6), 1e-14, 0, "two-valued row")
+    # constant rows give beta exactly
+    cols = 33
+    xc = np.repeat(r.standard_normal((4, 1)).astype(np.float32) * 50, cols, axis=1)
+    gamma = r.standard_normal(cols).astype(np.float32)
+    beta = r.standard_normal(cols).astype(np.float32)
+    y = oracle.add_layernorm_gelu(xc, None, gamma, beta, act=oracle.ACT_NONE, lib=lib)
+    assert np.array_equal(y, np.broadcast_to(beta.astype(np.float64), y.shape)), "constant row -> beta"
+    # gamma 1, beta 0: row mean 0, biased variance var/(var + eps)
+    x = (r.standard_normal((5, 64)) * np.array([[1e-3], [0.01], [1], [10], [100]])).astype(np.float32)
+    y = oracle.add_layernorm_gelu(x, None, np.ones(64, np.float32), np.zeros(64, np.float32),
+                                  act=oracle.ACT_NONE, lib=lib)
+    mpmath.mp.dps = 40
+    for i in range(5):
+        vv = [mpmath.mpf(float(t)) for t in x[i]]
+        mu = mpmath.fsum(vv) / 64
+        var = mpmath.fsum([(t - mu) ** 2 for t in vv]) / 64
+        want = float(var / (var + mpmath.mpf(1e-5)))
+        _close(y[i].mean(), 0.0, 0, 1e-13, "normalised row mean")
+        _close(np.mean(y[i] ** 2) - y[i].mean() ** 2, want, 1e-12, 0, "normalised biased variance")
+    # shift invariance: LN(x + c) == LN(x) (dyadic values, so x + 64 is exact in fp32)
+    xs = (np.round(r.standard_normal((3, 16)) * 8) / 8).astype(np.float32)
+    g1 = r.standard_normal(16).astype(np.float32)
+    b1 = r.standard_normal(16).astype(np.float32)
+    y0 = oracle.add_layernorm_gelu(xs, None, g1, b1, act=oracle.ACT_GELU_TANH, lib=lib)
+    y1 = oracle.add_layernorm_gelu(xs + np.float32(64), None, g1, b1, act=oracle.ACT_GELU_TANH, lib=lib)
+    _close(y1, y0, 1e-12, 1e-12, "shift invariance")
+
+
+def pin_ln_bruteforce(lib):
+    r = _rng(8)
+    for dt in ("f32", "bf16"):
+        x = r.standard_normal((4, 8)).astype(np.float32) * 3 + 1
+        res = r.standard_normal((4, 8)).astype(np.float32)
+        gamma = (1 + 0.1 * r.standard_normal(8)).astype(np.float32)
+        beta = (0.1 * r.standard_normal(8)).astype(np.float32)
+        if dt == "bf16":
+            args = [_torch_bf16_bits(a) for a in (x, res, gamma, beta)]
+            vals = [a.astype(np.uint32) << 16 for a in args]
+            x, res, gamma, beta = (v.view(np.float32) for v in vals)
+        else:
+            args = [x, res, gamma, beta]
+        for act in (oracle.ACT_NONE, oracle.ACT_GELU_TANH):
+            for with_res in (False, True):
+                y = oracle.add_layernorm_gelu(args[0], args[1] if with_res else None, args[2], args[3],
+                                              eps=1e-5, act=act, lib=lib)
+                for i in range(4):
+                    v = x[i].astype(np.float64) + (res[i] if with_res else 0)
+                    ref = _ln_mp(v, gamma, beta, 1e-5, act == oracle.ACT_GELU_TANH)
+                    _close(y[i], ref, 1e-12, 1e-13, f"LN {dt} act={act} res={with_res} vs mpmath")
+
+
+def pin_ln_torch(lib):
+    import torch
+    import torch.nn.functional as F
+    r = _rng(9)
+    rows, cols = 7, 301
+    x = (r.standard_normal((rows, cols)) * 2 + r.uniform(-100, 100, (rows, 1))).astype(np.float32)
+    res = r.standard_normal((rows, cols)).astype(np.float32)
+    gamma = (1 + 0.1 * r.standard_normal(cols)).astype(np.float32)
+    beta = (0.1 * r.standard_normal(cols)).astype(np.float32)
+    tx, tr = torch.from_numpy(x).double(), torch.from_numpy(res).double()
+    tg, tb = torch.from_numpy(gamma).double(), torch.from_numpy(beta).double()
+    ln = F.layer_norm(tx + tr, (cols,), tg, tb, eps=1e-5)
+    y = oracle.add_layernorm_gelu(x, res, gamma, beta, act=oracle.ACT_NONE, lib=lib)
+    _close(y, ln.numpy(), 1e-10, 1e-10, "LN vs torch float64 layer_norm")
+    # torch's tanh-GeLU uses sqrt(2/pi) = 0.7978845608028654; the pages' literal
+    # 0.7978845608 differs by 3.6e-12 relative, far inside this tolerance
+    g = F.gelu(ln, approximate="tanh")
+    y = oracle.add_layernorm_gelu(x, res, gamma, beta, act=oracle.ACT_GELU_TANH, lib=lib)
+    _close(y, g.numpy(), 1e-9, 1e-10, "LN + GeLU vs torch float64")
+
+
+def pin_gelu(lib):
+    g = read("gelu_values.txt")
+    got = oracle.gelu_tanh(np.array(g["u"]), lib=lib)
+    _close(got, g["g"], 1e-13, 1e-15, "GeLU worked values")
+    mpmath.mp.dps = 40
+    u = _rng(10).standard_normal(200) * 4
+    ref = [float(mpmath.mpf("0.5") * mpmath.mpf(t) * (1 + mpmath.tanh(
+        mpmath.mpf("0.7978845608") * (mpmath.mpf(t) + mpmath.mpf("0.044715") * mpmath.mpf(t) ** 3))))
+        for t in u]
+    # for u << 0 the literal 1 + tanh(z) cancels, so the error is absolute
+    # (about 1e-16 |u|), not relative
+    _close(oracle.gelu_tanh(u, lib=lib), ref, 1e-14, 1e-14, "GeLU vs mpmath")
+    # odd-part identity: g(u) - g(-u) = u
+    _close(oracle.gelu_tanh(u, lib=lib) - oracle.gelu_tanh(-u, lib=lib), u, 1e-14, 1e-300, "g(u)-g(-u)=u")
+
+
+def pin_residual_zero(lib):
+    r = _rng(11)
+    x = _torch_bf16_bits(r.standard_normal((3, 40)).astype(np.float32))
+    z = np.zeros_like(x)
+    g = _torch_bf16_bits((1 + 0.1 * r.standard_normal(40)).astype(np.float32))
+    b = _torch_bf16_bits((0.1 * r.standard_normal(40)).astype(np.float32))
+    for mode in (oracle.EXACT, oracle.SEQ, oracle.SEQ3):
+        y0 = oracle.add_layernorm_gelu(x, None, g, b, mode=mode, lib=lib)
+        y1 = oracle.add_layernorm_gelu(x, z, g, b, mode=mode, lib=lib)
+        assert np.array_equal(y0, y1), "a zero residual changes nothing"
+        y2 = oracle.add_layernorm_gelu(z, x, g, b, mode=mode, lib=lib)
+        assert np.array_equal(y0, y2), "x + r is symmetric"
+
+
+def _torch_bf16_bits(a):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def pin_bf16_encode(lib):
+    r = _rng(12)
+    bits = r.integers(0, 2 ** 32, 1 << 18, dtype=np.uint64).astype(np.uint32)
+    # ties and their neighbours, both signs, subnormals, the largest finite, infinities
+    ties = (r.integers(0, 2 ** 16, 4096, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    special = np.array([0, 0x80000000, 1, 0x807FFFFF, 0x7F7FFFFF, 0x7F800000, 0xFF800000,
+                        0x3F808000, 0x3F818000, 0x3F807FFF, 0x3F808001], np.uint32)
+    bits = np.concatenate([bits, ties, ties + 1, ties - 1, special])
+    f = bits.view(np.float32)
+    finite = np.isfinite(f) | np.isinf(f)
+    got = oracle.to_bf16(f, lib=lib)
+    want = _torch_bf16_bits(f)
+    assert np.array_equal(got[finite], want[finite]), "bf16 RNE vs torch"
+    nan = ~finite
+    assert ((got[nan] & 0x7F80) == 0x7F80).all() and ((got[nan] & 0x7F) != 0).all(), "NaN stays NaN"
+
+
+def pin_ln_seq(lib):
+    """SEQ mode of LayerNorm (+ residual, GeLU) against an op-by-op emulation
+    with numpy float32 arithmetic and torch's bfloat16 rounding."""
+    import torch
+    r = _rng(13)
+    rows, cols = 6, 64
+
+    def rb(a):  # fp32 -> bf16 -> fp32 through torch
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).float().numpy()
+
+    x = rb(r.standard_normal((rows, cols)).astype(np.float32))
+    res = rb(r.standard_normal((rows, cols)).astype(np.float32))
+    gamma = rb((1 + 0.1 * r.standard_normal(cols)).astype(np.float32))
+    beta = rb((0.1 * r.standard_normal(cols)).astype(np.float32))
+    v = rb(x + res)
+    mu = np.array([np.float32(math.fsum(map(float, row)) / cols) for row in v], np.float32)[:, None]
+    var = np.array([np.float32(math.fsum((float(t) - float(m)) ** 2 for t in row) / cols)
+                    for row, m in zip(v, mu[:, 0])], np.float32)[:, None]
+    cen = rb(v - mu)
+    sd = np.sqrt(var + np.float32(1e-5))
+    nrm = rb(cen / sd)
+    u = rb(nrm * gamma + beta)
+    bits = _torch_bf16_bits
+    y = oracle.add_layernorm_gelu(bits(x), bits(res), bits(gamma), bits(beta), act=oracle.ACT_NONE,
+                                  mode=oracle.SEQ, lib=lib)
+    assert np.array_equal(y, u.astype(np.float64)), "LN SEQ (bf16) must match op-by-op emulation"
+    # fp32 I/O: same chain with float32 storage
+    x32 = (r.standard_normal((rows, cols)) + 20).astype(np.float32)
+    g32 = (1 + 0.1 * r.standard_normal(cols)).astype(np.float32)
+    b32 = (0.1 * r.standard_normal(cols)).astype(np.float32)
+    mu = np.array([np.float32(math.fsum(map(float, row)) / cols) for row in x32], np.float32)[:, None]
+    var = np.array([np.float32(math.fsum((float(t) - float(m)) ** 2 for t in row) / cols)
+                    for row, m in zip(x32, mu[:, 0])], np.float32)[:, None]
+    ref = ((x32 - mu) / np.sqrt(var + np.float32(1e-5))) * g32 + b32
+    y = oracle.add_layernorm_gelu(x32, None, g32, b32, act=oracle.ACT_NONE, mode=oracle.SEQ, lib=lib)
+    assert np.array_equal(y, ref.astype(np.float64)), "LN SEQ (fp32) must match op-by-op emulation"
+
+
+ALL_PINS = [
+    pin_chain_worked, pin_chain_bruteforce, pin_chain_invariants, pin_chain_numpy,
+    pin_tenop_worked, pin_tenop_bruteforce, pin_tenop_invariants, pin_tenop_seq,
+    pin_ln_worked, pin_ln_closed_forms, pin_ln_bruteforce, pin_ln_torch, pin_gelu,
+    pin_residual_zero, pin_bf16_encode, pin_ln_seq,
+]

@@ -1,0 +1,57 @@
+"""Plant one plausible mistake at a time in a copy of the oracle's C source,
+build it on the CPU, and check that at least one pin catches it.  This is
+what makes the pins a check of the oracle rather than a restatement of it."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+# (what the mistake is, exact text in oracle.c, replacement)
+MUTANTS = [
+    ("chain: x - b1", "t[i] = (double)x[i] + (double)b1[i];", "t[i] = (double)x[i] - (double)b1[i];"),
+    ("chain: relu dropped", "r[i] = (t[i] < 0.0) ? 0.0 : t[i];", "r[i] = t[i];"),
+    ("chain: b1 used for b2", "y[i] = u[i] + (double)b2[i];", "y[i] = u[i] + (double)b1[i];"),
+    ("chain: scale ignored", "u[i] = r[i] * s;", "u[i] = r[i];"),
+    ("chain: SEQ rounding dropped", "if (seq) t[i] = r32(t[i]);", ""),
+    ("10-op: bias indexed by row", "RS(t1[i * cols + j] + (double)bias[j])", "RS(t1[i * cols + j] + (double)bias[i % cols])"),
+    ("10-op: mean over cols - 1", "m[i] = RS(acc / (double)cols);", "m[i] = RS(acc / (double)(cols - 1));"),
+    ("10-op: q from t not a", "q[k] = RS(a[k] * cc);", "q[k] = RS(t[k] * cc);"),
+    ("10-op: gamma and beta swapped", "* (double)gamma[j]);", "* (double)beta[j]);"),
+    ("10-op: mean indexed by column", "RS(s[i * cols + j] - m[i])", "RS(s[i * cols + j] - m[j % rows])"),
+    ("10-op: alpha rounded in exact mode", "const double al = seq ? r32(alpha) : alpha;", "const double al = r32(alpha);"),
+    ("LN: unbiased variance", "var[i] = acc / (double)cols;", "var[i] = acc / (double)(cols - 1);"),
+    ("LN: eps outside the root", "sqrt(var[i] + eps_used);", "(sqrt(var[i]) + eps_used);"),
+    ("LN: residual dropped", "xv = xv + load_elem(dtype, residual, k);", "xv = xv + 0.0;"),
+    ("LN: gamma/beta swapped", "double g = load_elem(dtype, gamma, j), b = load_elem(dtype, beta, j);",
+     "double g = load_elem(dtype, beta, j), b = load_elem(dtype, gamma, j);"),
+    ("LN: centring skipped in variance", "double dlt = v[i * cols + j] - mean[i];", "double dlt = v[i * cols + j];"),
+    ("GeLU: u^2 for u^3", "double u3 = u * u * u;", "double u3 = u * u;"),
+    ("GeLU: factor u dropped", "return 0.5 * u * (1.0 + tanh(z));", "return 0.5 * (1.0 + tanh(z));"),
+    ("GeLU: wrong constant", "0.7978845608 * inner", "0.7978845 * inner"),
+    ("bf16 decode shift", "uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    ("bf16 ties away from zero", "u += 0x7fffu + ((u >> 16) & 1u);", "u += 0x8000u;"),
+    ("LN SEQ: mean kept in binary64", "if (seq) mean[i] = r32(mean[i]);", ""),
+    ("LN SEQ: bf16 store skipped after the divide", "nrm[i * cols + j] = seq ? rstore(dtype, nv) : nv;",
+     "nrm[i * cols + j] = seq ? r32(nv) : nv;"),
+]
+
+
+@pytest.mark.parametrize("what,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(what, old, new, tmp_path):
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation site for '{what}' must appear exactly once"
+    mutant = tmp_path / "oracle_mutant.c"
+    mutant.write_text(src.replace(old, new))
+    so = str(tmp_path / "liboracle_mutant.so")
+    oracle.build(str(mutant), so)
+    lib = oracle.load(so)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError) as e:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake: {what}"
