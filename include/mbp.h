@@ -1,0 +1,191 @@
+/*
+ * mbp.h -- C ABI of libmbp: vertically fused memory-bound chains on gfx950.
+ *
+ * Every entry point takes plain device pointers and sizes, enqueues its work on
+ * the given HIP stream and returns at once (asynchronous, like a kernel launch).
+ * The caller owns every buffer: the library never allocates or frees device
+ * memory and keeps no mutable global state beyond a per-thread error message
+ * and a per-device cache of occupancy figures.
+ *
+ * Conventions shared by all entry points
+ *   - Tensors are dense and row-major (contiguous).  A [rows, cols] tensor has
+ *     element (i, j) at offset i*cols + j.  Vectors of length cols (bias, gamma,
+ *     beta) are broadcast over the rows (stride 0 along the row dimension), as
+ *     the TorchInductor post describes for bias in "TorchInductor Pipeline 与算子
+ *     融合", section 1.1.
+ *   - fp32 pointers must be 4-byte aligned and bf16 pointers 2-byte aligned;
+ *     16-byte alignment (with row lengths whose bytes are a multiple of 16)
+ *     selects the 128-bit load/store path, anything else a narrower path that
+ *     gives identical results.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *   - Arguments are validated on the host before anything is launched.  A bad
+ *     argument returns an error status and launches nothing.  A launch failure
+ *     reported by the HIP runtime returns MBP_ERR_HIP; faults inside a kernel
+ *     surface, as always with HIP, at the caller's next synchronisation.
+ *   - n == 0 or rows == 0 is a no-op that returns MBP_OK (pointers may be NULL).
+ *   - Fused entry points allow exact in-place use (y == x); any other overlap
+ *     between the output and an input returns MBP_ERR_OVERLAP.
+ *   - Results do not depend on the launch configuration or on the run: every
+ *     reduction uses a fixed lane-to-element map and a fixed combine order.
+ *
+ * Sources (the four pages on operator fusion):
+ *   [P1] PyTorch operator-fusion practice post (http://www.0539edu.com/news/5489619/)
+ *   [P2] "算子融合与 Kernel 优化：从 CUDA Graph 到 FlashAttention 的极致性能" (plumephp.com)
+ *   [P3] "4、算子融合（Kernel Fusion）：将多个小算子合并为一个，减少Kernel Launch开销" (5688vip.com)
+ *   [P4] "TorchInductor Pipeline 与算子融合" (blog.kkkzoz.top)
+ */
+#ifndef MBP_H
+#define MBP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MBP_ABI_VERSION 1
+
+/* Largest row length (cols) the row kernels accept: one row lives in registers. */
+#define MBP_MAX_COLS 16384
+
+typedef enum {
+  MBP_OK = 0,
+  MBP_ERR_NULL = 1,      /* a required pointer is NULL */
+  MBP_ERR_SHAPE = 2,     /* negative size, cols <= 0, cols > MBP_MAX_COLS, or size overflow */
+  MBP_ERR_DTYPE = 3,     /* unknown dtype or activation code */
+  MBP_ERR_ALIGN = 4,     /* pointer not aligned to its element size */
+  MBP_ERR_OVERLAP = 5,   /* output overlaps an input other than exactly (y == x) */
+  MBP_ERR_WORKSPACE = 6, /* workspace NULL, misaligned (256 B) or smaller than required */
+  MBP_ERR_HIP = 7,       /* the HIP runtime reported an error (see mbp_last_error) */
+  MBP_ERR_ARG = 8        /* other invalid argument: non-finite constant, eps < 0, bad op code */
+} mbp_status;
+
+typedef enum { MBP_F32 = 0, MBP_BF16 = 1 } mbp_dtype;
+
+typedef enum { MBP_ACT_NONE = 0, MBP_ACT_GELU_TANH = 1 } mbp_act;
+
+typedef enum { MBP_OP_CHAIN = 0, MBP_OP_ROW_MEAN = 1, MBP_OP_LAYERNORM = 2 } mbp_op;
+
+/* Granularity of the unfused variants. */
+#define MBP_UNFUSED_PRIMITIVE 0 /* one launch per primitive op (4 / 10 / 5 / 7 launches) */
+#define MBP_UNFUSED_EAGER 1     /* LayerNorm as one launch: add, layernorm, gelu (<= 3) */
+
+/* ------------------------------------------------------------------------- */
+/* Fused entry points: one launch; only the inputs are read and the output is
+ * written in HBM, every intermediate stays in registers (LDS holds only the
+ * per-wave partial sums of a row reduction).                                */
+
+/*
+ * y[i] = relu(x[i] + b1[i]) * scale + b2[i],  i < n.
+ * [P1] section 1.1 (the four eager steps add, relu, mul, add) and section 3.1
+ * (x, b1, b2 full fp32 tensors of one shape; scale 0.5 in the pages' example);
+ * section 3.2 is the fused float4 kernel this replaces, which dropped the n % 4
+ * tail -- here every n is handled.
+ * x, b1, b2: device fp32 [n], read only.  y: device fp32 [n], written; y == x,
+ * y == b1 or y == b2 is allowed.  scale: any finite double.  Arithmetic is
+ * binary64 inside the kernel with one rounding to fp32 at the store, so y is
+ * within 1 ulp of the exactly rounded result.  relu passes NaN through.
+ */
+mbp_status fused_pointwise_chain(const float* x, const float* b1, const float* b2, float* y,
+                                 int64_t n, double scale, void* stream);
+
+/*
+ * The 10-op graph of [P4] (the model at the top of the post; section 02,
+ * Table 2 lists its ten eager kernels), for every row i < rows:
+ *   t = x[i,:] * alpha + bias;  a = relu(t);  s = a*a + a*c;
+ *   m_i = (sum_j s[i,j]) / cols            (row sum, then divide: section 6.4)
+ *   y[i,:] = (s - m_i) * gamma + beta
+ * x, y: device fp32 [rows, cols]; bias, gamma, beta: device fp32 [cols].
+ * y == x is allowed.  alpha, c: finite doubles (1.1 and 0.1 in the pages).
+ * Arithmetic is binary64 inside the kernel; the row sum never leaves the chip.
+ */
+mbp_status fused_row_mean_epilogue(const float* x, const float* bias, const float* gamma,
+                                   const float* beta, float* y, int64_t rows, int64_t cols,
+                                   double alpha, double c, void* stream);
+
+/*
+ * Residual add + LayerNorm + tanh-GeLU, one row per lane group, for i < rows:
+ *   v = x[i,:] + residual[i,:]              (residual == NULL: v = x[i,:])
+ *   mu = mean(v);  var = mean((v - mu)^2)    (biased; [P3] section 4.3)
+ *   u = (v - mu) / sqrt(var + eps) * gamma + beta
+ *   y[i,:] = act == MBP_ACT_GELU_TANH ? 0.5 u (1 + tanh(0.7978845608 (u + 0.044715 u^3))) : u
+ * [P2] section 2.3 gives the fused residual + LayerNorm + GeLU kernel and its
+ * constants; [P3] section 4.3 the LayerNorm and its five unfused kernels.
+ * dtype MBP_F32: x, residual, gamma, beta, y are fp32; the statistics and the
+ * normalisation are computed in binary64.  dtype MBP_BF16: all five are bf16;
+ * arithmetic is fp32, the output is rounded to nearest even.  The statistics are
+ * two-pass over the register-resident row (mean first, then the centred sum of
+ * squares).  GeLU uses the identity 0.5 (1 + tanh z) = 1 / (1 + exp(-2 z)).
+ * x, residual: [rows, cols]; gamma, beta: [cols]; y: [rows, cols]; y == x or
+ * y == residual is allowed.  eps: finite, >= 0.  1 <= cols <= MBP_MAX_COLS.
+ */
+mbp_status fused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void* residual,
+                                    const void* gamma, const void* beta, void* y, int64_t rows,
+                                    int64_t cols, double eps, mbp_act act, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Unfused "before" variants: one launch per op, every intermediate written to
+ * and read back from the caller's workspace in the I/O type (row statistics in
+ * fp32), as eager execution does.  They exist for the before/after comparison.
+ * Each op rounds its result to the storage type; row reductions accumulate in
+ * binary64 and store fp32.  Workspace: device memory of at least
+ * mbp_unfused_workspace_bytes(...) bytes, 256-byte aligned, not overlapping any
+ * argument; its contents on entry do not matter.  The output may not alias an
+ * input.                                                                    */
+
+/* [P1] section 1.1: four launches add, relu, mul, add (fp32 intermediates). */
+mbp_status unfused_pointwise_chain(const float* x, const float* b1, const float* b2, float* y,
+                                   int64_t n, double scale, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* [P4] section 02, Table 2: ten launches mul, add, relu, mul, mul, add, mean,
+ * sub, mul, add (alpha and c rounded to fp32, as eager fp32 kernels do). */
+mbp_status unfused_row_mean_epilogue(const float* x, const float* bias, const float* gamma,
+                                     const float* beta, float* y, int64_t rows, int64_t cols,
+                                     double alpha, double c, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* [P3] section 4.3 and [P2] section 2.3.  granularity MBP_UNFUSED_PRIMITIVE:
+ * [add,] mean, var, sub, div, mul-add[, gelu]  (5 launches for plain
+ * LayerNorm, 7 with residual and GeLU).  granularity MBP_UNFUSED_EAGER:
+ * [add,] layernorm[, gelu] (the fused LayerNorm kernel as the middle launch). */
+mbp_status unfused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void* residual,
+                                      const void* gamma, const void* beta, void* y, int64_t rows,
+                                      int64_t cols, double eps, mbp_act act, int granularity,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace the unfused variant of `op` needs (bytes; 0 for a no-op shape).
+ * For MBP_OP_CHAIN pass rows = 1, cols = n.  has_residual and act matter only
+ * for MBP_OP_LAYERNORM.  Returns (size_t)-1 for invalid arguments. */
+size_t mbp_unfused_workspace_bytes(mbp_op op, mbp_dtype dtype, int64_t rows, int64_t cols,
+                                   int has_residual, mbp_act act, int granularity);
+
+/* Kernel launches one call makes (fused = 1: the fused entry point; fused = 0:
+ * the unfused one at `granularity`).  -1 for invalid arguments. */
+int mbp_launches_per_call(mbp_op op, int fused, int granularity, int has_residual, mbp_act act);
+
+/* ------------------------------------------------------------------------- */
+/* Calibration and diagnostics.                                              */
+
+/* Plain device-to-device copy of `bytes` bytes with 128-bit loads and stores
+ * (the same streaming pattern as the fused kernels, no arithmetic).  Used to
+ * measure attainable HBM bandwidth and to scale rocprofv3 byte counters.
+ * src and dst: device pointers, 16-byte aligned, not overlapping; bytes a
+ * multiple of 16. */
+mbp_status mbp_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+/* Static description of a status code. */
+const char* mbp_status_string(mbp_status s);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* mbp_last_error(void);
+
+/* MBP_ABI_VERSION of the built library. */
+int mbp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MBP_H */

@@ -1,0 +1,256 @@
+"""Python binding of libmbp, the gfx950 library of vertically fused memory-bound
+chains (C ABI in ``include/mbp.h``).
+
+This module only marshals arguments: it checks tensors, takes their device
+pointers and the current HIP stream, and calls the C entry point of the same
+name through ctypes.  Every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if ``libmbp.so`` has not been built the import
+fails, and a non-zero status from the library raises ``MbpError``.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmbp.so")
+
+F32, BF16 = 0, 1
+ACT_NONE, ACT_GELU_TANH = 0, 1
+OP_CHAIN, OP_ROW_MEAN, OP_LAYERNORM = 0, 1, 2
+UNFUSED_PRIMITIVE, UNFUSED_EAGER = 0, 1
+MAX_COLS = 16384
+
+STATUS_NAMES = {0: "MBP_OK", 1: "MBP_ERR_NULL", 2: "MBP_ERR_SHAPE", 3: "MBP_ERR_DTYPE",
+                4: "MBP_ERR_ALIGN", 5: "MBP_ERR_OVERLAP", 6: "MBP_ERR_WORKSPACE",
+                7: "MBP_ERR_HIP", 8: "MBP_ERR_ARG"}
+
+# (name, restype, argtypes) of every symbol that include/mbp.h declares
+_P, _I64, _D, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = [
+    ("fused_pointwise_chain", _I, [_P, _P, _P, _P, _I64, _D, _P]),
+    ("fused_row_mean_epilogue", _I, [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _P]),
+    ("fused_add_layernorm_gelu", _I, [_I, _P, _P, _P, _P, _P, _I64, _I64, _D, _I, _P]),
+    ("unfused_pointwise_chain", _I, [_P, _P, _P, _P, _I64, _D, _P, _SZ, _P]),
+    ("unfused_row_mean_epilogue", _I, [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _P, _SZ, _P]),
+    ("unfused_add_layernorm_gelu", _I, [_I, _P, _P, _P, _P, _P, _I64, _I64, _D, _I, _I, _P, _SZ, _P]),
+    ("mbp_unfused_workspace_bytes", _SZ, [_I, _I, _I64, _I64, _I, _I, _I]),
+    ("mbp_launches_per_call", _I, [_I, _I, _I, _I, _I]),
+    ("mbp_stream_copy", _I, [_P, _P, _SZ, _P]),
+    ("mbp_status_string", ctypes.c_char_p, [_I]),
+    ("mbp_last_error", ctypes.c_char_p, []),
+    ("mbp_abi_version", _I, []),
+]
+
+
+class MbpError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)}: {detail}")
+        self.status = status
+
+
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(
+            f"libmbp.so not found at {path}: build it first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    for name, res, args in SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(lib, name)(*args)
+    if st != 0:
+        raise MbpError(name, st, lib.mbp_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(t, name, dtypes, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dtype_code(t):
+    return BF16 if t.dtype == torch.bfloat16 else F32
+
+
+def _act_code(act):
+    if act in (None, "none", ACT_NONE):
+        return ACT_NONE
+    if act in ("gelu_tanh", "gelu", ACT_GELU_TANH):
+        return ACT_GELU_TANH
+    raise ValueError(f"unknown act {act!r}")
+
+
+def _rows_cols(x):
+    if x.dim() < 1:
+        raise ValueError("x must have at least one dimension")
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    return rows, cols
+
+
+# ------------------------------------------------------------------ fused
+
+def fused_pointwise_chain(x, b1, b2, scale=0.5, out=None):
+    """y = relu(x + b1) * scale + b2 on fp32 tensors of one shape (one launch)."""
+    for t, n in ((x, "x"), (b1, "b1"), (b2, "b2"), (out, "out")):
+        _check(t, n, (torch.float32,), x.device)
+    if not (x.shape == b1.shape == b2.shape):
+        raise ValueError("x, b1, b2 must have the same shape")
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape:
+        raise ValueError("out has the wrong shape")
+    _call("fused_pointwise_chain", _ptr(x), _ptr(b1), _ptr(b2), _ptr(y), x.numel(), float(scale),
+          _stream(x))
+    return y
+
+
+def fused_row_mean_epilogue(x, bias, gamma, beta, alpha=1.1, c=0.1, out=None):
+    """The 10-op graph: s = relu(x*alpha + bias)^2 + c*relu(...), y = (s - rowmean(s))*gamma + beta."""
+    for t, n in ((x, "x"), (bias, "bias"), (gamma, "gamma"), (beta, "beta"), (out, "out")):
+        _check(t, n, (torch.float32,), x.device)
+    rows, cols = _rows_cols(x)
+    for t, n in ((bias, "bias"), (gamma, "gamma"), (beta, "beta")):
+        if t.numel() != cols:
+            raise ValueError(f"{n} must have {cols} elements")
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape:
+        raise ValueError("out has the wrong shape")
+    _call("fused_row_mean_epilogue", _ptr(x), _ptr(bias), _ptr(gamma), _ptr(beta), _ptr(y), rows,
+          cols, float(alpha), float(c), _stream(x))
+    return y
+
+
+def fused_add_layernorm_gelu(x, residual, gamma, beta, eps=1e-5, act="gelu_tanh", out=None):
+    """gelu_tanh(LayerNorm(x + residual) * gamma + beta) over the last dimension.
+
+    fp32 or bf16 (all tensors one dtype); residual may be None; act "none"
+    gives plain LayerNorm."""
+    dts = (torch.float32, torch.bfloat16)
+    _check(x, "x", dts)
+    for t, n in ((residual, "residual"), (gamma, "gamma"), (beta, "beta"), (out, "out")):
+        _check(t, n, (x.dtype,), x.device)
+    rows, cols = _rows_cols(x)
+    if residual is not None and residual.shape != x.shape:
+        raise ValueError("residual must have x's shape")
+    for t, n in ((gamma, "gamma"), (beta, "beta")):
+        if t.numel() != cols:
+            raise ValueError(f"{n} must have {cols} elements")
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape:
+        raise ValueError("out has the wrong shape")
+    _call("fused_add_layernorm_gelu", _dtype_code(x), _ptr(x), _ptr(residual), _ptr(gamma),
+          _ptr(beta), _ptr(y), rows, cols, float(eps), _act_code(act), _stream(x))
+    return y
+
+
+def fused_layernorm(x, gamma, beta, eps=1e-5, out=None):
+    """Plain LayerNorm (no residual, no activation) over the last dimension."""
+    return fused_add_layernorm_gelu(x, None, gamma, beta, eps=eps, act="none", out=out)
+
+
+# ------------------------------------------------------------------ unfused
+
+def workspace_bytes(op, dtype, rows, cols, has_residual=False, act=ACT_NONE,
+                    granularity=UNFUSED_PRIMITIVE):
+    n = lib.mbp_unfused_workspace_bytes(op, dtype, rows, cols, int(bool(has_residual)),
+                                        _act_code(act), granularity)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid arguments for workspace size")
+    return n
+
+
+def launches_per_call(op, fused, granularity=UNFUSED_PRIMITIVE, has_residual=False, act=ACT_NONE):
+    return lib.mbp_launches_per_call(op, int(bool(fused)), granularity, int(bool(has_residual)),
+                                     _act_code(act))
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def unfused_pointwise_chain(x, b1, b2, scale=0.5, out=None, workspace=None):
+    """The chain as four launches (add, relu, mul, add) through HBM temporaries."""
+    for t, n in ((x, "x"), (b1, "b1"), (b2, "b2"), (out, "out")):
+        _check(t, n, (torch.float32,), x.device)
+    y = torch.empty_like(x) if out is None else out
+    nb = workspace_bytes(OP_CHAIN, F32, 1, x.numel())
+    ws = _workspace(nb, x.device, workspace)
+    _call("unfused_pointwise_chain", _ptr(x), _ptr(b1), _ptr(b2), _ptr(y), x.numel(), float(scale),
+          _ptr(ws), ws.numel() * ws.element_size(), _stream(x))
+    return y
+
+
+def unfused_row_mean_epilogue(x, bias, gamma, beta, alpha=1.1, c=0.1, out=None, workspace=None):
+    """The 10-op graph as ten launches through HBM temporaries."""
+    for t, n in ((x, "x"), (bias, "bias"), (gamma, "gamma"), (beta, "beta"), (out, "out")):
+        _check(t, n, (torch.float32,), x.device)
+    rows, cols = _rows_cols(x)
+    y = torch.empty_like(x) if out is None else out
+    nb = workspace_bytes(OP_ROW_MEAN, F32, rows, cols)
+    ws = _workspace(nb, x.device, workspace)
+    _call("unfused_row_mean_epilogue", _ptr(x), _ptr(bias), _ptr(gamma), _ptr(beta), _ptr(y), rows,
+          cols, float(alpha), float(c), _ptr(ws), ws.numel() * ws.element_size(), _stream(x))
+    return y
+
+
+def unfused_add_layernorm_gelu(x, residual, gamma, beta, eps=1e-5, act="gelu_tanh",
+                               granularity=UNFUSED_PRIMITIVE, out=None, workspace=None):
+    """Residual + LayerNorm + GeLU as one launch per op (granularity 0) or as
+    add / layernorm / gelu launches (granularity 1)."""
+    dts = (torch.float32, torch.bfloat16)
+    _check(x, "x", dts)
+    for t, n in ((residual, "residual"), (gamma, "gamma"), (beta, "beta"), (out, "out")):
+        _check(t, n, (x.dtype,), x.device)
+    rows, cols = _rows_cols(x)
+    y = torch.empty_like(x) if out is None else out
+    code = _act_code(act)
+    nb = workspace_bytes(OP_LAYERNORM, _dtype_code(x), rows, cols, residual is not None, code,
+                         granularity)
+    ws = _workspace(nb, x.device, workspace)
+    _call("unfused_add_layernorm_gelu", _dtype_code(x), _ptr(x), _ptr(residual), _ptr(gamma),
+          _ptr(beta), _ptr(y), rows, cols, float(eps), code, granularity, _ptr(ws),
+          ws.numel() * ws.element_size(), _stream(x))
+    return y
+
+
+def stream_copy(src, dst):
+    """Plain 128-bit streaming copy (bandwidth calibration)."""
+    _check(src, "src", (src.dtype,))
+    _check(dst, "dst", (dst.dtype,), src.device)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    _call("mbp_stream_copy", _ptr(src), _ptr(dst), nbytes, _stream(src))
+    return dst

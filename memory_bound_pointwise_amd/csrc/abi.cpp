@@ -1,0 +1,453 @@
+// abi.cpp -- the C ABI of libmbp (declared in include/mbp.h): host-side
+// argument validation, workspace carving for the unfused variants, and the
+// per-thread error message.  Nothing here touches the device until every
+// argument has been checked; then the launchers in fused_*.hip / unfused.hip
+// enqueue the work on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <initializer_list>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "mbp.h"
+#include "mbp_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mbp_status fail(mbp_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mbp_status fail(mbp_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+mbp_status ok() {
+  g_last_error.clear();
+  return MBP_OK;
+}
+
+mbp_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MBP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// A byte range [p, p + bytes).
+struct Span {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlaps(Span a, Span b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// The output may be exactly one of the inputs (same base, same extent) when
+// in-place use is allowed; any other intersection is an error.
+bool bad_overlap(Span out, Span in, bool exact_ok) {
+  if (!overlaps(out, in)) return false;
+  return !(exact_ok && out.p == in.p && out.bytes == in.bytes);
+}
+
+bool misaligned(const void* p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+constexpr int64_t kMaxElems = INT64_MAX / 64;
+
+// rows x cols with 0 <= rows, 1 <= cols <= MBP_MAX_COLS, product within range.
+mbp_status check_rows_cols(int64_t rows, int64_t cols) {
+  if (rows < 0) return fail(MBP_ERR_SHAPE, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (cols <= 0 || cols > MBP_MAX_COLS)
+    return fail(MBP_ERR_SHAPE, "cols must be in [1, %d] (got %lld)", MBP_MAX_COLS, (long long)cols);
+  if (rows > kMaxElems / cols) return fail(MBP_ERR_SHAPE, "rows * cols overflows");
+  return MBP_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// ---------------------------------------------------------------- workspace
+
+constexpr size_t kWsAlign = 256;
+size_t round_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+struct Carver {
+  char* base;
+  size_t used = 0;
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += round_up(bytes);
+    return p;
+  }
+};
+
+// Buffers of the unfused variants, carved in a fixed order from the workspace.
+struct ChainWs {
+  float *a, *b;
+};
+struct RowMeanWs {
+  float *a, *b, *c, *m;
+};
+struct LnWs {
+  void *r, *a, *b;
+  float *m, *v;
+};
+
+size_t chain_ws(char* base, int64_t n, ChainWs* w) {
+  Carver c{base};
+  ChainWs t;
+  t.a = (float*)c.take(n * 4);
+  t.b = (float*)c.take(n * 4);
+  if (w) *w = t;
+  return c.used;
+}
+
+size_t row_mean_ws(char* base, int64_t rows, int64_t cols, RowMeanWs* w) {
+  Carver c{base};
+  RowMeanWs t;
+  t.a = (float*)c.take(rows * cols * 4);
+  t.b = (float*)c.take(rows * cols * 4);
+  t.c = (float*)c.take(rows * cols * 4);
+  t.m = (float*)c.take(rows * 4);
+  if (w) *w = t;
+  return c.used;
+}
+
+size_t ln_ws(char* base, int dtype, int64_t rows, int64_t cols, bool res, bool gelu, int gran,
+             LnWs* w) {
+  Carver c{base};
+  const size_t es = dtype == MBP_BF16 ? 2 : 4;
+  const size_t full = (size_t)rows * cols * es;
+  LnWs t{nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (res) t.r = c.take(full);
+  if (gran == MBP_UNFUSED_PRIMITIVE) {
+    t.a = c.take(full);
+    t.b = c.take(full);
+    t.m = (float*)c.take(rows * 4);
+    t.v = (float*)c.take(rows * 4);
+  } else if (gelu) {
+    t.a = c.take(full);
+  }
+  if (w) *w = t;
+  return c.used;
+}
+
+mbp_status check_workspace(void* ws, size_t have, size_t need, std::initializer_list<Span> args) {
+  if (need == 0) return MBP_OK;
+  if (!ws) return fail(MBP_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (misaligned(ws, kWsAlign)) return fail(MBP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(MBP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+  for (const Span& a : args)
+    if (overlaps(Span{ws, need}, a)) return fail(MBP_ERR_OVERLAP, "workspace overlaps an argument");
+  return MBP_OK;
+}
+
+// ---------------------------------------------------------------- common checks
+
+mbp_status check_chain(const float* x, const float* b1, const float* b2, float* y, int64_t n,
+                       double scale, bool in_place_ok) {
+  if (n < 0 || n > kMaxElems) return fail(MBP_ERR_SHAPE, "n must be in [0, 2^57) (got %lld)", (long long)n);
+  if (n == 0) return MBP_OK;
+  if (!x || !b1 || !b2 || !y) return fail(MBP_ERR_NULL, "x, b1, b2 and y must be non-NULL");
+  if (misaligned(x, 4) || misaligned(b1, 4) || misaligned(b2, 4) || misaligned(y, 4))
+    return fail(MBP_ERR_ALIGN, "fp32 pointers must be 4-byte aligned");
+  if (!std::isfinite(scale)) return fail(MBP_ERR_ARG, "scale must be finite");
+  const size_t B = (size_t)n * 4;
+  const Span ys{y, B};
+  for (const void* in : {(const void*)x, (const void*)b1, (const void*)b2})
+    if (bad_overlap(ys, Span{in, B}, in_place_ok)) return fail(MBP_ERR_OVERLAP, "y overlaps an input");
+  return MBP_OK;
+}
+
+mbp_status check_row_mean(const float* x, const float* bias, const float* gamma,
+                          const float* beta, float* y, int64_t rows, int64_t cols, double alpha,
+                          double c, bool in_place_ok) {
+  mbp_status st = check_rows_cols(rows, cols);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return MBP_OK;
+  if (!x || !bias || !gamma || !beta || !y) return fail(MBP_ERR_NULL, "a required pointer is NULL");
+  for (const void* p : {(const void*)x, (const void*)bias, (const void*)gamma, (const void*)beta, (const void*)y})
+    if (misaligned(p, 4)) return fail(MBP_ERR_ALIGN, "fp32 pointers must be 4-byte aligned");
+  if (!std::isfinite(alpha) || !std::isfinite(c)) return fail(MBP_ERR_ARG, "alpha and c must be finite");
+  const size_t full = (size_t)rows * cols * 4, vec = (size_t)cols * 4;
+  const Span ys{y, full};
+  if (bad_overlap(ys, Span{x, full}, in_place_ok)) return fail(MBP_ERR_OVERLAP, "y overlaps x");
+  for (const void* p : {(const void*)bias, (const void*)gamma, (const void*)beta})
+    if (overlaps(ys, Span{p, vec})) return fail(MBP_ERR_OVERLAP, "y overlaps bias, gamma or beta");
+  return MBP_OK;
+}
+
+mbp_status check_ln(mbp_dtype dtype, const void* x, const void* residual, const void* gamma,
+                    const void* beta, void* y, int64_t rows, int64_t cols, double eps, mbp_act act,
+                    bool in_place_ok) {
+  if (dtype != MBP_F32 && dtype != MBP_BF16) return fail(MBP_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (act != MBP_ACT_NONE && act != MBP_ACT_GELU_TANH) return fail(MBP_ERR_DTYPE, "unknown act %d", (int)act);
+  mbp_status st = check_rows_cols(rows, cols);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return MBP_OK;
+  if (!x || !gamma || !beta || !y) return fail(MBP_ERR_NULL, "x, gamma, beta and y must be non-NULL");
+  const size_t es = dtype == MBP_BF16 ? 2 : 4;
+  for (const void* p : {x, residual, gamma, beta, (const void*)y})
+    if (misaligned(p, es)) return fail(MBP_ERR_ALIGN, "pointers must be aligned to the element size");
+  if (!std::isfinite(eps) || eps < 0) return fail(MBP_ERR_ARG, "eps must be finite and >= 0");
+  const size_t full = (size_t)rows * cols * es, vec = (size_t)cols * es;
+  const Span ys{y, full};
+  if (bad_overlap(ys, Span{x, full}, in_place_ok)) return fail(MBP_ERR_OVERLAP, "y overlaps x");
+  if (residual && bad_overlap(ys, Span{residual, full}, in_place_ok))
+    return fail(MBP_ERR_OVERLAP, "y overlaps residual");
+  if (overlaps(ys, Span{gamma, vec}) || overlaps(ys, Span{beta, vec}))
+    return fail(MBP_ERR_OVERLAP, "y overlaps gamma or beta");
+  return MBP_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launch helpers
+
+namespace mbp {
+
+const DeviceInfo& device_info() {
+  static std::mutex mu;
+  static std::map<int, DeviceInfo> cache;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it == cache.end()) {
+    DeviceInfo info{0};
+    if (hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        info.cus <= 0)
+      info.cus = 1;
+    it = cache.emplace(dev, info).first;
+  }
+  return it->second;
+}
+
+int persistent_grid(const void* kernel, int block, int64_t groups) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int per_cu = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({dev, kernel});
+    if (it != cache.end()) per_cu = it->second;
+  }
+  if (per_cu == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    std::lock_guard<std::mutex> lock(mu);
+    cache[{dev, kernel}] = per_cu;
+  }
+  const int64_t resident = (int64_t)per_cu * device_info().cus;
+  int64_t g = groups < resident ? groups : resident;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+}  // namespace mbp
+
+// ---------------------------------------------------------------- C ABI
+
+extern "C" {
+
+mbp_status fused_pointwise_chain(const float* x, const float* b1, const float* b2, float* y,
+                                 int64_t n, double scale, void* stream) {
+  mbp_status st = check_chain(x, b1, b2, y, n, scale, true);
+  if (st != MBP_OK) return st;
+  if (n == 0) return ok();
+  return from_hip(mbp::launch_chain(x, b1, b2, y, n, scale, as_stream(stream)), "fused_pointwise_chain");
+}
+
+mbp_status fused_row_mean_epilogue(const float* x, const float* bias, const float* gamma,
+                                   const float* beta, float* y, int64_t rows, int64_t cols,
+                                   double alpha, double c, void* stream) {
+  mbp_status st = check_row_mean(x, bias, gamma, beta, y, rows, cols, alpha, c, true);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  return from_hip(mbp::launch_row_mean(x, bias, gamma, beta, y, rows, cols, alpha, c, as_stream(stream)),
+                  "fused_row_mean_epilogue");
+}
+
+mbp_status fused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void* residual,
+                                    const void* gamma, const void* beta, void* y, int64_t rows,
+                                    int64_t cols, double eps, mbp_act act, void* stream) {
+  mbp_status st = check_ln(dtype, x, residual, gamma, beta, y, rows, cols, eps, act, true);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  return from_hip(mbp::launch_layernorm(dtype, x, residual, gamma, beta, y, rows, cols, eps, act,
+                                        as_stream(stream)),
+                  "fused_add_layernorm_gelu");
+}
+
+mbp_status unfused_pointwise_chain(const float* x, const float* b1, const float* b2, float* y,
+                                   int64_t n, double scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  mbp_status st = check_chain(x, b1, b2, y, n, scale, false);
+  if (st != MBP_OK) return st;
+  if (n == 0) return ok();
+  const size_t need = chain_ws(nullptr, n, nullptr);
+  const size_t B = (size_t)n * 4;
+  st = check_workspace(workspace, workspace_bytes, need, {{x, B}, {b1, B}, {b2, B}, {y, B}});
+  if (st != MBP_OK) return st;
+  ChainWs w;
+  chain_ws((char*)workspace, n, &w);
+  const float s32 = (float)scale;
+  hipStream_t s = as_stream(stream);
+  using namespace mbp;
+  hipError_t e = launch_ew(EW_ADD, MBP_F32, x, b1, IX_FULL, nullptr, 0, w.a, 1, n, 0.f, s);
+  if (e == hipSuccess) e = launch_ew(EW_RELU, MBP_F32, w.a, nullptr, 0, nullptr, 0, w.b, 1, n, 0.f, s);
+  if (e == hipSuccess) e = launch_ew(EW_MULS, MBP_F32, w.b, nullptr, 0, nullptr, 0, w.a, 1, n, s32, s);
+  if (e == hipSuccess) e = launch_ew(EW_ADD, MBP_F32, w.a, b2, IX_FULL, nullptr, 0, y, 1, n, 0.f, s);
+  return from_hip(e, "unfused_pointwise_chain");
+}
+
+mbp_status unfused_row_mean_epilogue(const float* x, const float* bias, const float* gamma,
+                                     const float* beta, float* y, int64_t rows, int64_t cols,
+                                     double alpha, double c, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  mbp_status st = check_row_mean(x, bias, gamma, beta, y, rows, cols, alpha, c, false);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  const size_t need = row_mean_ws(nullptr, rows, cols, nullptr);
+  const size_t full = (size_t)rows * cols * 4, vec = (size_t)cols * 4;
+  st = check_workspace(workspace, workspace_bytes, need,
+                       {{x, full}, {y, full}, {bias, vec}, {gamma, vec}, {beta, vec}});
+  if (st != MBP_OK) return st;
+  RowMeanWs w;
+  row_mean_ws((char*)workspace, rows, cols, &w);
+  const float a32 = (float)alpha, c32 = (float)c;
+  hipStream_t s = as_stream(stream);
+  using namespace mbp;
+  const int F = MBP_F32;
+  hipError_t e = launch_ew(EW_MULS, F, x, nullptr, 0, nullptr, 0, w.a, rows, cols, a32, s);     // x*alpha
+  if (e == hipSuccess) e = launch_ew(EW_ADD, F, w.a, bias, IX_COL, nullptr, 0, w.b, rows, cols, 0.f, s);  // t
+  if (e == hipSuccess) e = launch_ew(EW_RELU, F, w.b, nullptr, 0, nullptr, 0, w.a, rows, cols, 0.f, s);  // a
+  if (e == hipSuccess) e = launch_ew(EW_MUL, F, w.a, w.a, IX_FULL, nullptr, 0, w.b, rows, cols, 0.f, s);  // p
+  if (e == hipSuccess) e = launch_ew(EW_MULS, F, w.a, nullptr, 0, nullptr, 0, w.c, rows, cols, c32, s);   // q
+  if (e == hipSuccess) e = launch_ew(EW_ADD, F, w.b, w.c, IX_FULL, nullptr, 0, w.a, rows, cols, 0.f, s);  // s
+  if (e == hipSuccess) e = launch_row_mean_only(F, w.a, w.m, rows, cols, s);                            // m
+  if (e == hipSuccess) e = launch_ew(EW_SUB, F, w.a, w.m, IX_ROW, nullptr, 0, w.b, rows, cols, 0.f, s);  // s-m
+  if (e == hipSuccess) e = launch_ew(EW_MUL, F, w.b, gamma, IX_COL, nullptr, 0, w.c, rows, cols, 0.f, s); // *g
+  if (e == hipSuccess) e = launch_ew(EW_ADD, F, w.c, beta, IX_COL, nullptr, 0, y, rows, cols, 0.f, s);   // +b
+  return from_hip(e, "unfused_row_mean_epilogue");
+}
+
+mbp_status unfused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void* residual,
+                                      const void* gamma, const void* beta, void* y, int64_t rows,
+                                      int64_t cols, double eps, mbp_act act, int granularity,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  mbp_status st = check_ln(dtype, x, residual, gamma, beta, y, rows, cols, eps, act, false);
+  if (st != MBP_OK) return st;
+  if (granularity != MBP_UNFUSED_PRIMITIVE && granularity != MBP_UNFUSED_EAGER)
+    return fail(MBP_ERR_ARG, "unknown granularity %d", granularity);
+  if (rows == 0) return ok();
+  const bool res = residual != nullptr, gelu = act == MBP_ACT_GELU_TANH;
+  const size_t need = ln_ws(nullptr, dtype, rows, cols, res, gelu, granularity, nullptr);
+  const size_t es = dtype == MBP_BF16 ? 2 : 4;
+  const size_t full = (size_t)rows * cols * es, vec = (size_t)cols * es;
+  st = check_workspace(workspace, workspace_bytes, need,
+                       {{x, full}, {residual, full}, {y, full}, {gamma, vec}, {beta, vec}});
+  if (st != MBP_OK) return st;
+  LnWs w;
+  ln_ws((char*)workspace, dtype, rows, cols, res, gelu, granularity, &w);
+  hipStream_t s = as_stream(stream);
+  using namespace mbp;
+  const int D = dtype;
+  hipError_t e = hipSuccess;
+  const void* src = x;
+  if (res) {
+    e = launch_ew(EW_ADD, D, x, residual, IX_FULL, nullptr, 0, w.r, rows, cols, 0.f, s);
+    src = w.r;
+  }
+  void* ln_out = gelu ? w.a : y;
+  if (granularity == MBP_UNFUSED_PRIMITIVE) {
+    const float eps32 = (float)eps;
+    if (e == hipSuccess) e = launch_row_mean_only(D, src, w.m, rows, cols, s);
+    if (e == hipSuccess) e = launch_row_var(D, src, w.m, w.v, rows, cols, s);
+    if (e == hipSuccess) e = launch_ew(EW_SUB, D, src, w.m, IX_ROW, nullptr, 0, w.a, rows, cols, 0.f, s);
+    if (e == hipSuccess) e = launch_ew(EW_DIVSD, D, w.a, w.v, IX_ROW, nullptr, 0, w.b, rows, cols, eps32, s);
+    if (e == hipSuccess)
+      e = launch_ew(EW_MULADD, D, w.b, gamma, IX_COL, beta, IX_COL, ln_out, rows, cols, 0.f, s);
+  } else {
+    if (e == hipSuccess)
+      e = launch_layernorm(D, src, nullptr, gamma, beta, ln_out, rows, cols, eps, MBP_ACT_NONE, s);
+  }
+  if (gelu && e == hipSuccess)
+    e = launch_ew(EW_GELU, D, w.a, nullptr, 0, nullptr, 0, y, rows, cols, 0.f, s);
+  return from_hip(e, "unfused_add_layernorm_gelu");
+}
+
+size_t mbp_unfused_workspace_bytes(mbp_op op, mbp_dtype dtype, int64_t rows, int64_t cols,
+                                   int has_residual, mbp_act act, int granularity) {
+  if (rows < 0 || cols < 0) return (size_t)-1;
+  if (rows == 0 || cols == 0) return 0;
+  if (rows > kMaxElems / cols) return (size_t)-1;
+  switch (op) {
+    case MBP_OP_CHAIN: return chain_ws(nullptr, rows * cols, nullptr);
+    case MBP_OP_ROW_MEAN: return row_mean_ws(nullptr, rows, cols, nullptr);
+    case MBP_OP_LAYERNORM:
+      if (dtype != MBP_F32 && dtype != MBP_BF16) return (size_t)-1;
+      if (granularity != MBP_UNFUSED_PRIMITIVE && granularity != MBP_UNFUSED_EAGER) return (size_t)-1;
+      return ln_ws(nullptr, dtype, rows, cols, has_residual != 0, act == MBP_ACT_GELU_TANH,
+                   granularity, nullptr);
+    default: return (size_t)-1;
+  }
+}
+
+int mbp_launches_per_call(mbp_op op, int fused, int granularity, int has_residual, mbp_act act) {
+  if (fused) return (op >= MBP_OP_CHAIN && op <= MBP_OP_LAYERNORM) ? 1 : -1;
+  switch (op) {
+    case MBP_OP_CHAIN: return 4;
+    case MBP_OP_ROW_MEAN: return 10;
+    case MBP_OP_LAYERNORM: {
+      const int extra = (has_residual ? 1 : 0) + (act == MBP_ACT_GELU_TANH ? 1 : 0);
+      if (granularity == MBP_UNFUSED_PRIMITIVE) return 5 + extra;
+      if (granularity == MBP_UNFUSED_EAGER) return 1 + extra;
+      return -1;
+    }
+    default: return -1;
+  }
+}
+
+mbp_status mbp_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes == 0) return ok();
+  if (!src || !dst) return fail(MBP_ERR_NULL, "src and dst must be non-NULL");
+  if (misaligned(src, 16) || misaligned(dst, 16) || bytes % 16)
+    return fail(MBP_ERR_ALIGN, "src, dst and bytes must be multiples of 16");
+  if (overlaps(Span{src, bytes}, Span{dst, bytes})) return fail(MBP_ERR_OVERLAP, "src and dst overlap");
+  return from_hip(mbp::launch_copy(src, dst, bytes, as_stream(stream)), "mbp_stream_copy");
+}
+
+const char* mbp_status_string(mbp_status s) {
+  switch (s) {
+    case MBP_OK: return "ok";
+    case MBP_ERR_NULL: return "a required pointer is NULL";
+    case MBP_ERR_SHAPE: return "invalid shape";
+    case MBP_ERR_DTYPE: return "unknown dtype or activation";
+    case MBP_ERR_ALIGN: return "misaligned pointer";
+    case MBP_ERR_OVERLAP: return "output overlaps an input";
+    case MBP_ERR_WORKSPACE: return "invalid workspace";
+    case MBP_ERR_HIP: return "HIP runtime error";
+    case MBP_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+const char* mbp_last_error(void) { return g_last_error.c_str(); }
+
+int mbp_abi_version(void) { return MBP_ABI_VERSION; }
+
+}  // extern "C"

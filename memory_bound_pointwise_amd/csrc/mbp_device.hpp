@@ -1,0 +1,96 @@
+// mbp_device.hpp -- device-side building blocks shared by the HIP kernels of
+// libmbp: 128-bit vector types, bfloat16 unpack/pack, and the deterministic
+// lane-group sum used by every row reduction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mbp {
+
+// 16 bytes = one global_load_dwordx4 / global_store_dwordx4 per lane.
+struct alignas(16) u32x4 {
+  uint32_t w[4];
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// bfloat16 is the upper half of a binary32; widening is exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Two fp32 values -> one word of two bf16, round to nearest even
+// (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Element type traits for the I/O types.
+struct F32IO {
+  typedef float elem;
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+  __device__ __forceinline__ static float load1(const elem* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store1(elem* p, int64_t i, float v) { p[i] = v; }
+  __device__ __forceinline__ static float get(const u32x4& v, int e) { return __uint_as_float(v.w[e]); }
+};
+
+struct BF16IO {
+  typedef uint16_t elem;
+  static constexpr int kVec = 8;
+  __device__ __forceinline__ static float load1(const elem* p, int64_t i) { return bf16_to_f32(p[i]); }
+  __device__ __forceinline__ static void store1(elem* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+  __device__ __forceinline__ static float get(const u32x4& v, int e) {
+    return (e & 1) ? bf16_hi(v.w[e >> 1]) : bf16_lo(v.w[e >> 1]);
+  }
+};
+
+// tanh-approximated GeLU, 0.5 u (1 + tanh(k0 (u + k1 u^3))) with k0 = 0.7978845608,
+// k1 = 0.044715 ("算子融合与 Kernel 优化", section 2.3), evaluated through the exact
+// identity 0.5 (1 + tanh z) = 1 / (1 + exp(-2 z)) and exp(w) = exp2(w log2 e):
+// one v_exp_f32 and one v_rcp_f32.  For u << 0, exp2 overflows to +inf and the
+// result is -0, the limit of the formula.
+__device__ __forceinline__ float gelu_tanh_f32(float u) {
+  constexpr float kA = (float)(-2.0 * 0.7978845608 * 1.4426950408889634);
+  constexpr float kB = (float)(-2.0 * 0.7978845608 * 0.044715 * 1.4426950408889634);
+  const float u2 = u * u;
+  const float w = u * __builtin_fmaf(u2, kB, kA);
+  const float e = __builtin_amdgcn_exp2f(w);
+  return u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Sum of v over a group of LANES consecutive lanes (LANES a power of two).
+// Within a wave: xor butterfly.  Because a + b == b + a exactly in IEEE
+// arithmetic, both partners of every exchange compute the same value, so all
+// lanes of the group end with bitwise the same sum, independent of timing.
+// Groups wider than a wave: each wave writes its partial to LDS, one barrier,
+// and every lane adds the group's partials in wave order.  `lds` must hold one
+// slot per wave of the block and must not be rewritten by any lane before all
+// lanes have read it (callers alternate between slots).
+template <int LANES, int BLOCK, typename T>
+__device__ __forceinline__ T group_sum(T v, T* lds) {
+  constexpr int kIn = LANES < 64 ? LANES : 64;
+#pragma unroll
+  for (int m = 1; m < kIn; m <<= 1) v += __shfl_xor(v, m);
+  if constexpr (LANES <= 64) {
+    return v;
+  } else {
+    static_assert(LANES % 64 == 0 && BLOCK % LANES == 0, "wave-multiple groups");
+    constexpr int kWaves = LANES / 64;
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[wave] = v;
+    __syncthreads();
+    const int first = (threadIdx.x / LANES) * kWaves;
+    T s = lds[first];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) s += lds[first + w];
+    return s;
+  }
+}
+
+}  // namespace mbp

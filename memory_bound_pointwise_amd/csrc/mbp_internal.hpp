@@ -1,0 +1,57 @@
+// mbp_internal.hpp -- host-side launchers behind the C ABI.  Arguments reach
+// these functions already validated by abi.cpp; each launcher only picks a
+// launch configuration, enqueues its kernel(s) and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mbp {
+
+// Resident-wave figures of the current device (cached per device).
+struct DeviceInfo {
+  int cus;
+};
+const DeviceInfo& device_info();
+
+// Grid for a persistent row kernel: at most `groups` blocks, at most the number
+// that can be resident at once (occupancy x CUs).
+int persistent_grid(const void* kernel, int block, int64_t groups);
+
+hipError_t launch_chain(const float* x, const float* b1, const float* b2, float* y, int64_t n,
+                        double scale, hipStream_t s);
+hipError_t launch_row_mean(const float* x, const float* bias, const float* gamma,
+                           const float* beta, float* y, int64_t rows, int64_t cols, double alpha,
+                           double c, hipStream_t s);
+hipError_t launch_layernorm(int dtype, const void* x, const void* residual, const void* gamma,
+                            const void* beta, void* y, int64_t rows, int64_t cols, double eps,
+                            int act, hipStream_t s);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+// Unfused primitives (one launch each).
+enum EwOp {
+  EW_ADD = 0,      // a + b
+  EW_SUB = 1,      // a - b
+  EW_MUL = 2,      // a * b
+  EW_RELU = 3,     // a < 0 ? 0 : a
+  EW_MULS = 4,     // a * scalar
+  EW_DIVSD = 5,    // a / sqrt(b + scalar)     (b: per-row variance)
+  EW_MULADD = 6,   // a * b + c   (two roundings)
+  EW_GELU = 7,     // tanh-GeLU of a
+};
+// How operand b (and c) is indexed: full tensor, per column (vector of cols),
+// or per row (vector of rows, fp32).
+enum EwIndex { IX_FULL = 0, IX_COL = 1, IX_ROW = 2 };
+
+hipError_t launch_ew(int op, int dtype, const void* a, const void* b, int b_ix, const void* c,
+                     int c_ix, void* out, int64_t rows, int64_t cols, float scalar,
+                     hipStream_t s);
+// Row mean (fp32 out) and biased variance about a given mean (fp32 out) of a
+// [rows, cols] tensor; binary64 accumulation.
+hipError_t launch_row_mean_only(int dtype, const void* a, float* mean, int64_t rows,
+                                int64_t cols, hipStream_t s);
+hipError_t launch_row_var(int dtype, const void* a, const float* mean, float* var, int64_t rows,
+                          int64_t cols, hipStream_t s);
+
+}  // namespace mbp

@@ -1,0 +1,130 @@
+"""The C-ABI library on the host: it loads, exports every function that
+include/mbp.h declares, and rejects bad arguments before launching anything.
+No GPU: every call here fails host validation (or is pure host bookkeeping)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mbp.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def mbp():
+    import memory_bound_pointwise_amd as m
+    return m
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    for name in ("fused_pointwise_chain", "fused_row_mean_epilogue", "fused_add_layernorm_gelu",
+                 "unfused_pointwise_chain", "unfused_row_mean_epilogue", "unfused_add_layernorm_gelu"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(mbp):
+    out = subprocess.run(["nm", "-D", "--defined-only", mbp.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [f for f in header_functions() if f not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    bound = {name for name, _, _ in mbp.SIGNATURES}
+    assert bound == set(header_functions()), "the binding must cover exactly the declared functions"
+
+
+def test_abi_version_and_strings(mbp):
+    assert mbp.lib.mbp_abi_version() == 1
+    for code, name in mbp.STATUS_NAMES.items():
+        assert mbp.lib.mbp_status_string(code)
+    assert mbp.lib.mbp_status_string(99) == b"unknown status"
+
+
+L = None  # shorthand for the ctypes library, set in each test
+
+
+def st(name, *args):
+    return getattr(L, name)(*args)
+
+
+# Fake, never-dereferenced addresses: every call below fails validation first.
+A = 0x10000000
+B = 0x20000000
+Y = 0x30000000
+
+
+def test_chain_validation(mbp):
+    global L
+    L = mbp.lib
+    assert st("fused_pointwise_chain", A, B, B, Y, -1, 0.5, None) == 2            # SHAPE
+    assert st("fused_pointwise_chain", None, None, None, None, 0, 0.5, None) == 0  # n == 0: no-op
+    assert st("fused_pointwise_chain", A, None, B, Y, 8, 0.5, None) == 1          # NULL
+    assert st("fused_pointwise_chain", A + 2, B, B, Y, 8, 0.5, None) == 4         # ALIGN
+    assert st("fused_pointwise_chain", A, B, B, Y, 8, float("inf"), None) == 8    # ARG
+    assert st("fused_pointwise_chain", A, B, B, A + 4, 8, 0.5, None) == 5         # partial overlap
+    assert b"overlaps" in L.mbp_last_error()
+    # the unfused variant forbids even exact aliasing, and needs a workspace
+    assert st("unfused_pointwise_chain", A, B, B, A, 8, 0.5, Y + 4096, 4096, None) == 5
+    assert st("unfused_pointwise_chain", A, B, B, Y, 8, 0.5, None, 0, None) == 6
+    assert st("unfused_pointwise_chain", A, B, B, Y, 8, 0.5, Y + 0x10000 + 16, 1 << 20, None) == 6
+    assert st("unfused_pointwise_chain", A, B, B, Y, 8, 0.5, Y + 0x10000, 16, None) == 6
+    assert st("unfused_pointwise_chain", A, B, B, Y, 1024, 0.5, A + 256, 1 << 20, None) == 5
+
+
+def test_row_validation(mbp):
+    global L
+    L = mbp.lib
+    big = mbp.MAX_COLS + 1
+    assert st("fused_row_mean_epilogue", A, B, B, B, Y, 4, 0, 1.1, 0.1, None) == 2
+    assert st("fused_row_mean_epilogue", A, B, B, B, Y, 4, big, 1.1, 0.1, None) == 2
+    assert st("fused_row_mean_epilogue", A, B, B, B, Y, -1, 8, 1.1, 0.1, None) == 2
+    assert st("fused_row_mean_epilogue", A, B, B, B, Y, 2 ** 62, 8, 1.1, 0.1, None) == 2
+    assert st("fused_row_mean_epilogue", A, B, B, B, Y, 0, 8, 1.1, 0.1, None) == 0
+    assert st("fused_row_mean_epilogue", A, B, B, B, Y, 4, 8, float("nan"), 0.1, None) == 8
+    assert st("fused_row_mean_epilogue", A, B, Y + 8, B, Y, 4, 8, 1.1, 0.1, None) == 5  # y over gamma
+    assert st("fused_add_layernorm_gelu", 7, A, None, B, B, Y, 4, 8, 1e-5, 0, None) == 3
+    assert st("fused_add_layernorm_gelu", 0, A, None, B, B, Y, 4, 8, 1e-5, 9, None) == 3
+    assert st("fused_add_layernorm_gelu", 0, A, None, B, B, Y, 4, 8, -1.0, 0, None) == 8
+    assert st("fused_add_layernorm_gelu", 1, A + 1, None, B, B, Y, 4, 8, 1e-5, 0, None) == 4
+    assert st("fused_add_layernorm_gelu", 0, A + 2, None, B, B, Y, 4, 8, 1e-5, 0, None) == 4
+    assert st("fused_add_layernorm_gelu", 1, A, A + 2, B, B, A + 2, 4, 8, 1e-5, 1, None) == 5
+    assert st("fused_add_layernorm_gelu", 1, None, None, B, B, Y, 4, 8, 1e-5, 1, None) == 1
+    assert st("fused_add_layernorm_gelu", 1, A, None, B, B, Y, 4, big, 1e-5, 1, None) == 2
+    assert st("unfused_add_layernorm_gelu", 1, A, None, B, B, Y, 4, 8, 1e-5, 1, 5, None, 0, None) == 8
+
+
+def test_workspace_and_launch_counts(mbp):
+    m = mbp
+    assert m.launches_per_call(m.OP_CHAIN, True) == 1
+    assert m.launches_per_call(m.OP_CHAIN, False) == 4
+    assert m.launches_per_call(m.OP_ROW_MEAN, False) == 10
+    assert m.launches_per_call(m.OP_LAYERNORM, False) == 5
+    assert m.launches_per_call(m.OP_LAYERNORM, False, has_residual=True, act="gelu_tanh") == 7
+    assert m.launches_per_call(m.OP_LAYERNORM, False, m.UNFUSED_EAGER, True, "gelu_tanh") == 3
+    assert m.launches_per_call(m.OP_LAYERNORM, False, 7) == -1
+    n = 4 * 1024 * 1024
+    assert m.workspace_bytes(m.OP_CHAIN, m.F32, 1, n) == 2 * 4 * n
+    assert m.workspace_bytes(m.OP_ROW_MEAN, m.F32, 1024, 1024) == 3 * 4 * 1024 * 1024 + 4096
+    full = 16384 * 8192 * 2
+    assert m.workspace_bytes(m.OP_LAYERNORM, m.BF16, 16384, 8192, True, "gelu_tanh") == \
+        3 * full + 2 * 16384 * 4
+    assert m.workspace_bytes(m.OP_LAYERNORM, m.BF16, 16384, 8192, True, "gelu_tanh",
+                             m.UNFUSED_EAGER) == 2 * full
+    assert m.workspace_bytes(m.OP_LAYERNORM, m.F32, 0, 8) == 0
+    with pytest.raises(ValueError):
+        m.workspace_bytes(m.OP_LAYERNORM, 5, 4, 8)
+
+
+def test_binding_rejects_cpu_tensors(mbp):
+    import torch
+    x = torch.zeros(8)
+    with pytest.raises(ValueError):
+        mbp.fused_pointwise_chain(x, x, x)

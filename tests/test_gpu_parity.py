@@ -1,0 +1,279 @@
+"""GPU parity: every entry point of the C ABI (through the Python binding, which
+calls it via ctypes) against the CPU oracle on the same seeded inputs.
+
+Small and ragged sizes are compared element by element in full; the full
+workload sizes (the launch configurations the bench times) are compared in full
+where the oracle is quick (chain, 10-op graph) and on sampled rows otherwise
+(rows are independent, so a sampled row is computed by the oracle exactly as in
+the full run).  Row kernels are also checked for bitwise determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity_util import (as_f64, check_bf16, check_chain, check_f32, sample_rows, to_dev,
+                         to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mbp():
+    import memory_bound_pointwise_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def _chain_inputs(n, seed_sub=0):
+    w = W.scaled(W.BY_NAME["chain_4M_f32"], n=n)
+    return W.generate(w)
+
+
+# ------------------------------------------------------------------ pointwise chain
+
+@pytest.mark.parametrize("n", list(range(1, 34)) + [255, 256, 257, 1000, 4099, 65537, 1 << 20])
+def test_chain_sizes(mbp, n):
+    d = _chain_inputs(n)
+    y = mbp.fused_pointwise_chain(to_dev(d["x"]), to_dev(d["b1"]), to_dev(d["b2"]), 0.5)
+    check_chain(to_host(y), oracle.pointwise_chain(d["x"], d["b1"], d["b2"], 0.5), f"n={n}")
+
+
+@pytest.mark.parametrize("offs", [(1, 1, 1, 1), (2, 2, 2, 2), (3, 3, 3, 3), (0, 1, 2, 3), (1, 0, 0, 0),
+                                  (0, 0, 0, 2)])
+def test_chain_misaligned(mbp, offs):
+    n = 10007
+    d = _chain_inputs(n)
+    bufs = []
+    for k, name in enumerate(("x", "b1", "b2")):
+        b = torch.zeros(n + 8, device="cuda")
+        b[offs[k]:offs[k] + n] = to_dev(d[name])
+        bufs.append(b[offs[k]:offs[k] + n])
+    out = torch.full((n + 8,), 7.0, device="cuda")
+    y = out[offs[3]:offs[3] + n]
+    mbp.fused_pointwise_chain(*bufs, 0.5, out=y)
+    check_chain(to_host(y), oracle.pointwise_chain(d["x"], d["b1"], d["b2"], 0.5), f"offsets {offs}")
+    host = to_host(out)
+    assert (host[:offs[3]] == 7.0).all() and (host[offs[3] + n:] == 7.0).all(), "wrote outside y"
+
+
+def test_chain_in_place_and_scale(mbp):
+    d = _chain_inputs(4099)
+    x = to_dev(d["x"])
+    mbp.fused_pointwise_chain(x, to_dev(d["b1"]), to_dev(d["b2"]), 0.3, out=x)
+    check_chain(to_host(x), oracle.pointwise_chain(d["x"], d["b1"], d["b2"], 0.3), "in place, scale 0.3")
+
+
+def test_chain_special_values(mbp):
+    x = np.array([np.nan, np.inf, -np.inf, -0.0, 0.0, 3e38, -3e38, 1e-45, -1e-45, 1.0, -1.0, 2.0],
+                 np.float32)
+    b1 = np.array([0, 0, 0, 0, -0.0, 3e38, 0, -1e-45, 1e-45, -1.0, 1.0, -2.0], np.float32)
+    b2 = np.array([1, 1, 1, -0.0, -0.0, 0, 5, 0, 0, 1e-30, -1e-30, 0.5], np.float32)
+    y = to_host(mbp.fused_pointwise_chain(to_dev(x), to_dev(b1), to_dev(b2), 0.5))
+    ref = oracle.pointwise_chain(x, b1, b2, 0.5)
+    check_chain(y, ref, "special values")
+
+
+def test_chain_full_workload(mbp):
+    w = W.BY_NAME["chain_4M_f32"]
+    d = W.generate(w)
+    args = [to_dev(d[k]) for k in ("x", "b1", "b2")]
+    y1 = to_host(mbp.fused_pointwise_chain(*args, 0.5))
+    y2 = to_host(mbp.fused_pointwise_chain(*args, 0.5))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    worst = check_chain(y1, oracle.pointwise_chain(d["x"], d["b1"], d["b2"], 0.5), w.name)
+    print(f"{w.name}: max ulp {worst}")
+
+
+# ------------------------------------------------------------------ 10-op graph
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (1, 4), (3, 7), (2, 1024), (5, 1000), (33, 1024),
+                                       (4, 4096), (3, 4093), (2, 16384), (7, 16383), (300, 64)])
+def test_tenop_shapes(mbp, rows, cols):
+    w = W.scaled(W.BY_NAME["tenop_1024x1024_f32"], rows=rows)
+    d = W.generate(w, cols=cols)
+    y = mbp.fused_row_mean_epilogue(*(to_dev(d[k]) for k in ("x", "bias", "gamma", "beta")))
+    ref = oracle.row_mean_epilogue(d["x"], d["bias"], d["gamma"], d["beta"])
+    check_f32(to_host(y), ref, f"10-op {rows}x{cols}")
+
+
+def test_tenop_in_place_and_misaligned(mbp):
+    w = W.scaled(W.BY_NAME["tenop_1024x1024_f32"], rows=6)
+    d = W.generate(w, cols=1024)
+    ref = oracle.row_mean_epilogue(d["x"], d["bias"], d["gamma"], d["beta"])
+    x = to_dev(d["x"])
+    mbp.fused_row_mean_epilogue(x, *(to_dev(d[k]) for k in ("bias", "gamma", "beta")), out=x)
+    check_f32(to_host(x), ref, "in place")
+    buf = torch.zeros(6 * 1024 + 1, device="cuda")
+    xs = buf[1:].view(6, 1024)
+    xs.copy_(to_dev(d["x"]))
+    y = mbp.fused_row_mean_epilogue(xs, *(to_dev(d[k]) for k in ("bias", "gamma", "beta")))
+    check_f32(to_host(y), ref, "misaligned x (scalar path)")
+
+
+def test_tenop_full_workload(mbp):
+    w = W.BY_NAME["tenop_1024x1024_f32"]
+    d = W.generate(w)
+    args = [to_dev(d[k]) for k in ("x", "bias", "gamma", "beta")]
+    y1 = to_host(mbp.fused_row_mean_epilogue(*args, alpha=1.1, c=0.1))
+    y2 = to_host(mbp.fused_row_mean_epilogue(*args, alpha=1.1, c=0.1))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "not deterministic"
+    err, relaxed = check_f32(y1, oracle.row_mean_epilogue(d["x"], d["bias"], d["gamma"], d["beta"]), w.name)
+    print(f"{w.name}: max abs err {err:.3g}, elements with |y| >= 256: {relaxed}")
+    # constant gamma: each output row has mean(beta) as its mean
+    g = torch.full_like(args[2], 1.5)
+    y = mbp.fused_row_mean_epilogue(args[0], args[1], g, args[3]).double()
+    assert torch.allclose(y.mean(dim=1), args[3].double().mean().expand(1024), atol=1e-4)
+
+
+# ------------------------------------------------------------------ LayerNorm family
+
+def _ln_case(name, rows, cols, residual=None, act=None):
+    w = W.scaled(W.BY_NAME[name], rows=rows)
+    d = W.generate(w, cols=cols)
+    if residual is True and d.get("residual") is None:
+        # the fp32 workload has no residual: take N(0, 1) rows of the 10-op workload's x
+        d["residual"] = W.generate(W.scaled(W.BY_NAME["tenop_1024x1024_f32"], rows=rows), cols=cols)["x"]
+    if residual is False:
+        d["residual"] = None
+    act = w.act if act is None else act
+    return w, d, act
+
+
+def _ln_run(mbp, d, act, out=None):
+    return mbp.fused_add_layernorm_gelu(to_dev(d["x"]), to_dev(d.get("residual")), to_dev(d["gamma"]),
+                                        to_dev(d["beta"]), eps=1e-5, act=act, out=out)
+
+
+def _ln_ref(d, act, rows=None, mode=oracle.EXACT):
+    pick = (lambda a: a) if rows is None else (lambda a: None if a is None else a[rows])
+    code = oracle.ACT_GELU_TANH if act == "gelu_tanh" else oracle.ACT_NONE
+    return oracle.add_layernorm_gelu(pick(d["x"]), pick(d.get("residual")), d["gamma"], d["beta"],
+                                     eps=1e-5, act=code, mode=mode)
+
+
+F32_COLS = [1, 3, 4, 5, 64, 255, 256, 257, 1000, 1024, 4095, 4096, 8192, 16384]
+BF16_COLS = [1, 7, 8, 9, 33, 255, 256, 257, 768, 1023, 1024, 4095, 4096, 8192, 12288, 16384]
+
+
+@pytest.mark.parametrize("cols", F32_COLS)
+@pytest.mark.parametrize("residual,act", [(False, "none"), (True, "none"), (True, "gelu_tanh")])
+def test_ln_f32_shapes(mbp, cols, residual, act):
+    w, d, act = _ln_case("ln_8192x4096_f32", 5, cols, residual, act)
+    y = to_host(_ln_run(mbp, d, act))
+    check_f32(y, _ln_ref(d, act), f"fp32 {cols} residual={residual} act={act}")
+
+
+@pytest.mark.parametrize("cols", BF16_COLS)
+@pytest.mark.parametrize("residual,act", [(True, "gelu_tanh"), (False, "none"), (False, "gelu_tanh")])
+def test_ln_bf16_shapes(mbp, cols, residual, act):
+    w, d, act = _ln_case("addln_gelu_16384x8192_bf16", 5, cols, residual, act)
+    y = to_host(_ln_run(mbp, d, act))
+    check_bf16(y, _ln_ref(d, act), f"bf16 {cols} residual={residual} act={act}")
+
+
+@pytest.mark.parametrize("dtype_name", ["ln_8192x4096_f32", "addln_gelu_16384x8192_bf16"])
+def test_ln_misaligned_and_in_place(mbp, dtype_name):
+    w, d, act = _ln_case(dtype_name, 7, 1024)
+    ref = _ln_ref(d, act)
+    chk = check_bf16 if w.dtype == "bf16" else check_f32
+    x = to_dev(d["x"])
+    buf = torch.zeros(x.numel() + 1, dtype=x.dtype, device="cuda")
+    xs = buf[1:].view(x.shape)
+    xs.copy_(x)
+    y = mbp.fused_add_layernorm_gelu(xs, to_dev(d.get("residual")), to_dev(d["gamma"]),
+                                     to_dev(d["beta"]), act=act)
+    chk(to_host(y), ref, "misaligned x (scalar path)")
+    mbp.fused_add_layernorm_gelu(x, to_dev(d.get("residual")), to_dev(d["gamma"]), to_dev(d["beta"]),
+                                 act=act, out=x)
+    chk(to_host(x), ref, "in place")
+
+
+def test_ln_constant_rows_give_beta(mbp):
+    for name in ("ln_8192x4096_f32", "addln_gelu_16384x8192_bf16"):
+        w, d, _ = _ln_case(name, 4, 4096, residual=False)
+        d["x"] = np.repeat(d["x"][:, :1], 4096, axis=1)
+        y = to_host(_ln_run(mbp, d, "none"))
+        assert np.array_equal(y, np.broadcast_to(d["beta"], y.shape)), f"{name}: constant row != beta"
+
+
+LN_FULL = ["ln_8192x4096_f32", "addln_gelu_16384x8192_bf16", "addln_gelu_262144x768_bf16",
+           "addln_gelu_32768x4095_bf16", "addln_gelu_16384x12288_bf16"]
+
+
+@pytest.mark.parametrize("name", LN_FULL)
+def test_ln_full_workload(mbp, name):
+    w = W.BY_NAME[name]
+    d = W.generate(w)
+    args = [to_dev(d["x"]), to_dev(d["residual"]), to_dev(d["gamma"]), to_dev(d["beta"])]
+    y1 = mbp.fused_add_layernorm_gelu(*args, eps=1e-5, act=w.act)
+    y2 = mbp.fused_add_layernorm_gelu(*args, eps=1e-5, act=w.act)
+    assert torch.equal(y1.view(torch.int16) if y1.dtype == torch.bfloat16 else y1.view(torch.int32),
+                       y2.view(torch.int16) if y2.dtype == torch.bfloat16 else y2.view(torch.int32)), \
+        "not deterministic"
+    rows = sample_rows(w.rows)
+    y = to_host(y1)[rows]
+    ref = _ln_ref(d, w.act, rows)
+    chk = check_bf16 if w.dtype == "bf16" else check_f32
+    err, relaxed = chk(y, ref, name)
+    print(f"{name}: {len(rows)} sampled rows, max abs err {err:.3g}, half-ulp-gated elements {relaxed}")
+    # a property that holds over the whole output: no NaN or Inf
+    assert torch.isfinite(y1.float()).all()
+
+
+# ------------------------------------------------------------------ unfused variants
+
+def test_unfused_chain_bit_exact(mbp):
+    for n in (1, 7, 4099, 4 * 1024 * 1024):
+        d = _chain_inputs(n)
+        y = to_host(mbp.unfused_pointwise_chain(to_dev(d["x"]), to_dev(d["b1"]), to_dev(d["b2"]), 0.5))
+        ref = oracle.pointwise_chain(d["x"], d["b1"], d["b2"], 0.5, mode=oracle.SEQ)
+        assert np.array_equal(y.astype(np.float64), ref), f"unfused chain n={n} not bit-exact vs SEQ"
+
+
+@pytest.mark.parametrize("rows,cols", [(3, 7), (33, 1000), (1024, 1024)])
+def test_unfused_tenop(mbp, rows, cols):
+    d = W.generate(W.scaled(W.BY_NAME["tenop_1024x1024_f32"], rows=rows), cols=cols)
+    y = to_host(mbp.unfused_row_mean_epilogue(*(to_dev(d[k]) for k in ("x", "bias", "gamma", "beta"))))
+    ref = oracle.row_mean_epilogue(d["x"], d["bias"], d["gamma"], d["beta"], mode=oracle.SEQ)
+    check_f32(y, ref, f"unfused 10-op {rows}x{cols} vs SEQ")
+
+
+@pytest.mark.parametrize("name,rows", [("ln_8192x4096_f32", 64), ("addln_gelu_16384x8192_bf16", 16),
+                                       ("addln_gelu_32768x4095_bf16", 16), ("addln_gelu_262144x768_bf16", 64)])
+@pytest.mark.parametrize("gran", [0, 1])
+def test_unfused_layernorm(mbp, name, rows, gran):
+    w = W.scaled(W.BY_NAME[name], rows=rows)
+    d = W.generate(w)
+    y = mbp.unfused_add_layernorm_gelu(to_dev(d["x"]), to_dev(d["residual"]), to_dev(d["gamma"]),
+                                       to_dev(d["beta"]), eps=1e-5, act=w.act, granularity=gran)
+    mode = oracle.SEQ if gran == 0 else oracle.SEQ3
+    ref = _ln_ref(d, w.act, mode=mode)
+    chk = check_bf16 if w.dtype == "bf16" else check_f32
+    chk(to_host(y), ref, f"unfused {name} granularity {gran}")
+
+
+# ------------------------------------------------------------------ misc
+
+def test_empty_inputs(mbp):
+    e = torch.empty(0, device="cuda")
+    assert mbp.fused_pointwise_chain(e, e, e).numel() == 0
+    x = torch.empty(0, 64, device="cuda")
+    v = torch.zeros(64, device="cuda")
+    assert mbp.fused_row_mean_epilogue(x, v, v, v).numel() == 0
+    assert mbp.fused_add_layernorm_gelu(x, None, v, v).numel() == 0
+
+
+def test_stream_copy(mbp):
+    src = torch.arange(1 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.zeros_like(src)
+    mbp.stream_copy(src, dst)
+    assert torch.equal(src, dst)
+
+
+def test_error_is_raised(mbp):
+    x = torch.zeros(4, 8, device="cuda")
+    with pytest.raises(mbp.MbpError):
+        mbp.fused_add_layernorm_gelu(x, None, torch.zeros(8, device="cuda"), torch.zeros(8, device="cuda"),
+                                     eps=-1.0)
