@@ -22,7 +22,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmbp.so")
 ARCH = os.environ.get("MBP_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["abi.cpp", "fused_pointwise.hip", "fused_rows.hip", "unfused.hip"]
+SOURCES = ["abi.cpp", "fused_pointwise.hip", "fused_tenop.hip", "fused_ln_f32.hip",
+           "fused_ln_bf16.hip", "unfused.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

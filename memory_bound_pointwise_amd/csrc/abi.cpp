@@ -12,6 +12,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <utility>
 
 #include "mbp.h"
@@ -233,23 +234,24 @@ const DeviceInfo& device_info() {
   return it->second;
 }
 
-int persistent_grid(const void* kernel, int block, int64_t groups) {
+int persistent_grid(const void* kernel, int block, int64_t groups, size_t lds) {
   static std::mutex mu;
-  static std::map<std::pair<int, const void*>, int> cache;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;
   int dev = 0;
   (void)hipGetDevice(&dev);
+  const auto key = std::make_tuple(dev, kernel, lds);
   int per_cu = 0;
   {
     std::lock_guard<std::mutex> lock(mu);
-    auto it = cache.find({dev, kernel});
+    auto it = cache.find(key);
     if (it != cache.end()) per_cu = it->second;
   }
   if (per_cu == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, lds) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
     std::lock_guard<std::mutex> lock(mu);
-    cache[{dev, kernel}] = per_cu;
+    cache[key] = per_cu;
   }
   const int64_t resident = (int64_t)per_cu * device_info().cus;
   int64_t g = groups < resident ? groups : resident;

@@ -1,0 +1,14 @@
+// fused_ln_bf16.hip -- the bf16 instantiation of the residual + LayerNorm +
+// tanh-GeLU kernels (fused_ln_impl.hpp); its own translation unit so that the
+// two element types compile in parallel.
+#include "fused_ln_impl.hpp"
+
+namespace mbp {
+
+hipError_t launch_layernorm_bf16(const void* x, const void* residual, const void* gamma,
+                                 const void* beta, void* y, int64_t rows, int64_t cols, double eps,
+                                 int act, hipStream_t s) {
+  return ln::launch<BF16IO>(x, residual, gamma, beta, y, rows, cols, eps, act, s);
+}
+
+}  // namespace mbp

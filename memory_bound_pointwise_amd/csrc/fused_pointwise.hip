@@ -5,8 +5,8 @@
 // (0539edu.com), section 1.1 (four eager kernels add -> relu -> mul -> add, each
 // a full HBM round trip) and section 3.2 (one fused kernel with 16-byte loads).
 // Here one launch reads x, b1, b2 once and writes y once (16 bytes per element),
-// with 128-bit loads/stores on the aligned body and scalar handling of the
-// unaligned head and the n % 4 tail.  The arithmetic is binary64: the exact sum
+// with 128-bit nontemporal loads/stores on the aligned body and scalar handling
+// of the unaligned head and the n % 4 tail.  The arithmetic is binary64: the exact sum
 // x + b1 (rounded once to binary64), the relu select, one fused multiply-add with
 // b2, and one rounding to fp32 at the store.  On gfx950 binary64 FMA runs at the
 // same lane rate as fp32, and this kernel needs about 8 VALU ops per 16 bytes.
@@ -45,9 +45,9 @@ __global__ __launch_bounds__(kBlock) void chain_kernel(const float* x, const flo
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + (int64_t)u * kBlock;
       if (i < n4) {
-        xv[u] = X[i];
-        av[u] = A[i];
-        bv[u] = B[i];
+        xv[u] = load_nt(X + i);
+        av[u] = load_nt(A + i);
+        bv[u] = load_nt(B + i);
       }
     }
 #pragma unroll
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kBlock) void chain_kernel(const float* x, const flo
         o.y = chain_op(xv[u].y, av[u].y, bv[u].y, scale);
         o.z = chain_op(xv[u].z, av[u].z, bv[u].z, scale);
         o.w = chain_op(xv[u].w, av[u].w, bv[u].w, scale);
-        Y[i] = o;
+        store_nt(Y + i, o);
       } else if (i < items) {
         const int64_t k = i - n4;
         const int64_t e = (k < h) ? k : 4 * n4 + k;
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kBlock) void chain_kernel(const float* x, const flo
 __global__ __launch_bounds__(kBlock) void copy_kernel(const u32x4* src, u32x4* dst, int64_t n16) {
   for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n16;
        i += (int64_t)gridDim.x * kBlock)
-    dst[i] = src[i];
+    store_nt(dst + i, load_nt(src + i));
 }
 
 constexpr int kChainUnroll = 1;

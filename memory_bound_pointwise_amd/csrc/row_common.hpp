@@ -1,0 +1,80 @@
+// row_common.hpp -- pieces shared by the one-pass row kernels (LayerNorm family
+// and the 10-op graph): block sizing, the (lanes, vectors-per-lane) layout
+// tables, and small arithmetic helpers.
+//
+// Layout.  A row is served by a group of LANES consecutive lanes (16 ... 1024).
+// Lane l of the group holds the vectors l, l + LANES, l + 2*LANES, ... of the
+// row (VPL of them), so each load instruction of the group covers a contiguous
+// stretch of the row (coalesced).  A vector is 16 bytes (4 fp32 / 8 bf16).
+// Groups of up to 256 lanes run in 256-lane blocks (several rows per block);
+// wider groups are one block.  Blocks are persistent (no more than can be
+// resident) and stride over the row groups, so the per-column vectors (gamma,
+// beta, bias) are loaded once per block.
+#pragma once
+
+#include "mbp_device.hpp"
+
+namespace mbp {
+namespace rows {
+
+constexpr int kMinBlock = 256;
+
+// Block size for a group of LANES lanes: at least kMinBlock, one group if wider.
+constexpr int block_for(int lanes) { return lanes > kMinBlock ? lanes : kMinBlock; }
+
+// An empty asm that claims to rewrite its operand: the value is unchanged, but
+// the compiler must treat it as new at this point of the program (used to keep
+// a loop-invariant value from being widened once and held wide across a loop).
+__device__ __forceinline__ void opaque(float& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(u32x4& v) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) opaque(v.w[w]);
+}
+
+// fused multiply-add in the type of the operands (__builtin_fma is binary64)
+__device__ __forceinline__ float fma_t(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double fma_t(double a, double b, double c) { return __builtin_fma(a, b, c); }
+
+__device__ __forceinline__ float inv_sqrt(float a) { return 1.0f / __builtin_sqrtf(a); }
+__device__ __forceinline__ double inv_sqrt(double a) { return 1.0 / __builtin_sqrt(a); }
+
+// (LANES, VPL) layouts.  The first layout whose LANES * VPL vectors cover the
+// row is used.  At most 5 vectors (40 bf16 / 20 fp32 values) per lane keeps the
+// kernels free of register spills; wider rows take wider groups.
+struct Shape {
+  int lanes, vpl;
+};
+constexpr Shape kShapes[] = {{16, 2},  {32, 2},  {32, 3},  {32, 4},   {64, 4},   {128, 4},
+                             {128, 5}, {256, 4}, {512, 3}, {512, 4},  {1024, 3}, {1024, 4}};
+constexpr int kNumShapes = sizeof(kShapes) / sizeof(Shape);
+
+inline int pick_shape(int64_t nvec) {
+  for (int i = 0; i < kNumShapes; ++i)
+    if ((int64_t)kShapes[i].lanes * kShapes[i].vpl >= nvec) return i;
+  return -1;
+}
+
+// Kernel pointer of layout i: K<LANES, VPL>::ptr().
+template <template <int, int> class K>
+const void* shape_kernel(int i) {
+  switch (i) {
+    case 0: return K<16, 2>::ptr();
+    case 1: return K<32, 2>::ptr();
+    case 2: return K<32, 3>::ptr();
+    case 3: return K<32, 4>::ptr();
+    case 4: return K<64, 4>::ptr();
+    case 5: return K<128, 4>::ptr();
+    case 6: return K<128, 5>::ptr();
+    case 7: return K<256, 4>::ptr();
+    case 8: return K<512, 3>::ptr();
+    case 9: return K<512, 4>::ptr();
+    case 10: return K<1024, 3>::ptr();
+    default: return K<1024, 4>::ptr();
+  }
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace rows
+}  // namespace mbp

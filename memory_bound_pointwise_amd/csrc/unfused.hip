@@ -154,7 +154,7 @@ hipError_t launch_row_mean_only(int dtype, const void* a, float* mean, int64_t r
   const void* k = dtype == 1 ? reinterpret_cast<const void*>(&row_stat_kernel<BF16IO, 0>)
                              : reinterpret_cast<const void*>(&row_stat_kernel<F32IO, 0>);
   const float* none = nullptr;
-  const int grid = persistent_grid(k, kBlock, rows);
+  const int grid = persistent_grid(k, kBlock, rows, 0);
   void* args[] = {&a, &none, &mean, &rows, &cols};
   return hipLaunchKernel(k, dim3(grid), dim3(kBlock), args, 0, s);
 }
@@ -163,7 +163,7 @@ hipError_t launch_row_var(int dtype, const void* a, const float* mean, float* va
                           int64_t cols, hipStream_t s) {
   const void* k = dtype == 1 ? reinterpret_cast<const void*>(&row_stat_kernel<BF16IO, 1>)
                              : reinterpret_cast<const void*>(&row_stat_kernel<F32IO, 1>);
-  const int grid = persistent_grid(k, kBlock, rows);
+  const int grid = persistent_grid(k, kBlock, rows, 0);
   void* args[] = {&a, &mean, &var, &rows, &cols};
   return hipLaunchKernel(k, dim3(grid), dim3(kBlock), args, 0, s);
 }

@@ -19,11 +19,7 @@ import workloads as W
 
 
 def to_dev(a, dev="cuda"):
-    if a is None:
-        return None
-    if a.dtype == np.uint16:
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return W.to_device(a, dev)
 
 
 def to_host(t):

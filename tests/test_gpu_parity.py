@@ -190,6 +190,34 @@ def test_ln_misaligned_and_in_place(mbp, dtype_name):
     chk(to_host(x), ref, "in place")
 
 
+@pytest.mark.parametrize("dtype_name,cols,shift", [("addln_gelu_16384x8192_bf16", 4095, 1),
+                                                    ("addln_gelu_16384x8192_bf16", 768, 3),
+                                                    ("addln_gelu_16384x8192_bf16", 8192, 7),
+                                                    ("ln_8192x4096_f32", 4093, 1), ("ln_8192x4096_f32", 1024, 2)])
+def test_ln_common_misalignment(mbp, dtype_name, cols, shift):
+    """x, residual and y all start `shift` elements past a 16-byte boundary:
+    the windowed path, including the first and last window of the tensor."""
+    w, d, act = _ln_case(dtype_name, 9, cols, residual=True)
+    ref = _ln_ref(d, act)
+    chk = check_bf16 if w.dtype == "bf16" else check_f32
+
+    def place(a):
+        t = to_dev(a)
+        buf = torch.zeros(t.numel() + 16, dtype=t.dtype, device="cuda")
+        v = buf[shift:shift + t.numel()].view(t.shape)
+        v.copy_(t)
+        return v, buf
+
+    x, xb = place(d["x"])
+    r, rb = place(d["residual"])
+    yb = torch.full((x.numel() + 16,), 3.0, dtype=x.dtype, device="cuda")
+    y = yb[shift:shift + x.numel()].view(x.shape)
+    mbp.fused_add_layernorm_gelu(x, r, to_dev(d["gamma"]), to_dev(d["beta"]), act=act, out=y)
+    chk(to_host(y), ref, f"common misalignment {shift}")
+    host = to_host(yb).astype(np.float64) if yb.dtype != torch.bfloat16 else as_f64(to_host(yb))
+    assert (host[:shift] == 3.0).all() and (host[shift + x.numel():] == 3.0).all(), "wrote outside y"
+
+
 def test_ln_constant_rows_give_beta(mbp):
     for name in ("ln_8192x4096_f32", "addln_gelu_16384x8192_bf16"):
         w, d, _ = _ln_case(name, 4, 4096, residual=False)

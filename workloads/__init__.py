@@ -183,3 +183,14 @@ def generate(w: Workload, cols: int | None = None) -> dict:
     return dict(x=x, residual=r,
                 gamma=f32_to_bf16_bits(gamma64.astype(np.float32)),
                 beta=f32_to_bf16_bits(beta64.astype(np.float32)))
+
+
+def to_device(a, device="cuda"):
+    """Copy a host array to a torch tensor on `device` (bf16 bit patterns become
+    a bfloat16 tensor).  None passes through."""
+    if a is None:
+        return None
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
