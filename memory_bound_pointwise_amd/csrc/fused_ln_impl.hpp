@@ -8,8 +8,7 @@
 // The row is loaded once into registers, reduced twice (the mean, then the sum
 // of squared deviations from it: the pages' one-pass E[v^2] - mean^2 loses the
 // variance when |mean| >> std), normalised and stored once.  Only the inputs
-// and the output touch HBM; LDS holds the per-wave partial sums (and, on the
-// window path, gamma/beta).
+// and the output touch HBM; LDS holds only the per-wave partial sums.
 //
 // Number types: bf16 I/O computes in fp32 (the statistics included); fp32 I/O
 // computes the statistics and the normalisation in binary64 and rounds once to
@@ -21,12 +20,8 @@
 //    and beta stay in registers for all rows a block processes.
 //  * ln_win_kernel: x, residual and y share one misalignment mod 16 (e.g. bf16
 //    rows of 4095 elements, 8190 bytes): each row is covered by the 16-byte
-//    aligned windows that overlap it, so every load and store is a 128-bit
-//    access; elements of a window outside the row are masked out, and windows
-//    that stick out of the row are stored element by element.  A window that
-//    reaches outside the tensor itself is loaded element by element, so no
-//    byte outside the tensor is touched.  The column of a register slot moves
-//    with the row's offset, so gamma/beta are read from LDS.
+//    aligned windows that overlap it, so the loads and the interior stores are
+//    128-bit accesses (details at the kernel).
 //  * ln_scalar_kernel: anything else (pointers with different misalignments);
 //    one element per lane and load.
 #pragma once
@@ -209,14 +204,29 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
 
 // ------------------------------------------------------------ windowed rows
 
-// Dynamic LDS: (gamma, beta) of column c at index c + V, zero-padded by V
-// entries on both sides, so a window's slot e of row-relative vector j reads
-// index V*j + e - s + V >= 0 for every row offset s in [0, V).
+// Rows that do not start on 16-byte boundaries, with x, residual and y sharing
+// one misalignment mb.  Each row is covered by the aligned 16-byte windows that
+// overlap it (window q = bytes [16q, 16q + 16) above the boundary below the
+// base pointer); slot j of a row holds window q0 + j, whose element e is column
+// V*j + e - s, where s is the row's start inside its first window.  s repeats
+// with period P = 16 / gcd(16, cols * sizeof(E)) over the rows, so each block
+// serves one residue class of rows (row = r0 + cls + P*t) in which s, the
+// number of windows nv and the element masks of the first and last window are
+// constants; gamma/beta are gathered once per block into that shifted layout.
+// The rows handled here are the interior rows [r0, r1) whose windows lie inside
+// the tensor; the few rows at either end whose windows would reach outside it
+// are done element by element by the blocks past the last residue block.  So
+// the hot loop differs from the aligned kernel only in its addressing and in
+// the two partial windows per row (masked out of the sums, stored element by
+// element).  Slots past a row's last window are skipped.  The block is
+// persistent, so the next row's windows are loaded while the current row is
+// reduced and written.
 template <class IO, int LANES, int VPL, bool RES, bool GELU>
 __global__ __launch_bounds__(block_for(LANES)) void ln_win_kernel(
     const typename IO::elem* x, const typename IO::elem* res,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
-    typename IO::elem* y, int64_t rows, int cols, double eps_d) {
+    typename IO::elem* y, int64_t rows, int cols, double eps_d, int period, int64_t r0,
+    int64_t r1, int main_blocks) {
   typedef typename IO::elem E;
   typedef typename Types<IO, RES>::acc Acc;
   typedef typename Types<IO, RES>::val Val;
@@ -225,104 +235,156 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_win_kernel(
   constexpr int BLOCK = block_for(LANES);
   constexpr int RPB = BLOCK / LANES;
   constexpr bool kInPlace = std::is_same<Acc, Val>::value;
+  constexpr unsigned kFull = (1u << V) - 1;
   __shared__ Acc red[2][BLOCK / 64];
-  extern __shared__ float2 gb[];
+  const Acc eps = (Acc)eps_d;
 
-  for (int i = threadIdx.x; i < cols + 2 * V; i += BLOCK) {
-    const int c = i - V;
-    float2 p = make_float2(0.0f, 0.0f);
-    if (c >= 0 && c < cols) p = make_float2(IO::load1(gamma, c), IO::load1(beta, c));
-    gb[i] = p;
+  if ((int)blockIdx.x >= main_blocks) {
+    // an edge row: the whole block, one element per lane and load
+    const int64_t i = (int64_t)blockIdx.x - main_blocks;
+    const int64_t row = i < r0 ? i : r1 + (i - r0);
+    const int64_t e0 = row * (int64_t)cols;
+    Acc sum = 0;
+    for (int c = threadIdx.x; c < cols; c += BLOCK) {
+      Val t = (Val)IO::load1(x, e0 + c);
+      if constexpr (RES) t += (Val)IO::load1(res, e0 + c);
+      sum += (Acc)t;
+    }
+    const Acc mean = group_sum<BLOCK, BLOCK>(sum, red[0]) / (Acc)cols;
+    Acc m2 = 0;
+    for (int c = threadIdx.x; c < cols; c += BLOCK) {
+      Val t = (Val)IO::load1(x, e0 + c);
+      if constexpr (RES) t += (Val)IO::load1(res, e0 + c);
+      const Acc d = (Acc)t - mean;
+      m2 = fma_t(d, d, m2);
+    }
+    const Acc rstd = inv_sqrt(group_sum<BLOCK, BLOCK>(m2, red[1]) / (Acc)cols + eps);
+    for (int c = threadIdx.x; c < cols; c += BLOCK) {
+      Val t = (Val)IO::load1(x, e0 + c);
+      if constexpr (RES) t += (Val)IO::load1(res, e0 + c);
+      IO::store1(y, e0 + c, finish<Acc, GELU>((Acc)t - mean, rstd, (Acc)IO::load1(gamma, c),
+                                             (Acc)IO::load1(beta, c)));
+    }
+    return;
   }
-  __syncthreads();
 
   const int lane = threadIdx.x % LANES;
   const int sub = threadIdx.x / LANES;
-  const Acc eps = (Acc)eps_d;
-  // x, residual and y share the misalignment mb; windows are indexed from the
-  // 16-byte boundary just below each base pointer.
   const int mb = (int)(reinterpret_cast<uintptr_t>(x) & 15);
   const u32x4* xw = reinterpret_cast<const u32x4*>(reinterpret_cast<uintptr_t>(x) - mb);
   const u32x4* rw = RES ? reinterpret_cast<const u32x4*>(reinterpret_cast<uintptr_t>(res) - mb) : nullptr;
   u32x4* yw = reinterpret_cast<u32x4*>(reinterpret_cast<uintptr_t>(y) - mb);
-  const int64_t total = rows * (int64_t)cols;
-  const int64_t end_byte = mb + (int64_t)ES * total;  // tensor = bytes [mb, end_byte) of the windows
+  const int64_t row_bytes = (int64_t)ES * cols;
 
-  const int64_t groups = (rows + RPB - 1) / RPB;
-  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
-    const int64_t row = grp * RPB + sub;
-    const bool live = row < rows;
-    const int64_t e0 = (live ? row : rows - 1) * (int64_t)cols;  // past the end: reread the last row
-    const int64_t off = mb + (int64_t)ES * e0;
-    const int64_t q0 = off >> 4;
-    const int s = (int)(off & 15) / ES;                              // row start within window q0
-    const int nv = (int)(((off + (int64_t)ES * cols + 15) >> 4) - q0);  // windows overlapping the row
+  // this block's residue class: rows r0 + cls + P*t, t < cls_rows
+  const int cls = blockIdx.x % period;
+  const int per_cls = main_blocks / period;
+  const int64_t span = r1 - r0 - cls;
+  const int64_t cls_rows = span > 0 ? (span + period - 1) / period : 0;
+  const int64_t groups = (cls_rows + RPB - 1) / RPB;
+  const int s = (int)((mb + row_bytes * (r0 + cls)) & 15) / ES;
+  const int nv = (s * ES + (int)row_bytes + 15) >> 4;  // windows per row
 
+  // per slot: which elements belong to the row (only the first and last
+  // window are partial), and gamma/beta gathered into the shifted layout
+  unsigned emask[VPL];
+  u32x4 graw[VPL], braw[VPL];
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int j = lane + k * LANES;
+    emask[k] = 0;
+    graw[k] = braw[k] = u32x4{{0u, 0u, 0u, 0u}};
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int c = V * j + e - s;
+      if (j < nv && c >= 0 && c < cols) {
+        emask[k] |= 1u << e;
+        set_elem<IO>(graw[k], e, gamma[c]);
+        set_elem<IO>(braw[k], e, beta[c]);
+      }
+    }
+  }
+
+  // row of group grp for this lane group (past the class's end: its last row)
+  auto row_of = [&](int64_t grp, bool& live) {
+    const int64_t t = grp * RPB + sub;
+    live = t < cls_rows;
+    return r0 + cls + (int64_t)period * (live ? t : cls_rows - 1);
+  };
+  // the windows of a row; slots without row elements load nothing
+  auto load_row = [&](int64_t row, u32x4* xv, u32x4* rv) {
+    const int64_t q0 = (mb + row_bytes * row) >> 4;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      if (emask[k] == 0) continue;
+      xv[k] = load_nt(xw + q0 + lane + k * LANES);
+      if constexpr (RES) rv[k] = load_nt(rw + q0 + lane + k * LANES);
+    }
+  };
+
+  // the next row's windows are loaded while the current row is reduced
+  u32x4 nx[VPL], nr[VPL];
+  if (blockIdx.x / period < groups) {
+    bool live;
+    load_row(row_of(blockIdx.x / period, live), nx, nr);
+  }
+  for (int64_t grp = blockIdx.x / period; grp < groups; grp += per_cls) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      opaque(graw[k]);
+      opaque(braw[k]);
+    }
+    bool live;
+    const int64_t row = row_of(grp, live);
+    const int64_t q0 = (mb + row_bytes * row) >> 4;
     u32x4 xv[VPL], rv[VPL];
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int j = lane + k * LANES;
-      xv[k] = rv[k] = u32x4{{0u, 0u, 0u, 0u}};
-      if (j < nv) {
-        const int64_t q = q0 + j;
-        if (16 * q >= mb && 16 * q + 16 <= end_byte) {
-          xv[k] = load_nt(xw + q);
-          if constexpr (RES) rv[k] = load_nt(rw + q);
-        } else {
-          // the first window of the tensor or its last: only elements inside
-#pragma unroll
-          for (int e = 0; e < V; ++e) {
-            const int64_t f = (16 * q + ES * e - mb) / ES;
-            if (f >= 0 && f < total) {
-              set_elem<IO>(xv[k], e, x[f]);
-              if constexpr (RES) set_elem<IO>(rv[k], e, res[f]);
-            }
-          }
-        }
-      }
+      xv[k] = nx[k];
+      if constexpr (RES) rv[k] = nr[k];
+    }
+    if (grp + per_cls < groups) {
+      bool nlive;
+      load_row(row_of(grp + per_cls, nlive), nx, nr);
     }
 
     Val v[VPL][V];
     Acc sum = 0;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int j = lane + k * LANES;
-      const bool inrow = V * j - s >= 0 && V * j + V - s <= cols;
+      if (emask[k] == 0) continue;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        Val t = (Val)IO::get(xv[k], e);
-        if constexpr (RES) t += (Val)IO::get(rv[k], e);
-        v[k][e] = t;
+        Val tv = (Val)IO::get(xv[k], e);
+        if constexpr (RES) tv += (Val)IO::get(rv[k], e);
+        v[k][e] = tv;
       }
-      if (!inrow) {
+      if (emask[k] != kFull) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const int c = V * j + e - s;
-          if (c < 0 || c >= cols) v[k][e] = 0;
-        }
+        for (int e = 0; e < V; ++e)
+          if (!((emask[k] >> e) & 1u)) v[k][e] = 0;
       }
+      Acc part = 0;
 #pragma unroll
-      for (int e = 0; e < V; ++e) sum += (Acc)v[k][e];
+      for (int e = 0; e < V; ++e) part += (Acc)v[k][e];
+      sum += part;
     }
     const Acc mean = group_sum<LANES, BLOCK>(sum, red[0]) / (Acc)cols;
 
     Acc m2 = 0;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int j = lane + k * LANES;
-      const bool inrow = V * j - s >= 0 && V * j + V - s <= cols;
+      if (emask[k] == 0) continue;
       Acc dd[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         dd[e] = (Acc)v[k][e] - mean;
         if constexpr (kInPlace) v[k][e] = dd[e];
       }
-      if (!inrow) {
+      if (emask[k] != kFull) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const int c = V * j + e - s;
-          if (c < 0 || c >= cols) dd[e] = 0;
-        }
+        for (int e = 0; e < V; ++e)
+          if (!((emask[k] >> e) & 1u)) dd[e] = 0;
       }
       Acc part = 0;
 #pragma unroll
@@ -331,26 +393,24 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_win_kernel(
     }
     const Acc rstd = inv_sqrt(group_sum<LANES, BLOCK>(m2, red[1]) / (Acc)cols + eps);
 
+    if (!live) continue;
+    const int64_t e0 = row * (int64_t)cols;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int j = lane + k * LANES;
-      if (!(live && j < nv)) continue;
-      const float2* gbj = gb + (V * j - s + V);
+      if (emask[k] == 0) continue;
       float o[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        const float2 p = gbj[e];
         const Acc d = kInPlace ? (Acc)v[k][e] : (Acc)v[k][e] - mean;
-        o[e] = finish<Acc, GELU>(d, rstd, (Acc)p.x, (Acc)p.y);
+        o[e] = finish<Acc, GELU>(d, rstd, (Acc)IO::get(graw[k], e), (Acc)IO::get(braw[k], e));
       }
-      if (V * j - s >= 0 && V * j + V - s <= cols) {
+      const int j = lane + k * LANES;
+      if (emask[k] == kFull) {
         store_nt(yw + q0 + j, pack_vec<IO>(o));
       } else {
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const int c = V * j + e - s;
-          if (c >= 0 && c < cols) IO::store1(y, e0 + c, o[e]);
-        }
+        for (int e = 0; e < V; ++e)
+          if ((emask[k] >> e) & 1u) IO::store1(y, e0 + V * j + e - s, o[e]);
       }
     }
   }
@@ -417,6 +477,32 @@ struct VecSel {
     static const void* ptr() { return reinterpret_cast<const void*>(&ln_vec_kernel<IO, L, P, RES, GELU>); }
   };
 };
+// Window layouts: at most 3 windows per lane (the gathered gamma/beta take as
+// many registers as the data); the last slot is only partly used.
+constexpr Shape kWinShapes[] = {{16, 2},  {32, 2},  {32, 3},  {64, 3},   {128, 3},
+                                {256, 3}, {512, 3}, {1024, 3}};
+constexpr int kNumWin = sizeof(kWinShapes) / sizeof(Shape);
+
+inline int pick_win_shape(int64_t nvec) {
+  for (int i = 0; i < kNumWin; ++i)
+    if ((int64_t)kWinShapes[i].lanes * kWinShapes[i].vpl >= nvec) return i;
+  return -1;
+}
+
+template <template <int, int> class K>
+const void* win_kernel(int i) {
+  switch (i) {
+    case 0: return K<16, 2>::ptr();
+    case 1: return K<32, 2>::ptr();
+    case 2: return K<32, 3>::ptr();
+    case 3: return K<64, 3>::ptr();
+    case 4: return K<128, 3>::ptr();
+    case 5: return K<256, 3>::ptr();
+    case 6: return K<512, 3>::ptr();
+    default: return K<1024, 3>::ptr();
+  }
+}
+
 template <class IO, bool RES, bool GELU>
 struct WinSel {
   template <int L, int P>
@@ -444,11 +530,10 @@ hipError_t launch_flags(const void* x, const void* res, const void* gamma, const
     k = shape_kernel<VecSel<IO, RES, GELU>::template K>(i);
     lanes = kShapes[i].lanes;
   } else if (congruent) {
-    const int i = pick_shape(cols / V + 2);
+    const int i = pick_win_shape(cols / V + 2);
     if (i < 0) return hipErrorInvalidValue;
-    k = shape_kernel<WinSel<IO, RES, GELU>::template K>(i);
-    lanes = kShapes[i].lanes;
-    lds = (size_t)(cols + 2 * V) * sizeof(float2);
+    k = win_kernel<WinSel<IO, RES, GELU>::template K>(i);
+    lanes = kWinShapes[i].lanes;
   } else if (cols <= 64 * 16) {
     k = reinterpret_cast<const void*>(&ln_scalar_kernel<IO, 64, 16, RES, GELU>);
     lanes = 64;
@@ -459,13 +544,40 @@ hipError_t launch_flags(const void* x, const void* res, const void* gamma, const
   const int block = block_for(lanes);
   const int rpb = block / lanes;
   const int64_t groups = (rows + rpb - 1) / rpb;
-  // Aligned rows: one block per row group (new blocks start as old ones finish,
-  // which keeps more loads in flight than a persistent loop).  Windowed rows
-  // stage gamma/beta in LDS per block, so a block takes several row groups.
-  const int grid = aligned ? (int)(groups < kMaxGrid ? groups : kMaxGrid)
-                           : persistent_grid(k, block, groups, lds);
   int icols = (int)cols;
-  void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &eps};
+  if (aligned || !congruent) {
+    // One block per row group: new blocks start as old ones finish, which keeps
+    // more loads in flight than a persistent loop.
+    const int grid = (int)(groups < kMaxGrid ? groups : kMaxGrid);
+    void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &eps};
+    return hipLaunchKernel(k, dim3(grid), dim3(block), args, lds, s);
+  }
+  // Windowed rows: interior rows [r0, r1) (their windows lie inside the
+  // tensor) in persistent blocks, a whole number per residue class of the row
+  // shift; then one block per edge row.
+  const int es = (int)sizeof(typename IO::elem);
+  const int64_t row_bytes = (int64_t)es * cols;
+  const int64_t mbi = (int64_t)mb, end_byte = mbi + row_bytes * rows;
+  auto inside = [&](int64_t r) {
+    const int64_t off = mbi + row_bytes * r;
+    const int64_t q0 = off >> 4, nv = ((off & 15) + row_bytes + 15) >> 4;
+    return 16 * q0 >= mbi && 16 * (q0 + nv) <= end_byte;
+  };
+  int64_t r0 = 0, r1 = rows;
+  while (r0 < rows && !inside(r0)) ++r0;
+  while (r1 > r0 && !inside(r1 - 1)) --r1;
+  const int64_t edge_rows = rows - (r1 - r0);
+  int period = 1;
+  while (period < 16 && (row_bytes * period) % 16 != 0) period *= 2;
+  const int64_t cls_groups = ((r1 - r0 + period - 1) / period + rpb - 1) / rpb;
+  const int resident = persistent_grid(k, block, (int64_t)1 << 30, lds);
+  int64_t per_cls = resident / period;
+  if (per_cls < 1) per_cls = 1;
+  if (per_cls > cls_groups) per_cls = cls_groups;
+  int main_blocks = (int)(per_cls * period);
+  if (r1 == r0) main_blocks = 0;
+  const int grid = (int)(main_blocks + edge_rows);
+  void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &eps, &period, &r0, &r1, &main_blocks};
   return hipLaunchKernel(k, dim3(grid), dim3(block), args, lds, s);
 }
 

@@ -190,14 +190,19 @@ def test_ln_misaligned_and_in_place(mbp, dtype_name):
     chk(to_host(x), ref, "in place")
 
 
-@pytest.mark.parametrize("dtype_name,cols,shift", [("addln_gelu_16384x8192_bf16", 4095, 1),
-                                                    ("addln_gelu_16384x8192_bf16", 768, 3),
-                                                    ("addln_gelu_16384x8192_bf16", 8192, 7),
-                                                    ("ln_8192x4096_f32", 4093, 1), ("ln_8192x4096_f32", 1024, 2)])
-def test_ln_common_misalignment(mbp, dtype_name, cols, shift):
+@pytest.mark.parametrize("dtype_name,cols,shift,rows", [
+    ("addln_gelu_16384x8192_bf16", 4095, 1, 9), ("addln_gelu_16384x8192_bf16", 4095, 0, 33),
+    ("addln_gelu_16384x8192_bf16", 4095, 5, 1), ("addln_gelu_16384x8192_bf16", 4095, 3, 2),
+    ("addln_gelu_16384x8192_bf16", 768, 3, 9), ("addln_gelu_16384x8192_bf16", 8192, 7, 9),
+    ("addln_gelu_16384x8192_bf16", 3, 5, 40), ("addln_gelu_16384x8192_bf16", 1, 7, 21),
+    ("addln_gelu_16384x8192_bf16", 13, 2, 300), ("addln_gelu_16384x8192_bf16", 12290, 1, 5),
+    ("ln_8192x4096_f32", 4093, 1, 9), ("ln_8192x4096_f32", 1024, 2, 9), ("ln_8192x4096_f32", 5, 3, 40),
+    ("ln_8192x4096_f32", 6, 0, 17)])
+def test_ln_common_misalignment(mbp, dtype_name, cols, shift, rows):
     """x, residual and y all start `shift` elements past a 16-byte boundary:
-    the windowed path, including the first and last window of the tensor."""
-    w, d, act = _ln_case(dtype_name, 9, cols, residual=True)
+    the windowed path (rows off 16-byte boundaries, residue classes of the row
+    shift), including the edge rows whose windows would leave the tensor."""
+    w, d, act = _ln_case(dtype_name, rows, cols, residual=True)
     ref = _ln_ref(d, act)
     chk = check_bf16 if w.dtype == "bf16" else check_f32
 
