@@ -14,16 +14,14 @@
 // computes the statistics and the normalisation in binary64 and rounds once to
 // fp32 at the store.
 //
-// Three kernels, chosen by the host from pointer alignment and row length:
+// Two kernels, chosen by the host from pointer alignment and row length:
 //  * ln_vec_kernel: rows start on 16-byte boundaries (x, residual, y, gamma,
 //    beta 16-byte aligned and cols a whole number of 16-byte vectors).  gamma
-//    and beta stay in registers for all rows a block processes.
-//  * ln_win_kernel: x, residual and y share one misalignment mod 16 (e.g. bf16
-//    rows of 4095 elements, 8190 bytes): each row is covered by the 16-byte
-//    aligned windows that overlap it, so the loads and the interior stores are
-//    128-bit accesses (details at the kernel).
-//  * ln_scalar_kernel: anything else (pointers with different misalignments);
-//    one element per lane and load.
+//    and beta are loaded once per block into registers.
+//  * ln_shift_kernel: anything else (rows off 16-byte boundaries such as
+//    bf16 rows of 4095 elements, any pointer misalignment): the same register
+//    layout, filled from and drained to aligned 16-byte windows with lane
+//    shifts (details at the kernel).
 #pragma once
 
 #include <type_traits>
@@ -109,8 +107,12 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
   const int nvec = cols / V;
   const Acc eps = (Acc)eps_d;
 
-  // gamma / beta of this lane's columns, as fp32 for all rows of the block
+  // gamma / beta of this lane's columns.  Wide bf16 rows keep them packed
+  // (widened at each use, one shift or mask per element): measured faster on
+  // the 8192- and 12288-wide rows than holding 2 * VPL * 8 fp32 registers.
+  constexpr bool kPacked = sizeof(typename IO::elem) == 2 && LANES >= 128 && VPL >= 3;
   float g[VPL][V], b[VPL][V];
+  u32x4 gp[VPL], bp[VPL];
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
     const int vi = lane + k * LANES;
@@ -119,6 +121,8 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
       gv = load_vec<IO>(gamma, vi);
       bv = load_vec<IO>(beta, vi);
     }
+    gp[k] = gv;
+    bp[k] = bv;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
       g[k][e] = IO::get(gv, e);
@@ -128,6 +132,13 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
 
   const int64_t groups = (rows + RPB - 1) / RPB;
   for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    if constexpr (kPacked) {
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) {
+        opaque(gp[k]);
+        opaque(bp[k]);
+      }
+    }
     if constexpr (sizeof(Acc) == 8) {
       // fp32 gamma/beta are widened to binary64 at each use; without this the
       // compiler would widen them once and hold twice the registers.
@@ -195,275 +206,400 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const Acc d = kInPlace ? (Acc)v[k][e] : (Acc)v[k][e] - mean;
-        o[e] = finish<Acc, GELU>(d, rstd, (Acc)g[k][e], (Acc)b[k][e]);
+        if constexpr (kPacked)
+          o[e] = finish<Acc, GELU>(d, rstd, (Acc)IO::get(gp[k], e), (Acc)IO::get(bp[k], e));
+        else
+          o[e] = finish<Acc, GELU>(d, rstd, (Acc)g[k][e], (Acc)b[k][e]);
       }
       store_nt(reinterpret_cast<u32x4*>(yr) + vi, pack_vec<IO>(o));
     }
   }
 }
 
-// ------------------------------------------------------------ windowed rows
+// ------------------------------------------------------------ rows off 16-byte boundaries
 
-// Rows that do not start on 16-byte boundaries, with x, residual and y sharing
-// one misalignment mb.  Each row is covered by the aligned 16-byte windows that
-// overlap it (window q = bytes [16q, 16q + 16) above the boundary below the
-// base pointer); slot j of a row holds window q0 + j, whose element e is column
-// V*j + e - s, where s is the row's start inside its first window.  s repeats
-// with period P = 16 / gcd(16, cols * sizeof(E)) over the rows, so each block
-// serves one residue class of rows (row = r0 + cls + P*t) in which s, the
-// number of windows nv and the element masks of the first and last window are
-// constants; gamma/beta are gathered once per block into that shifted layout.
-// The rows handled here are the interior rows [r0, r1) whose windows lie inside
-// the tensor; the few rows at either end whose windows would reach outside it
-// are done element by element by the blocks past the last residue block.  So
-// the hot loop differs from the aligned kernel only in its addressing and in
-// the two partial windows per row (masked out of the sums, stored element by
-// element).  Slots past a row's last window are skipped.  The block is
-// persistent, so the next row's windows are loaded while the current row is
-// reduced and written.
+// Rows that do not start on 16-byte boundaries (e.g. bf16 rows of 4095
+// elements, 8190 bytes), with any misalignment of x, residual, y, gamma and
+// beta.  The register layout and the arithmetic are those of ln_vec_kernel;
+// only the way vectors reach and leave the registers differs.
+//
+// Window space: window q of a tensor is bytes [16q, 16q + 16) above the
+// 16-byte boundary at or below its base pointer.  Loads: the row vector in
+// slot j (row bytes [16j, 16j + 16)) is the byte funnel of windows j and j+1
+// of the row at the row's byte offset in its first window.  Every slot loads
+// its window j; window j+1 is the window of the neighbouring slot, fetched
+// with a DPP lane shift, except for the one slot per wave (or row group)
+// whose neighbour sits in another wave, which loads it itself.  Stores: output
+// window j is the funnel of output vectors j-1 and j at the output row's
+// offset; vector j-1 comes from the neighbouring lane the same way, and the
+// two windows per wave whose halves sit in different waves are written half
+// by half with element stores.  Windows shared with the neighbouring rows (the
+// first and last of a row) are written element by element, so no byte of
+// another row is written.  A row whose first or last window reaches outside a
+// tensor (only the tensor's first and last row can) is read element by
+// element, so no byte outside the tensors is read.
+//
+// Slots: for groups of at least a wave, wave w of the group holds the slots
+// w*64*VPL + k*64 + l (round k, wave lane l), so each wave covers one
+// contiguous stretch of the row and a load instruction 64 consecutive
+// windows.  Narrower groups use slot k*LANES + lane as ln_vec_kernel does.
+
+// Geometry of one tensor's window space.  The base is derived from the
+// tensor pointer by pointer arithmetic (never through an integer), so the
+// compiler keeps it in the global address space and emits global (not flat)
+// memory instructions, whose completion does not hold up LDS waits.
+struct Win {
+  const char* base;  // 16-byte boundary at or below the tensor pointer
+  int mb;            // tensor pointer - base (bytes)
+  int64_t end;       // one past the tensor's last byte, relative to base
+};
+
+template <class IO>
+__device__ __forceinline__ Win make_win(const void* p, int64_t total) {
+  Win w;
+  w.mb = (int)(reinterpret_cast<uintptr_t>(p) & 15);
+  w.base = static_cast<const char*>(p) - w.mb;
+  w.end = w.mb + (int64_t)sizeof(typename IO::elem) * total;
+  return w;
+}
+
+// DPP lane moves inside a wave (lane l of the result):
+//   shl1: lane l+1 of v (lane 63 keeps old);  rol1: lane (l+1) mod 64 of v;
+//   shr1: lane l-1 of v (lane 0 keeps old);   ror1: lane (l-1) mod 64 of v.
+__device__ __forceinline__ uint32_t dpp_shl1(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, 0x130, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t dpp_rol1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x134, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t dpp_shr1(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, 0x138, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t dpp_ror1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x13C, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t lane_read(uint32_t v, int src_lane) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)v);
+}
+
+// Word t of the slot after this one (next) or before it (prev), given the
+// slot's round-k value c and the value a of the adjacent round (k+1 for next,
+// k-1 for prev).
+template <int LANES>
+__device__ __forceinline__ uint32_t next_word(uint32_t c, uint32_t a) {
+  if constexpr (LANES >= 64) {
+    return dpp_shl1(dpp_rol1(a), c);
+  } else {
+    const int wl = threadIdx.x & 63;
+    const uint32_t far = lane_read(a, wl & ~(LANES - 1));  // the group's lane 0
+    const uint32_t near = dpp_shl1(0u, c);
+    return ((wl & (LANES - 1)) == LANES - 1) ? far : near;
+  }
+}
+template <int LANES>
+__device__ __forceinline__ uint32_t prev_word(uint32_t c, uint32_t a) {
+  if constexpr (LANES >= 64) {
+    return dpp_shr1(dpp_ror1(a), c);
+  } else {
+    const int wl = threadIdx.x & 63;
+    const uint32_t far = lane_read(a, wl | (LANES - 1));  // the group's last lane
+    const uint32_t near = dpp_shr1(0u, c);
+    return ((wl & (LANES - 1)) == 0) ? far : near;
+  }
+}
+
+// Bytes [4Q + bb, 4Q + bb + 16) of the 32 bytes lo || hi (bb = 0 or 2).
+template <int ES, int Q>
+__device__ __forceinline__ u32x4 funnel(const u32x4& lo, const uint32_t* hi, int bb) {
+  uint32_t w[8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    w[t] = lo.w[t];
+    w[4 + t] = hi[t];
+  }
+  u32x4 r;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (ES == 4) r.w[t] = w[Q + t];
+    else r.w[t] = __builtin_amdgcn_alignbyte(w[Q + t + 1], w[Q + t], bb);
+  }
+  return r;
+}
+
+// Row vectors of all rounds from windows c[0..VPL] (c[VPL]: the slot after
+// the last round, needed only where next_word reads it) at byte offset sb.
+// The word shift is uniform over the row; for groups of at least a wave it is
+// made wave-uniform so the switch is a scalar branch and each case moves only
+// the words it needs.
+template <class IO, int LANES, int VPL>
+__device__ __forceinline__ void realign_in(const u32x4 (&c)[VPL + 1], int sb, u32x4 (&out)[VPL]) {
+  constexpr int ES = (int)sizeof(typename IO::elem);
+  constexpr int XW = ES == 2 ? 1 : 0;  // bf16 shifts by half-words need one more word
+  int q = sb >> 2;
+  const int bb = sb & 3;
+  if constexpr (LANES >= 64) q = __builtin_amdgcn_readfirstlane(q);
+  uint32_t n[VPL][4];
+  if constexpr (LANES < 64) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) n[k][t] = next_word<LANES>(c[k].w[t], c[k + 1].w[t]);
+  }
+#define MBP_REALIGN_CASE(Q)                                                            \
+  case Q:                                                                              \
+    _Pragma("unroll") for (int k = 0; k < VPL; ++k) {                                  \
+      if constexpr (LANES >= 64) {                                                     \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t) n[k][t] =                        \
+            (t < Q + XW) ? next_word<LANES>(c[k].w[t], c[k + 1].w[t]) : 0u;           \
+      }                                                                                \
+      out[k] = funnel<ES, Q>(c[k], n[k], bb);                                          \
+    }                                                                                  \
+    break;
+  switch (q) {
+    MBP_REALIGN_CASE(0)
+    MBP_REALIGN_CASE(1)
+    MBP_REALIGN_CASE(2)
+    default: MBP_REALIGN_CASE(3)
+  }
+#undef MBP_REALIGN_CASE
+}
+
 template <class IO, int LANES, int VPL, bool RES, bool GELU>
-__global__ __launch_bounds__(block_for(LANES)) void ln_win_kernel(
+__global__ __launch_bounds__(block_for(LANES)) void ln_shift_kernel(
     const typename IO::elem* x, const typename IO::elem* res,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
-    typename IO::elem* y, int64_t rows, int cols, double eps_d, int period, int64_t r0,
-    int64_t r1, int main_blocks) {
+    typename IO::elem* y, int64_t rows, int cols, double eps_d) {
   typedef typename IO::elem E;
   typedef typename Types<IO, RES>::acc Acc;
   typedef typename Types<IO, RES>::val Val;
-  constexpr int V = IO::kVec;
   constexpr int ES = (int)sizeof(E);
+  constexpr int V = IO::kVec;
   constexpr int BLOCK = block_for(LANES);
   constexpr int RPB = BLOCK / LANES;
+  constexpr int WL = LANES < 64 ? LANES : 64;  // lanes of a group inside one wave
   constexpr bool kInPlace = std::is_same<Acc, Val>::value;
-  constexpr unsigned kFull = (1u << V) - 1;
   __shared__ Acc red[2][BLOCK / 64];
-  const Acc eps = (Acc)eps_d;
-
-  if ((int)blockIdx.x >= main_blocks) {
-    // an edge row: the whole block, one element per lane and load
-    const int64_t i = (int64_t)blockIdx.x - main_blocks;
-    const int64_t row = i < r0 ? i : r1 + (i - r0);
-    const int64_t e0 = row * (int64_t)cols;
-    Acc sum = 0;
-    for (int c = threadIdx.x; c < cols; c += BLOCK) {
-      Val t = (Val)IO::load1(x, e0 + c);
-      if constexpr (RES) t += (Val)IO::load1(res, e0 + c);
-      sum += (Acc)t;
-    }
-    const Acc mean = group_sum<BLOCK, BLOCK>(sum, red[0]) / (Acc)cols;
-    Acc m2 = 0;
-    for (int c = threadIdx.x; c < cols; c += BLOCK) {
-      Val t = (Val)IO::load1(x, e0 + c);
-      if constexpr (RES) t += (Val)IO::load1(res, e0 + c);
-      const Acc d = (Acc)t - mean;
-      m2 = fma_t(d, d, m2);
-    }
-    const Acc rstd = inv_sqrt(group_sum<BLOCK, BLOCK>(m2, red[1]) / (Acc)cols + eps);
-    for (int c = threadIdx.x; c < cols; c += BLOCK) {
-      Val t = (Val)IO::load1(x, e0 + c);
-      if constexpr (RES) t += (Val)IO::load1(res, e0 + c);
-      IO::store1(y, e0 + c, finish<Acc, GELU>((Acc)t - mean, rstd, (Acc)IO::load1(gamma, c),
-                                             (Acc)IO::load1(beta, c)));
-    }
-    return;
-  }
 
   const int lane = threadIdx.x % LANES;
   const int sub = threadIdx.x / LANES;
-  const int mb = (int)(reinterpret_cast<uintptr_t>(x) & 15);
-  const u32x4* xw = reinterpret_cast<const u32x4*>(reinterpret_cast<uintptr_t>(x) - mb);
-  const u32x4* rw = RES ? reinterpret_cast<const u32x4*>(reinterpret_cast<uintptr_t>(res) - mb) : nullptr;
-  u32x4* yw = reinterpret_cast<u32x4*>(reinterpret_cast<uintptr_t>(y) - mb);
-  const int64_t row_bytes = (int64_t)ES * cols;
+  const int wl = lane % WL;
+  const int nvec = (cols + V - 1) / V;  // the last vector may be partial
+  const int rem = cols - V * (nvec - 1);  // its elements inside the row (1 .. V)
+  const Acc eps = (Acc)eps_d;
+  const int64_t total = rows * (int64_t)cols;
+  const Win wx = make_win<IO>(x, total);
+  const Win wr = RES ? make_win<IO>(res, total) : wx;
+  const Win wy = make_win<IO>(y, total);
+  auto slot = [&](int k) -> int {
+    return LANES >= 64 ? (lane / 64) * 64 * VPL + k * 64 + wl : k * LANES + lane;
+  };
 
-  // this block's residue class: rows r0 + cls + P*t, t < cls_rows
-  const int cls = blockIdx.x % period;
-  const int per_cls = main_blocks / period;
-  const int64_t span = r1 - r0 - cls;
-  const int64_t cls_rows = span > 0 ? (span + period - 1) / period : 0;
-  const int64_t groups = (cls_rows + RPB - 1) / RPB;
-  const int s = (int)((mb + row_bytes * (r0 + cls)) & 15) / ES;
-  const int nv = (s * ES + (int)row_bytes + 15) >> 4;  // windows per row
-
-  // per slot: which elements belong to the row (only the first and last
-  // window are partial), and gamma/beta gathered into the shifted layout
-  unsigned emask[VPL];
-  u32x4 graw[VPL], braw[VPL];
+  // gamma / beta of this lane's slots, packed
+  const bool gvec = (((uintptr_t)gamma | (uintptr_t)beta) & 15) == 0;
+  u32x4 gp[VPL], bp[VPL];
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
-    const int j = lane + k * LANES;
-    emask[k] = 0;
-    graw[k] = braw[k] = u32x4{{0u, 0u, 0u, 0u}};
+    const int j = slot(k);
+    u32x4 gv = {{0u, 0u, 0u, 0u}}, bv = {{0u, 0u, 0u, 0u}};
+    if (gvec && V * j + V <= cols) {
+      gv = load_vec<IO>(gamma, j);
+      bv = load_vec<IO>(beta, j);
+    } else if (j < nvec) {
 #pragma unroll
-    for (int e = 0; e < V; ++e) {
-      const int c = V * j + e - s;
-      if (j < nv && c >= 0 && c < cols) {
-        emask[k] |= 1u << e;
-        set_elem<IO>(graw[k], e, gamma[c]);
-        set_elem<IO>(braw[k], e, beta[c]);
+      for (int e = 0; e < V; ++e)
+        if (V * j + e < cols) {
+          set_elem<IO>(gv, e, gamma[V * j + e]);
+          set_elem<IO>(bv, e, beta[V * j + e]);
+        }
+    }
+    gp[k] = gv;
+    bp[k] = bv;
+  }
+
+  const int64_t groups = (rows + RPB - 1) / RPB;
+  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      opaque(gp[k]);
+      opaque(bp[k]);
+    }
+    const int64_t row = grp * RPB + sub;
+    const bool live = row < rows;
+    const int64_t e0 = (live ? row : rows - 1) * (int64_t)cols;
+
+    // row vectors of x and residual
+    u32x4 xa[VPL], ra[VPL];
+    {
+      const int64_t offx = wx.mb + (int64_t)ES * e0, offr = wr.mb + (int64_t)ES * e0;
+      const int64_t qx = offx >> 4, qr = offr >> 4;
+      const int nvx = (int)(((offx & 15) + (int64_t)ES * cols + 15) >> 4);
+      const int nvr = (int)(((offr & 15) + (int64_t)ES * cols + 15) >> 4);
+      bool inside = 16 * qx >= wx.mb && 16 * (qx + nvx) <= wx.end;
+      if constexpr (RES) inside = inside && 16 * qr >= wr.mb && 16 * (qr + nvr) <= wr.end;
+      if (inside) {
+        const u32x4* sx = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(x) - wx.mb) + qx;
+        const u32x4* sr = RES ? reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(res) - wr.mb) + qr
+                              : nullptr;
+        u32x4 cx[VPL + 1], cr[VPL + 1];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+          cx[k] = load_nt(sx + min(slot(k), nvx - 1));
+          if constexpr (RES) cr[k] = load_nt(sr + min(slot(k), nvr - 1));
+        }
+        cx[VPL] = cr[VPL] = u32x4{{0u, 0u, 0u, 0u}};
+        if (wl == 0) {  // the slot after this wave's (group's) last one
+          cx[VPL] = load_nt(sx + min(slot(VPL), nvx - 1));
+          if constexpr (RES) cr[VPL] = load_nt(sr + min(slot(VPL), nvr - 1));
+        }
+        realign_in<IO, LANES, VPL>(cx, (int)(offx & 15), xa);
+        if constexpr (RES) realign_in<IO, LANES, VPL>(cr, (int)(offr & 15), ra);
+      } else {
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+          // elements of the slot inside the row; opaque so the per-element
+          // tests stay in this rarely taken branch instead of being hoisted
+          int lim = cols - V * slot(k);
+          opaque(lim);
+          xa[k] = ra[k] = u32x4{{0u, 0u, 0u, 0u}};
+#pragma unroll
+          for (int e = 0; e < V; ++e)
+            if (e < lim) {
+              set_elem<IO>(xa[k], e, x[e0 + V * slot(k) + e]);
+              if constexpr (RES) set_elem<IO>(ra[k], e, res[e0 + V * slot(k) + e]);
+            }
+        }
       }
-    }
-  }
-
-  // row of group grp for this lane group (past the class's end: its last row)
-  auto row_of = [&](int64_t grp, bool& live) {
-    const int64_t t = grp * RPB + sub;
-    live = t < cls_rows;
-    return r0 + cls + (int64_t)period * (live ? t : cls_rows - 1);
-  };
-  // the windows of a row; slots without row elements load nothing
-  auto load_row = [&](int64_t row, u32x4* xv, u32x4* rv) {
-    const int64_t q0 = (mb + row_bytes * row) >> 4;
-#pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-      if (emask[k] == 0) continue;
-      xv[k] = load_nt(xw + q0 + lane + k * LANES);
-      if constexpr (RES) rv[k] = load_nt(rw + q0 + lane + k * LANES);
-    }
-  };
-
-  // the next row's windows are loaded while the current row is reduced
-  u32x4 nx[VPL], nr[VPL];
-  if (blockIdx.x / period < groups) {
-    bool live;
-    load_row(row_of(blockIdx.x / period, live), nx, nr);
-  }
-  for (int64_t grp = blockIdx.x / period; grp < groups; grp += per_cls) {
-#pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-      opaque(graw[k]);
-      opaque(braw[k]);
-    }
-    bool live;
-    const int64_t row = row_of(grp, live);
-    const int64_t q0 = (mb + row_bytes * row) >> 4;
-    u32x4 xv[VPL], rv[VPL];
-#pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-      xv[k] = nx[k];
-      if constexpr (RES) rv[k] = nr[k];
-    }
-    if (grp + per_cls < groups) {
-      bool nlive;
-      load_row(row_of(grp + per_cls, nlive), nx, nr);
     }
 
     Val v[VPL][V];
     Acc sum = 0;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      if (emask[k] == 0) continue;
+      const int j = slot(k);
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        Val tv = (Val)IO::get(xv[k], e);
-        if constexpr (RES) tv += (Val)IO::get(rv[k], e);
-        v[k][e] = tv;
+        Val t = (Val)IO::get(xa[k], e);
+        if constexpr (RES) t += (Val)IO::get(ra[k], e);
+        v[k][e] = t;
       }
-      if (emask[k] != kFull) {
+      if (j == nvec - 1) {  // the last vector: elements from rem on lie past the row
 #pragma unroll
         for (int e = 0; e < V; ++e)
-          if (!((emask[k] >> e) & 1u)) v[k][e] = 0;
+          if (e >= rem) v[k][e] = 0;
       }
       Acc part = 0;
 #pragma unroll
       for (int e = 0; e < V; ++e) part += (Acc)v[k][e];
-      sum += part;
+      if (j < nvec) sum += part;
     }
     const Acc mean = group_sum<LANES, BLOCK>(sum, red[0]) / (Acc)cols;
 
     Acc m2 = 0;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      if (emask[k] == 0) continue;
+      const int j = slot(k);
       Acc dd[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         dd[e] = (Acc)v[k][e] - mean;
         if constexpr (kInPlace) v[k][e] = dd[e];
       }
-      if (emask[k] != kFull) {
+      if (j == nvec - 1) {
 #pragma unroll
         for (int e = 0; e < V; ++e)
-          if (!((emask[k] >> e) & 1u)) dd[e] = 0;
+          if (e >= rem) dd[e] = 0;
       }
       Acc part = 0;
 #pragma unroll
       for (int e = 0; e < V; ++e) part = fma_t(dd[e], dd[e], part);
-      m2 += part;
+      if (j < nvec) m2 += part;
     }
     const Acc rstd = inv_sqrt(group_sum<LANES, BLOCK>(m2, red[1]) / (Acc)cols + eps);
 
-    if (!live) continue;
-    const int64_t e0 = row * (int64_t)cols;
+    u32x4 ov[VPL + 1];
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      if (emask[k] == 0) continue;
       float o[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const Acc d = kInPlace ? (Acc)v[k][e] : (Acc)v[k][e] - mean;
-        o[e] = finish<Acc, GELU>(d, rstd, (Acc)IO::get(graw[k], e), (Acc)IO::get(braw[k], e));
+        o[e] = finish<Acc, GELU>(d, rstd, (Acc)IO::get(gp[k], e), (Acc)IO::get(bp[k], e));
       }
-      const int j = lane + k * LANES;
-      if (emask[k] == kFull) {
-        store_nt(yw + q0 + j, pack_vec<IO>(o));
+      ov[k] = pack_vec<IO>(o);
+    }
+    ov[VPL] = ov[VPL - 1];
+
+    // Output window j = bytes [16 - sb, 32 - sb) of vectors j-1 || j (sb > 0),
+    // or vector j (sb == 0).  Slot j writes window j; its bytes from vector
+    // j-1 only where that vector is known here (not in the first slot of a
+    // wave or group), and the slot after the last one (k == VPL, lane 0 of
+    // the wave or group) writes the bytes of the last slot's vector.
+    const int64_t offy = wy.mb + (int64_t)ES * (row * (int64_t)cols);
+    const int sb = (int)(offy & 15);
+    const int nvy = (int)((sb + (int64_t)ES * cols + 15) >> 4);
+    u32x4* dy = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(y) - wy.mb) + (offy >> 4);
+    E* yrow = y + row * (int64_t)cols;
+    const int rbytes = ES * cols;
+    // window of each round (k == VPL: the slot after the last)
+    u32x4 win[VPL + 1];
+    {
+      int q = ((16 - sb) & 15) >> 2;
+      const int bb = (16 - sb) & 3;
+      if constexpr (LANES >= 64) q = __builtin_amdgcn_readfirstlane(q);
+      if (sb == 0) {
+#pragma unroll
+        for (int k = 0; k <= VPL; ++k) win[k] = ov[k];
       } else {
+        // prev[k]: vector of slot j-1 (round k); its word t from the lane before
+        uint32_t pw[VPL + 1][4];
 #pragma unroll
-        for (int e = 0; e < V; ++e)
-          if ((emask[k] >> e) & 1u) IO::store1(y, e0 + V * j + e - s, o[e]);
+        for (int k = 0; k <= VPL; ++k)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            pw[k][t] = prev_word<LANES>(ov[k].w[t], ov[k > 0 ? k - 1 : 0].w[t]);
+#define MBP_OUT_CASE(Q)                                                          \
+  case Q:                                                                        \
+    _Pragma("unroll") for (int k = 0; k <= VPL; ++k) {                           \
+      u32x4 p;                                                                   \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) p.w[t] = pw[k][t];           \
+      win[k] = funnel<ES, Q>(p, ov[k].w, bb);                                    \
+    }                                                                            \
+    break;
+        switch (q) {
+          MBP_OUT_CASE(0)
+          MBP_OUT_CASE(1)
+          MBP_OUT_CASE(2)
+          default: MBP_OUT_CASE(3)
+        }
+#undef MBP_OUT_CASE
       }
     }
-  }
-}
-
-// ------------------------------------------------------------ any pointers
-
-template <class IO, int LANES, int EPL, bool RES, bool GELU>
-__global__ __launch_bounds__(block_for(LANES)) void ln_scalar_kernel(
-    const typename IO::elem* x, const typename IO::elem* res,
-    const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
-    typename IO::elem* y, int64_t rows, int cols, double eps_d) {
-  typedef typename Types<IO, RES>::acc Acc;
-  typedef typename Types<IO, RES>::val Val;
-  constexpr int BLOCK = block_for(LANES);
-  constexpr int RPB = BLOCK / LANES;
-  __shared__ Acc red[2][BLOCK / 64];
-  const int lane = threadIdx.x % LANES;
-  const int sub = threadIdx.x / LANES;
-  const Acc eps = (Acc)eps_d;
-  const int64_t groups = (rows + RPB - 1) / RPB;
-  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
-    const int64_t row = grp * RPB + sub;
-    const bool live = row < rows;
-    const int64_t e0 = row * (int64_t)cols;
-    Val v[EPL];
-    Acc sum = 0;
+    if (live) {
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) {
-      const int c = lane + k * LANES;
-      Val t = 0;
-      if (live && c < cols) {
-        t = (Val)IO::load1(x, e0 + c);
-        if constexpr (RES) t += (Val)IO::load1(res, e0 + c);
+      for (int k = 0; k <= VPL; ++k) {
+        if (k == VPL && wl != 0) continue;
+        const int j = slot(k);
+        if (j >= nvy) continue;
+        const int a = 16 * j - sb;  // row byte of the window's first byte
+        const bool prev_ok = sb != 0 && !(k == 0 && wl == 0);
+        const bool cur_ok = k < VPL;
+        const int lo = max(prev_ok ? a : 16 * j, 0);
+        const int hi = min(cur_ok ? a + 16 : 16 * j, rbytes);
+        if (lo == a && hi == a + 16) {
+          store_nt(dy + j, win[k]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            const int rb = a + ES * e;
+            if (rb >= lo && rb < hi) {
+              if constexpr (ES == 2)
+                yrow[rb / ES] = (E)(win[k].w[e >> 1] >> (16 * (e & 1)));
+              else
+                yrow[rb / ES] = __uint_as_float(win[k].w[e]);
+            }
+          }
+        }
       }
-      v[k] = t;
-      sum += (Acc)t;
-    }
-    const Acc mean = group_sum<LANES, BLOCK>(sum, red[0]) / (Acc)cols;
-    Acc m2 = 0;
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) {
-      const Acc d = (Acc)v[k] - mean;
-      if (lane + k * LANES < cols) m2 = fma_t(d, d, m2);
-    }
-    const Acc rstd = inv_sqrt(group_sum<LANES, BLOCK>(m2, red[1]) / (Acc)cols + eps);
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) {
-      const int c = lane + k * LANES;
-      if (!(live && c < cols)) continue;
-      const Acc d = (Acc)v[k] - mean;
-      IO::store1(y, e0 + c,
-                 finish<Acc, GELU>(d, rstd, (Acc)IO::load1(gamma, c), (Acc)IO::load1(beta, c)));
     }
   }
 }
@@ -477,108 +613,39 @@ struct VecSel {
     static const void* ptr() { return reinterpret_cast<const void*>(&ln_vec_kernel<IO, L, P, RES, GELU>); }
   };
 };
-// Window layouts: at most 3 windows per lane (the gathered gamma/beta take as
-// many registers as the data); the last slot is only partly used.
-constexpr Shape kWinShapes[] = {{16, 2},  {32, 2},  {32, 3},  {64, 3},   {128, 3},
-                                {256, 3}, {512, 3}, {1024, 3}};
-constexpr int kNumWin = sizeof(kWinShapes) / sizeof(Shape);
-
-inline int pick_win_shape(int64_t nvec) {
-  for (int i = 0; i < kNumWin; ++i)
-    if ((int64_t)kWinShapes[i].lanes * kWinShapes[i].vpl >= nvec) return i;
-  return -1;
-}
-
-template <template <int, int> class K>
-const void* win_kernel(int i) {
-  switch (i) {
-    case 0: return K<16, 2>::ptr();
-    case 1: return K<32, 2>::ptr();
-    case 2: return K<32, 3>::ptr();
-    case 3: return K<64, 3>::ptr();
-    case 4: return K<128, 3>::ptr();
-    case 5: return K<256, 3>::ptr();
-    case 6: return K<512, 3>::ptr();
-    default: return K<1024, 3>::ptr();
-  }
-}
-
 template <class IO, bool RES, bool GELU>
-struct WinSel {
+struct ShiftSel {
   template <int L, int P>
   struct K {
-    static const void* ptr() { return reinterpret_cast<const void*>(&ln_win_kernel<IO, L, P, RES, GELU>); }
+    static const void* ptr() { return reinterpret_cast<const void*>(&ln_shift_kernel<IO, L, P, RES, GELU>); }
   };
 };
-
 constexpr int64_t kMaxGrid = 1 << 30;
+constexpr int64_t kShiftGroups = 4;
 
 template <class IO, bool RES, bool GELU>
 hipError_t launch_flags(const void* x, const void* res, const void* gamma, const void* beta,
                         void* y, int64_t rows, int64_t cols, double eps, hipStream_t s) {
   constexpr int V = IO::kVec;
-  const uintptr_t mb = reinterpret_cast<uintptr_t>(x) & 15;
-  const bool congruent = ((reinterpret_cast<uintptr_t>(y) & 15) == mb) &&
-                         (!res || (reinterpret_cast<uintptr_t>(res) & 15) == mb);
-  const bool aligned = congruent && mb == 0 && cols % V == 0 && aligned16(gamma) && aligned16(beta);
-  const void* k;
-  int lanes;
-  size_t lds = 0;
-  if (aligned) {
-    const int i = pick_shape(cols / V);
-    if (i < 0) return hipErrorInvalidValue;
-    k = shape_kernel<VecSel<IO, RES, GELU>::template K>(i);
-    lanes = kShapes[i].lanes;
-  } else if (congruent) {
-    const int i = pick_win_shape(cols / V + 2);
-    if (i < 0) return hipErrorInvalidValue;
-    k = win_kernel<WinSel<IO, RES, GELU>::template K>(i);
-    lanes = kWinShapes[i].lanes;
-  } else if (cols <= 64 * 16) {
-    k = reinterpret_cast<const void*>(&ln_scalar_kernel<IO, 64, 16, RES, GELU>);
-    lanes = 64;
-  } else {
-    k = reinterpret_cast<const void*>(&ln_scalar_kernel<IO, 1024, 16, RES, GELU>);
-    lanes = 1024;
-  }
+  const bool aligned = aligned16(x) && aligned16(y) && (!res || aligned16(res)) && aligned16(gamma) &&
+                       aligned16(beta) && cols % V == 0;
+  const int i = pick_shape((cols + V - 1) / V);
+  if (i < 0) return hipErrorInvalidValue;
+  const int lanes = kShapes[i].lanes;
   const int block = block_for(lanes);
   const int rpb = block / lanes;
   const int64_t groups = (rows + rpb - 1) / rpb;
+  const int grid = (int)(groups < kMaxGrid ? groups : kMaxGrid);  // one block per row group
   int icols = (int)cols;
-  if (aligned || !congruent) {
-    // One block per row group: new blocks start as old ones finish, which keeps
-    // more loads in flight than a persistent loop.
-    const int grid = (int)(groups < kMaxGrid ? groups : kMaxGrid);
-    void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &eps};
-    return hipLaunchKernel(k, dim3(grid), dim3(block), args, lds, s);
+  void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &eps};
+  if (aligned) {
+    const void* k = shape_kernel<VecSel<IO, RES, GELU>::template K>(i);
+    return hipLaunchKernel(k, dim3(grid), dim3(block), args, 0, s);
   }
-  // Windowed rows: interior rows [r0, r1) (their windows lie inside the
-  // tensor) in persistent blocks, a whole number per residue class of the row
-  // shift; then one block per edge row.
-  const int es = (int)sizeof(typename IO::elem);
-  const int64_t row_bytes = (int64_t)es * cols;
-  const int64_t mbi = (int64_t)mb, end_byte = mbi + row_bytes * rows;
-  auto inside = [&](int64_t r) {
-    const int64_t off = mbi + row_bytes * r;
-    const int64_t q0 = off >> 4, nv = ((off & 15) + row_bytes + 15) >> 4;
-    return 16 * q0 >= mbi && 16 * (q0 + nv) <= end_byte;
-  };
-  int64_t r0 = 0, r1 = rows;
-  while (r0 < rows && !inside(r0)) ++r0;
-  while (r1 > r0 && !inside(r1 - 1)) --r1;
-  const int64_t edge_rows = rows - (r1 - r0);
-  int period = 1;
-  while (period < 16 && (row_bytes * period) % 16 != 0) period *= 2;
-  const int64_t cls_groups = ((r1 - r0 + period - 1) / period + rpb - 1) / rpb;
-  const int resident = persistent_grid(k, block, (int64_t)1 << 30, lds);
-  int64_t per_cls = resident / period;
-  if (per_cls < 1) per_cls = 1;
-  if (per_cls > cls_groups) per_cls = cls_groups;
-  int main_blocks = (int)(per_cls * period);
-  if (r1 == r0) main_blocks = 0;
-  const int grid = (int)(main_blocks + edge_rows);
-  void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &eps, &period, &r0, &r1, &main_blocks};
-  return hipLaunchKernel(k, dim3(grid), dim3(block), args, lds, s);
+  // kShiftGroups row groups per block amortise the per-block gamma/beta set-up
+  const void* k = shape_kernel<ShiftSel<IO, RES, GELU>::template K>(i);
+  const int sgrid = (int)((groups + kShiftGroups - 1) / kShiftGroups);
+  return hipLaunchKernel(k, dim3(sgrid), dim3(block), args, 0, s);
 }
 
 template <class IO>

@@ -89,6 +89,14 @@ __device__ __forceinline__ float gelu_tanh_f32(float u) {
   return u * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Workgroup barrier for LDS traffic only: wait for this wave's LDS operations,
+// then s_barrier.  Unlike __syncthreads() it does not wait for outstanding
+// global stores (a workgroup release fence would add s_waitcnt vmcnt(0)),
+// which lets the streaming stores of one row overlap the next row's work.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Sum of v over a group of LANES consecutive lanes (LANES a power of two).
 // Within a wave: xor butterfly.  Because a + b == b + a exactly in IEEE
 // arithmetic, both partners of every exchange compute the same value, so all
@@ -109,7 +117,7 @@ __device__ __forceinline__ T group_sum(T v, T* lds) {
     constexpr int kWaves = LANES / 64;
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) lds[wave] = v;
-    __syncthreads();
+    lds_barrier();
     const int first = (threadIdx.x / LANES) * kWaves;
     T s = lds[first];
 #pragma unroll
