@@ -259,21 +259,6 @@ int persistent_grid(const void* kernel, int block, int64_t groups, size_t lds) {
   return (int)g;
 }
 
-hipError_t allow_dynamic_lds(const void* kernel, size_t bytes) {
-  if (bytes <= 65536) return hipSuccess;
-  static std::mutex mu;
-  static std::map<std::pair<int, const void*>, size_t> done;
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  std::lock_guard<std::mutex> lock(mu);
-  size_t& have = done[{dev, kernel}];
-  if (have >= bytes) return hipSuccess;
-  const hipError_t e =
-      hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) have = bytes;
-  return e;
-}
-
 }  // namespace mbp
 
 // ---------------------------------------------------------------- C ABI

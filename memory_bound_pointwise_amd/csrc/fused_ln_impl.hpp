@@ -80,6 +80,27 @@ __device__ __forceinline__ void set_elem(u32x4& v, int e, typename IO::elem val)
   }
 }
 
+// Element e of a vector, as stored bits.
+template <class IO>
+__device__ __forceinline__ typename IO::elem elem_bits(const u32x4& v, int e) {
+  if constexpr (IO::kVec == 8) return (typename IO::elem)(v.w[e >> 1] >> (16 * (e & 1)));
+  else return __uint_as_float(v.w[e]);
+}
+
+// Elements c0 .. c0 + V - 1 of a vector of n elements, zero past n (c0 < n):
+// clamped loads that do not depend on each other, so they issue together.
+template <class IO>
+__device__ __forceinline__ u32x4 partial_vec(const typename IO::elem* p, int c0, int n) {
+  typename IO::elem t[IO::kVec];
+#pragma unroll
+  for (int e = 0; e < IO::kVec; ++e) t[e] = p[min(c0 + e, n - 1)];
+  u32x4 r = {{0u, 0u, 0u, 0u}};
+#pragma unroll
+  for (int e = 0; e < IO::kVec; ++e)
+    if (c0 + e < n) set_elem<IO>(r, e, t[e]);
+  return r;
+}
+
 template <class Acc, bool GELU>
 __device__ __forceinline__ float finish(Acc d, Acc rstd, Acc g, Acc b) {
   const float u = (float)fma_t(d * rstd, g, b);
@@ -216,33 +237,7 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
   }
 }
 
-// ------------------------------------------------------------ rows off 16-byte boundaries
-
-// Rows that do not start on 16-byte boundaries (e.g. bf16 rows of 4095
-// elements, 8190 bytes), with any misalignment of x, residual, y, gamma and
-// beta.  The register layout and the arithmetic are those of ln_vec_kernel;
-// only the way vectors reach and leave the registers differs.
-//
-// Window space: window q of a tensor is bytes [16q, 16q + 16) above the
-// 16-byte boundary at or below its base pointer.  Loads: the row vector in
-// slot j (row bytes [16j, 16j + 16)) is the byte funnel of windows j and j+1
-// of the row at the row's byte offset in its first window.  Every slot loads
-// its window j; window j+1 is the window of the neighbouring slot, fetched
-// with a DPP lane shift, except for the one slot per wave (or row group)
-// whose neighbour sits in another wave, which loads it itself.  Stores: output
-// window j is the funnel of output vectors j-1 and j at the output row's
-// offset; vector j-1 comes from the neighbouring lane the same way, and the
-// two windows per wave whose halves sit in different waves are written half
-// by half with element stores.  Windows shared with the neighbouring rows (the
-// first and last of a row) are written element by element, so no byte of
-// another row is written.  A row whose first or last window reaches outside a
-// tensor (only the tensor's first and last row can) is read element by
-// element, so no byte outside the tensors is read.
-//
-// Slots: for groups of at least a wave, wave w of the group holds the slots
-// w*64*VPL + k*64 + l (round k, wave lane l), so each wave covers one
-// contiguous stretch of the row and a load instruction 64 consecutive
-// windows.  Narrower groups use slot k*LANES + lane as ln_vec_kernel does.
+// ------------------------------------------------------------ 16-byte windows
 
 // Geometry of one tensor's window space.  The base is derived from the
 // tensor pointer by pointer arithmetic (never through an integer), so the
@@ -326,6 +321,317 @@ __device__ __forceinline__ u32x4 funnel(const u32x4& lo, const uint32_t* hi, int
   return r;
 }
 
+// ------------------------------------------------------------ rows congruent modulo 16 bytes
+
+// Rows off 16-byte boundaries whose x, residual and y share one alignment
+// (the usual case: e.g. bf16 rows of 4095 elements in freshly allocated
+// tensors).  The byte offset of row r in its first 16-byte window is then
+// (base + r * row_bytes) mod 16, which repeats with period P = 16 / gcd(16,
+// row_bytes) rows; the rows with one offset form a class.  A block serves
+// one class, so the offset s (in elements) is uniform over the block, and the
+// row is processed directly in window space: slot j of the ln_vec_kernel
+// layout holds window j of the row, element e of it being column
+// V*j + e - s.  gamma and beta are gathered once per block into that layout.
+//
+// A row spans nvec = ceil(cols / V) windows, or one more when its offset
+// pushes its tail into window nvec.  In that case the tail (fewer than s
+// elements) is moved into the unused head of slot 0 (whose first s elements
+// belong to the previous row), so VPL is the same as for aligned rows.  Only
+// slot 0 and slot nvec - 1 hold elements outside the row: they are zeroed in
+// the packed inputs, their (0 - mean)^2 terms are taken out of the variance
+// sum again, and their windows (and the folded one) are stored element by
+// element.
+//
+// The host passes [r_lo, r_hi), the rows whose windows lie inside the
+// tensors; the rest (at most the first and last few rows: rows starting
+// within 16 bytes of a tensor's unaligned start or end) take the first
+// `edge_blocks` blocks of the grid, which handle them element by element.
+template <class IO, int LANES, int VPL, bool RES, bool GELU>
+__global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
+    const typename IO::elem* x, const typename IO::elem* res,
+    const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
+    typename IO::elem* y, int64_t rows, int cols, double eps_d, int period, int64_t r_lo,
+    int64_t r_hi, int edge_blocks) {
+  typedef typename IO::elem E;
+  typedef typename Types<IO, RES>::acc Acc;
+  typedef typename Types<IO, RES>::val Val;
+  constexpr int ES = (int)sizeof(E);
+  constexpr int V = IO::kVec;
+  constexpr int BLOCK = block_for(LANES);
+  constexpr int RPB = BLOCK / LANES;
+  constexpr bool kInPlace = std::is_same<Acc, Val>::value;
+  __shared__ Acc red[2][BLOCK / 64];
+
+  const int lane = threadIdx.x % LANES;
+  const int sub = threadIdx.x / LANES;
+  const Acc eps = (Acc)eps_d;
+
+  if ((int)blockIdx.x < edge_blocks) {
+    // edge rows: lane l takes columns l, l + LANES, ...; three passes over
+    // the row (sum, squared deviations, output), the later ones from cache
+    const int64_t i = (int64_t)blockIdx.x * RPB + sub;
+    const int64_t n_edge = r_lo + (rows - r_hi);
+    const bool live = i < n_edge;
+    const int64_t row = !live ? 0 : (i < r_lo ? i : r_hi + (i - r_lo));
+    const int64_t e0 = row * (int64_t)cols;
+    auto val = [&](int c) -> Val {
+      Val t = (Val)IO::load1(x, e0 + c);
+      if constexpr (RES) t += (Val)IO::load1(res, e0 + c);
+      return t;
+    };
+    Acc sum = 0;
+    for (int c = lane; c < cols; c += LANES) sum += (Acc)val(c);
+    const Acc mean = group_sum<LANES, BLOCK>(sum, red[0]) / (Acc)cols;
+    Acc m2 = 0;
+    for (int c = lane; c < cols; c += LANES) {
+      const Acc d = (Acc)val(c) - mean;
+      m2 = fma_t(d, d, m2);
+    }
+    const Acc rstd = inv_sqrt(group_sum<LANES, BLOCK>(m2, red[1]) / (Acc)cols + eps);
+    if (live)
+      for (int c = lane; c < cols; c += LANES)
+        IO::store1(y, e0 + c,
+                   finish<Acc, GELU>((Acc)val(c) - mean, rstd, (Acc)IO::load1(gamma, c), (Acc)IO::load1(beta, c)));
+    return;
+  }
+
+  const int bid = (int)blockIdx.x - edge_blocks;
+  const int cls = bid % period;
+  const int64_t blk = bid / period;
+  const int64_t nblk = ((int)gridDim.x - edge_blocks) / period;
+  const int64_t first = r_lo + cls;  // first row of the class
+  if (first >= r_hi) return;         // an empty class: the whole block leaves
+  const int64_t crows = (r_hi - 1 - first) / period + 1;
+  const int64_t cgroups = (crows + RPB - 1) / RPB;
+  const int64_t last_row = first + (int64_t)period * (crows - 1);
+
+  const int mb = (int)(reinterpret_cast<uintptr_t>(x) & 15);
+  const int sb = (int)((mb + (int64_t)ES * first * cols) & 15);  // the class's byte offset
+  const int s = sb / ES;
+  const int nvec = (cols + V - 1) / V;
+  const int nv = (sb + ES * cols + 15) >> 4;
+  const bool fold = nv > nvec;
+  const int klast = (nvec - 1) / LANES;
+
+  // column of element e of slot j (-1: outside the row)
+  auto col_of = [&](int j, int e) -> int {
+    if (j == 0 && e < s) return fold ? V * nvec + e - s : -1;
+    return V * j + e - s;
+  };
+  // Elements of slot 0 and slot nvec - 1 outside the row, as per-word masks
+  // of the packed words (all ones: inside) and as counts.
+  uint32_t mk0[4], mkl[4];
+  int n0 = 0, nl = 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) mk0[t] = mkl[t] = 0u;
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    const int c0 = col_of(0, e), cl = col_of(nvec - 1, e);
+    const uint32_t bits = ES == 2 ? (0xffffu << (16 * (e & 1))) : 0xffffffffu;
+    if (c0 >= 0 && c0 < cols) mk0[e * ES / 4] |= bits; else ++n0;
+    if (cl >= 0 && cl < cols) mkl[e * ES / 4] |= bits; else ++nl;
+  }
+
+  // gamma / beta in the class's window layout: slot j holds columns
+  // V*j - s + e, i.e. bytes [16 - sb, 32 - sb) of vectors j-1 || j; slot 0
+  // takes vector nvec - 1 as its "j-1", which yields exactly the folded tail
+  // columns V*nvec - s + e, e < s.  A partial last vector is read element by
+  // element (zero past the end), so no byte past gamma or beta is read.
+  u32x4 gp[VPL], bp[VPL];
+  if (((reinterpret_cast<uintptr_t>(gamma) | reinterpret_cast<uintptr_t>(beta)) & 15) == 0) {
+    auto vec_at = [&](const E* p, int jv) -> u32x4 {
+      if (V * jv + V <= cols) return load_vec<IO>(p, jv);
+      return partial_vec<IO>(p, V * jv, cols);
+    };
+    const int q = ((16 - sb) & 15) >> 2, bb = (16 - sb) & 3;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int jc = min(lane + k * LANES, nvec - 1);
+      const int jp = jc == 0 ? nvec - 1 : jc - 1;
+      const u32x4 ga = vec_at(gamma, jp), gb = vec_at(gamma, jc);
+      const u32x4 ba = vec_at(beta, jp), bv = vec_at(beta, jc);
+      switch (sb == 0 ? -1 : q) {
+        case -1: gp[k] = gb; bp[k] = bv; break;
+        case 0: gp[k] = funnel<ES, 0>(ga, gb.w, bb); bp[k] = funnel<ES, 0>(ba, bv.w, bb); break;
+        case 1: gp[k] = funnel<ES, 1>(ga, gb.w, bb); bp[k] = funnel<ES, 1>(ba, bv.w, bb); break;
+        case 2: gp[k] = funnel<ES, 2>(ga, gb.w, bb); bp[k] = funnel<ES, 2>(ba, bv.w, bb); break;
+        default: gp[k] = funnel<ES, 3>(ga, gb.w, bb); bp[k] = funnel<ES, 3>(ba, bv.w, bb); break;
+      }
+    }
+  } else {
+    // element gather; clamped unconditional loads, so they issue together
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int j = lane + k * LANES;
+      u32x4 gv = {{0u, 0u, 0u, 0u}}, bv = {{0u, 0u, 0u, 0u}};
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const int c = col_of(j, e);
+        const int cc = min(max(c, 0), cols - 1);
+        const E ge = gamma[cc], be = beta[cc];
+        if (j < nvec && c >= 0 && c < cols) {
+          set_elem<IO>(gv, e, ge);
+          set_elem<IO>(bv, e, be);
+        }
+      }
+      gp[k] = gv;
+      bp[k] = bv;
+    }
+  }
+
+  for (int64_t grp = blk; grp < cgroups; grp += nblk) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      opaque(gp[k]);
+      opaque(bp[k]);
+    }
+    const int64_t row = first + (int64_t)period * (grp * RPB + sub);
+    const bool live = row <= last_row;
+    const int64_t e0 = (live ? row : last_row) * (int64_t)cols;
+    const int64_t q0 = (mb + (int64_t)ES * e0) >> 4;
+
+    // every window of the row lies inside the tensors (rows in [r_lo, r_hi))
+    const u32x4* sx = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(x) - mb) + q0;
+    const u32x4* sr = RES ? reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(res) - mb) + q0
+                          : nullptr;
+    u32x4 xw[VPL], rw[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int j = min(lane + k * LANES, nvec - 1);
+      xw[k] = load_nt(sx + j);
+      if constexpr (RES) rw[k] = load_nt(sr + j);
+    }
+    if (fold && lane == 0) {  // slot 0 takes the row's last window into its bytes [0, sb)
+      int sbv = sb;
+      opaque(sbv);
+      const u32x4 xf = load_nt(sx + nvec);
+      u32x4 rf = {{0u, 0u, 0u, 0u}};
+      if constexpr (RES) rf = load_nt(sr + nvec);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int sh = min(max(sbv - 4 * t, 0), 4);  // bytes of word t taken from the tail
+        const uint32_t keep = sh == 4 ? 0u : 0xffffffffu << (8 * sh);
+        xw[0].w[t] = (xw[0].w[t] & keep) | (xf.w[t] & ~keep);
+        if constexpr (RES) rw[0].w[t] = (rw[0].w[t] & keep) | (rf.w[t] & ~keep);
+      }
+    }
+    // zero the elements outside the row (slot 0 and slot nvec - 1 only)
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      if (k != 0 && k != klast) continue;
+      const int j = lane + k * LANES;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t m = (j == 0 ? mk0[t] : 0xffffffffu) & (j == nvec - 1 ? mkl[t] : 0xffffffffu);
+        xw[k].w[t] &= m;
+        if constexpr (RES) rw[k].w[t] &= m;
+      }
+    }
+
+    Val v[VPL][V];
+    Acc sum = 0;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int j = lane + k * LANES;
+      Acc part = 0;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        Val t = (Val)IO::get(xw[k], e);
+        if constexpr (RES) t += (Val)IO::get(rw[k], e);
+        v[k][e] = t;
+        part += (Acc)t;
+      }
+      if (j < nvec) sum += part;
+    }
+    const Acc mean = group_sum<LANES, BLOCK>(sum, red[0]) / (Acc)cols;
+
+    Acc m2 = 0;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int j = lane + k * LANES;
+      Acc part = 0;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const Acc d = (Acc)v[k][e] - mean;
+        if constexpr (kInPlace) v[k][e] = d;
+        part = fma_t(d, d, part);
+      }
+      if (k == 0 || k == klast) {
+        // a zeroed element contributed (0 - mean)^2 to this slot's
+        // eight-term partial; take it out again
+        const int nout = (j == 0 ? n0 : 0) + (j == nvec - 1 && j != 0 ? nl : 0);
+        part -= (Acc)nout * (mean * mean);
+      }
+      if (j < nvec) m2 += part;
+    }
+    const Acc rstd = inv_sqrt(group_sum<LANES, BLOCK>(m2, red[1]) / (Acc)cols + eps);
+
+    if (!live) continue;
+    u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(y) - mb) + q0;
+    E* yrow = y + row * (int64_t)cols;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int j = lane + k * LANES;
+      if (j >= nvec) continue;
+      float o[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const Acc d = kInPlace ? (Acc)v[k][e] : (Acc)v[k][e] - mean;
+        o[e] = finish<Acc, GELU>(d, rstd, (Acc)IO::get(gp[k], e), (Acc)IO::get(bp[k], e));
+      }
+      const u32x4 ov = pack_vec<IO>(o);
+      // window j holds columns V*j - s + e; slot 0 and slot nvec - 1 may
+      // share their window with a neighbouring row: store only [ea, eb)
+      int ea = j == 0 ? s : 0;
+      int eb = min(V, cols - (V * j - s));
+      if (ea == 0 && eb == V) {
+        store_nt(dst + j, ov);
+      } else {
+        opaque(ea);  // keep the per-element tests in this branch
+        opaque(eb);
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+          if (e >= ea && e < eb) yrow[V * j - s + e] = elem_bits<IO>(ov, e);
+        if (fold && j == 0) {  // the folded tail: columns V*nvec - s + e
+          int fb = cols - (V * nvec - s);
+          opaque(fb);
+#pragma unroll
+          for (int e = 0; e < V; ++e)
+            if (e < fb) yrow[V * nvec - s + e] = elem_bits<IO>(ov, e);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ rows off 16-byte boundaries
+
+// Rows that do not start on 16-byte boundaries (e.g. bf16 rows of 4095
+// elements, 8190 bytes), with any misalignment of x, residual, y, gamma and
+// beta.  The register layout and the arithmetic are those of ln_vec_kernel;
+// only the way vectors reach and leave the registers differs.
+//
+// Window space: window q of a tensor is bytes [16q, 16q + 16) above the
+// 16-byte boundary at or below its base pointer.  Loads: the row vector in
+// slot j (row bytes [16j, 16j + 16)) is the byte funnel of windows j and j+1
+// of the row at the row's byte offset in its first window.  Every slot loads
+// its window j; window j+1 is the window of the neighbouring slot, fetched
+// with a DPP lane shift, except for the one slot per wave (or row group)
+// whose neighbour sits in another wave, which loads it itself.  Stores: output
+// window j is the funnel of output vectors j-1 and j at the output row's
+// offset; vector j-1 comes from the neighbouring lane the same way, and the
+// two windows per wave whose halves sit in different waves are written half
+// by half with element stores.  Windows shared with the neighbouring rows (the
+// first and last of a row) are written element by element, so no byte of
+// another row is written.  A row whose first or last window reaches outside a
+// tensor (only the tensor's first and last row can) is read element by
+// element, so no byte outside the tensors is read.
+//
+// Slots: for groups of at least a wave, wave w of the group holds the slots
+// w*64*VPL + k*64 + l (round k, wave lane l), so each wave covers one
+// contiguous stretch of the row and a load instruction 64 consecutive
+// windows.  Narrower groups use slot k*LANES + lane as ln_vec_kernel does.
+
 // Row vectors of all rounds from windows c[0..VPL] (c[VPL]: the slot after
 // the last round, needed only where next_word reads it) at byte offset sb.
 // The word shift is uniform over the row; for groups of at least a wave it is
@@ -405,12 +711,8 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_shift_kernel(
       gv = load_vec<IO>(gamma, j);
       bv = load_vec<IO>(beta, j);
     } else if (j < nvec) {
-#pragma unroll
-      for (int e = 0; e < V; ++e)
-        if (V * j + e < cols) {
-          set_elem<IO>(gv, e, gamma[V * j + e]);
-          set_elem<IO>(bv, e, beta[V * j + e]);
-        }
+      gv = partial_vec<IO>(gamma, V * j, cols);
+      bv = partial_vec<IO>(beta, V * j, cols);
     }
     gp[k] = gv;
     bp[k] = bv;
@@ -614,6 +916,13 @@ struct VecSel {
   };
 };
 template <class IO, bool RES, bool GELU>
+struct ClassSel {
+  template <int L, int P>
+  struct K {
+    static const void* ptr() { return reinterpret_cast<const void*>(&ln_class_kernel<IO, L, P, RES, GELU>); }
+  };
+};
+template <class IO, bool RES, bool GELU>
 struct ShiftSel {
   template <int L, int P>
   struct K {
@@ -622,6 +931,7 @@ struct ShiftSel {
 };
 constexpr int64_t kMaxGrid = 1 << 30;
 constexpr int64_t kShiftGroups = 4;
+constexpr int64_t kClassGroups = 4;
 
 template <class IO, bool RES, bool GELU>
 hipError_t launch_flags(const void* x, const void* res, const void* gamma, const void* beta,
@@ -641,6 +951,34 @@ hipError_t launch_flags(const void* x, const void* res, const void* gamma, const
   if (aligned) {
     const void* k = shape_kernel<VecSel<IO, RES, GELU>::template K>(i);
     return hipLaunchKernel(k, dim3(grid), dim3(block), args, 0, s);
+  }
+  const uintptr_t ax = reinterpret_cast<uintptr_t>(x);
+  const bool congruent = ((ax ^ reinterpret_cast<uintptr_t>(y)) & 15) == 0 &&
+                         (!res || ((ax ^ reinterpret_cast<uintptr_t>(res)) & 15) == 0);
+  if (congruent) {
+    // Rows whose windows lie inside the tensors: [r_lo, r_hi).  A row
+    // starting fewer than 16 - (x mod 16) bytes past an unaligned start, or
+    // ending fewer than (end mod 16) bytes before an unaligned end, has a
+    // window that reaches outside.
+    const int64_t rb = (int64_t)sizeof(typename IO::elem) * cols;
+    const int64_t mb = (int64_t)(ax & 15);
+    const int64_t me = (int64_t)((ax + (uintptr_t)(rb * rows)) & 15);
+    int64_t r_lo = mb == 0 ? 0 : (16 - mb + rb - 1) / rb;
+    int64_t r_hi = me == 0 ? rows : rows - (me + rb - 1) / rb;
+    if (r_lo > rows) r_lo = rows;
+    if (r_hi < r_lo) r_hi = r_lo;
+    const int64_t n_edge = r_lo + (rows - r_hi);
+    const int edge_blocks = (int)((n_edge + rpb - 1) / rpb);
+    // P classes of rows with one offset; each block takes up to kClassGroups
+    // row groups of its class.
+    int period = 16;
+    while (period > 1 && (rb * (period / 2)) % 16 == 0) period /= 2;
+    const int64_t cgroups = ((r_hi - r_lo + period - 1) / period + rpb - 1) / rpb;
+    int64_t nblk = (cgroups + kClassGroups - 1) / kClassGroups;
+    if (nblk > kMaxGrid / period) nblk = kMaxGrid / period;
+    const void* k = shape_kernel<ClassSel<IO, RES, GELU>::template K>(i);
+    void* cargs[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &eps, &period, &r_lo, &r_hi, (void*)&edge_blocks};
+    return hipLaunchKernel(k, dim3((unsigned)(edge_blocks + period * nblk)), dim3(block), cargs, 0, s);
   }
   // kShiftGroups row groups per block amortise the per-block gamma/beta set-up
   const void* k = shape_kernel<ShiftSel<IO, RES, GELU>::template K>(i);

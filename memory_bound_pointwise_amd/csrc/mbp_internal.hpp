@@ -19,9 +19,6 @@ const DeviceInfo& device_info();
 // that can be resident at once (occupancy with `lds` bytes of dynamic LDS x CUs).
 int persistent_grid(const void* kernel, int block, int64_t groups, size_t lds);
 
-// Let `kernel` launch with `bytes` of dynamic LDS (needed above 64 KiB).
-hipError_t allow_dynamic_lds(const void* kernel, size_t bytes);
-
 hipError_t launch_chain(const float* x, const float* b1, const float* b2, float* y, int64_t n,
                         double scale, hipStream_t s);
 hipError_t launch_row_mean(const float* x, const float* bias, const float* gamma,

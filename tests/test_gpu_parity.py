@@ -223,6 +223,46 @@ def test_ln_common_misalignment(mbp, dtype_name, cols, shift, rows):
     assert (host[:shift] == 3.0).all() and (host[shift + x.numel():] == 3.0).all(), "wrote outside y"
 
 
+@pytest.mark.parametrize("dtype_name,cols,offs,rows", [
+    ("addln_gelu_16384x8192_bf16", 4095, (1, 2, 3, 0, 0), 9),
+    ("addln_gelu_16384x8192_bf16", 4096, (0, 1, 0, 0, 0), 5),
+    ("addln_gelu_16384x8192_bf16", 1023, (3, 0, 7, 1, 2), 17),
+    ("addln_gelu_16384x8192_bf16", 7, (1, 3, 0, 0, 0), 40),
+    ("addln_gelu_16384x8192_bf16", 33, (2, 5, 1, 0, 0), 33),
+    ("addln_gelu_16384x8192_bf16", 300, (0, 6, 6, 0, 0), 21),
+    ("addln_gelu_16384x8192_bf16", 12288, (0, 0, 1, 0, 0), 3),
+    ("addln_gelu_16384x8192_bf16", 8192, (0, 0, 0, 1, 3), 9),
+    ("addln_gelu_16384x8192_bf16", 4095, (2, 2, 2, 5, 1), 11),
+    ("ln_8192x4096_f32", 4093, (1, 2, 0, 0, 0), 9),
+    ("ln_8192x4096_f32", 5, (0, 1, 2, 0, 0), 40),
+    ("ln_8192x4096_f32", 1024, (0, 0, 3, 1, 1), 9),
+    ("ln_8192x4096_f32", 130, (3, 1, 2, 2, 0), 19)])
+def test_ln_independent_misalignment(mbp, dtype_name, cols, offs, rows):
+    """x, residual, y, gamma and beta each `offs` elements past a 16-byte
+    boundary.  Different offsets of x, residual and y take the lane-shift
+    path; equal ones the per-class window path, here with gamma and beta off
+    their boundaries."""
+    w, d, act = _ln_case(dtype_name, rows, cols, residual=True)
+    ref = _ln_ref(d, act)
+    chk = check_bf16 if w.dtype == "bf16" else check_f32
+
+    def place(a, off, fill=0.0):
+        t = to_dev(a)
+        buf = torch.full((t.numel() + 16,), fill, dtype=t.dtype, device="cuda")
+        v = buf[off:off + t.numel()].view(t.shape)
+        v.copy_(t)
+        return v
+
+    x, r = place(d["x"], offs[0]), place(d["residual"], offs[1])
+    g, b = place(d["gamma"], offs[3]), place(d["beta"], offs[4])
+    yb = torch.full((x.numel() + 16,), 3.0, dtype=x.dtype, device="cuda")
+    y = yb[offs[2]:offs[2] + x.numel()].view(x.shape)
+    mbp.fused_add_layernorm_gelu(x, r, g, b, act=act, out=y)
+    chk(to_host(y), ref, f"offsets {offs}")
+    host = to_host(yb).astype(np.float64) if yb.dtype != torch.bfloat16 else as_f64(to_host(yb))
+    assert (host[:offs[2]] == 3.0).all() and (host[offs[2] + x.numel():] == 3.0).all(), "wrote outside y"
+
+
 def test_ln_constant_rows_give_beta(mbp):
     for name in ("ln_8192x4096_f32", "addln_gelu_16384x8192_bf16"):
         w, d, _ = _ln_case(name, 4, 4096, residual=False)
