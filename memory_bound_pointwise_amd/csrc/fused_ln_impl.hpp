@@ -344,7 +344,7 @@ __device__ __forceinline__ u32x4 funnel(const u32x4& lo, const uint32_t* hi, int
 //
 // The host passes [r_lo, r_hi), the rows whose windows lie inside the
 // tensors; the rest (at most the first and last few rows: rows starting
-// within 16 bytes of a tensor's unaligned start or end) take the first
+// within 16 bytes of a tensor's unaligned start or end) take the last
 // `edge_blocks` blocks of the grid, which handle them element by element.
 template <class IO, int LANES, int VPL, bool RES, bool GELU>
 __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
@@ -366,10 +366,11 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
   const int sub = threadIdx.x / LANES;
   const Acc eps = (Acc)eps_d;
 
-  if ((int)blockIdx.x < edge_blocks) {
+  const int nb = (int)gridDim.x - edge_blocks;  // class blocks
+  if ((int)blockIdx.x >= nb) {
     // edge rows: lane l takes columns l, l + LANES, ...; three passes over
     // the row (sum, squared deviations, output), the later ones from cache
-    const int64_t i = (int64_t)blockIdx.x * RPB + sub;
+    const int64_t i = (int64_t)((int)blockIdx.x - nb) * RPB + sub;
     const int64_t n_edge = r_lo + (rows - r_hi);
     const bool live = i < n_edge;
     const int64_t row = !live ? 0 : (i < r_lo ? i : r_hi + (i - r_lo));
@@ -395,15 +396,20 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
     return;
   }
 
-  const int bid = (int)blockIdx.x - edge_blocks;
-  const int cls = bid % period;
-  const int64_t blk = bid / period;
-  const int64_t nblk = ((int)gridDim.x - edge_blocks) / period;
+  // period: a power of two (1 .. 16)
+  const int lp = __builtin_ctz((unsigned)period);
+  // Consecutive blocks take the classes of consecutive rows, so the whole
+  // grid sweeps the tensors front to back together (measured faster than
+  // giving each XCD a contiguous run of rows).
+  const int bid = (int)blockIdx.x;
+  const int cls = bid & (period - 1);
+  const int64_t blk = bid >> lp;
+  const int64_t nblk = nb >> lp;
   const int64_t first = r_lo + cls;  // first row of the class
   if (first >= r_hi) return;         // an empty class: the whole block leaves
-  const int64_t crows = (r_hi - 1 - first) / period + 1;
+  const int64_t crows = ((r_hi - 1 - first) >> lp) + 1;
   const int64_t cgroups = (crows + RPB - 1) / RPB;
-  const int64_t last_row = first + (int64_t)period * (crows - 1);
+  const int64_t last_row = first + ((crows - 1) << lp);
 
   const int mb = (int)(reinterpret_cast<uintptr_t>(x) & 15);
   const int sb = (int)((mb + (int64_t)ES * first * cols) & 15);  // the class's byte offset
@@ -418,38 +424,61 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
     if (j == 0 && e < s) return fold ? V * nvec + e - s : -1;
     return V * j + e - s;
   };
-  // Elements of slot 0 and slot nvec - 1 outside the row, as per-word masks
-  // of the packed words (all ones: inside) and as counts.
+  // Elements of slot 0 and slot nvec - 1 inside the row (bit e): slot 0
+  // holds columns e - s for e in [s, min(V, s + cols)) and, folded, the tail
+  // columns for e < cols - (V*nvec - s); slot nvec - 1 (when not slot 0)
+  // columns up to cols - 1, i.e. e < cols - V*(nvec - 1) + s.
+  auto low = [](int n) -> uint32_t { return n <= 0 ? 0u : (1u << n) - 1u; };
+  const uint32_t in0 = (low(min(V, s + cols)) & ~low(s)) | (fold ? low(cols - (V * nvec - s)) : 0u);
+  const uint32_t inl = nvec == 1 ? in0 : low(min(V, cols - V * (nvec - 1) + s));
+  const int n0 = V - __builtin_popcount(in0), nl = V - __builtin_popcount(inl);
+  // the same as masks of the packed words (all ones: inside)
   uint32_t mk0[4], mkl[4];
-  int n0 = 0, nl = 0;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) mk0[t] = mkl[t] = 0u;
-#pragma unroll
-  for (int e = 0; e < V; ++e) {
-    const int c0 = col_of(0, e), cl = col_of(nvec - 1, e);
-    const uint32_t bits = ES == 2 ? (0xffffu << (16 * (e & 1))) : 0xffffffffu;
-    if (c0 >= 0 && c0 < cols) mk0[e * ES / 4] |= bits; else ++n0;
-    if (cl >= 0 && cl < cols) mkl[e * ES / 4] |= bits; else ++nl;
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (ES == 2) {
+      mk0[t] = (((in0 >> (2 * t)) & 1u) ? 0xffffu : 0u) | (((in0 >> (2 * t + 1)) & 1u) ? 0xffff0000u : 0u);
+      mkl[t] = (((inl >> (2 * t)) & 1u) ? 0xffffu : 0u) | (((inl >> (2 * t + 1)) & 1u) ? 0xffff0000u : 0u);
+    } else {
+      mk0[t] = ((in0 >> t) & 1u) ? 0xffffffffu : 0u;
+      mkl[t] = ((inl >> t) & 1u) ? 0xffffffffu : 0u;
+    }
   }
 
   // gamma / beta in the class's window layout: slot j holds columns
   // V*j - s + e, i.e. bytes [16 - sb, 32 - sb) of vectors j-1 || j; slot 0
   // takes vector nvec - 1 as its "j-1", which yields exactly the folded tail
-  // columns V*nvec - s + e, e < s.  A partial last vector is read element by
-  // element (zero past the end), so no byte past gamma or beta is read.
+  // columns V*nvec - s + e, e < s.  Whole vectors are loaded with clamped
+  // indices; a partial last vector is read once element by element (zero
+  // past the end, no byte past gamma or beta) and selected where needed.
   u32x4 gp[VPL], bp[VPL];
   if (((reinterpret_cast<uintptr_t>(gamma) | reinterpret_cast<uintptr_t>(beta)) & 15) == 0) {
-    auto vec_at = [&](const E* p, int jv) -> u32x4 {
-      if (V * jv + V <= cols) return load_vec<IO>(p, jv);
-      return partial_vec<IO>(p, V * jv, cols);
-    };
+    const bool partial = (cols % V) != 0;
+    const int jfull = partial ? nvec - 2 : nvec - 1;  // last whole vector (-1: none)
+    u32x4 pg = {{0u, 0u, 0u, 0u}}, pb = {{0u, 0u, 0u, 0u}};
+    if (partial) {
+      pg = partial_vec<IO>(gamma, V * (nvec - 1), cols);
+      pb = partial_vec<IO>(beta, V * (nvec - 1), cols);
+    }
     const int q = ((16 - sb) & 15) >> 2, bb = (16 - sb) & 3;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       const int jc = min(lane + k * LANES, nvec - 1);
       const int jp = jc == 0 ? nvec - 1 : jc - 1;
-      const u32x4 ga = vec_at(gamma, jp), gb = vec_at(gamma, jc);
-      const u32x4 ba = vec_at(beta, jp), bv = vec_at(beta, jc);
+      u32x4 ga = pg, gb = pg, ba = pb, bv = pb;
+      if (jfull >= 0) {
+        ga = load_vec<IO>(gamma, min(jp, jfull));
+        gb = load_vec<IO>(gamma, min(jc, jfull));
+        ba = load_vec<IO>(beta, min(jp, jfull));
+        bv = load_vec<IO>(beta, min(jc, jfull));
+        if (k == 0 || k == klast) {  // the partial vector appears only in these rounds
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (jp > jfull) { ga.w[t] = pg.w[t]; ba.w[t] = pb.w[t]; }
+            if (jc > jfull) { gb.w[t] = pg.w[t]; bv.w[t] = pb.w[t]; }
+          }
+        }
+      }
       switch (sb == 0 ? -1 : q) {
         case -1: gp[k] = gb; bp[k] = bv; break;
         case 0: gp[k] = funnel<ES, 0>(ga, gb.w, bb); bp[k] = funnel<ES, 0>(ba, bv.w, bb); break;
@@ -975,7 +1004,7 @@ hipError_t launch_flags(const void* x, const void* res, const void* gamma, const
     while (period > 1 && (rb * (period / 2)) % 16 == 0) period /= 2;
     const int64_t cgroups = ((r_hi - r_lo + period - 1) / period + rpb - 1) / rpb;
     int64_t nblk = (cgroups + kClassGroups - 1) / kClassGroups;
-    if (nblk > kMaxGrid / period) nblk = kMaxGrid / period;
+    if (nblk > kMaxGrid / 16) nblk = kMaxGrid / 16;
     const void* k = shape_kernel<ClassSel<IO, RES, GELU>::template K>(i);
     void* cargs[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &eps, &period, &r_lo, &r_hi, (void*)&edge_blocks};
     return hipLaunchKernel(k, dim3((unsigned)(edge_blocks + period * nblk)), dim3(block), cargs, 0, s);
