@@ -11,12 +11,16 @@ kernel finds its inputs evicted from the 256 MB Infinity Cache by the others
 Printed: one JSON line with
   value        whole-step effective bandwidth: compulsory bytes of all seven
                calls / wall time per step (GB/s, 1e9 B/s);
-  per_workload per kernel: mean/median duration from HIP events on the launch
-               stream (a pass of K steps before the timed region, every call
-               bracketed), effective GB/s, fraction of 8 TB/s, the unfused
-               variant's time (all its launches) and the speedup;
-  roofline     the dominant kernel (largest time per step), its duration from
-               HIP events around it inside the timed region, against 8 TB/s;
+  per_workload per kernel: time per call from batches of N back-to-back calls
+               between two HIP events on the launch stream (N such that a
+               batch takes about 1 ms; median, min and p90 over the batches),
+               the calls rotating over B copies of the inputs and outputs with
+               B x working set >= 1 GiB so every call starts cold; effective
+               GB/s, fraction of 8 TB/s; the unfused variant timed the same way
+               (all its launches per call) and the speedup;
+  roofline     the dominant kernel (largest time per call), its duration from
+               HIP events around each of its calls inside the timed region,
+               against 8 TB/s;
   cpu_baseline the CPU oracle timed on a bounded sample of the same workloads.
 
 Other modes (for rocprofv3 counter runs): --only NAME runs just one workload's
@@ -45,7 +49,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--unfused-reps", type=int, default=20)
+    p.add_argument("--unfused-reps", type=int, default=20, help="batches for the unfused timing (0: skip)")
+    p.add_argument("--batches", type=int, default=20, help="batches per workload for the per-call times")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=2,
                    help="the oracle runs on 1/K of each workload's rows")
@@ -121,47 +126,55 @@ def main():
         names = [args.unfused_only]
     wl = [W.BY_NAME[n] for n in names]
 
-    # ---- inputs resident in HBM
+    # ---- inputs resident in HBM: B copies per workload (B x working set >= 1 GiB)
+    def n_sets(w):
+        if args.only or args.unfused_only:
+            return 1
+        return max(1, min(128, -(-(1 << 30) // w.compulsory_bytes)))
+
+    def build(w, d):
+        """(fused call, unfused call) on fresh device copies of the inputs."""
+        if w.kind == "chain":
+            x, b1, b2 = (to_dev(d[k]) for k in ("x", "b1", "b2"))
+            y, uy = torch.empty_like(x), torch.empty_like(x)
+            s = w.params["scale"]
+            return (lambda: mbp.fused_pointwise_chain(x, b1, b2, s, out=y),
+                    lambda ws: mbp.unfused_pointwise_chain(x, b1, b2, s, out=uy, workspace=ws))
+        if w.kind == "row_mean":
+            x, bias, g, b = (to_dev(d[k]) for k in ("x", "bias", "gamma", "beta"))
+            y, uy = torch.empty_like(x), torch.empty_like(x)
+            al, c = w.params["alpha"], w.params["c"]
+            return (lambda: mbp.fused_row_mean_epilogue(x, bias, g, b, al, c, out=y),
+                    lambda ws: mbp.unfused_row_mean_epilogue(x, bias, g, b, al, c, out=uy, workspace=ws))
+        x, r, g, b = (to_dev(d[k]) for k in ("x", "residual", "gamma", "beta"))
+        y, uy = torch.empty_like(x), torch.empty_like(x)
+        eps, act = w.params["eps"], w.act
+        return (lambda: mbp.fused_add_layernorm_gelu(x, r, g, b, eps, act, out=y),
+                lambda ws: mbp.unfused_add_layernorm_gelu(x, r, g, b, eps, act, out=uy, workspace=ws))
+
     t_gen = time.time()
-    host, calls, ucalls, uinfo = {}, {}, {}, {}
+    host, sets, usets, uinfo = {}, {}, {}, {}
     for w in wl:
         d = W.generate(w)
         host[w.name] = d
         if w.kind == "chain":
-            x, b1, b2 = (to_dev(d[k]) for k in ("x", "b1", "b2"))
-            y = torch.empty_like(x)
-            s = w.params["scale"]
-            ws = torch.empty(mbp.workspace_bytes(mbp.OP_CHAIN, mbp.F32, 1, w.n), dtype=torch.uint8, device=dev)
-            uy = torch.empty_like(x)
-            calls[w.name] = lambda x=x, b1=b1, b2=b2, y=y, s=s: mbp.fused_pointwise_chain(x, b1, b2, s, out=y)
-            ucalls[w.name] = lambda x=x, b1=b1, b2=b2, y=uy, s=s, ws=ws: mbp.unfused_pointwise_chain(
-                x, b1, b2, s, out=y, workspace=ws)
+            ws_bytes = mbp.workspace_bytes(mbp.OP_CHAIN, mbp.F32, 1, w.n)
             uinfo[w.name] = mbp.launches_per_call(mbp.OP_CHAIN, False)
         elif w.kind == "row_mean":
-            x, bias, g, b = (to_dev(d[k]) for k in ("x", "bias", "gamma", "beta"))
-            y = torch.empty_like(x)
-            al, c = w.params["alpha"], w.params["c"]
-            ws = torch.empty(mbp.workspace_bytes(mbp.OP_ROW_MEAN, mbp.F32, w.rows, w.cols), dtype=torch.uint8,
-                             device=dev)
-            uy = torch.empty_like(x)
-            calls[w.name] = lambda x=x, bias=bias, g=g, b=b, y=y, al=al, c=c: mbp.fused_row_mean_epilogue(
-                x, bias, g, b, al, c, out=y)
-            ucalls[w.name] = lambda x=x, bias=bias, g=g, b=b, y=uy, al=al, c=c, ws=ws: \
-                mbp.unfused_row_mean_epilogue(x, bias, g, b, al, c, out=y, workspace=ws)
+            ws_bytes = mbp.workspace_bytes(mbp.OP_ROW_MEAN, mbp.F32, w.rows, w.cols)
             uinfo[w.name] = mbp.launches_per_call(mbp.OP_ROW_MEAN, False)
         else:
-            x, r, g, b = (to_dev(d[k]) for k in ("x", "residual", "gamma", "beta"))
-            y = torch.empty_like(x)
-            eps, act = w.params["eps"], w.act
+            has_r = d.get("residual") is not None
             dcode = mbp.BF16 if w.dtype == "bf16" else mbp.F32
-            ws = torch.empty(mbp.workspace_bytes(mbp.OP_LAYERNORM, dcode, w.rows, w.cols, r is not None, act),
-                             dtype=torch.uint8, device=dev)
-            uy = torch.empty_like(x)
-            calls[w.name] = lambda x=x, r=r, g=g, b=b, y=y, eps=eps, act=act: mbp.fused_add_layernorm_gelu(
-                x, r, g, b, eps, act, out=y)
-            ucalls[w.name] = lambda x=x, r=r, g=g, b=b, y=uy, eps=eps, act=act, ws=ws: \
-                mbp.unfused_add_layernorm_gelu(x, r, g, b, eps, act, out=y, workspace=ws)
-            uinfo[w.name] = mbp.launches_per_call(mbp.OP_LAYERNORM, False, has_residual=r is not None, act=act)
+            ws_bytes = mbp.workspace_bytes(mbp.OP_LAYERNORM, dcode, w.rows, w.cols, has_r, w.act)
+            uinfo[w.name] = mbp.launches_per_call(mbp.OP_LAYERNORM, False, has_residual=has_r, act=w.act)
+        # one workspace per workload, shared by its copies (as a caching allocator would)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        pairs = [build(w, d) for _ in range(n_sets(w))]
+        sets[w.name] = [f for f, _ in pairs]
+        usets[w.name] = [lambda u=u, ws=ws: u(ws) for _, u in pairs]
+    calls = {n: sets[n][0] for n in names}
+    ucalls = {n: usets[n][0] for n in names}
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 
@@ -174,27 +187,36 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
-    def step_events(k_steps):
-        """k_steps steps with every fused call bracketed by HIP events on its
-        launch stream; returns per-workload durations in us."""
-        ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(k_steps)] for n in names}
-        for k in range(k_steps):
-            for n in names:
-                e0, e1 = ev[n][k]
-                e0.record(stream)
-                calls[n]()
-                e1.record(stream)
+    def batch_times(fns, batches):
+        """Per-call times (us) of `batches` batches of N back-to-back calls
+        rotating over `fns`, each batch between two events on the stream."""
+        for f in fns[:3]:
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(3):
+            fns[i % len(fns)]()
+        e1.record(stream)
         torch.cuda.synchronize()
-        return {n: [ev[n][k][0].elapsed_time(ev[n][k][1]) * 1e3 for k in range(k_steps)] for n in names}
+        est = e0.elapsed_time(e1) * 1e3 / 3
+        n_calls = max(1, min(2000, int(1000.0 / max(est, 1e-3))))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(batches)]
+        k = 0
+        for a, b in ev:
+            a.record(stream)
+            for _ in range(n_calls):
+                fns[k % len(fns)]()
+                k += 1
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 / n_calls for a, b in ev], n_calls
 
-    # ---- per-kernel pass: every call timed on its own (not the timed region;
-    # the events between kernels add launch gaps that the timed region avoids)
+    # ---- per-call times, one workload at a time (not the timed region)
+    fused_us, fused_n = {}, {}
     for n in names:
-        calls[n]()
-    torch.cuda.synchronize()
-    fused_us = step_events(args.steps)
-    dominant = max(names, key=lambda n: statistics.fmean(fused_us[n]))
+        fused_us[n], fused_n[n] = batch_times(sets[n], args.batches)
+    dominant = max(names, key=lambda n: statistics.median(fused_us[n]))
 
     for _ in range(args.warmup):
         for n in names:
@@ -220,23 +242,11 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     dom_us_live = [a.elapsed_time(b) * 1e3 for a, b in dom_ev]
 
-    # ---- unfused variants, same interleaved protocol
+    # ---- unfused variants, same batch protocol
     unf_us = {n: [] for n in names}
     if args.unfused_reps and not args.only:
         for n in names:
-            ucalls[n]()
-        torch.cuda.synchronize()
-        uev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.unfused_reps)] for n in names}
-        for k in range(args.unfused_reps):
-            for n in names:
-                e0, e1 = uev[n][k]
-                e0.record(stream)
-                ucalls[n]()
-                e1.record(stream)
-        torch.cuda.synchronize()
-        unf_us = {n: [uev[n][k][0].elapsed_time(uev[n][k][1]) * 1e3 for k in range(args.unfused_reps)]
-                  for n in names}
+            unf_us[n], _ = batch_times(usets[n], args.unfused_reps)
 
     per = {}
     total_bytes = 0
@@ -244,15 +254,17 @@ def main():
         n = w.name
         B = w.compulsory_bytes
         total_bytes += B
-        mean_us = statistics.fmean(fused_us[n])
         med_us = statistics.median(fused_us[n])
+        srt = sorted(fused_us[n])
         rec = {
             "compulsory_bytes": B,
-            "fused_us_mean": round(mean_us, 3),
             "fused_us_median": round(med_us, 3),
-            "fused_us_min": round(min(fused_us[n]), 3),
-            "gbps": round(B / (mean_us * 1e-6) / 1e9, 1),
-            "frac_of_peak": round(B / (mean_us * 1e-6) / 1e9 / PEAK_GBPS, 4),
+            "fused_us_min": round(srt[0], 3),
+            "fused_us_p90": round(srt[min(len(srt) - 1, int(0.9 * len(srt)))], 3),
+            "calls_per_batch": fused_n[n],
+            "input_copies": len(sets[n]),
+            "gbps": round(B / (med_us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(B / (med_us * 1e-6) / 1e9 / PEAK_GBPS, 4),
             "launches_fused": 1,
         }
         if unf_us[n]:
