@@ -9,8 +9,6 @@
 #include <cstdarg>
 #include <initializer_list>
 #include <cstdio>
-#include <map>
-#include <mutex>
 #include <string>
 #include <tuple>
 #include <utility>
@@ -213,53 +211,6 @@ mbp_status check_ln(mbp_dtype dtype, const void* x, const void* residual, const 
 
 }  // namespace
 
-// ---------------------------------------------------------------- launch helpers
-
-namespace mbp {
-
-const DeviceInfo& device_info() {
-  static std::mutex mu;
-  static std::map<int, DeviceInfo> cache;
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find(dev);
-  if (it == cache.end()) {
-    DeviceInfo info{0};
-    if (hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        info.cus <= 0)
-      info.cus = 1;
-    it = cache.emplace(dev, info).first;
-  }
-  return it->second;
-}
-
-int persistent_grid(const void* kernel, int block, int64_t groups, size_t lds) {
-  static std::mutex mu;
-  static std::map<std::tuple<int, const void*, size_t>, int> cache;
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  const auto key = std::make_tuple(dev, kernel, lds);
-  int per_cu = 0;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    auto it = cache.find(key);
-    if (it != cache.end()) per_cu = it->second;
-  }
-  if (per_cu == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, lds) != hipSuccess ||
-        per_cu <= 0)
-      per_cu = 1;
-    std::lock_guard<std::mutex> lock(mu);
-    cache[key] = per_cu;
-  }
-  const int64_t resident = (int64_t)per_cu * device_info().cus;
-  int64_t g = groups < resident ? groups : resident;
-  if (g < 1) g = 1;
-  return (int)g;
-}
-
-}  // namespace mbp
 
 // ---------------------------------------------------------------- C ABI
 

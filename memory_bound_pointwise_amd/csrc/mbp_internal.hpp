@@ -9,16 +9,6 @@
 
 namespace mbp {
 
-// Resident-wave figures of the current device (cached per device).
-struct DeviceInfo {
-  int cus;
-};
-const DeviceInfo& device_info();
-
-// Grid for a persistent row kernel: at most `groups` blocks, at most the number
-// that can be resident at once (occupancy with `lds` bytes of dynamic LDS x CUs).
-int persistent_grid(const void* kernel, int block, int64_t groups, size_t lds);
-
 hipError_t launch_chain(const float* x, const float* b1, const float* b2, float* y, int64_t n,
                         double scale, hipStream_t s);
 hipError_t launch_row_mean(const float* x, const float* bias, const float* gamma,

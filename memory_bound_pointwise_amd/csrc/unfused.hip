@@ -9,8 +9,9 @@
 // storage type (fp32, or bf16 round-to-nearest-even).  The explicit _rn
 // intrinsics keep the compiler from contracting a multiply and an add.  Row
 // reductions (mean, variance) accumulate in binary64 and store fp32.  The
-// kernels stream with 128-bit loads/stores where every full-tensor operand is
-// 16-byte aligned and the row length is a whole number of vectors, so the
+// element-wise kernels use 128-bit loads/stores wherever every full-size
+// operand is 16-byte aligned (any row length: broadcast operands are indexed
+// per element), and the row reductions read aligned 16-byte windows, so the
 // comparison with the fused kernels is one of bytes and launches, not of load
 // width.
 #include "mbp_device.hpp"
@@ -44,33 +45,62 @@ __device__ __forceinline__ float operand(const void* p, int ix, int64_t i, int64
   return static_cast<const float*>(p)[i / cols];
 }
 
-// One element per work item (VW == 1) or one 16-byte vector (VW == IO::kVec).
+// Operand element e of the vector starting at flat index i0 = row0 * cols +
+// col0 (col0 < cols, cols >= VW: the vector wraps into the next row at most once).
+template <class IO, int VW>
+__device__ __forceinline__ float vec_operand(const void* p, int ix, const u32x4& full, int e, int64_t row0,
+                                             int64_t col0, int64_t cols) {
+  if (p == nullptr) return 0.0f;
+  if (ix == IX_FULL) return IO::get(full, e);
+  const bool wrap = col0 + e >= cols;
+  if (ix == IX_COL) return IO::load1(static_cast<const typename IO::elem*>(p), wrap ? col0 + e - cols : col0 + e);
+  return static_cast<const float*>(p)[wrap ? row0 + 1 : row0];
+}
+
+// One element per work item (VW == 1), or one 16-byte vector (VW == IO::kVec)
+// for items below n / VW and single elements for the n % VW tail.  The vector
+// form needs every full-size operand 16-byte aligned and, when an operand is
+// broadcast, cols >= VW.
 template <class IO, int OP, int VW>
 __global__ __launch_bounds__(kBlock) void ew_kernel(const typename IO::elem* a, const void* b,
                                                     int b_ix, const void* c, int c_ix,
                                                     typename IO::elem* out, int64_t n,
                                                     int64_t cols, float scalar) {
-  const int64_t items = n / VW;
+  const int64_t nv = n / VW;
+  const int64_t items = nv + (n - nv * VW);
+  const bool bcast = (b && b_ix != IX_FULL) || (c && c_ix != IX_FULL);
+  const bool col_vec = VW > 1 && cols % VW == 0 && (!b || b_ix != IX_COL || ((uintptr_t)b & 15) == 0) &&
+                       (!c || c_ix != IX_COL || ((uintptr_t)c & 15) == 0);
   for (int64_t it = (int64_t)blockIdx.x * kBlock + threadIdx.x; it < items;
        it += (int64_t)gridDim.x * kBlock) {
-    if constexpr (VW == 1) {
-      const float r = ew_apply<OP>(IO::load1(a, it), operand<IO>(b, b_ix, it, cols),
-                                   operand<IO>(c, c_ix, it, cols), scalar);
-      IO::store1(out, it, r);
+    if (VW == 1 || it >= nv) {
+      const int64_t i = VW == 1 ? it : nv * VW + (it - nv);
+      const float r = ew_apply<OP>(IO::load1(a, i), operand<IO>(b, b_ix, i, cols),
+                                   operand<IO>(c, c_ix, i, cols), scalar);
+      IO::store1(out, i, r);
     } else {
       const int64_t i0 = it * VW;
+      int64_t row0 = 0, col0 = 0;
+      if (bcast) {
+        row0 = i0 / cols;
+        col0 = i0 - row0 * cols;
+      }
       const u32x4 av = reinterpret_cast<const u32x4*>(a)[it];
+      // a column-broadcast operand whose vectors line up with the row (cols a
+      // multiple of VW, 16-byte aligned) is read as one vector, as if full
+      int bx = b_ix, cx = c_ix;
+      if (bx == IX_COL && col_vec) bx = IX_FULL;
+      if (cx == IX_COL && col_vec) cx = IX_FULL;
       u32x4 bv = {{0u, 0u, 0u, 0u}}, cv = {{0u, 0u, 0u, 0u}};
       if (b && b_ix == IX_FULL) bv = reinterpret_cast<const u32x4*>(b)[it];
-      if (b && b_ix == IX_COL) bv = reinterpret_cast<const u32x4*>(b)[(i0 % cols) / VW];
-      if (c && c_ix == IX_COL) cv = reinterpret_cast<const u32x4*>(c)[(i0 % cols) / VW];
-      const float brow = (b && b_ix == IX_ROW) ? static_cast<const float*>(b)[i0 / cols] : 0.0f;
+      if (b && b_ix == IX_COL && col_vec) bv = reinterpret_cast<const u32x4*>(b)[col0 / VW];
+      if (c && c_ix == IX_FULL) cv = reinterpret_cast<const u32x4*>(c)[it];
+      if (c && c_ix == IX_COL && col_vec) cv = reinterpret_cast<const u32x4*>(c)[col0 / VW];
       float r[VW];
 #pragma unroll
-      for (int e = 0; e < VW; ++e) {
-        const float bb = (b_ix == IX_ROW) ? brow : IO::get(bv, e);
-        r[e] = ew_apply<OP>(IO::get(av, e), bb, IO::get(cv, e), scalar);
-      }
+      for (int e = 0; e < VW; ++e)
+        r[e] = ew_apply<OP>(IO::get(av, e), vec_operand<IO, VW>(b, bx, bv, e, row0, col0, cols),
+                            vec_operand<IO, VW>(c, cx, cv, e, row0, col0, cols), scalar);
       u32x4 ov;
       if constexpr (VW == 8) {
 #pragma unroll
@@ -84,30 +114,87 @@ __global__ __launch_bounds__(kBlock) void ew_kernel(const typename IO::elem* a, 
   }
 }
 
-// Row statistics: one 256-lane block per row (blocks stride over rows); each
-// lane sums its columns j = lane, lane + 256, ... in binary64, then a fixed-order
-// block reduction.  MODE 0: mean; MODE 1: biased variance about `mean`.
-template <class IO, int MODE>
+// Row statistics: one 256-lane block per row, binary64 accumulation, then a
+// fixed-order block reduction.  MODE 0: mean; MODE 1: biased variance about
+// `mean`.  The row is read in aligned 16-byte windows (window q: bytes
+// [16q, 16q + 16) above the 16-byte boundary at or below `a`), kU windows per
+// lane in flight; elements of a window outside the row are skipped, and a
+// window reaching outside the tensor (at its first or last row only) is read
+// element by element.
+constexpr int kU = 4;
+
+template <class IO>
+__device__ __forceinline__ u32x4 stat_window(const typename IO::elem* a, const u32x4* win, int mb, int64_t end,
+                                             int64_t q) {
+  typedef typename IO::elem E;
+  constexpr int ES = (int)sizeof(E);
+  const int64_t wb = 16 * q;
+  if (wb >= mb && wb + 16 <= end) return win[q];
+  u32x4 w = {{0u, 0u, 0u, 0u}};
+#pragma unroll
+  for (int e = 0; e < IO::kVec; ++e) {
+    const int64_t bb = wb + ES * e;
+    if (bb >= mb && bb < end) {
+      const E v = a[(bb - mb) / ES];
+      if constexpr (IO::kVec == 8) {
+        const uint32_t h = (uint32_t)v;
+        w.w[e >> 1] |= (e & 1) ? (h << 16) : h;
+      } else {
+        w.w[e] = __float_as_uint(v);
+      }
+    }
+  }
+  return w;
+}
+
+template <class IO, int MODE, int LANES>
 __global__ __launch_bounds__(kBlock) void row_stat_kernel(const typename IO::elem* a,
                                                           const float* mean, float* out,
                                                           int64_t rows, int64_t cols) {
+  constexpr int ES = (int)sizeof(typename IO::elem);
+  constexpr int V = IO::kVec;
+  constexpr int RPB = kBlock / LANES;  // rows per block, one group of LANES lanes each
   __shared__ double red[2][kBlock / 64];
+  const int mb = (int)(reinterpret_cast<uintptr_t>(a) & 15);
+  const u32x4* win = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a) - mb);
+  const int64_t end = mb + (int64_t)ES * rows * cols;  // tensor bytes, relative to the window base
+  const int lane = threadIdx.x % LANES;
   int parity = 0;
-  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x, parity ^= 1) {
-    const typename IO::elem* ar = a + row * cols;
-    const double mu = MODE == 1 ? (double)mean[row] : 0.0;
+  for (int64_t grp = blockIdx.x; grp * RPB < rows; grp += gridDim.x, parity ^= 1) {
+    const int64_t row = grp * RPB + threadIdx.x / LANES;
+    const bool live = row < rows;
+    const int64_t lo = mb + (int64_t)ES * (live ? row : 0) * cols, hi = live ? lo + (int64_t)ES * cols : lo;
+    const int64_t q_end = (hi + 15) >> 4;
+    const double mu = MODE == 1 && live ? (double)mean[row] : 0.0;
     double acc = 0.0;
-    for (int64_t j = threadIdx.x; j < cols; j += kBlock) {
-      const double v = (double)IO::load1(ar, j);
-      if constexpr (MODE == 0) {
-        acc += v;
-      } else {
-        const double d = v - mu;
-        acc += d * d;
+    for (int64_t q0 = (lo >> 4) + lane; q0 < q_end; q0 += kU * LANES) {
+      u32x4 w[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t q = q0 + u * LANES;
+        w[u] = q < q_end ? stat_window<IO>(a, win, mb, end, q) : u32x4{{0u, 0u, 0u, 0u}};
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t wb = 16 * (q0 + u * LANES);
+        const bool inner = wb >= lo && wb + 16 <= hi;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const int64_t bb = wb + ES * e;
+          if (inner || (bb >= lo && bb < hi)) {
+            const double v = (double)IO::get(w[u], e);
+            if constexpr (MODE == 0) {
+              acc += v;
+            } else {
+              const double d = v - mu;
+              acc += d * d;
+            }
+          }
+        }
       }
     }
-    const double tot = group_sum<kBlock, kBlock>(acc, red[parity]);
-    if (threadIdx.x == 0) out[row] = (float)(tot / (double)cols);
+    const double tot = group_sum<LANES, kBlock>(acc, red[parity]);
+    if (live && lane == 0) out[row] = (float)(tot / (double)cols);
   }
 }
 
@@ -128,6 +215,21 @@ const void* ew_ptr(int op) {
 
 bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Rows of up to 4 KiB: one wave per row (4 rows per block); longer rows: the
+// whole 256-lane block.
+template <class IO, int MODE>
+const void* stat_ptr(int64_t cols) {
+  return cols * (int64_t)sizeof(typename IO::elem) <= 4096
+             ? reinterpret_cast<const void*>(&row_stat_kernel<IO, MODE, 64>)
+             : reinterpret_cast<const void*>(&row_stat_kernel<IO, MODE, kBlock>);
+}
+
+int64_t stat_grid(int64_t rows, int64_t cols, int es) {
+  const int64_t rpb = cols * es <= 4096 ? kBlock / 64 : 1;
+  const int64_t g = (rows + rpb - 1) / rpb;  // one block per row group
+  return g < kMaxGrid ? g : kMaxGrid;
+}
+
 }  // namespace
 
 hipError_t launch_ew(int op, int dtype, const void* a, const void* b, int b_ix, const void* c,
@@ -135,14 +237,17 @@ hipError_t launch_ew(int op, int dtype, const void* a, const void* b, int b_ix, 
                      hipStream_t s) {
   const int64_t n = rows * cols;
   const int vec = dtype == 1 ? 8 : 4;
-  bool vector_ok = (cols % vec) == 0 && a16(a) && a16(out);
-  if (b && b_ix != IX_ROW) vector_ok = vector_ok && a16(b);
-  if (c) vector_ok = vector_ok && a16(c);
+  // 128-bit form: every full-size operand 16-byte aligned; a broadcast
+  // operand needs cols >= vec (a vector then wraps into the next row at most once)
+  const bool bcast = (b && b_ix != IX_FULL) || (c && c_ix != IX_FULL);
+  bool vector_ok = a16(a) && a16(out) && (!bcast || cols >= vec);
+  if (b && b_ix == IX_FULL) vector_ok = vector_ok && a16(b);
+  if (c && c_ix == IX_FULL) vector_ok = vector_ok && a16(c);
   const int vw = vector_ok ? vec : 1;
   const void* k = dtype == 1 ? (vector_ok ? ew_ptr<BF16IO, 8>(op) : ew_ptr<BF16IO, 1>(op))
                              : (vector_ok ? ew_ptr<F32IO, 4>(op) : ew_ptr<F32IO, 1>(op));
   if (!k) return hipErrorInvalidValue;
-  int64_t grid = (n / vw + kBlock - 1) / kBlock;
+  int64_t grid = (n / vw + n % vw + kBlock - 1) / kBlock;
   if (grid > kMaxGrid) grid = kMaxGrid;
   if (grid < 1) grid = 1;
   void* args[] = {&a, &b, &b_ix, &c, &c_ix, &out, (void*)&n, &cols, &scalar};
@@ -151,19 +256,17 @@ hipError_t launch_ew(int op, int dtype, const void* a, const void* b, int b_ix, 
 
 hipError_t launch_row_mean_only(int dtype, const void* a, float* mean, int64_t rows,
                                 int64_t cols, hipStream_t s) {
-  const void* k = dtype == 1 ? reinterpret_cast<const void*>(&row_stat_kernel<BF16IO, 0>)
-                             : reinterpret_cast<const void*>(&row_stat_kernel<F32IO, 0>);
+  const void* k = dtype == 1 ? stat_ptr<BF16IO, 0>(cols) : stat_ptr<F32IO, 0>(cols);
   const float* none = nullptr;
-  const int grid = persistent_grid(k, kBlock, rows, 0);
+  const int grid = (int)stat_grid(rows, cols, dtype == 1 ? 2 : 4);
   void* args[] = {&a, &none, &mean, &rows, &cols};
   return hipLaunchKernel(k, dim3(grid), dim3(kBlock), args, 0, s);
 }
 
 hipError_t launch_row_var(int dtype, const void* a, const float* mean, float* var, int64_t rows,
                           int64_t cols, hipStream_t s) {
-  const void* k = dtype == 1 ? reinterpret_cast<const void*>(&row_stat_kernel<BF16IO, 1>)
-                             : reinterpret_cast<const void*>(&row_stat_kernel<F32IO, 1>);
-  const int grid = persistent_grid(k, kBlock, rows, 0);
+  const void* k = dtype == 1 ? stat_ptr<BF16IO, 1>(cols) : stat_ptr<F32IO, 1>(cols);
+  const int grid = (int)stat_grid(rows, cols, dtype == 1 ? 2 : 4);
   void* args[] = {&a, &mean, &var, &rows, &cols};
   return hipLaunchKernel(k, dim3(grid), dim3(kBlock), args, 0, s);
 }

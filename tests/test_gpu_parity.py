@@ -327,6 +327,31 @@ def test_unfused_layernorm(mbp, name, rows, gran):
     chk(to_host(y), ref, f"unfused {name} granularity {gran}")
 
 
+@pytest.mark.parametrize("name,cols,rows,off", [
+    ("addln_gelu_16384x8192_bf16", 5, 9, 0), ("addln_gelu_16384x8192_bf16", 33, 7, 0),
+    ("addln_gelu_16384x8192_bf16", 1023, 5, 3), ("addln_gelu_16384x8192_bf16", 4095, 3, 1),
+    ("ln_8192x4096_f32", 3, 11, 0), ("ln_8192x4096_f32", 7, 11, 1), ("ln_8192x4096_f32", 1001, 3, 2)])
+@pytest.mark.parametrize("gran", [0, 1])
+def test_unfused_layernorm_shapes(mbp, name, cols, rows, off, gran):
+    """Rows narrower than a vector, odd widths, and x and residual `off`
+    elements past a 16-byte boundary: the element-wise fallback, vectors
+    wrapping into the next row, and row windows at the tensor's ends."""
+    w, d, act = _ln_case(name, rows, cols, residual=True)
+
+    def place(a):
+        t = to_dev(a)
+        buf = torch.zeros(t.numel() + 16, dtype=t.dtype, device="cuda")
+        v = buf[off:off + t.numel()].view(t.shape)
+        v.copy_(t)
+        return v
+
+    y = mbp.unfused_add_layernorm_gelu(place(d["x"]), place(d["residual"]), to_dev(d["gamma"]),
+                                       to_dev(d["beta"]), eps=1e-5, act=act, granularity=gran)
+    ref = _ln_ref(d, act, mode=oracle.SEQ if gran == 0 else oracle.SEQ3)
+    chk = check_bf16 if w.dtype == "bf16" else check_f32
+    chk(to_host(y), ref, f"unfused {name} {rows}x{cols} offset {off} granularity {gran}")
+
+
 # ------------------------------------------------------------------ misc
 
 def test_empty_inputs(mbp):
