@@ -65,6 +65,10 @@ def _bind(lib):
     lib.oracle_gelu_tanh.restype = None
     lib.oracle_to_bf16.argtypes = [P, I64, P]
     lib.oracle_to_bf16.restype = None
+    lib.oracle_round_to_f16.argtypes = [P, I64, P]
+    lib.oracle_round_to_f16.restype = None
+    lib.oracle_round_to_bf16.argtypes = [P, I64, P]
+    lib.oracle_round_to_bf16.restype = None
     return lib
 
 
@@ -145,4 +149,15 @@ def to_bf16(x, lib=None):
     x = _f32(x)
     out = np.empty(x.shape, dtype=np.uint16)
     lib.oracle_to_bf16(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def round_bits(x, fmt, lib=None):
+    """float64 -> bit patterns (uint16) of binary16 ("f16") or bfloat16
+    ("bf16"), rounded once to nearest even directly from binary64."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    fn = {"f16": lib.oracle_round_to_f16, "bf16": lib.oracle_round_to_bf16}[fmt]
+    fn(_ptr(x), x.size, _ptr(out))
     return out

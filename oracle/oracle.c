@@ -33,6 +33,12 @@
  * All outputs are written as binary64 (the stored value, widened, in SEQ modes).
  * Return value: 0 on success, negative on a bad argument or allocation failure.
  *
+ * Storage formats.  oracle_round_to_f16 / oracle_round_to_bf16 round binary64
+ * values once, to nearest even, to binary16 / bfloat16 bit patterns: the
+ * expected stored result of a kernel that computes in binary64 and stores a
+ * 16-bit type (binary16 and bfloat16 inputs widen exactly to binary32, so the
+ * chain and the 10-op graph take them through their binary32 interfaces).
+ *
  * Sources (the four pages on operator fusion):
  *   [P1] PyTorch operator-fusion practice post, 0539edu.com/news/5489619
  *        section 1.1 (the add/relu/mul/add step table), section 3.1 (baseline
@@ -108,6 +114,61 @@ void oracle_gelu_tanh(const double* u, int64_t n, double* out) {
  * independent library conversion. */
 void oracle_to_bf16(const float* in, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = float_to_bf16_rne(in[i]);
+}
+
+/* ---- binary64 -> a narrower binary format, one rounding -------------------
+ * IEEE 754 binary formats with p significand bits (the leading one counted),
+ * smallest normal exponent emin and largest exponent emax: binary16 (p = 11,
+ * emin = -14, emax = 15) and bfloat16 (p = 8, emin = -126, emax = 127).  Round
+ * to nearest, ties to even, directly from the binary64 value: scale by a power
+ * of two so that the last significand bit of the result has weight 1 (below
+ * the normal range that weight is fixed at 2^(emin - p + 1)), round to an
+ * integer with rint() (ties to even in the default rounding mode), scale back.
+ * Both scalings are exact.  A result above the largest finite value becomes
+ * infinity; zeros, infinities and NaN pass through. */
+static double round_binary(double v, int p, int emin, int emax) {
+  if (v != v || v == 0.0 || isinf(v)) return v;
+  double a = fabs(v);
+  int e;
+  frexp(a, &e); /* a = f * 2^e with f in [0.5, 1): the leading bit has weight 2^(e - 1) */
+  int lead = e - 1;
+  if (lead < emin) lead = emin;
+  int q = lead - (p - 1); /* weight of the last significand bit: 2^q */
+  double r = ldexp(rint(ldexp(a, -q)), q);
+  double maxf = ldexp(2.0 - ldexp(1.0, 1 - p), emax);
+  if (r > maxf) r = INFINITY;
+  return v < 0 ? -r : r;
+}
+
+/* bit pattern of a value representable in binary16 */
+static uint16_t encode_binary16(double r) {
+  uint16_t s = signbit(r) ? 0x8000u : 0u;
+  if (r != r) return 0x7e00u;
+  double a = fabs(r);
+  if (isinf(a)) return (uint16_t)(s | 0x7c00u);
+  if (a < ldexp(1.0, -14)) return (uint16_t)(s | (uint16_t)ldexp(a, 24)); /* zero or subnormal */
+  int e;
+  double f = frexp(a, &e); /* a = f * 2^e, f in [0.5, 1) */
+  uint16_t frac = (uint16_t)(ldexp(f, 11) - 1024.0);
+  return (uint16_t)(s | (uint16_t)((e - 1 + 15) << 10) | frac);
+}
+
+/* bit pattern of a value representable in bfloat16: the upper half of its
+ * (exact) binary32 pattern */
+static uint16_t encode_bfloat16(double r) {
+  if (r != r) return 0x7fc0u;
+  float f = (float)r;
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+void oracle_round_to_f16(const double* in, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = encode_binary16(round_binary(in[i], 11, -14, 15));
+}
+
+void oracle_round_to_bf16(const double* in, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = encode_bfloat16(round_binary(in[i], 8, -126, 127));
 }
 
 /* ---- (a) pointwise chain --------------------------------------------------

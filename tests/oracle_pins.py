@@ -389,9 +389,96 @@ def pin_ln_seq(lib):
     assert np.array_equal(y, ref.astype(np.float64)), "LN SEQ (fp32) must match op-by-op emulation"
 
 
+def _nearest_even_bits(x, table_vals, table_bits, max_bits, inf_bits):
+    """Brute force: the bit pattern of the value in `table_vals` (all finite
+    non-negative values of a format, ascending, with their patterns) nearest to
+    |x|, ties to the even pattern; beyond the largest finite value by half an
+    ulp or more, infinity.  Exact comparisons in binary64 (every candidate and
+    every midpoint used here is exact in binary64)."""
+    out = np.empty(x.shape, np.uint16)
+    for i, v in enumerate(x):
+        a = abs(float(v))
+        sign = 0x8000 if math.copysign(1.0, float(v)) < 0 else 0
+        k = int(np.searchsorted(table_vals, a))
+        if k == len(table_vals):
+            hi_v = table_vals[-1] + (table_vals[-1] - table_vals[-2])  # next binade step past the max
+            mid = (table_vals[-1] + hi_v) / 2
+            b = inf_bits if a >= mid else max_bits
+        elif table_vals[k] == a:
+            b = table_bits[k]
+        else:
+            lo, hi = table_vals[k - 1], table_vals[k]
+            mid = (lo + hi) / 2
+            if a < mid:
+                b = table_bits[k - 1]
+            elif a > mid:
+                b = table_bits[k]
+            else:
+                b = table_bits[k - 1] if table_bits[k - 1] % 2 == 0 else table_bits[k]
+            if b == max_bits + 1:  # rounded up past the largest finite value
+                b = inf_bits
+        out[i] = sign | b
+    return out
+
+
+def _round_cases(r, emin, emax, p):
+    """Random doubles over the format's range (subnormals to overflow), exact
+    ties, ties nudged by less than binary32 can hold, and edge values."""
+    e = r.integers(emin - p - 2, emax + 2, 4000)
+    vals = r.uniform(1.0, 2.0, 4000) * np.exp2(e.astype(np.float64))
+    sig = r.integers(0, 2 ** p, 2000)
+    ex = r.integers(emin, emax + 1, 2000)
+    ties = (1.0 + (2 * sig + 1) * 2.0 ** (-p)) * np.exp2(ex.astype(np.float64))
+    nudged = ties * (1 + 2.0 ** -40)
+    vals = np.concatenate([vals, -vals[:500], ties, ties * (1 - 2.0 ** -40), nudged])
+    return vals
+
+
+def pin_round_f16(lib):
+    """binary16: against numpy's float64 -> float16 conversion (a direct,
+    correctly rounded library routine) and against brute force."""
+    r = _rng(20)
+    x = _round_cases(r, -14, 15, 11)
+    x = np.concatenate([x, [0.0, -0.0, 65504.0, 65519.99, 65520.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26,
+                            1 + 2.0 ** -11 + 2.0 ** -40, np.inf, -np.inf]])
+    got = oracle.round_bits(x, "f16", lib=lib)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want), f"f16 rounding vs numpy: {int((got != want).sum())} mismatches"
+    allbits = np.arange(0, 0x7C00, dtype=np.uint16)
+    vals = allbits.view(np.float16).astype(np.float64)
+    sub = r.choice(len(x), 1500, replace=False)
+    fin = x[sub][np.isfinite(x[sub])]
+    bf = _nearest_even_bits(fin, vals, allbits, 0x7BFF, 0x7C00)
+    assert np.array_equal(oracle.round_bits(fin, "f16", lib=lib), bf), "f16 rounding vs brute force"
+    nan = oracle.round_bits(np.array([np.nan]), "f16", lib=lib)[0]
+    assert (nan & 0x7C00) == 0x7C00 and (nan & 0x3FF) != 0, "NaN stays NaN"
+
+
+def pin_round_bf16(lib):
+    """bfloat16 directly from binary64: brute force over every finite pattern,
+    agreement with the binary32 encoder (pinned against torch) on values that
+    are binary32, and the double-rounding trap that a conversion through
+    binary32 gets wrong."""
+    r = _rng(21)
+    x = _round_cases(r, -126, 127, 8)
+    allbits = np.arange(0, 0x7F80, dtype=np.uint32)
+    vals = (allbits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    sub = r.choice(len(x), 3000, replace=False)
+    fin = x[sub][np.isfinite(x[sub])]
+    bf = _nearest_even_bits(fin, vals, allbits.astype(np.uint16), 0x7F7F, 0x7F80)
+    assert np.array_equal(oracle.round_bits(fin, "bf16", lib=lib), bf), "bf16 rounding vs brute force"
+    f32 = r.standard_normal(20000).astype(np.float32)
+    assert np.array_equal(oracle.round_bits(f32.astype(np.float64), "bf16", lib=lib),
+                          oracle.to_bf16(f32, lib=lib)), "bf16 from binary64 vs from binary32 on binary32 values"
+    trap = np.array([1 + 2.0 ** -8 + 2.0 ** -40, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 3.4e38, -3.0e38])
+    assert list(oracle.round_bits(trap, "bf16", lib=lib)) == [0x3F81, 0x3F80, 0x3F82, 0x7F80, 0xFF62], \
+        "bf16 rounding edge cases"
+
+
 ALL_PINS = [
     pin_chain_worked, pin_chain_bruteforce, pin_chain_invariants, pin_chain_numpy,
     pin_tenop_worked, pin_tenop_bruteforce, pin_tenop_invariants, pin_tenop_seq,
     pin_ln_worked, pin_ln_closed_forms, pin_ln_bruteforce, pin_ln_torch, pin_gelu,
-    pin_residual_zero, pin_bf16_encode, pin_ln_seq,
+    pin_residual_zero, pin_bf16_encode, pin_ln_seq, pin_round_f16, pin_round_bf16,
 ]

@@ -36,6 +36,12 @@ MUTANTS = [
     ("LN SEQ: mean kept in binary64", "if (seq) mean[i] = r32(mean[i]);", ""),
     ("LN SEQ: bf16 store skipped after the divide", "nrm[i * cols + j] = seq ? rstore(dtype, nv) : nv;",
      "nrm[i * cols + j] = seq ? r32(nv) : nv;"),
+    ("round: truncation for nearest", "double r = ldexp(rint(ldexp(a, -q)), q);", "double r = ldexp(floor(ldexp(a, -q)), q);"),
+    ("round: one significand bit short", "int q = lead - (p - 1);", "int q = lead - (p - 2);"),
+    ("round: no subnormal floor", "if (lead < emin) lead = emin;", ""),
+    ("round: no overflow to infinity", "if (r > maxf) r = INFINITY;", ""),
+    ("f16 encode: exponent bias off by one", "(uint16_t)((e - 1 + 15) << 10)", "(uint16_t)((e + 15) << 10)"),
+    ("f16 encode: subnormal scale", "(uint16_t)ldexp(a, 24)); /* zero or subnormal */", "(uint16_t)ldexp(a, 23)); /* zero or subnormal */"),
 ]
 
 
