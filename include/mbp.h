@@ -4,8 +4,7 @@
  * Every entry point takes plain device pointers and sizes, enqueues its work on
  * the given HIP stream and returns at once (asynchronous, like a kernel launch).
  * The caller owns every buffer: the library never allocates or frees device
- * memory and keeps no mutable global state beyond a per-thread error message
- * and a per-device cache of occupancy figures.
+ * memory and keeps no mutable global state beyond a per-thread error message.
  *
  * Conventions shared by all entry points
  *   - Tensors are dense and row-major (contiguous).  A [rows, cols] tensor has
@@ -44,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MBP_ABI_VERSION 1
+#define MBP_ABI_VERSION 2
 
 /* Largest row length (cols) the row kernels accept: one row lives in registers. */
 #define MBP_MAX_COLS 16384
@@ -61,7 +60,8 @@ typedef enum {
   MBP_ERR_ARG = 8        /* other invalid argument: non-finite constant, eps < 0, bad op code */
 } mbp_status;
 
-typedef enum { MBP_F32 = 0, MBP_BF16 = 1 } mbp_dtype;
+/* Storage types.  MBP_F16 (IEEE binary16) is accepted by the *_2d entry points. */
+typedef enum { MBP_F32 = 0, MBP_BF16 = 1, MBP_F16 = 2 } mbp_dtype;
 
 typedef enum { MBP_ACT_NONE = 0, MBP_ACT_GELU_TANH = 1 } mbp_act;
 
@@ -123,6 +123,44 @@ mbp_status fused_row_mean_epilogue(const float* x, const float* bias, const floa
 mbp_status fused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void* residual,
                                     const void* gamma, const void* beta, void* y, int64_t rows,
                                     int64_t cols, double eps, mbp_act act, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Two-dimensional forms with row strides and 16-bit storage.  The pages'
+ * chain and 10-op graph written for any storage type of one tensor family
+ * (MBP_F32, MBP_BF16, MBP_F16: every operand in `dtype`) and for operands
+ * that are not dense: element (i, j) of an operand with row stride ld is at
+ * offset i*ld + j (unit stride along a row).  An input with ld == 0 is one
+ * row used for every row (a broadcast bias, stride 0 as in [P4] section 1.1);
+ * [P1] section 6.2 warns that a non-contiguous input otherwise costs a hidden
+ * .contiguous() copy.  Arithmetic is binary64; each result is rounded once, to
+ * nearest even, to `dtype` at the store (through a round-to-odd binary32 for
+ * the 16-bit types, which equals one rounding from binary64).
+ * Strides: an input's ld is 0 or >= cols; the output's ldy >= cols (any ldy
+ * when rows == 1).  Pointers aligned to the element size.  In-place use needs
+ * y == x and ldy == ldx; any other overlap of the output's extent with an
+ * input's extent returns MBP_ERR_OVERLAP.  rows == 0 is a no-op.
+ */
+
+/*
+ * y[i,j] = relu(x[i,j] + b1[i,j]) * scale + b2[i,j] for i < rows, j < cols,
+ * with row strides ldx, ldb1, ldb2, ldy.  [P1] sections 1.1 and 3.1 (the
+ * chain; b1 and b2 full tensors there, broadcast rows here when ld == 0).
+ * cols: any positive length (no MBP_MAX_COLS bound: nothing is held per row).
+ */
+mbp_status fused_pointwise_chain_2d(mbp_dtype dtype, const void* x, int64_t ldx, const void* b1,
+                                    int64_t ldb1, const void* b2, int64_t ldb2, void* y,
+                                    int64_t ldy, int64_t rows, int64_t cols, double scale,
+                                    void* stream);
+
+/*
+ * The 10-op graph of [P4] (as fused_row_mean_epilogue) with x and y of row
+ * strides ldx and ldy and every operand in `dtype`; bias, gamma, beta: dense
+ * [cols] vectors in `dtype`.  cols <= MBP_MAX_COLS.
+ */
+mbp_status fused_row_mean_epilogue_2d(mbp_dtype dtype, const void* x, int64_t ldx,
+                                      const void* bias, const void* gamma, const void* beta,
+                                      void* y, int64_t ldy, int64_t rows, int64_t cols,
+                                      double alpha, double c, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Unfused "before" variants: one launch per op, every intermediate written to

@@ -19,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmbp.so")
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 ACT_NONE, ACT_GELU_TANH = 0, 1
 OP_CHAIN, OP_ROW_MEAN, OP_LAYERNORM = 0, 1, 2
 UNFUSED_PRIMITIVE, UNFUSED_EAGER = 0, 1
@@ -35,6 +35,8 @@ SIGNATURES = [
     ("fused_pointwise_chain", _I, [_P, _P, _P, _P, _I64, _D, _P]),
     ("fused_row_mean_epilogue", _I, [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _P]),
     ("fused_add_layernorm_gelu", _I, [_I, _P, _P, _P, _P, _P, _I64, _I64, _D, _I, _P]),
+    ("fused_pointwise_chain_2d", _I, [_I, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _D, _P]),
+    ("fused_row_mean_epilogue_2d", _I, [_I, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _D, _D, _P]),
     ("unfused_pointwise_chain", _I, [_P, _P, _P, _P, _I64, _D, _P, _SZ, _P]),
     ("unfused_row_mean_epilogue", _I, [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _P, _SZ, _P]),
     ("unfused_add_layernorm_gelu", _I, [_I, _P, _P, _P, _P, _P, _I64, _I64, _D, _I, _I, _P, _SZ, _P]),
@@ -176,6 +178,82 @@ def fused_add_layernorm_gelu(x, residual, gamma, beta, eps=1e-5, act="gelu_tanh"
 def fused_layernorm(x, gamma, beta, eps=1e-5, out=None):
     """Plain LayerNorm (no residual, no activation) over the last dimension."""
     return fused_add_layernorm_gelu(x, None, gamma, beta, eps=eps, act="none", out=out)
+
+
+# ------------------------------------------------------------------ two-dimensional forms
+
+_DTYPES_2D = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+def _matrix(t, name, rows, cols, dtype, device, broadcast_ok):
+    """(pointer, row stride in elements) of a [rows, cols] operand whose rows
+    are contiguous.  A 1-D [cols] tensor, or a 2-D one whose row stride is 0
+    (``expand``), is one row used for every row."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.dim() == 1:
+        if t.shape[0] != cols or (cols > 1 and t.stride(0) != 1):
+            raise ValueError(f"{name} must be [{cols}] with unit stride or [{rows}, {cols}]")
+        ld = 0
+    elif t.dim() == 2:
+        if tuple(t.shape) != (rows, cols):
+            raise ValueError(f"{name} must be [{rows}, {cols}] (got {tuple(t.shape)})")
+        if cols > 1 and t.stride(1) != 1:
+            raise ValueError(f"{name}: elements of a row must be contiguous (column stride 1)")
+        ld = t.stride(0) if rows > 1 else 0
+    else:
+        raise ValueError(f"{name} must be 1-D or 2-D")
+    if ld == 0 and rows > 1 and not broadcast_ok:
+        raise ValueError(f"{name} cannot be a broadcast row")
+    return t.data_ptr(), ld
+
+
+def _out_2d(out, rows, cols, dtype, device):
+    if out is None:
+        out = torch.empty((rows, cols), dtype=dtype, device=device)
+    ptr, ld = _matrix(out, "out", rows, cols, dtype, device, broadcast_ok=False)
+    return out, ptr, (ld if rows > 1 else cols)
+
+
+def fused_pointwise_chain_2d(x, b1, b2, scale=0.5, out=None):
+    """y = relu(x + b1) * scale + b2 on [rows, cols] operands with any row
+    stride (x, b1, b2 may be broadcast rows: 1-D or expanded), fp32 / bf16 /
+    fp16 (one dtype).  Returns out, or a new dense [rows, cols] tensor."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.device.type != "cuda":
+        raise ValueError("x must be a 2-D GPU tensor")
+    if x.dtype not in _DTYPES_2D:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    rows, cols = x.shape
+    args = [_matrix(t, n, rows, cols, x.dtype, x.device, True) for t, n in ((x, "x"), (b1, "b1"), (b2, "b2"))]
+    y, yp, ldy = _out_2d(out, rows, cols, x.dtype, x.device)
+    (xp, ldx), (ap, lda), (bp, ldb) = args
+    _call("fused_pointwise_chain_2d", _DTYPES_2D[x.dtype], xp, ldx, ap, lda, bp, ldb, yp, ldy, rows, cols,
+          float(scale), _stream(x))
+    return y
+
+
+def fused_row_mean_epilogue_2d(x, bias, gamma, beta, alpha=1.1, c=0.1, out=None):
+    """The 10-op graph on a [rows, cols] x with any row stride, fp32 / bf16 /
+    fp16 (every operand one dtype); bias, gamma, beta dense [cols]."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.device.type != "cuda":
+        raise ValueError("x must be a 2-D GPU tensor")
+    if x.dtype not in _DTYPES_2D:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    rows, cols = x.shape
+    xp, ldx = _matrix(x, "x", rows, cols, x.dtype, x.device, True)
+    vec = []
+    for t, n in ((bias, "bias"), (gamma, "gamma"), (beta, "beta")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 1:
+            raise ValueError(f"{n} must be a 1-D tensor of {cols} elements")
+        vec.append(_matrix(t, n, rows, cols, x.dtype, x.device, True)[0])
+    y, yp, ldy = _out_2d(out, rows, cols, x.dtype, x.device)
+    _call("fused_row_mean_epilogue_2d", _DTYPES_2D[x.dtype], xp, ldx, vec[0], vec[1], vec[2], yp, ldy, rows,
+          cols, float(alpha), float(c), _stream(x))
+    return y
 
 
 # ------------------------------------------------------------------ unfused

@@ -209,6 +209,51 @@ mbp_status check_ln(mbp_dtype dtype, const void* x, const void* residual, const 
   return MBP_OK;
 }
 
+size_t dtype_size(mbp_dtype d) { return d == MBP_F32 ? 4 : 2; }
+
+// Bytes spanned by a [rows, cols] operand with row stride ld (0: one row).
+size_t extent(int64_t rows, int64_t cols, int64_t ld, size_t es) {
+  return es * (size_t)((rows - 1) * ld + cols);
+}
+
+// Shared checks of the *_2d entry points.  `ins` are the [rows, cols] inputs
+// with their strides; the output may be exactly the input `inplace` (same
+// pointer and stride), if given.
+struct Operand2d {
+  const void* p;
+  int64_t ld;
+};
+
+mbp_status check_2d(mbp_dtype dtype, std::initializer_list<Operand2d> ins, void* y, int64_t ldy,
+                    int64_t rows, int64_t cols, int64_t max_cols, const void* inplace) {
+  if (dtype != MBP_F32 && dtype != MBP_BF16 && dtype != MBP_F16)
+    return fail(MBP_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (rows < 0) return fail(MBP_ERR_SHAPE, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (cols <= 0 || cols > max_cols)
+    return fail(MBP_ERR_SHAPE, "cols must be in [1, %lld] (got %lld)", (long long)max_cols, (long long)cols);
+  if (rows == 0) return MBP_OK;
+  const size_t es = dtype_size(dtype);
+  if (!y) return fail(MBP_ERR_NULL, "y must be non-NULL");
+  if (misaligned(y, es)) return fail(MBP_ERR_ALIGN, "pointers must be aligned to the element size");
+  if (rows > 1 && ldy < cols) return fail(MBP_ERR_SHAPE, "ldy must be >= cols (got %lld)", (long long)ldy);
+  if (ldy < 0) return fail(MBP_ERR_SHAPE, "ldy must be >= 0");
+  const int64_t lim = kMaxElems / 2;
+  if (rows > lim / (ldy > cols ? ldy : cols)) return fail(MBP_ERR_SHAPE, "rows * ldy overflows");
+  const Span ys{y, extent(rows, cols, rows > 1 ? ldy : 0, es)};
+  for (const Operand2d& in : ins) {
+    if (!in.p) return fail(MBP_ERR_NULL, "a required pointer is NULL");
+    if (misaligned(in.p, es)) return fail(MBP_ERR_ALIGN, "pointers must be aligned to the element size");
+    if (in.ld != 0 && in.ld < cols)
+      return fail(MBP_ERR_SHAPE, "an input stride must be 0 or >= cols (got %lld)", (long long)in.ld);
+    if (in.ld < 0) return fail(MBP_ERR_SHAPE, "strides must be >= 0");
+    if (in.ld > 0 && rows > lim / in.ld) return fail(MBP_ERR_SHAPE, "rows * ld overflows");
+    const Span is{in.p, extent(rows, cols, in.ld, es)};
+    const bool same = in.p == inplace && in.p == y && (in.ld == ldy || rows == 1);
+    if (overlaps(ys, is) && !same) return fail(MBP_ERR_OVERLAP, "y overlaps an input");
+  }
+  return MBP_OK;
+}
+
 }  // namespace
 
 
@@ -243,6 +288,36 @@ mbp_status fused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void* 
   return from_hip(mbp::launch_layernorm(dtype, x, residual, gamma, beta, y, rows, cols, eps, act,
                                         as_stream(stream)),
                   "fused_add_layernorm_gelu");
+}
+
+mbp_status fused_pointwise_chain_2d(mbp_dtype dtype, const void* x, int64_t ldx, const void* b1,
+                                    int64_t ldb1, const void* b2, int64_t ldb2, void* y,
+                                    int64_t ldy, int64_t rows, int64_t cols, double scale,
+                                    void* stream) {
+  if (!std::isfinite(scale)) return fail(MBP_ERR_ARG, "scale must be finite");
+  // element-wise: y may be exactly any one of the inputs (the first that equals it)
+  const void* inplace = y == x ? x : (y == b1 ? b1 : (y == b2 ? b2 : nullptr));
+  mbp_status st = check_2d(dtype, {{x, ldx}, {b1, ldb1}, {b2, ldb2}}, y, ldy, rows, cols, kMaxElems, inplace);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  return from_hip(mbp::launch_chain_2d(dtype, x, ldx, b1, ldb1, b2, ldb2, y, ldy, rows, cols, scale,
+                                       as_stream(stream)),
+                  "fused_pointwise_chain_2d");
+}
+
+mbp_status fused_row_mean_epilogue_2d(mbp_dtype dtype, const void* x, int64_t ldx,
+                                      const void* bias, const void* gamma, const void* beta,
+                                      void* y, int64_t ldy, int64_t rows, int64_t cols,
+                                      double alpha, double c, void* stream) {
+  if (!std::isfinite(alpha) || !std::isfinite(c)) return fail(MBP_ERR_ARG, "alpha and c must be finite");
+  // bias, gamma and beta are one row each (stride 0); y may be exactly x
+  mbp_status st = check_2d(dtype, {{x, ldx}, {bias, 0}, {gamma, 0}, {beta, 0}}, y, ldy, rows, cols,
+                           MBP_MAX_COLS, x);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  return from_hip(mbp::launch_row_mean_2d(dtype, x, ldx, bias, gamma, beta, y, ldy, rows, cols, alpha, c,
+                                          as_stream(stream)),
+                  "fused_row_mean_epilogue_2d");
 }
 
 mbp_status unfused_pointwise_chain(const float* x, const float* b1, const float* b2, float* y,

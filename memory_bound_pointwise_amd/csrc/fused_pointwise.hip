@@ -17,6 +17,8 @@ namespace mbp {
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int kChainUnroll = 1;
+constexpr int64_t kMaxGrid = 1 << 30;
 
 __device__ __forceinline__ float chain_op(float x, float b1, float b2, double scale) {
   const double t = (double)x + (double)b1;
@@ -69,14 +71,80 @@ __global__ __launch_bounds__(kBlock) void chain_kernel(const float* x, const flo
   }
 }
 
+// Two-dimensional form: rows x cols, a row stride per operand (0: one row
+// used for every row), fp32 / bf16 / fp16 storage.  An item is one 16-byte
+// vector of a row (VW = IO::kVec; every operand row starts on a 16-byte
+// boundary and cols is a whole number of vectors) or one element (VW = 1).
+// Binary64 arithmetic as above, one rounding to the storage type at the store.
+template <class IO>
+__device__ __forceinline__ double chain_op_d(float x, float b1, float b2, double scale) {
+  const double t = (double)x + (double)b1;
+  const double r = (t < 0.0) ? 0.0 : t;
+  return __builtin_fma(r, scale, (double)b2);
+}
+
+template <class IO, int VW>
+__global__ __launch_bounds__(kBlock) void chain2d_kernel(
+    const typename IO::elem* x, int64_t ldx, const typename IO::elem* b1, int64_t ldb1,
+    const typename IO::elem* b2, int64_t ldb2, typename IO::elem* y, int64_t ldy, int64_t rows,
+    int64_t cols, double scale) {
+  typedef typename IO::elem E;
+  const int64_t per_row = cols / VW;
+  const int64_t items = rows * per_row;
+  for (int64_t it = (int64_t)blockIdx.x * kBlock + threadIdx.x; it < items;
+       it += (int64_t)gridDim.x * kBlock) {
+    const int64_t row = it / per_row;
+    const int64_t c0 = (it - row * per_row) * VW;
+    if constexpr (VW == 1) {
+      const double r = chain_op_d<IO>(IO::load1(x, row * ldx + c0), IO::load1(b1, row * ldb1 + c0),
+                                      IO::load1(b2, row * ldb2 + c0), scale);
+      const uint32_t bits = narrow_bits<IO>(r);
+      if constexpr (sizeof(E) == 4) y[row * ldy + c0] = __uint_as_float(bits);
+      else y[row * ldy + c0] = (uint16_t)bits;
+    } else {
+      const u32x4 xv = load_nt(reinterpret_cast<const u32x4*>(x + row * ldx + c0));
+      const u32x4 av = *reinterpret_cast<const u32x4*>(b1 + row * ldb1 + c0);
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(b2 + row * ldb2 + c0);
+      u32x4 ov = {{0u, 0u, 0u, 0u}};
+#pragma unroll
+      for (int e = 0; e < VW; ++e) {
+        const uint32_t bits =
+            narrow_bits<IO>(chain_op_d<IO>(IO::get(xv, e), IO::get(av, e), IO::get(bv, e), scale));
+        if constexpr (sizeof(E) == 4) ov.w[e] = bits;
+        else ov.w[e >> 1] |= bits << (16 * (e & 1));
+      }
+      store_nt(reinterpret_cast<u32x4*>(y + row * ldy + c0), ov);
+    }
+  }
+}
+
+template <class IO>
+hipError_t launch_chain2d_io(const void* x, int64_t ldx, const void* b1, int64_t ldb1, const void* b2,
+                             int64_t ldb2, void* y, int64_t ldy, int64_t rows, int64_t cols, double scale,
+                             hipStream_t s) {
+  typedef typename IO::elem E;
+  constexpr int V = IO::kVec;
+  auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  auto row16 = [](int64_t ld) { return (ld * (int64_t)sizeof(E)) % 16 == 0; };
+  const bool vec = cols % V == 0 && a16(x) && a16(b1) && a16(b2) && a16(y) && row16(ldx) && row16(ldb1) &&
+                   row16(ldb2) && row16(ldy);
+  const int vw = vec ? V : 1;
+  int64_t grid = (rows * (cols / vw) + kBlock - 1) / kBlock;
+  if (grid > kMaxGrid) grid = kMaxGrid;
+  const void* k = vec ? reinterpret_cast<const void*>(&chain2d_kernel<IO, V>)
+                      : reinterpret_cast<const void*>(&chain2d_kernel<IO, 1>);
+  const E *xe = static_cast<const E*>(x), *ae = static_cast<const E*>(b1), *be = static_cast<const E*>(b2);
+  E* ye = static_cast<E*>(y);
+  void* args[] = {&xe, &ldx, &ae, &ldb1, &be, &ldb2, &ye, &ldy, &rows, &cols, &scale};
+  return hipLaunchKernel(k, dim3((unsigned)grid), dim3(kBlock), args, 0, s);
+}
+
 __global__ __launch_bounds__(kBlock) void copy_kernel(const u32x4* src, u32x4* dst, int64_t n16) {
   for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n16;
        i += (int64_t)gridDim.x * kBlock)
     store_nt(dst + i, load_nt(src + i));
 }
 
-constexpr int kChainUnroll = 1;
-constexpr int64_t kMaxGrid = 1 << 30;
 
 }  // namespace
 
@@ -101,6 +169,19 @@ hipError_t launch_chain(const float* x, const float* b1, const float* b2, float*
   hipLaunchKernelGGL(chain_kernel<kChainUnroll>, dim3((unsigned)grid), dim3(kBlock), 0, s, x, b1,
                      b2, y, h, n4, nscal, scale);
   return hipGetLastError();
+}
+
+hipError_t launch_chain_2d(int dtype, const void* x, int64_t ldx, const void* b1, int64_t ldb1,
+                          const void* b2, int64_t ldb2, void* y, int64_t ldy, int64_t rows, int64_t cols,
+                          double scale, hipStream_t s) {
+  // dense fp32 (every stride == cols, or one row): the one-dimensional kernel
+  const bool dense = rows == 1 || (ldx == cols && ldb1 == cols && ldb2 == cols && ldy == cols);
+  if (dtype == 0 && dense)
+    return launch_chain(static_cast<const float*>(x), static_cast<const float*>(b1),
+                        static_cast<const float*>(b2), static_cast<float*>(y), rows * cols, scale, s);
+  if (dtype == 0) return launch_chain2d_io<F32IO>(x, ldx, b1, ldb1, b2, ldb2, y, ldy, rows, cols, scale, s);
+  if (dtype == 1) return launch_chain2d_io<BF16IO>(x, ldx, b1, ldb1, b2, ldb2, y, ldy, rows, cols, scale, s);
+  return launch_chain2d_io<F16IO>(x, ldx, b1, ldb1, b2, ldb2, y, ldy, rows, cols, scale, s);
 }
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {

@@ -13,7 +13,8 @@
 // reduced across the group, and the epilogue writes y.  Arithmetic is binary64
 // (fp32 in and out), so the result is the exactly rounded value up to a few
 // binary64 roundings.  Rows that do not start on 16-byte boundaries take the
-// same kernel with one element per load.
+// same kernel with one element per load.  The same kernel serves bf16 and fp16
+// storage and row-strided x / y (each result rounded once to the storage type).
 #include "mbp_internal.hpp"
 #include "row_common.hpp"
 
@@ -24,10 +25,43 @@ using namespace rows;
 
 // ---------------------------------------------------------------- 10-op graph
 
-template <int LANES, int VPL, int VW>
+// Four consecutive elements: one 16-byte access for fp32, one 8-byte access
+// for the 16-bit types (nontemporal: x is read once, y written once).
+template <class IO>
+__device__ __forceinline__ void load4_nt(const typename IO::elem* p, float* v) {
+  if constexpr (sizeof(typename IO::elem) == 4) {
+    const u32x4 t = load_nt(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(t.w[e]);
+  } else {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    const uint32_t w0 = __builtin_nontemporal_load(q), w1 = __builtin_nontemporal_load(q + 1);
+    u32x4 t = {{w0, w1, 0u, 0u}};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = IO::get(t, e);
+  }
+}
+template <class IO>
+__device__ __forceinline__ void store4_nt(typename IO::elem* p, const uint32_t* bits) {
+  if constexpr (sizeof(typename IO::elem) == 4) {
+    store_nt(reinterpret_cast<u32x4*>(p), u32x4{{bits[0], bits[1], bits[2], bits[3]}});
+  } else {
+    uint32_t* q = reinterpret_cast<uint32_t*>(p);
+    __builtin_nontemporal_store(bits[0] | (bits[1] << 16), q);
+    __builtin_nontemporal_store(bits[2] | (bits[3] << 16), q + 1);
+  }
+}
+
+// IO: storage type of every operand (fp32, bf16, fp16).  VW: elements per
+// access (4: rows aligned to 4 elements; 1: one element).  x and y rows are
+// ldx and ldy elements apart.  Every type holds the same number of elements
+// per lane for a layout, so the 16-bit kernels use the fp32 kernel's registers.
+template <class IO, int LANES, int VPL, int VW>
 __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
-    const float* x, const float* __restrict__ bias, const float* __restrict__ gamma,
-    const float* __restrict__ beta, float* y, int64_t rows, int cols, double alpha, double c) {
+    const typename IO::elem* x, int64_t ldx, const typename IO::elem* __restrict__ bias,
+    const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
+    typename IO::elem* y, int64_t ldy, int64_t rows, int cols, double alpha, double c) {
+  typedef typename IO::elem E;
   constexpr int BLOCK = block_for(LANES);
   constexpr int RPB = BLOCK / LANES;
   __shared__ double red[2][BLOCK / 64];
@@ -44,16 +78,17 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
     for (int e = 0; e < VW; ++e) {
       const int j = vi * VW + e;
       const bool ok = vi < nvec;
-      bi[k][e] = ok ? bias[j] : 0.0f;
-      g[k][e] = ok ? gamma[j] : 0.0f;
-      be[k][e] = ok ? beta[j] : 0.0f;
+      bi[k][e] = ok ? IO::load1(bias, j) : 0.0f;
+      g[k][e] = ok ? IO::load1(gamma, j) : 0.0f;
+      be[k][e] = ok ? IO::load1(beta, j) : 0.0f;
     }
   }
 
   const int64_t groups = (rows + RPB - 1) / RPB;
   int parity = 0;
   for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x, parity ^= 1) {
-    // the parameters stay fp32 across rows (see ln_kernel)
+    // the parameters stay fp32 across rows (an empty asm keeps the compiler
+    // from widening them to binary64 once and holding the wide copies)
 #pragma unroll
     for (int k = 0; k < VPL; ++k)
 #pragma unroll
@@ -66,19 +101,15 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
     const bool live = row < rows;
     // past the last row: reread the last row, store nothing; slots past the
     // row's end reread its last vector and stay out of the sum (no branches)
-    const float* xr = x + (live ? row : rows - 1) * (int64_t)cols;
-    float* yr = y + row * (int64_t)cols;
+    const E* xr = x + (live ? row : rows - 1) * ldx;
+    E* yr = y + row * ldy;
 
     float xv[VPL][VW];
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       const int vi = min(lane + k * LANES, nvec - 1);
-      if constexpr (VW == 1) {
-        xv[k][0] = xr[vi];
-      } else {
-        const float4 t = load_nt(reinterpret_cast<const float4*>(xr) + vi);
-        xv[k][0] = t.x; xv[k][1] = t.y; xv[k][2] = t.z; xv[k][3] = t.w;
-      }
+      if constexpr (VW == 1) xv[k][0] = IO::load1(xr, vi);
+      else load4_nt<IO>(xr + 4 * vi, xv[k]);
     }
     double s[VPL][VW];
     double sum = 0.0;
@@ -100,46 +131,72 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
     for (int k = 0; k < VPL; ++k) {
       const int vi = lane + k * LANES;
       if (!(live && vi < nvec)) continue;
-      float o[VW];
+      uint32_t o[VW];
 #pragma unroll
       for (int e = 0; e < VW; ++e)
-        o[e] = (float)__builtin_fma(s[k][e] - m, (double)g[k][e], (double)be[k][e]);
+        o[e] = narrow_bits<IO>(__builtin_fma(s[k][e] - m, (double)g[k][e], (double)be[k][e]));
       if constexpr (VW == 1) {
-        yr[vi] = o[0];
+        if constexpr (sizeof(E) == 4) yr[vi] = __uint_as_float(o[0]);
+        else yr[vi] = (uint16_t)o[0];
       } else {
-        store_nt(reinterpret_cast<float4*>(yr) + vi, make_float4(o[0], o[1], o[2], o[3]));
+        store4_nt<IO>(yr + 4 * vi, o);
       }
     }
   }
 }
 
-
-template <int VW>
+// Kernel of layout (L, V) of the row tables: V groups of 4 elements per lane,
+// or, on the element path, the same elements one at a time.
+template <class IO, bool VEC>
 struct TenopSel {
   template <int L, int V>
   struct K {
-    static const void* ptr() { return reinterpret_cast<const void*>(&tenop_kernel<L, (VW == 1 ? 4 * V : V), VW>); }
+    static const void* ptr() {
+      return VEC ? reinterpret_cast<const void*>(&tenop_kernel<IO, L, V, 4>)
+                 : reinterpret_cast<const void*>(&tenop_kernel<IO, L, 4 * V, 1>);
+    }
   };
 };
 
-}  // namespace
-
-hipError_t launch_row_mean(const float* x, const float* bias, const float* gamma,
-                           const float* beta, float* y, int64_t rows, int64_t cols, double alpha,
-                           double c, hipStream_t s) {
-  const bool vector_ok = (cols % 4) == 0 && aligned16(x) && aligned16(bias) && aligned16(gamma) &&
-                         aligned16(beta) && aligned16(y);
-  // the scalar path holds 4x the vectors of a layout, one element each
-  const int shape = pick_shape(vector_ok ? cols / 4 : (cols + 3) / 4);
+template <class IO>
+hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void* gamma, const void* beta,
+                        void* y, int64_t ldy, int64_t rows, int64_t cols, double alpha, double c,
+                        hipStream_t s) {
+  typedef typename IO::elem E;
+  // 4-element accesses: every row start on a 4-element boundary
+  constexpr uintptr_t A4 = 4 * sizeof(E);
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) % A4) == 0; };
+  const bool vector_ok = (cols % 4) == 0 && al(x) && al(y) && ldx % 4 == 0 && ldy % 4 == 0;
+  const int shape = pick_shape((cols + 3) / 4);
   if (shape < 0) return hipErrorInvalidValue;
-  const void* k = vector_ok ? shape_kernel<TenopSel<4>::K>(shape) : shape_kernel<TenopSel<1>::K>(shape);
+  const void* k = vector_ok ? shape_kernel<TenopSel<IO, true>::template K>(shape)
+                            : shape_kernel<TenopSel<IO, false>::template K>(shape);
   const int block = block_for(kShapes[shape].lanes);
   const int rpb = block / kShapes[shape].lanes;
   const int64_t groups = (rows + rpb - 1) / rpb;
   const int grid = (int)(groups < (1 << 30) ? groups : (1 << 30));  // one block per row group
   int icols = (int)cols;
-  void* args[] = {&x, &bias, &gamma, &beta, &y, &rows, &icols, &alpha, &c};
+  const E *xe = static_cast<const E*>(x), *bie = static_cast<const E*>(bias);
+  const E *ge = static_cast<const E*>(gamma), *bee = static_cast<const E*>(beta);
+  E* ye = static_cast<E*>(y);
+  void* args[] = {&xe, &ldx, &bie, &ge, &bee, &ye, &ldy, &rows, &icols, &alpha, &c};
   return hipLaunchKernel(k, dim3(grid), dim3(block), args, 0, s);
+}
+
+}  // namespace
+
+hipError_t launch_row_mean_2d(int dtype, const void* x, int64_t ldx, const void* bias, const void* gamma,
+                              const void* beta, void* y, int64_t ldy, int64_t rows, int64_t cols,
+                              double alpha, double c, hipStream_t s) {
+  if (dtype == 0) return launch_tenop<F32IO>(x, ldx, bias, gamma, beta, y, ldy, rows, cols, alpha, c, s);
+  if (dtype == 1) return launch_tenop<BF16IO>(x, ldx, bias, gamma, beta, y, ldy, rows, cols, alpha, c, s);
+  return launch_tenop<F16IO>(x, ldx, bias, gamma, beta, y, ldy, rows, cols, alpha, c, s);
+}
+
+hipError_t launch_row_mean(const float* x, const float* bias, const float* gamma,
+                           const float* beta, float* y, int64_t rows, int64_t cols, double alpha,
+                           double c, hipStream_t s) {
+  return launch_row_mean_2d(0, x, cols, bias, gamma, beta, y, cols, rows, cols, alpha, c, s);
 }
 
 }  // namespace mbp

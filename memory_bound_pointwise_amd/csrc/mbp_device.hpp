@@ -75,6 +75,48 @@ struct BF16IO {
   }
 };
 
+// IEEE binary16; widening to fp32 is exact, narrowing (v_cvt_f16_f32) rounds
+// to nearest even.
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+struct F16IO {
+  typedef uint16_t elem;
+  static constexpr int kVec = 8;
+  __device__ __forceinline__ static float load1(const elem* p, int64_t i) { return f16_to_f32(p[i]); }
+  __device__ __forceinline__ static void store1(elem* p, int64_t i, float v) { p[i] = f32_to_f16(v); }
+  __device__ __forceinline__ static float get(const u32x4& v, int e) {
+    return f16_to_f32((uint16_t)(v.w[e >> 1] >> (16 * (e & 1))));
+  }
+};
+
+// binary64 -> binary32 rounded to odd: truncate toward zero, then set the
+// last significand bit if anything was dropped.  Rounding that value to
+// nearest even into a format with at most 22 significand bits (binary16,
+// bfloat16) equals rounding the binary64 value directly (round-to-odd as the
+// intermediate of a double rounding: S. Boldo and G. Melquiond, "Emulation of
+// FMA and correctly rounded sums: proved algorithms using rounding to odd",
+// IEEE Trans. Computers 57(4), 2008).
+__device__ __forceinline__ float round_odd_f32(double d) {
+  float r = (float)d;  // nearest even
+  const double back = (double)r;
+  if (back != d && d == d) {
+    uint32_t u = __float_as_uint(r);
+    if (__builtin_fabs(back) > __builtin_fabs(d)) u -= 1;  // rounded away from zero: step back
+    u |= 1u;                                                // sticky bit
+    r = __uint_as_float(u);
+  }
+  return r;
+}
+
+// The stored bits of a binary64 value, rounded once to nearest even.
+template <class IO>
+__device__ __forceinline__ uint32_t narrow_bits(double d) {
+  if constexpr (sizeof(typename IO::elem) == 4) return __float_as_uint((float)d);
+  else if constexpr (IO::kVec == 8 && __is_same(IO, BF16IO)) return f32_to_bf16(round_odd_f32(d));
+  else return f32_to_f16(round_odd_f32(d));
+}
+
 // tanh-approximated GeLU, 0.5 u (1 + tanh(k0 (u + k1 u^3))) with k0 = 0.7978845608,
 // k1 = 0.044715 ("算子融合与 Kernel 优化", section 2.3), evaluated through the exact
 // identity 0.5 (1 + tanh z) = 1 / (1 + exp(-2 z)) and exp(w) = exp2(w log2 e):

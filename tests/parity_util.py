@@ -5,7 +5,10 @@ Gates (fused kernels against the oracle's binary64 result):
 * pointwise chain: at most 2 ulp between the fp32 output and the exact result
   rounded to fp32 (ulp distance on the ordered integer line, +0 == -0);
 * fp32 row kernels: |y - exact| <= max(1e-5, half an fp32 ulp of exact);
-* bf16 row kernels: |y - exact| <= max(2e-2, half a bf16 ulp of exact).
+* bf16 row kernels: |y - exact| <= max(2e-2, half a bf16 ulp of exact);
+* 16-bit outputs of the two-dimensional forms (binary64 inside, one rounding
+  at the store): at most 1 ulp, on the ordered bit line, from the exact result
+  rounded once to the format by the oracle.
 The half-ulp term only matters where no output of the storage type can be
 within 1e-5 (|exact| >= 256 in fp32) or 2e-2 (|exact| >= 8 in bf16) of the
 exact value; those elements are counted and reported.
@@ -75,6 +78,32 @@ def check_f32(y, exact, what=""):
 
 def check_bf16(y, exact, what=""):
     return check_abs(y, exact, 2e-2, 7, what)
+
+
+def bits16(t):
+    """bit patterns (uint16) of a bf16 / fp16 device tensor"""
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def ordered16(b):
+    i = np.asarray(b).astype(np.int64)
+    return np.where(i & 0x8000, -(i & 0x7FFF), i)
+
+
+def is_nan16(b, fmt):
+    b = np.asarray(b).astype(np.int64)
+    e, m = (0x7C00, 0x3FF) if fmt == "f16" else (0x7F80, 0x7F)
+    return ((b & e) == e) & ((b & m) != 0)
+
+
+def check_ulp16(bits, exact, fmt, what=""):
+    import oracle
+    want = oracle.round_bits(exact, fmt)
+    nan_e, nan_y = np.isnan(exact), is_nan16(bits, fmt)
+    assert (nan_e == nan_y).all(), f"{what}: NaN mismatch"
+    d = np.where(nan_e, 0, np.abs(ordered16(bits) - ordered16(want)))
+    assert d.max(initial=0) <= 1, f"{what}: max {d.max()} ulp at {np.unravel_index(np.argmax(d), d.shape)}"
+    return int(d.max(initial=0)), int((d > 0).sum())
 
 
 def sample_rows(rows, k=48, seed=7):

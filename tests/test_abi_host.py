@@ -27,6 +27,7 @@ def mbp():
 def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("fused_pointwise_chain", "fused_row_mean_epilogue", "fused_add_layernorm_gelu",
+                 "fused_pointwise_chain_2d", "fused_row_mean_epilogue_2d",
                  "unfused_pointwise_chain", "unfused_row_mean_epilogue", "unfused_add_layernorm_gelu"):
         assert name in fns
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(mbp):
 
 
 def test_abi_version_and_strings(mbp):
-    assert mbp.lib.mbp_abi_version() == 1
+    assert mbp.lib.mbp_abi_version() == 2
     for code, name in mbp.STATUS_NAMES.items():
         assert mbp.lib.mbp_status_string(code)
     assert mbp.lib.mbp_status_string(99) == b"unknown status"
@@ -99,6 +100,37 @@ def test_row_validation(mbp):
     assert st("fused_add_layernorm_gelu", 1, None, None, B, B, Y, 4, 8, 1e-5, 1, None) == 1
     assert st("fused_add_layernorm_gelu", 1, A, None, B, B, Y, 4, big, 1e-5, 1, None) == 2
     assert st("unfused_add_layernorm_gelu", 1, A, None, B, B, Y, 4, 8, 1e-5, 1, 5, None, 0, None) == 8
+
+
+def test_2d_validation(mbp):
+    global L
+    L = mbp.lib
+    c2 = "fused_pointwise_chain_2d"
+    # dtype, x, ldx, b1, ldb1, b2, ldb2, y, ldy, rows, cols, scale, stream
+    assert st(c2, 5, A, 8, B, 0, B, 0, Y, 8, 4, 8, 0.5, None) == 3                # DTYPE
+    assert st(c2, 2, A, 8, B, 0, B, 0, Y, 8, -1, 8, 0.5, None) == 2               # rows < 0
+    assert st(c2, 2, A, 8, B, 0, B, 0, Y, 8, 0, 8, 0.5, None) == 0                # rows == 0: no-op
+    assert st(c2, 2, A, 8, B, 0, B, 0, Y, 8, 4, 0, 0.5, None) == 2                # cols == 0
+    assert st(c2, 2, None, 8, B, 0, B, 0, Y, 8, 4, 8, 0.5, None) == 1             # NULL
+    assert st(c2, 2, A + 1, 8, B, 0, B, 0, Y, 8, 4, 8, 0.5, None) == 4            # fp16 misaligned
+    assert st(c2, 0, A + 2, 8, B, 0, B, 0, Y, 8, 4, 8, 0.5, None) == 4            # fp32 misaligned
+    assert st(c2, 2, A, 4, B, 0, B, 0, Y, 8, 4, 8, 0.5, None) == 2                # 0 < ldx < cols
+    assert st(c2, 2, A, 8, B, 0, B, 0, Y, 4, 4, 8, 0.5, None) == 2                # ldy < cols
+    assert st(c2, 2, A, 8, B, 0, B, 0, Y, 0, 4, 8, 0.5, None) == 2                # broadcast output
+    assert st(c2, 2, A, 8, B, -8, B, 0, Y, 8, 4, 8, 0.5, None) == 2               # negative stride
+    assert st(c2, 2, A, 8, B, 0, B, 0, Y, 8, 4, 8, float("inf"), None) == 8       # ARG
+    assert st(c2, 2, A, 8, B, 0, B, 0, A + 2, 8, 4, 8, 0.5, None) == 5            # partial overlap
+    assert st(c2, 2, A, 8, B, 0, B, 0, A, 16, 4, 8, 0.5, None) == 5               # y == x, other stride
+    assert st(c2, 2, A, 8, Y + 4, 0, B, 0, Y, 8, 4, 8, 0.5, None) == 5            # y over a broadcast b1
+    r2 = "fused_row_mean_epilogue_2d"
+    # dtype, x, ldx, bias, gamma, beta, y, ldy, rows, cols, alpha, c, stream
+    assert st(r2, 1, A, 8, B, B, B, Y, 8, 4, mbp.MAX_COLS + 1, 1.1, 0.1, None) == 2
+    assert st(r2, 1, A, 8, B, B, B, Y, 8, 4, 8, float("nan"), 0.1, None) == 8
+    assert st(r2, 1, A, 8, B, Y + 2, B, Y, 8, 4, 8, 1.1, 0.1, None) == 5          # y over gamma
+    assert st(r2, 1, A, 8, None, B, B, Y, 8, 4, 8, 1.1, 0.1, None) == 1
+    assert st(r2, 1, A, 8, B, B, B, A, 12, 4, 8, 1.1, 0.1, None) == 5             # y == x, other stride
+    # fp16 is for the two-dimensional forms only
+    assert st("fused_add_layernorm_gelu", 2, A, None, B, B, Y, 4, 8, 1e-5, 0, None) == 3
 
 
 def test_workspace_and_launch_counts(mbp):

@@ -14,7 +14,7 @@ import torch
 import oracle
 import workloads as W
 from parity_util import (as_f64, check_bf16, check_chain, check_f32, sample_rows, to_dev,
-                         to_host)
+                         to_host, bits16, check_ulp16)
 
 pytestmark = pytest.mark.gpu
 
@@ -293,6 +293,100 @@ def test_ln_full_workload(mbp, name):
     print(f"{name}: {len(rows)} sampled rows, max abs err {err:.3g}, half-ulp-gated elements {relaxed}")
     # a property that holds over the whole output: no NaN or Inf
     assert torch.isfinite(y1.float()).all()
+
+
+# ------------------------------------------------------------------ two-dimensional forms
+
+DT2D = [("f32", torch.float32), ("bf16", torch.bfloat16), ("f16", torch.float16)]
+
+
+def _stored(rng, shape, dtype, scale=1.0):
+    """seeded N(0, scale^2) values stored in `dtype`: (host tensor, float32 copy of the stored values)"""
+    t = torch.from_numpy(rng.standard_normal(shape) * scale).to(dtype)
+    return t, t.float().numpy()
+
+
+def _padded(host, pad, sentinel=None):
+    """a device view of `host` [rows, cols] inside a [rows, cols + pad] buffer"""
+    rows, cols = host.shape
+    fill = 0.0 if sentinel is None else sentinel
+    big = torch.full((rows, cols + pad), fill, dtype=host.dtype, device="cuda")
+    v = big[:, :cols]
+    v.copy_(host.cuda())
+    return v, big
+
+
+def _bias_operand(rng, rows, cols, dtype, mode):
+    """b as a dense [rows, cols] tensor, a 1-D row, or a row expanded over rows
+    (stride 0); returns (device operand, float32 [rows, cols] of its values)"""
+    if mode == "full":
+        t, f = _stored(rng, (rows, cols), dtype)
+        return t.cuda(), f
+    t, f = _stored(rng, (cols,), dtype)
+    d = t.cuda()
+    full = np.ascontiguousarray(np.broadcast_to(f, (rows, cols)))
+    return (d if mode == "row" else d.expand(rows, cols)), full
+
+
+def _gate_2d(y, exact, fmt, what, row_kernel=False):
+    if fmt == "f32":
+        return check_f32(to_host(y), exact, what) if row_kernel else check_chain(to_host(y), exact, what)
+    return check_ulp16(bits16(y), exact, fmt, what)
+
+
+CHAIN_2D = [  # rows, cols, x pad, y pad, b1, b2
+    (37, 1000, 0, 0, "full", "full"), (37, 1003, 0, 0, "full", "full"),
+    (19, 512, 8, 24, "row", "full"), (19, 515, 3, 5, "expand", "row"),
+    (1, 4099, 0, 0, "row", "row"), (64, 8, 0, 0, "expand", "expand"), (300, 24, 8, 0, "row", "expand")]
+
+
+@pytest.mark.parametrize("fmt,dtype", DT2D, ids=[d[0] for d in DT2D])
+@pytest.mark.parametrize("rows,cols,xpad,ypad,m1,m2", CHAIN_2D)
+def test_chain_2d(mbp, fmt, dtype, rows, cols, xpad, ypad, m1, m2):
+    rng = np.random.default_rng([11, rows, cols, xpad])
+    xh, xf = _stored(rng, (rows, cols), dtype)
+    x, _ = _padded(xh, xpad)
+    b1, b1f = _bias_operand(rng, rows, cols, dtype, m1)
+    b2, b2f = _bias_operand(rng, rows, cols, dtype, m2)
+    y, ybig = _padded(torch.zeros((rows, cols), dtype=dtype), ypad, sentinel=3.0)
+    mbp.fused_pointwise_chain_2d(x, b1, b2, 0.5, out=y)
+    exact = oracle.pointwise_chain(xf, b1f, b2f, 0.5)
+    _gate_2d(y, exact, fmt, f"chain 2d {fmt} {rows}x{cols} pads {xpad},{ypad} {m1},{m2}")
+    if ypad:
+        assert (ybig[:, cols:].float() == 3.0).all(), "wrote outside the output rows"
+
+
+def test_chain_2d_in_place(mbp):
+    rng = np.random.default_rng(12)
+    for dtype, fmt in ((torch.bfloat16, "bf16"), (torch.float16, "f16")):
+        xh, xf = _stored(rng, (16, 264), dtype)
+        x, _ = _padded(xh, 8)
+        b1, b1f = _bias_operand(rng, 16, 264, dtype, "row")
+        b2, b2f = _bias_operand(rng, 16, 264, dtype, "full")
+        mbp.fused_pointwise_chain_2d(x, b1, b2, 0.5, out=x)
+        _gate_2d(x, oracle.pointwise_chain(xf, b1f, b2f, 0.5), fmt, f"chain 2d in place {fmt}")
+
+
+TENOP_2D = [(64, 1024, 0, 0), (33, 1001, 0, 0), (40, 512, 8, 16), (21, 515, 5, 3), (1, 4096, 0, 0),
+            (9, 4000, 0, 8)]
+
+
+@pytest.mark.parametrize("fmt,dtype", DT2D, ids=[d[0] for d in DT2D])
+@pytest.mark.parametrize("rows,cols,xpad,ypad", TENOP_2D)
+def test_tenop_2d(mbp, fmt, dtype, rows, cols, xpad, ypad):
+    rng = np.random.default_rng([13, rows, cols, xpad])
+    xh, xf = _stored(rng, (rows, cols), dtype)
+    x, _ = _padded(xh, xpad)
+    vecs = [_stored(rng, (cols,), dtype) for _ in range(3)]
+    y, ybig = _padded(torch.zeros((rows, cols), dtype=dtype), ypad, sentinel=3.0)
+    mbp.fused_row_mean_epilogue_2d(x, *(v[0].cuda() for v in vecs), alpha=1.1, c=0.1, out=y)
+    exact = oracle.row_mean_epilogue(xf, *(v[1] for v in vecs), 1.1, 0.1)
+    _gate_2d(y, exact, fmt, f"10-op 2d {fmt} {rows}x{cols} pads {xpad},{ypad}", row_kernel=True)
+    if ypad:
+        assert (ybig[:, cols:].float() == 3.0).all(), "wrote outside the output rows"
+    # in place, on the padded x
+    mbp.fused_row_mean_epilogue_2d(x, *(v[0].cuda() for v in vecs), alpha=1.1, c=0.1, out=x)
+    _gate_2d(x, exact, fmt, f"10-op 2d in place {fmt} {rows}x{cols}", row_kernel=True)
 
 
 # ------------------------------------------------------------------ unfused variants
