@@ -21,7 +21,10 @@ Printed: one JSON line with
   roofline     the dominant kernel (largest time per call), its duration from
                HIP events around each of its calls inside the timed region,
                against 8 TB/s;
-  cpu_baseline the CPU oracle timed on a bounded sample of the same workloads.
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workloads;
+  next         the two-dimensional forms (bf16 chain with a broadcast bias
+               row, fp16 10-op graph on padded rows), same batch protocol,
+               not part of `value`.
 
 Other modes (for rocprofv3 counter runs): --only NAME runs just one workload's
 fused kernel; --copy-bytes B runs the library's streaming copy of B bytes.
@@ -55,6 +58,7 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=2,
                    help="the oracle runs on 1/K of each workload's rows")
     p.add_argument("--only", default=None, help="run only this workload's fused kernel")
+    p.add_argument("--no-next", action="store_true", help="skip the two-dimensional forms")
     p.add_argument("--unfused-only", default=None, help="run only this workload's unfused variant")
     p.add_argument("--copy-bytes", type=int, default=0, help="run the streaming copy of this size")
     return p.parse_args()
@@ -248,6 +252,39 @@ def main():
         for n in names:
             unf_us[n], _ = batch_times(usets[n], args.unfused_reps)
 
+    # ---- the two-dimensional forms (16-bit storage, broadcast rows, row
+    # strides): same batch protocol, reported beside the step, not in `value`
+    nxt = {}
+    if not args.only and not args.no_next:
+        def build_next(w, d):
+            if w.kind == "chain2d":
+                x, b1, b2 = (to_dev(d[k]) for k in ("x", "b1", "b2"))
+                y = torch.empty_like(x)
+                sc = w.params["scale"]
+                return lambda: mbp.fused_pointwise_chain_2d(x, b1, b2, sc, out=y)
+            xd = to_dev(d["x"])
+            ld = w.params["ld"]
+            xb = torch.zeros((w.rows, ld), dtype=xd.dtype, device=dev)
+            x = xb[:, :w.cols]
+            x.copy_(xd)
+            y = torch.empty_like(xb)[:, :w.cols]
+            vec = [to_dev(d[k]) for k in ("bias", "gamma", "beta")]
+            al, c = w.params["alpha"], w.params["c"]
+            return lambda: mbp.fused_row_mean_epilogue_2d(x, *vec, alpha=al, c=c, out=y)
+
+        for w in W.NEXT_WORKLOADS:
+            d = W.generate(w)
+            fns = [build_next(w, d) for _ in range(n_sets(w))]
+            us, ncalls = batch_times(fns, args.batches)
+            med = statistics.median(us)
+            nxt[w.name] = {"compulsory_bytes": w.compulsory_bytes, "fused_us_median": round(med, 3),
+                           "fused_us_min": round(min(us), 3), "calls_per_batch": ncalls,
+                           "input_copies": len(fns),
+                           "gbps": round(w.compulsory_bytes / (med * 1e-6) / 1e9, 1),
+                           "frac_of_peak": round(w.compulsory_bytes / (med * 1e-6) / 1e9 / PEAK_GBPS, 4)}
+            del fns
+        torch.cuda.synchronize()
+
     per = {}
     total_bytes = 0
     for w in wl:
@@ -305,6 +342,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_workload": per,
+        "next": nxt,
         "library_sha256": sha[:16],
         "setup_s": round(t_gen, 1),
     }

@@ -42,6 +42,19 @@ __device__ __forceinline__ void load4_nt(const typename IO::elem* p, float* v) {
   }
 }
 template <class IO>
+__device__ __forceinline__ void load4(const typename IO::elem* p, float* v) {
+  if constexpr (sizeof(typename IO::elem) == 4) {
+    const u32x4 t = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(t.w[e]);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    u32x4 t = {{w.x, w.y, 0u, 0u}};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = IO::get(t, e);
+  }
+}
+template <class IO>
 __device__ __forceinline__ void store4_nt(typename IO::elem* p, const uint32_t* bits) {
   if constexpr (sizeof(typename IO::elem) == 4) {
     store_nt(reinterpret_cast<u32x4*>(p), u32x4{{bits[0], bits[1], bits[2], bits[3]}});
@@ -73,14 +86,17 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
   float bi[VPL][VW], g[VPL][VW], be[VPL][VW];
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
-    const int vi = lane + k * LANES;
-#pragma unroll
-    for (int e = 0; e < VW; ++e) {
-      const int j = vi * VW + e;
-      const bool ok = vi < nvec;
-      bi[k][e] = ok ? IO::load1(bias, j) : 0.0f;
-      g[k][e] = ok ? IO::load1(gamma, j) : 0.0f;
-      be[k][e] = ok ? IO::load1(beta, j) : 0.0f;
+    // 4-element accesses (the host requires bias, gamma, beta aligned for
+    // them); a slot past the row rereads the last group and stays unused
+    const int vi = min(lane + k * LANES, nvec - 1);
+    if constexpr (VW == 4) {
+      load4<IO>(bias + 4 * vi, bi[k]);
+      load4<IO>(gamma + 4 * vi, g[k]);
+      load4<IO>(beta + 4 * vi, be[k]);
+    } else {
+      bi[k][0] = IO::load1(bias, vi);
+      g[k][0] = IO::load1(gamma, vi);
+      be[k][0] = IO::load1(beta, vi);
     }
   }
 
@@ -166,7 +182,8 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
   // 4-element accesses: every row start on a 4-element boundary
   constexpr uintptr_t A4 = 4 * sizeof(E);
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) % A4) == 0; };
-  const bool vector_ok = (cols % 4) == 0 && al(x) && al(y) && ldx % 4 == 0 && ldy % 4 == 0;
+  const bool vector_ok = (cols % 4) == 0 && al(x) && al(y) && al(bias) && al(gamma) && al(beta) &&
+                         ldx % 4 == 0 && ldy % 4 == 0;
   const int shape = pick_shape((cols + 3) / 4);
   if (shape < 0) return hipErrorInvalidValue;
   const void* k = vector_ok ? shape_kernel<TenopSel<IO, true>::template K>(shape)

@@ -389,6 +389,50 @@ def test_tenop_2d(mbp, fmt, dtype, rows, cols, xpad, ypad):
     _gate_2d(x, exact, fmt, f"10-op 2d in place {fmt} {rows}x{cols}", row_kernel=True)
 
 
+def _as_f32(a):
+    """host storage array (bf16 bit patterns, float16 or float32) -> float32 values"""
+    if a.dtype == np.uint16:
+        return W.bf16_bits_to_f32(a)
+    return a.astype(np.float32)
+
+
+@pytest.mark.parametrize("name", [w.name for w in W.NEXT_WORKLOADS])
+def test_next_full_workload(mbp, name):
+    """The two-dimensional forms at the bench's full size and launch
+    configuration, sampled rows against the oracle."""
+    w = W.NEXT_BY_NAME[name]
+    d = W.generate(w)
+    fmt = w.dtype
+    rows = sample_rows(w.rows)
+    if w.kind == "chain2d":
+        x, b1, b2 = (to_dev(d[k]) for k in ("x", "b1", "b2"))
+        y1 = mbp.fused_pointwise_chain_2d(x, b1, b2, w.params["scale"])
+        y2 = mbp.fused_pointwise_chain_2d(x, b1, b2, w.params["scale"])
+        b1f = np.ascontiguousarray(np.broadcast_to(_as_f32(d["b1"]), (len(rows), w.cols)))
+        exact = oracle.pointwise_chain(_as_f32(d["x"])[rows], b1f, _as_f32(d["b2"])[rows], w.params["scale"])
+        ys = y1[torch.from_numpy(rows).cuda()]
+    else:
+        xd = to_dev(d["x"])
+        ld = w.params["ld"]
+        xb = torch.zeros((w.rows, ld), dtype=xd.dtype, device="cuda")
+        x = xb[:, :w.cols]
+        x.copy_(xd)
+        vec = [to_dev(d[k]) for k in ("bias", "gamma", "beta")]
+        outs = []
+        for _ in range(2):
+            yb = torch.full((w.rows, ld), 3.0, dtype=xd.dtype, device="cuda")
+            mbp.fused_row_mean_epilogue_2d(x, *vec, alpha=w.params["alpha"], c=w.params["c"], out=yb[:, :w.cols])
+            assert (yb[:, w.cols:].float() == 3.0).all(), "wrote into the row padding"
+            outs.append(yb[:, :w.cols])
+        y1, y2 = outs
+        exact = oracle.row_mean_epilogue(_as_f32(d["x"])[rows], *(_as_f32(d[k]) for k in ("bias", "gamma", "beta")),
+                                         w.params["alpha"], w.params["c"])
+        ys = y1[torch.from_numpy(rows).cuda()]
+    assert torch.equal(y1.contiguous().view(torch.int16), y2.contiguous().view(torch.int16)), "not deterministic"
+    worst, n_off = check_ulp16(bits16(ys), exact, fmt, name)
+    print(f"{name}: {len(rows)} sampled rows, max {worst} ulp, {n_off} elements 1 ulp off")
+
+
 # ------------------------------------------------------------------ unfused variants
 
 def test_unfused_chain_bit_exact(mbp):

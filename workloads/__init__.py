@@ -14,7 +14,8 @@ drawn in parallel threads with the same result as sequentially):
 * parameter vectors (bias, gamma, beta) and per-row offsets are drawn in
   float64 and rounded once to the storage type;
 * bfloat16 values are produced from float32 by round-to-nearest-even on the
-  dropped 16 bits and handled as uint16 bit patterns.
+  dropped 16 bits and handled as uint16 bit patterns; binary16 values by
+  numpy's float32 -> float16 conversion (round to nearest even).
 
 The shapes and distributions are those the pages use: ``randn`` tensors for the
 pointwise chain (PyTorch operator-fusion practice post, section 3.1), the 10-op
@@ -33,13 +34,13 @@ import numpy as np
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "chain" | "row_mean" | "layernorm"
+    kind: str            # "chain" | "row_mean" | "layernorm" | "chain2d" | "row_mean2d"
     seed: int
     sub: int = 0
     n: int = 0           # chain: element count
     rows: int = 0
     cols: int = 0
-    dtype: str = "f32"   # layernorm: "f32" or "bf16"
+    dtype: str = "f32"   # "f32", "bf16" (layernorm, 2-D forms) or "f16" (2-D forms)
     residual: bool = False
     act: str = "none"    # "none" | "gelu_tanh"
     std: float = 1.0     # std of x (and residual) for bf16 layernorm
@@ -56,6 +57,11 @@ class Workload:
             return 4 * 4 * self.n                      # x, b1, b2 in; y out (fp32)
         if self.kind == "row_mean":
             return 4 * 2 * self.rows * self.cols + 4 * 3 * self.cols   # x in, y out; bias/gamma/beta
+        es = 4 if self.dtype == "f32" else 2
+        if self.kind == "chain2d":
+            return es * (3 * self.rows * self.cols + self.cols)        # x, b2 in, y out; b1 one row
+        if self.kind == "row_mean2d":
+            return es * (2 * self.rows * self.cols + 3 * self.cols)    # x in, y out; bias/gamma/beta
         es = 2 if self.dtype == "bf16" else 4
         tensors = 3 if self.residual else 2           # x (+ residual) in, y out
         return es * tensors * self.rows * self.cols + es * 2 * self.cols   # + gamma, beta
@@ -77,6 +83,20 @@ WORKLOADS = [
              dtype="bf16", residual=True, act="gelu_tanh", std=2.0, params=dict(eps=1e-5)),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
+
+# The two-dimensional forms (16-bit storage, broadcast rows, row strides):
+# measured beside the workloads above, not part of the headline figure.
+#   chain2d: x [rows, cols] and b2 [rows, cols] dense, b1 one row [cols] used
+#            for every row (stride 0), y dense; bf16.
+#   row_mean2d: x and y [rows, cols] inside rows of params["ld"] elements
+#            (padded rows), bias / gamma / beta [cols]; fp16.
+NEXT_WORKLOADS = [
+    Workload("chain2d_16384x4096_bf16_bcast", "chain2d", seed=6, rows=16384, cols=4096, dtype="bf16",
+             params=dict(scale=0.5)),
+    Workload("tenop2d_8192x1024_f16_ld1056", "row_mean2d", seed=7, rows=8192, cols=1024, dtype="f16",
+             params=dict(alpha=1.1, c=0.1, ld=1056)),
+]
+NEXT_BY_NAME = {w.name: w for w in NEXT_WORKLOADS}
 
 
 def scaled(w: Workload, rows: int | None = None, n: int | None = None) -> Workload:
@@ -155,6 +175,16 @@ def _normal_f32(key, rows: int, cols: int, std: float = 1.0, offsets=None) -> np
     return out
 
 
+def store(a: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values in a storage type: bf16 as uint16 bit patterns, f16 as
+    numpy float16 (both round to nearest even)."""
+    if dtype == "bf16":
+        return f32_to_bf16_bits(a)
+    if dtype == "f16":
+        return np.asarray(a, dtype=np.float32).astype(np.float16)
+    return np.asarray(a, dtype=np.float32)
+
+
 def generate(w: Workload, cols: int | None = None) -> dict:
     """Inputs of workload ``w`` as host numpy arrays (``cols`` overrides the width).
 
@@ -166,6 +196,14 @@ def generate(w: Workload, cols: int | None = None) -> dict:
                      for k in range(3))
         return dict(x=x, b1=b1, b2=b2)
     rows, c = w.rows, cols or w.cols
+    if w.kind == "chain2d":
+        return dict(x=store(_normal_f32((s, u, 0), rows, c), w.dtype),
+                    b1=store(_rng(s, u, 1).standard_normal(c).astype(np.float32), w.dtype),
+                    b2=store(_normal_f32((s, u, 2), rows, c), w.dtype))
+    if w.kind == "row_mean2d":
+        return dict(x=store(_normal_f32((s, u, 0), rows, c), w.dtype),
+                    **{k: store(_rng(s, u, i + 1).standard_normal(c).astype(np.float32), w.dtype)
+                       for i, k in enumerate(("bias", "gamma", "beta"))})
     if w.kind == "row_mean":
         return dict(x=_normal_f32((s, u, 0), rows, c),
                     bias=_rng(s, u, 1).standard_normal(c).astype(np.float32),
