@@ -69,6 +69,8 @@ def _bind(lib):
     lib.oracle_round_to_f16.restype = None
     lib.oracle_round_to_bf16.argtypes = [P, I64, P]
     lib.oracle_round_to_bf16.restype = None
+    lib.oracle_softmax.argtypes = [P, I64, I64, P]
+    lib.oracle_softmax.restype = I
     return lib
 
 
@@ -161,3 +163,15 @@ def round_bits(x, fmt, lib=None):
     fn = {"f16": lib.oracle_round_to_f16, "bf16": lib.oracle_round_to_bf16}[fmt]
     fn(_ptr(x), x.size, _ptr(out))
     return out
+
+
+def softmax(x, lib=None):
+    """Row softmax over the last dimension of a 2-D array of stored values
+    (float32; 16-bit inputs widened to float32 first)."""
+    lib = lib or load()
+    x = _f32(x)
+    if x.ndim != 2:
+        raise ValueError("x must be 2-D")
+    y = np.empty(x.shape, dtype=np.float64)
+    _check(lib.oracle_softmax(_ptr(x), x.shape[0], x.shape[1], _ptr(y)), "softmax")
+    return y

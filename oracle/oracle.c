@@ -364,3 +364,47 @@ int oracle_add_layernorm_gelu(int dtype, const void* x, const void* residual, co
   free(v); free(mean); free(var); free(cen); free(nrm); free(u);
   return 0;
 }
+
+/* ---- row softmax ------------------------------------------------------------
+ * [P1] section 4.2 and [P2] section 3.2 (step 3): softmax over the last
+ * dimension, normalised relative to the row maximum so that no exponential
+ * overflows:
+ *   m_i = max_j x_ij;   e_ij = exp(x_ij - m_i);   l_i = sum_j e_ij;   y_ij = e_ij / l_i.
+ * The ops run in that order, each intermediate materialised, in binary64 on
+ * the stored values (widened exactly; 16-bit inputs arrive as binary32).  The
+ * pages' running-max update (a new maximum rescales the partial sum by
+ * exp(m_old - m_new)) reaches the same values in exact arithmetic; this is
+ * the plain definition.  A NaN anywhere in a row makes its sum NaN, so the row
+ * is NaN; a row of -inf only is 0/0 = NaN (both as torch.softmax). */
+int oracle_softmax(const float* x, int64_t rows, int64_t cols, double* y) {
+  if (rows < 0 || (rows > 0 && cols <= 0)) return -1;
+  if (rows == 0) return 0;
+  const int64_t n = rows * cols;
+  double* m = alloc_d(rows);
+  double* e = alloc_d(n);
+  double* l = alloc_d(rows);
+  if (!m || !e || !l) { free(m); free(e); free(l); return -2; }
+  /* op 1: row maximum (NaN is skipped here and propagates through op 3) */
+  for (int64_t i = 0; i < rows; ++i) {
+    double mi = -INFINITY;
+    for (int64_t j = 0; j < cols; ++j) {
+      double v = (double)x[i * cols + j];
+      if (v > mi) mi = v;
+    }
+    m[i] = mi;
+  }
+  /* op 2: shifted exponentials */
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t j = 0; j < cols; ++j) e[i * cols + j] = exp((double)x[i * cols + j] - m[i]);
+  /* op 3: row sum */
+  for (int64_t i = 0; i < rows; ++i) {
+    double acc = 0.0;
+    for (int64_t j = 0; j < cols; ++j) acc += e[i * cols + j];
+    l[i] = acc;
+  }
+  /* op 4: divide */
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t j = 0; j < cols; ++j) y[i * cols + j] = e[i * cols + j] / l[i];
+  free(m); free(e); free(l);
+  return 0;
+}

@@ -476,9 +476,72 @@ def pin_round_bf16(lib):
         "bf16 rounding edge cases"
 
 
+def pin_softmax_worked(lib):
+    g = read("softmax_worked.txt")
+    for k in range(3):
+        x = np.array([g[f"x{k}"]], np.float32)
+        y = oracle.softmax(x, lib=lib)[0]
+        want = np.array(g[f"y{k}"])
+        assert np.all(np.abs(y - want) <= g["tol"]), f"softmax worked row {k}: {y}"
+        assert np.array_equal(y == 0, want == 0), "masked entries must be exactly 0"
+
+
+def pin_softmax_closed_forms(lib):
+    r = _rng(30)
+    # equal entries: 1/n, correctly rounded (exp(0) = 1 exactly, n exactly, one division)
+    for n in (1, 3, 7, 64, 1000):
+        y = oracle.softmax(np.full((2, n), -1.25, np.float32), lib=lib)
+        assert np.all(y == 1.0 / n), f"uniform row of {n}"
+    # two entries: the logistic function of the difference (40-digit mpmath)
+    a = r.standard_normal((50, 2)).astype(np.float32) * 4
+    y = oracle.softmax(a, lib=lib)
+    mpmath.mp.dps = 40
+    want = np.array([[float(1 / (1 + mpmath.exp(mpmath.mpf(float(b)) - mpmath.mpf(float(c)))))
+                      for c, b in ((row[0], row[1]), (row[1], row[0]))] for row in a])
+    _close(y, want, 1e-14, 0, "two-entry softmax vs logistic")
+    # large entries: exact only if the maximum is subtracted before exp
+    big = np.array([[1000.0, 1000.0 + math.log(3.0)], [-1000.0, -1000.0]], np.float32)
+    y = oracle.softmax(big, lib=lib)
+    _close(y[1], [0.5, 0.5], 0, 0, "equal large negative entries")
+    assert np.all(np.isfinite(y)) and abs(y[0].sum() - 1) < 1e-12, f"no overflow: {y[0]}"
+
+
+def pin_softmax_bruteforce(lib):
+    r = _rng(31)
+    x = (r.standard_normal((6, 17)) * 3).astype(np.float32)
+    x[2, 5] = -np.inf
+    x[4, :] = x[4, 0]
+    y = oracle.softmax(x, lib=lib)
+    mpmath.mp.dps = 40
+    for i in range(x.shape[0]):
+        row = [mpmath.mpf(float(v)) if np.isfinite(v) else mpmath.mpf("-inf") for v in x[i]]
+        m = max(row)
+        ex = [mpmath.exp(v - m) for v in row]
+        tot = mpmath.fsum(ex)
+        want = np.array([float(e / tot) for e in ex])
+        _close(y[i], want, 1e-14, 0, f"softmax row {i} vs 40-digit mpmath")
+
+
+def pin_softmax_torch(lib):
+    """torch.softmax on CPU float64 (an independent implementation), with
+    masked (-inf) entries and rows of very different scales."""
+    import torch
+    r = _rng(32)
+    x = (r.standard_normal((40, 300)) * np.exp2(r.integers(-4, 6, (40, 1)))).astype(np.float32)
+    x[r.random(x.shape) < 0.1] = -np.inf
+    x[:, 0] = r.standard_normal(40).astype(np.float32)  # no row fully masked
+    y = oracle.softmax(x, lib=lib)
+    want = torch.softmax(torch.from_numpy(x.astype(np.float64)), dim=-1).numpy()
+    _close(y, want, 1e-13, 1e-300, "softmax vs torch float64")
+    assert np.array_equal(y == 0, np.isneginf(x)), "exactly the masked entries are 0"
+    s = y.sum(axis=1)
+    assert np.all(np.abs(s - 1) < 1e-13), "rows sum to 1"
+
+
 ALL_PINS = [
     pin_chain_worked, pin_chain_bruteforce, pin_chain_invariants, pin_chain_numpy,
     pin_tenop_worked, pin_tenop_bruteforce, pin_tenop_invariants, pin_tenop_seq,
     pin_ln_worked, pin_ln_closed_forms, pin_ln_bruteforce, pin_ln_torch, pin_gelu,
     pin_residual_zero, pin_bf16_encode, pin_ln_seq, pin_round_f16, pin_round_bf16,
+    pin_softmax_worked, pin_softmax_closed_forms, pin_softmax_bruteforce, pin_softmax_torch,
 ]

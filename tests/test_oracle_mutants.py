@@ -42,6 +42,10 @@ MUTANTS = [
     ("round: no overflow to infinity", "if (r > maxf) r = INFINITY;", ""),
     ("f16 encode: exponent bias off by one", "(uint16_t)((e - 1 + 15) << 10)", "(uint16_t)((e + 15) << 10)"),
     ("f16 encode: subnormal scale", "(uint16_t)ldexp(a, 24)); /* zero or subnormal */", "(uint16_t)ldexp(a, 23)); /* zero or subnormal */"),
+    ("softmax: maximum not subtracted", "e[i * cols + j] = exp((double)x[i * cols + j] - m[i]);", "e[i * cols + j] = exp((double)x[i * cols + j]);"),
+    ("softmax: minimum for maximum", "if (v > mi) mi = v;", "if (v < mi || mi == -INFINITY) mi = v;"),
+    ("softmax: sum skips the last column", "for (int64_t j = 0; j < cols; ++j) acc += e[i * cols + j];", "for (int64_t j = 0; j + 1 < cols; ++j) acc += e[i * cols + j];"),
+    ("softmax: divide by cols", "y[i * cols + j] = e[i * cols + j] / l[i];", "y[i * cols + j] = e[i * cols + j] / (double)cols;"),
 ]
 
 
