@@ -23,7 +23,8 @@ Printed: one JSON line with
                against 8 TB/s;
   cpu_baseline the CPU oracle timed on a bounded sample of the same workloads;
   next         the two-dimensional forms (bf16 chain with a broadcast bias
-               row, fp16 10-op graph on padded rows), same batch protocol,
+               row, fp16 10-op graph on padded rows) and the row softmax
+               (bf16, attention-probability shape), same batch protocol,
                not part of `value`.
 
 Other modes (for rocprofv3 counter runs): --only NAME runs just one workload's
@@ -253,10 +254,15 @@ def main():
             unf_us[n], _ = batch_times(usets[n], args.unfused_reps)
 
     # ---- the two-dimensional forms (16-bit storage, broadcast rows, row
-    # strides): same batch protocol, reported beside the step, not in `value`
+    # strides) and the row softmax: same batch protocol, reported beside the
+    # step, not in `value`
     nxt = {}
     if not args.only and not args.no_next:
         def build_next(w, d):
+            if w.kind == "softmax":
+                x = to_dev(d["x"])
+                y = torch.empty_like(x)
+                return lambda: mbp.fused_softmax(x, out=y)
             if w.kind == "chain2d":
                 x, b1, b2 = (to_dev(d[k]) for k in ("x", "b1", "b2"))
                 y = torch.empty_like(x)

@@ -60,7 +60,8 @@ typedef enum {
   MBP_ERR_ARG = 8        /* other invalid argument: non-finite constant, eps < 0, bad op code */
 } mbp_status;
 
-/* Storage types.  MBP_F16 (IEEE binary16) is accepted by the *_2d entry points. */
+/* Storage types.  MBP_F16 (IEEE binary16) is accepted by the *_2d entry points
+ * and by fused_softmax. */
 typedef enum { MBP_F32 = 0, MBP_BF16 = 1, MBP_F16 = 2 } mbp_dtype;
 
 typedef enum { MBP_ACT_NONE = 0, MBP_ACT_GELU_TANH = 1 } mbp_act;
@@ -123,6 +124,21 @@ mbp_status fused_row_mean_epilogue(const float* x, const float* bias, const floa
 mbp_status fused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void* residual,
                                     const void* gamma, const void* beta, void* y, int64_t rows,
                                     int64_t cols, double eps, mbp_act act, void* stream);
+
+/*
+ * Row softmax over the last dimension, for every row i < rows:
+ *   m_i = max_j x[i,j];  l_i = sum_j exp(x[i,j] - m_i);  y[i,j] = exp(x[i,j] - m_i) / l_i
+ * ([P1] section 4.2: normalised by the row maximum, with the running
+ * max / sum statistics; [P3] section 4.2 lists softmax as the "Reduce +
+ * Element-wise" fusion pattern).  One launch; the row is read once and
+ * written once.  x, y: device [rows, cols], dense, in `dtype` (MBP_F32,
+ * MBP_BF16 or MBP_F16); y == x is allowed.  cols <= MBP_MAX_COLS.
+ * Arithmetic in fp32 with one rounding to `dtype` at the store; -inf entries
+ * (masks) give exactly 0, a row of -inf only gives NaN (0/0), a NaN makes its
+ * row NaN.  Results are deterministic (fixed reduction order).
+ */
+mbp_status fused_softmax(mbp_dtype dtype, const void* x, void* y, int64_t rows, int64_t cols,
+                         void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Two-dimensional forms with row strides and 16-bit storage.  The pages'

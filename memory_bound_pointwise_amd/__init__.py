@@ -35,6 +35,7 @@ SIGNATURES = [
     ("fused_pointwise_chain", _I, [_P, _P, _P, _P, _I64, _D, _P]),
     ("fused_row_mean_epilogue", _I, [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _P]),
     ("fused_add_layernorm_gelu", _I, [_I, _P, _P, _P, _P, _P, _I64, _I64, _D, _I, _P]),
+    ("fused_softmax", _I, [_I, _P, _P, _I64, _I64, _P]),
     ("fused_pointwise_chain_2d", _I, [_I, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _D, _P]),
     ("fused_row_mean_epilogue_2d", _I, [_I, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _D, _D, _P]),
     ("unfused_pointwise_chain", _I, [_P, _P, _P, _P, _I64, _D, _P, _SZ, _P]),
@@ -253,6 +254,22 @@ def fused_row_mean_epilogue_2d(x, bias, gamma, beta, alpha=1.1, c=0.1, out=None)
     y, yp, ldy = _out_2d(out, rows, cols, x.dtype, x.device)
     _call("fused_row_mean_epilogue_2d", _DTYPES_2D[x.dtype], xp, ldx, vec[0], vec[1], vec[2], yp, ldy, rows,
           cols, float(alpha), float(c), _stream(x))
+    return y
+
+
+def fused_softmax(x, out=None):
+    """Row softmax over the last dimension (fp32, bf16 or fp16; one launch)."""
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    if x.dtype not in _DTYPES_2D:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    _check(x, "x", (x.dtype,))
+    _check(out, "out", (x.dtype,), x.device)
+    rows, cols = _rows_cols(x)
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape:
+        raise ValueError("out has the wrong shape")
+    _call("fused_softmax", _DTYPES_2D[x.dtype], _ptr(x), _ptr(y), rows, cols, _stream(x))
     return y
 
 

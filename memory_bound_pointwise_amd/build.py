@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libmbp.so")
 ARCH = os.environ.get("MBP_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["abi.cpp", "fused_pointwise.hip", "fused_tenop.hip", "fused_ln_f32.hip",
-           "fused_ln_bf16.hip", "unfused.hip"]
+           "fused_ln_bf16.hip", "fused_softmax.hip", "unfused.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

@@ -320,6 +320,14 @@ mbp_status fused_row_mean_epilogue_2d(mbp_dtype dtype, const void* x, int64_t ld
                   "fused_row_mean_epilogue_2d");
 }
 
+mbp_status fused_softmax(mbp_dtype dtype, const void* x, void* y, int64_t rows, int64_t cols,
+                         void* stream) {
+  mbp_status st = check_2d(dtype, {{x, cols}}, y, cols, rows, cols, MBP_MAX_COLS, x);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  return from_hip(mbp::launch_softmax(dtype, x, y, rows, cols, as_stream(stream)), "fused_softmax");
+}
+
 mbp_status unfused_pointwise_chain(const float* x, const float* b1, const float* b2, float* y,
                                    int64_t n, double scale, void* workspace,
                                    size_t workspace_bytes, void* stream) {

@@ -15,6 +15,8 @@ hipError_t launch_chain(const float* x, const float* b1, const float* b2, float*
 hipError_t launch_chain_2d(int dtype, const void* x, int64_t ldx, const void* b1, int64_t ldb1,
                           const void* b2, int64_t ldb2, void* y, int64_t ldy, int64_t rows, int64_t cols,
                           double scale, hipStream_t s);
+// row softmax over the last dimension (dtype 0 fp32, 1 bf16, 2 fp16)
+hipError_t launch_softmax(int dtype, const void* x, void* y, int64_t rows, int64_t cols, hipStream_t s);
 hipError_t launch_row_mean_2d(int dtype, const void* x, int64_t ldx, const void* bias, const void* gamma,
                               const void* beta, void* y, int64_t ldy, int64_t rows, int64_t cols,
                               double alpha, double c, hipStream_t s);

@@ -404,7 +404,13 @@ def test_next_full_workload(mbp, name):
     d = W.generate(w)
     fmt = w.dtype
     rows = sample_rows(w.rows)
-    if w.kind == "chain2d":
+    if w.kind == "softmax":
+        x = to_dev(d["x"])
+        y1 = mbp.fused_softmax(x)
+        y2 = mbp.fused_softmax(x)
+        exact = oracle.softmax(_as_f32(d["x"])[rows])
+        ys = y1[torch.from_numpy(rows).cuda()]
+    elif w.kind == "chain2d":
         x, b1, b2 = (to_dev(d[k]) for k in ("x", "b1", "b2"))
         y1 = mbp.fused_pointwise_chain_2d(x, b1, b2, w.params["scale"])
         y2 = mbp.fused_pointwise_chain_2d(x, b1, b2, w.params["scale"])
@@ -431,6 +437,64 @@ def test_next_full_workload(mbp, name):
     assert torch.equal(y1.contiguous().view(torch.int16), y2.contiguous().view(torch.int16)), "not deterministic"
     worst, n_off = check_ulp16(bits16(ys), exact, fmt, name)
     print(f"{name}: {len(rows)} sampled rows, max {worst} ulp, {n_off} elements 1 ulp off")
+
+
+# ------------------------------------------------------------------ row softmax
+
+SM_COLS = [1, 7, 8, 33, 255, 256, 1000, 1024, 4095, 4096, 8192, 12288, 16384]
+
+
+def _softmax_gate(y, exact, fmt, what):
+    if fmt == "f32":
+        return check_f32(to_host(y), exact, what)
+    return check_ulp16(bits16(y), exact, fmt, what)
+
+
+@pytest.mark.parametrize("fmt,dtype", DT2D, ids=[d[0] for d in DT2D])
+@pytest.mark.parametrize("cols", SM_COLS)
+@pytest.mark.parametrize("scale", [1.0, 8.0])
+def test_softmax_shapes(mbp, fmt, dtype, cols, scale):
+    rng = np.random.default_rng([21, cols, int(scale)])
+    rows = 9 if cols > 4096 else 37
+    xh, xf = _stored(rng, (rows, cols), dtype, scale)
+    y = mbp.fused_softmax(xh.cuda())
+    _softmax_gate(y, oracle.softmax(xf), fmt, f"softmax {fmt} {rows}x{cols} scale {scale}")
+
+
+@pytest.mark.parametrize("fmt,dtype", DT2D, ids=[d[0] for d in DT2D])
+def test_softmax_masks_in_place_and_misaligned(mbp, fmt, dtype):
+    rng = np.random.default_rng(22)
+    rows, cols = 24, 1024
+    xh, xf = _stored(rng, (rows, cols), dtype, 3.0)
+    mask = rng.random((rows, cols)) < 0.3
+    mask[5, :] = True                  # a fully masked row: 0/0 = NaN
+    mask[6, :] = True
+    mask[6, 777] = False               # a single surviving entry: 1 there, 0 elsewhere
+    xh[torch.from_numpy(mask)] = float("-inf")
+    xf = xh.float().numpy()
+    exact = oracle.softmax(xf)
+    assert np.isnan(exact[5]).all() and exact[6, 777] == 1.0
+    y = mbp.fused_softmax(xh.cuda())
+    yh = y.float().cpu().numpy()
+    assert np.isnan(yh[5]).all(), "a fully masked row must be NaN"
+    ok = np.ones(rows, bool)
+    ok[5] = False
+    # masked entries are exactly 0 (unmasked ones may round to 0 too in fp16:
+    # the gate below compares them with the exact value rounded once)
+    assert (yh[ok][mask[ok]] == 0).all(), "masked entries must be exactly 0"
+    assert yh[6, 777] == 1.0
+    _softmax_gate(y[torch.from_numpy(ok).cuda()], exact[ok], fmt, f"softmax masked {fmt}")
+    # in place
+    xd = xh.cuda()
+    mbp.fused_softmax(xd, out=xd)
+    assert torch.equal(xd.view(torch.int16) if xd.element_size() == 2 else xd.view(torch.int32),
+                       y.view(torch.int16) if y.element_size() == 2 else y.view(torch.int32)), "in place differs"
+    # x one element past a 16-byte boundary: the element path, same results
+    buf = torch.zeros(rows * cols + 8, dtype=dtype, device="cuda")
+    xs = buf[1:1 + rows * cols].view(rows, cols)
+    xs.copy_(xh.cuda())
+    y2 = mbp.fused_softmax(xs)
+    _softmax_gate(y2[torch.from_numpy(ok).cuda()], exact[ok], fmt, f"softmax misaligned {fmt}")
 
 
 # ------------------------------------------------------------------ unfused variants

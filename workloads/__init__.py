@@ -34,7 +34,7 @@ import numpy as np
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "chain" | "row_mean" | "layernorm" | "chain2d" | "row_mean2d"
+    kind: str            # "chain" | "row_mean" | "layernorm" | "chain2d" | "row_mean2d" | "softmax"
     seed: int
     sub: int = 0
     n: int = 0           # chain: element count
@@ -62,6 +62,8 @@ class Workload:
             return es * (3 * self.rows * self.cols + self.cols)        # x, b2 in, y out; b1 one row
         if self.kind == "row_mean2d":
             return es * (2 * self.rows * self.cols + 3 * self.cols)    # x in, y out; bias/gamma/beta
+        if self.kind == "softmax":
+            return es * 2 * self.rows * self.cols                      # x in, y out
         es = 2 if self.dtype == "bf16" else 4
         tensors = 3 if self.residual else 2           # x (+ residual) in, y out
         return es * tensors * self.rows * self.cols + es * 2 * self.cols   # + gamma, beta
@@ -90,11 +92,16 @@ BY_NAME = {w.name: w for w in WORKLOADS}
 #            for every row (stride 0), y dense; bf16.
 #   row_mean2d: x and y [rows, cols] inside rows of params["ld"] elements
 #            (padded rows), bias / gamma / beta [cols]; fp16.
+#   softmax: x [rows, cols] ~ N(0, 1), y dense; bf16.
 NEXT_WORKLOADS = [
     Workload("chain2d_16384x4096_bf16_bcast", "chain2d", seed=6, rows=16384, cols=4096, dtype="bf16",
              params=dict(scale=0.5)),
     Workload("tenop2d_8192x1024_f16_ld1056", "row_mean2d", seed=7, rows=8192, cols=1024, dtype="f16",
              params=dict(alpha=1.1, c=0.1, ld=1056)),
+    # row softmax at the attention-probability shape of the PyTorch
+    # operator-fusion practice post, section 4.1 (batch 1, 32 heads,
+    # seq_len 4096: probs of 32 x 4096 x 4096, i.e. 131072 rows of 4096)
+    Workload("softmax_131072x4096_bf16", "softmax", seed=8, rows=131072, cols=4096, dtype="bf16"),
 ]
 NEXT_BY_NAME = {w.name: w for w in NEXT_WORKLOADS}
 
@@ -200,6 +207,8 @@ def generate(w: Workload, cols: int | None = None) -> dict:
         return dict(x=store(_normal_f32((s, u, 0), rows, c), w.dtype),
                     b1=store(_rng(s, u, 1).standard_normal(c).astype(np.float32), w.dtype),
                     b2=store(_normal_f32((s, u, 2), rows, c), w.dtype))
+    if w.kind == "softmax":
+        return dict(x=store(_normal_f32((s, u, 0), rows, c), w.dtype))
     if w.kind == "row_mean2d":
         return dict(x=store(_normal_f32((s, u, 0), rows, c), w.dtype),
                     **{k: store(_rng(s, u, i + 1).standard_normal(c).astype(np.float32), w.dtype)
