@@ -71,6 +71,11 @@ def _bind(lib):
     lib.oracle_round_to_bf16.restype = None
     lib.oracle_softmax.argtypes = [P, I64, I64, P]
     lib.oracle_softmax.restype = I
+    lib.oracle_philox4x32_10.argtypes = [P, P, I64, P]
+    lib.oracle_philox4x32_10.restype = None
+    U32, U64 = ctypes.c_uint32, ctypes.c_uint64
+    lib.oracle_ln_relu_dropout.argtypes = [I, P, P, P, I64, I64, D, U32, I, D, U64, U64, I, P]
+    lib.oracle_ln_relu_dropout.restype = I
     return lib
 
 
@@ -174,4 +179,45 @@ def softmax(x, lib=None):
         raise ValueError("x must be 2-D")
     y = np.empty(x.shape, dtype=np.float64)
     _check(lib.oracle_softmax(_ptr(x), x.shape[0], x.shape[1], _ptr(y)), "softmax")
+    return y
+
+
+def philox4x32_10(ctr, key, lib=None):
+    """Philox4x32-10 blocks: ctr [n, 4] uint32, key [n, 2] uint32 -> [n, 4] uint32."""
+    lib = lib or load()
+    ctr = np.ascontiguousarray(ctr, dtype=np.uint32).reshape(-1, 4)
+    key = np.ascontiguousarray(key, dtype=np.uint32).reshape(-1, 2)
+    out = np.empty_like(ctr)
+    lib.oracle_philox4x32_10(_ptr(ctr), _ptr(key), ctr.shape[0], _ptr(out))
+    return out
+
+
+def dropout_threshold(p):
+    """(threshold, threshold_hi, scale) of drop probability p: an element is
+    dropped when its random word is below round(p * 2^32); kept ones are
+    scaled by 1 / (1 - p)."""
+    if not 0.0 <= p <= 1.0:
+        raise ValueError("p must be in [0, 1]")
+    t = int(round(p * 2.0 ** 32))
+    scale = 0.0 if p == 1.0 else 1.0 / (1.0 - p)
+    return (t & 0xFFFFFFFF, 1 if t >= 2 ** 32 else 0, scale)
+
+
+def ln_relu_dropout(x, gamma, beta, p=0.1, seed=0, offset=0, eps=1e-5, mode=EXACT, lib=None):
+    """LayerNorm -> ReLU -> Dropout (training semantics) over the last dimension."""
+    lib = lib or load()
+    if x.dtype == np.uint16:
+        dtype, cast = BF16, (lambda a: np.ascontiguousarray(a, dtype=np.uint16))
+    elif x.dtype == np.float32:
+        dtype, cast = F32, _f32
+    else:
+        raise TypeError("x must be float32 or uint16 (bf16 bits)")
+    x, gamma, beta = cast(x), cast(gamma), cast(beta)
+    rows, cols = x.shape
+    if gamma.shape != (cols,) or beta.shape != (cols,):
+        raise ValueError("gamma/beta length must equal cols")
+    t, thi, scale = dropout_threshold(p)
+    y = np.empty((rows, cols), dtype=np.float64)
+    _check(lib.oracle_ln_relu_dropout(dtype, _ptr(x), _ptr(gamma), _ptr(beta), rows, cols, eps, t, thi,
+                                      scale, seed, offset, mode, _ptr(y)), "ln_relu_dropout")
     return y

@@ -408,3 +408,86 @@ int oracle_softmax(const float* x, int64_t rows, int64_t cols, double* y) {
   free(m); free(e); free(l);
   return 0;
 }
+
+/* ---- counter-based random numbers: Philox4x32-10 ---------------------------
+ * J. K. Salmon, M. A. Moraes, R. O. Dror and D. E. Shaw, "Parallel random
+ * numbers: as easy as 1, 2, 3" (SC'11), the Philox-4x32 generator with 10
+ * rounds: a 128-bit counter (c0..c3) and a 64-bit key (k0, k1).  One round
+ * multiplies c0 and c2 by the constants 0xD2511F53 and 0xCD9E8D57 into 64-bit
+ * products (hi, lo) and forms the new counter
+ *   (hi(c2 * M1) ^ c1 ^ k0,  lo(c2 * M1),  hi(c0 * M0) ^ c3 ^ k1,  lo(c0 * M0));
+ * between rounds the key is bumped by the Weyl constants 0x9E3779B9 and
+ * 0xBB67AE85.  The output of 10 rounds is four 32-bit words. */
+static void philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+  uint32_t c[4] = {ctr_in[0], ctr_in[1], ctr_in[2], ctr_in[3]};
+  uint32_t k0 = key_in[0], k1 = key_in[1];
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    uint32_t n1 = (uint32_t)p1;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    uint32_t n3 = (uint32_t)p0;
+    c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
+  }
+  out[0] = c[0]; out[1] = c[1]; out[2] = c[2]; out[3] = c[3];
+}
+
+/* exported for the known-answer pins: n blocks, counters and keys interleaved
+ * (ctr: 4 words per block, key: 2 words per block) */
+void oracle_philox4x32_10(const uint32_t* ctr, const uint32_t* key, int64_t n, uint32_t* out) {
+  for (int64_t i = 0; i < n; ++i) philox4x32_10(ctr + 4 * i, key + 2 * i, out + 4 * i);
+}
+
+/* The random word of element i of a call with (seed, offset): word i mod 4 of
+ * Philox4x32-10 with key = (seed low, seed high) and counter =
+ * (q low, q high, offset low, offset high), q = i div 4. */
+static uint32_t dropout_word(uint64_t seed, uint64_t offset, uint64_t i) {
+  const uint64_t q = i >> 2;
+  const uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), (uint32_t)offset, (uint32_t)(offset >> 32)};
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  philox4x32_10(ctr, key, out);
+  return out[i & 3];
+}
+
+/* ---- LayerNorm -> ReLU -> Dropout ------------------------------------------
+ * [P2] section 2.1: y = dropout(relu(layer_norm(x, weight, bias)), p), three
+ * element-wise stages after the row statistics, fused there into one kernel.
+ * Ops in order:
+ *   u = LayerNorm(x) * gamma + beta      (biased variance, eps inside the root,
+ *                                          as oracle_add_layernorm_gelu)
+ *   r = max(u, 0)                         (relu; NaN passes through)
+ *   y = keep_i ? r * scale : 0            (dropout; training semantics)
+ * keep_i: element i = row * cols + col is kept iff its random word (above) is
+ * >= threshold; threshold = round(p * 2^32), so an element is dropped with
+ * probability threshold / 2^32 = p to within 2^-33; scale = 1 / (1 - p).  The
+ * caller passes threshold and scale (p = 1: threshold 2^32 drops everything).
+ * Modes: ORACLE_EXACT, binary64 throughout; ORACLE_SEQ3 stores u, r and y in
+ * the I/O type (three eager launches).  dtype ORACLE_F32 / ORACLE_BF16 as for
+ * the LayerNorm oracle; threshold_hi = 1 means threshold 2^32. */
+int oracle_ln_relu_dropout(int dtype, const void* x, const void* gamma, const void* beta, int64_t rows,
+                           int64_t cols, double eps, uint32_t threshold, int threshold_hi, double scale,
+                           uint64_t seed, uint64_t offset, int mode, double* y) {
+  if (mode != ORACLE_EXACT && mode != ORACLE_SEQ3) return -1;
+  const int seq3 = mode == ORACLE_SEQ3;
+  int rc = oracle_add_layernorm_gelu(dtype, x, NULL, gamma, beta, rows, cols, eps, ORACLE_ACT_NONE,
+                                     mode, y);
+  if (rc != 0) return rc;
+  const int64_t n = rows * cols;
+  /* op: relu */
+  for (int64_t k = 0; k < n; ++k) y[k] = (y[k] < 0.0) ? 0.0 : y[k];
+  /* op: dropout */
+  for (int64_t k = 0; k < n; ++k) {
+    const uint32_t w = dropout_word(seed, offset, (uint64_t)k);
+    const int keep = !threshold_hi && w >= threshold;
+    double v = keep ? y[k] * scale : 0.0;
+    if (seq3) v = rstore(dtype, v);
+    y[k] = v;
+  }
+  return 0;
+}

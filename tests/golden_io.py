@@ -12,6 +12,6 @@ def read(name):
             if not line or line.startswith("#"):
                 continue
             key, vals = line.split(":", 1)
-            nums = [float(v) for v in vals.split()]
+            nums = [int(v, 16) if v.startswith("0x") else float(v) for v in vals.split()]
             out[key.strip()] = nums[0] if len(nums) == 1 else nums
     return out

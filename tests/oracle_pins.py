@@ -538,10 +538,64 @@ def pin_softmax_torch(lib):
     assert np.all(np.abs(s - 1) < 1e-13), "rows sum to 1"
 
 
+def pin_philox_kat(lib):
+    g = read("philox_kat.txt")
+    for k in range(3):
+        ctr = np.array([g[f"ctr{k}"]], np.uint32)
+        key = np.array([g[f"key{k}"]], np.uint32)
+        out = oracle.philox4x32_10(ctr, key, lib=lib)[0]
+        assert list(out) == g[f"out{k}"], f"Philox4x32-10 known answer {k}: {[hex(v) for v in out]}"
+
+
+def _ln_case_pin(r, rows, cols, dtype="f32"):
+    x = (r.standard_normal((rows, cols)) * 2 + 0.3).astype(np.float32)
+    g = (1 + 0.1 * r.standard_normal(cols)).astype(np.float32)
+    b = (0.1 * r.standard_normal(cols)).astype(np.float32)
+    if dtype == "bf16":
+        to = lambda a: oracle.to_bf16(a, lib=None)
+        return to(x), to(g), to(b)
+    return x, g, b
+
+
+def pin_dropout(lib):
+    r = _rng(40)
+    x, g, b = _ln_case_pin(r, 64, 1000)
+    relu_ln = np.maximum(oracle.add_layernorm_gelu(x, None, g, b, act=oracle.ACT_NONE, lib=lib), 0.0)
+    # p = 0 keeps everything unscaled; p = 1 drops everything
+    assert np.array_equal(oracle.ln_relu_dropout(x, g, b, p=0.0, seed=5, lib=lib), relu_ln), "p = 0"
+    assert not oracle.ln_relu_dropout(x, g, b, p=1.0, seed=5, lib=lib).any(), "p = 1"
+    # p = 0.1: kept values are relu * 1/(1 - p) exactly, dropped ones 0, and
+    # the kept set is word >= round(p 2^32) for word i mod 4 of block (i div 4, offset)
+    p, seed, offset = 0.1, 0x123456789ABC, 7
+    y = oracle.ln_relu_dropout(x, g, b, p=p, seed=seed, offset=offset, lib=lib)
+    n = x.size
+    q = np.arange((n + 3) // 4, dtype=np.uint64)
+    ctr = np.stack([q & 0xFFFFFFFF, q >> 32, np.full_like(q, offset & 0xFFFFFFFF),
+                    np.full_like(q, offset >> 32)], axis=1).astype(np.uint32)
+    key = np.tile(np.array([seed & 0xFFFFFFFF, seed >> 32], np.uint32), (len(q), 1))
+    words = oracle.philox4x32_10(ctr, key, lib=lib).reshape(-1)[:n].reshape(x.shape)
+    keep = words >= np.uint32(round(p * 2 ** 32))
+    assert np.array_equal(y[keep], relu_ln[keep] * (1.0 / (1.0 - p))), "kept values"
+    assert not y[~keep].any(), "dropped values are 0"
+    # the drop fraction is p within 5 binomial standard deviations
+    frac = 1.0 - keep.mean()
+    assert abs(frac - p) < 5 * math.sqrt(p * (1 - p) / n), f"drop fraction {frac}"
+    # the mask does not depend on the data; another offset or seed gives another mask
+    x2, _, _ = _ln_case_pin(_rng(41), 64, 1000)
+    y2 = oracle.ln_relu_dropout(x2, g, b, p=p, seed=seed, offset=offset, lib=lib)
+    pos = (relu_ln > 0) & (np.maximum(oracle.add_layernorm_gelu(x2, None, g, b, act=oracle.ACT_NONE, lib=lib), 0) > 0)
+    assert np.array_equal((y != 0)[pos], (y2 != 0)[pos]), "mask independent of the data"
+    for s2, o2 in ((seed, offset + 1), (seed + 1, offset)):
+        y3 = oracle.ln_relu_dropout(x, g, b, p=p, seed=s2, offset=o2, lib=lib)
+        agree = ((y3 != 0) == (y != 0))[relu_ln > 0].mean()
+        assert abs(agree - (p * p + (1 - p) ** 2)) < 0.02, f"masks of other (seed, offset) agree {agree}"
+
+
 ALL_PINS = [
     pin_chain_worked, pin_chain_bruteforce, pin_chain_invariants, pin_chain_numpy,
     pin_tenop_worked, pin_tenop_bruteforce, pin_tenop_invariants, pin_tenop_seq,
     pin_ln_worked, pin_ln_closed_forms, pin_ln_bruteforce, pin_ln_torch, pin_gelu,
     pin_residual_zero, pin_bf16_encode, pin_ln_seq, pin_round_f16, pin_round_bf16,
     pin_softmax_worked, pin_softmax_closed_forms, pin_softmax_bruteforce, pin_softmax_torch,
+    pin_philox_kat, pin_dropout,
 ]
