@@ -74,7 +74,7 @@ def _bind(lib):
     lib.oracle_philox4x32_10.argtypes = [P, P, I64, P]
     lib.oracle_philox4x32_10.restype = None
     U32, U64 = ctypes.c_uint32, ctypes.c_uint64
-    lib.oracle_ln_relu_dropout.argtypes = [I, P, P, P, I64, I64, D, U32, I, D, U64, U64, I, P]
+    lib.oracle_ln_relu_dropout.argtypes = [I, P, P, P, I64, I64, D, U32, D, U64, U64, I, P]
     lib.oracle_ln_relu_dropout.restype = I
     return lib
 
@@ -193,14 +193,14 @@ def philox4x32_10(ctr, key, lib=None):
 
 
 def dropout_threshold(p):
-    """(threshold, threshold_hi, scale) of drop probability p: an element is
-    dropped when its random word is below round(p * 2^32); kept ones are
-    scaled by 1 / (1 - p)."""
+    """(threshold, scale) of drop probability p: an element is dropped when
+    its 16 random bits are below round(p * 2^16); kept ones are scaled by
+    1 / (1 - p)."""
     if not 0.0 <= p <= 1.0:
         raise ValueError("p must be in [0, 1]")
-    t = int(round(p * 2.0 ** 32))
+    t = int(round(p * 65536.0))
     scale = 0.0 if p == 1.0 else 1.0 / (1.0 - p)
-    return (t & 0xFFFFFFFF, 1 if t >= 2 ** 32 else 0, scale)
+    return t, scale
 
 
 def ln_relu_dropout(x, gamma, beta, p=0.1, seed=0, offset=0, eps=1e-5, mode=EXACT, lib=None):
@@ -216,8 +216,8 @@ def ln_relu_dropout(x, gamma, beta, p=0.1, seed=0, offset=0, eps=1e-5, mode=EXAC
     rows, cols = x.shape
     if gamma.shape != (cols,) or beta.shape != (cols,):
         raise ValueError("gamma/beta length must equal cols")
-    t, thi, scale = dropout_threshold(p)
+    t, scale = dropout_threshold(p)
     y = np.empty((rows, cols), dtype=np.float64)
-    _check(lib.oracle_ln_relu_dropout(dtype, _ptr(x), _ptr(gamma), _ptr(beta), rows, cols, eps, t, thi,
+    _check(lib.oracle_ln_relu_dropout(dtype, _ptr(x), _ptr(gamma), _ptr(beta), rows, cols, eps, t,
                                       scale, seed, offset, mode, _ptr(y)), "ln_relu_dropout")
     return y

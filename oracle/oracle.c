@@ -443,16 +443,18 @@ void oracle_philox4x32_10(const uint32_t* ctr, const uint32_t* key, int64_t n, u
   for (int64_t i = 0; i < n; ++i) philox4x32_10(ctr + 4 * i, key + 2 * i, out + 4 * i);
 }
 
-/* The random word of element i of a call with (seed, offset): word i mod 4 of
- * Philox4x32-10 with key = (seed low, seed high) and counter =
- * (q low, q high, offset low, offset high), q = i div 4. */
-static uint32_t dropout_word(uint64_t seed, uint64_t offset, uint64_t i) {
-  const uint64_t q = i >> 2;
+/* The 16 random bits of element i of a call with (seed, offset): half i mod 8
+ * of Philox4x32-10 with key = (seed low, seed high) and counter =
+ * (q low, q high, offset low, offset high), q = i div 8 -- word (i mod 8) div 2,
+ * its low half for even i, its high half for odd i. */
+static uint32_t dropout_bits(uint64_t seed, uint64_t offset, uint64_t i) {
+  const uint64_t q = i >> 3;
   const uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), (uint32_t)offset, (uint32_t)(offset >> 32)};
   const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
   uint32_t out[4];
   philox4x32_10(ctr, key, out);
-  return out[i & 3];
+  const uint32_t w = out[(i & 7) >> 1];
+  return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
 /* ---- LayerNorm -> ReLU -> Dropout ------------------------------------------
@@ -463,16 +465,16 @@ static uint32_t dropout_word(uint64_t seed, uint64_t offset, uint64_t i) {
  *                                          as oracle_add_layernorm_gelu)
  *   r = max(u, 0)                         (relu; NaN passes through)
  *   y = keep_i ? r * scale : 0            (dropout; training semantics)
- * keep_i: element i = row * cols + col is kept iff its random word (above) is
- * >= threshold; threshold = round(p * 2^32), so an element is dropped with
- * probability threshold / 2^32 = p to within 2^-33; scale = 1 / (1 - p).  The
- * caller passes threshold and scale (p = 1: threshold 2^32 drops everything).
- * Modes: ORACLE_EXACT, binary64 throughout; ORACLE_SEQ3 stores u, r and y in
- * the I/O type (three eager launches).  dtype ORACLE_F32 / ORACLE_BF16 as for
- * the LayerNorm oracle; threshold_hi = 1 means threshold 2^32. */
+ * keep_i: element i = row * cols + col is kept iff its 16 random bits (above)
+ * are >= threshold; threshold = round(p * 2^16) in [0, 65536], so an element
+ * is dropped with probability threshold / 2^16 = p to within 2^-17 (65536
+ * drops everything); scale = 1 / (1 - p).  The caller passes threshold and
+ * scale.  Modes: ORACLE_EXACT, binary64 throughout; ORACLE_SEQ3 stores u, r
+ * and y in the I/O type (three eager launches).  dtype ORACLE_F32 /
+ * ORACLE_BF16 as for the LayerNorm oracle. */
 int oracle_ln_relu_dropout(int dtype, const void* x, const void* gamma, const void* beta, int64_t rows,
-                           int64_t cols, double eps, uint32_t threshold, int threshold_hi, double scale,
-                           uint64_t seed, uint64_t offset, int mode, double* y) {
+                           int64_t cols, double eps, uint32_t threshold, double scale, uint64_t seed,
+                           uint64_t offset, int mode, double* y) {
   if (mode != ORACLE_EXACT && mode != ORACLE_SEQ3) return -1;
   const int seq3 = mode == ORACLE_SEQ3;
   int rc = oracle_add_layernorm_gelu(dtype, x, NULL, gamma, beta, rows, cols, eps, ORACLE_ACT_NONE,
@@ -483,8 +485,8 @@ int oracle_ln_relu_dropout(int dtype, const void* x, const void* gamma, const vo
   for (int64_t k = 0; k < n; ++k) y[k] = (y[k] < 0.0) ? 0.0 : y[k];
   /* op: dropout */
   for (int64_t k = 0; k < n; ++k) {
-    const uint32_t w = dropout_word(seed, offset, (uint64_t)k);
-    const int keep = !threshold_hi && w >= threshold;
+    const uint32_t w = dropout_bits(seed, offset, (uint64_t)k);
+    const int keep = w >= threshold;
     double v = keep ? y[k] * scale : 0.0;
     if (seq3) v = rstore(dtype, v);
     y[k] = v;

@@ -565,16 +565,17 @@ def pin_dropout(lib):
     assert np.array_equal(oracle.ln_relu_dropout(x, g, b, p=0.0, seed=5, lib=lib), relu_ln), "p = 0"
     assert not oracle.ln_relu_dropout(x, g, b, p=1.0, seed=5, lib=lib).any(), "p = 1"
     # p = 0.1: kept values are relu * 1/(1 - p) exactly, dropped ones 0, and
-    # the kept set is word >= round(p 2^32) for word i mod 4 of block (i div 4, offset)
+    # the kept set is bits >= round(p 2^16) for half i mod 8 of block (i div 8, offset)
     p, seed, offset = 0.1, 0x123456789ABC, 7
     y = oracle.ln_relu_dropout(x, g, b, p=p, seed=seed, offset=offset, lib=lib)
     n = x.size
-    q = np.arange((n + 3) // 4, dtype=np.uint64)
+    q = np.arange((n + 7) // 8, dtype=np.uint64)
     ctr = np.stack([q & 0xFFFFFFFF, q >> 32, np.full_like(q, offset & 0xFFFFFFFF),
                     np.full_like(q, offset >> 32)], axis=1).astype(np.uint32)
     key = np.tile(np.array([seed & 0xFFFFFFFF, seed >> 32], np.uint32), (len(q), 1))
-    words = oracle.philox4x32_10(ctr, key, lib=lib).reshape(-1)[:n].reshape(x.shape)
-    keep = words >= np.uint32(round(p * 2 ** 32))
+    words = oracle.philox4x32_10(ctr, key, lib=lib).reshape(-1)
+    halves = np.stack([words & 0xFFFF, words >> 16], axis=1).reshape(-1)[:n].reshape(x.shape)
+    keep = halves >= round(p * 65536)
     assert np.array_equal(y[keep], relu_ln[keep] * (1.0 / (1.0 - p))), "kept values"
     assert not y[~keep].any(), "dropped values are 0"
     # the drop fraction is p within 5 binomial standard deviations

@@ -49,8 +49,9 @@ MUTANTS = [
     ("philox: nine rounds", "for (int r = 0; r < 10; ++r) {", "for (int r = 0; r < 9; ++r) {"),
     ("philox: no key bump", "k0 += 0x9E3779B9u;", ""),
     ("philox: c1 and c3 swapped", "uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;", "uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[3] ^ k0;"),
-    ("dropout: word 0 for every element", "return out[i & 3];", "return out[0];"),
-    ("dropout: keep below the threshold", "const int keep = !threshold_hi && w >= threshold;", "const int keep = !threshold_hi && w < threshold;"),
+    ("dropout: word 0 for every element", "const uint32_t w = out[(i & 7) >> 1];", "const uint32_t w = out[0];"),
+    ("dropout: low half for every element", "return (i & 1) ? (w >> 16) : (w & 0xFFFFu);", "return w & 0xFFFFu;"),
+    ("dropout: keep below the threshold", "const int keep = w >= threshold;", "const int keep = w < threshold;"),
     ("dropout: no rescale", "double v = keep ? y[k] * scale : 0.0;", "double v = keep ? y[k] : 0.0;"),
     ("dropout: relu dropped", "for (int64_t k = 0; k < n; ++k) y[k] = (y[k] < 0.0) ? 0.0 : y[k];", ""),
 ]
