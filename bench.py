@@ -259,6 +259,12 @@ def main():
     nxt = {}
     if not args.only and not args.no_next:
         def build_next(w, d):
+            if w.kind == "ln_relu_dropout":
+                x, g, b = (to_dev(d[k]) for k in ("x", "gamma", "beta"))
+                y = torch.empty_like(x)
+                pr = w.params
+                return lambda: mbp.fused_layernorm_relu_dropout(x, g, b, pr["p"], pr["seed"], pr["offset"],
+                                                                pr["eps"], out=y)
             if w.kind == "softmax":
                 x = to_dev(d["x"])
                 y = torch.empty_like(x)
@@ -289,6 +295,20 @@ def main():
                            "gbps": round(w.compulsory_bytes / (med * 1e-6) / 1e9, 1),
                            "frac_of_peak": round(w.compulsory_bytes / (med * 1e-6) / 1e9 / PEAK_GBPS, 4)}
             del fns
+            if w.kind == "ln_relu_dropout" and args.unfused_reps:
+                # the three eager launches of the same expression
+                x, g, b = (to_dev(d[k]) for k in ("x", "gamma", "beta"))
+                y = torch.empty_like(x)
+                ws = torch.empty(mbp.workspace_bytes(mbp.OP_LN_RELU_DROPOUT, mbp.BF16, w.rows, w.cols),
+                                 dtype=torch.uint8, device=dev)
+                pr = w.params
+                ufn = lambda: mbp.unfused_layernorm_relu_dropout(x, g, b, pr["p"], pr["seed"], pr["offset"],
+                                                                 pr["eps"], out=y, workspace=ws)
+                uus, _ = batch_times([ufn], args.unfused_reps)
+                um = statistics.median(uus)
+                nxt[w.name].update({"unfused_us_median": round(um, 3), "launches_unfused": 3,
+                                    "speedup_vs_unfused": round(um / med, 3)})
+                del x, g, b, y, ws
         torch.cuda.synchronize()
 
     per = {}

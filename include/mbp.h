@@ -66,7 +66,12 @@ typedef enum { MBP_F32 = 0, MBP_BF16 = 1, MBP_F16 = 2 } mbp_dtype;
 
 typedef enum { MBP_ACT_NONE = 0, MBP_ACT_GELU_TANH = 1 } mbp_act;
 
-typedef enum { MBP_OP_CHAIN = 0, MBP_OP_ROW_MEAN = 1, MBP_OP_LAYERNORM = 2 } mbp_op;
+typedef enum {
+  MBP_OP_CHAIN = 0,
+  MBP_OP_ROW_MEAN = 1,
+  MBP_OP_LAYERNORM = 2,
+  MBP_OP_LN_RELU_DROPOUT = 3
+} mbp_op;
 
 /* Granularity of the unfused variants. */
 #define MBP_UNFUSED_PRIMITIVE 0 /* one launch per primitive op (4 / 10 / 5 / 7 launches) */
@@ -124,6 +129,26 @@ mbp_status fused_row_mean_epilogue(const float* x, const float* bias, const floa
 mbp_status fused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void* residual,
                                     const void* gamma, const void* beta, void* y, int64_t rows,
                                     int64_t cols, double eps, mbp_act act, void* stream);
+
+/*
+ * LayerNorm -> ReLU -> Dropout ([P2] section 2.1: layer_norm, relu, dropout
+ * with p = 0.1 there, three memory round trips fused into one kernel), for
+ * every row i < rows and column j < cols:
+ *   u = (x[i,:] - mean) / sqrt(var + eps) * gamma + beta   (as the LayerNorm above)
+ *   r = max(u, 0);   y[i,j] = keep(k) ? r / (1 - p) : 0,   k = i*cols + j
+ * Dropout in training semantics.  keep(k): the 16 random bits of element k
+ * -- half k mod 8 of the Philox4x32-10 block (counter = (k div 8, offset),
+ * key = seed; J. K. Salmon et al., "Parallel random numbers: as easy as 1, 2,
+ * 3", SC'11) -- are >= round(p * 2^16); p is realised to within 2^-17.  The
+ * mask depends only on (seed, offset, k): the same call gives the same mask,
+ * a caller advances `offset` to draw a new one.  x, y: device [rows, cols] in
+ * `dtype` (MBP_F32 or MBP_BF16); gamma, beta: [cols]; y == x allowed.
+ * p in [0, 1] (p == 1: y = 0).  Arithmetic as fused_add_layernorm_gelu.
+ */
+mbp_status fused_layernorm_relu_dropout(mbp_dtype dtype, const void* x, const void* gamma,
+                                        const void* beta, void* y, int64_t rows, int64_t cols,
+                                        double eps, double p, uint64_t seed, uint64_t offset,
+                                        void* stream);
 
 /*
  * Row softmax over the last dimension, for every row i < rows:
@@ -208,6 +233,17 @@ mbp_status unfused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void
                                       const void* gamma, const void* beta, void* y, int64_t rows,
                                       int64_t cols, double eps, mbp_act act, int granularity,
                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * LayerNorm -> ReLU -> Dropout as the three eager launches of [P2] section
+ * 2.1 (layer_norm, relu, dropout), each result stored in `dtype` in the
+ * workspace (two [rows, cols] buffers; mbp_unfused_workspace_bytes with
+ * MBP_OP_LN_RELU_DROPOUT).  Same mask as the fused entry point.
+ */
+mbp_status unfused_layernorm_relu_dropout(mbp_dtype dtype, const void* x, const void* gamma,
+                                          const void* beta, void* y, int64_t rows, int64_t cols,
+                                          double eps, double p, uint64_t seed, uint64_t offset,
+                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace the unfused variant of `op` needs (bytes; 0 for a no-op shape).
  * For MBP_OP_CHAIN pass rows = 1, cols = n.  has_residual and act matter only

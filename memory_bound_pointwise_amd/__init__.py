@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libmbp.so")
 
 F32, BF16, F16 = 0, 1, 2
 ACT_NONE, ACT_GELU_TANH = 0, 1
-OP_CHAIN, OP_ROW_MEAN, OP_LAYERNORM = 0, 1, 2
+OP_CHAIN, OP_ROW_MEAN, OP_LAYERNORM, OP_LN_RELU_DROPOUT = 0, 1, 2, 3
 UNFUSED_PRIMITIVE, UNFUSED_EAGER = 0, 1
 MAX_COLS = 16384
 
@@ -31,11 +31,14 @@ STATUS_NAMES = {0: "MBP_OK", 1: "MBP_ERR_NULL", 2: "MBP_ERR_SHAPE", 3: "MBP_ERR_
 
 # (name, restype, argtypes) of every symbol that include/mbp.h declares
 _P, _I64, _D, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double, ctypes.c_int, ctypes.c_size_t
+_U64 = ctypes.c_uint64
 SIGNATURES = [
     ("fused_pointwise_chain", _I, [_P, _P, _P, _P, _I64, _D, _P]),
     ("fused_row_mean_epilogue", _I, [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _P]),
     ("fused_add_layernorm_gelu", _I, [_I, _P, _P, _P, _P, _P, _I64, _I64, _D, _I, _P]),
     ("fused_softmax", _I, [_I, _P, _P, _I64, _I64, _P]),
+    ("fused_layernorm_relu_dropout", _I, [_I, _P, _P, _P, _P, _I64, _I64, _D, _D, _U64, _U64, _P]),
+    ("unfused_layernorm_relu_dropout", _I, [_I, _P, _P, _P, _P, _I64, _I64, _D, _D, _U64, _U64, _P, _SZ, _P]),
     ("fused_pointwise_chain_2d", _I, [_I, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _D, _P]),
     ("fused_row_mean_epilogue_2d", _I, [_I, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _D, _D, _P]),
     ("unfused_pointwise_chain", _I, [_P, _P, _P, _P, _I64, _D, _P, _SZ, _P]),
@@ -179,6 +182,44 @@ def fused_add_layernorm_gelu(x, residual, gamma, beta, eps=1e-5, act="gelu_tanh"
 def fused_layernorm(x, gamma, beta, eps=1e-5, out=None):
     """Plain LayerNorm (no residual, no activation) over the last dimension."""
     return fused_add_layernorm_gelu(x, None, gamma, beta, eps=eps, act="none", out=out)
+
+
+def _ln_drop_args(x, gamma, beta, out):
+    dts = (torch.float32, torch.bfloat16)
+    _check(x, "x", dts)
+    for t, n in ((gamma, "gamma"), (beta, "beta"), (out, "out")):
+        _check(t, n, (x.dtype,), x.device)
+    rows, cols = _rows_cols(x)
+    for t, n in ((gamma, "gamma"), (beta, "beta")):
+        if t.numel() != cols:
+            raise ValueError(f"{n} must have {cols} elements")
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape:
+        raise ValueError("out has the wrong shape")
+    return rows, cols, y
+
+
+def fused_layernorm_relu_dropout(x, gamma, beta, p=0.1, seed=0, offset=0, eps=1e-5, out=None):
+    """dropout(relu(LayerNorm(x) * gamma + beta), p) over the last dimension,
+    training semantics, one launch.  The mask is a function of (seed, offset,
+    element index): Philox4x32-10, 16 bits per element."""
+    rows, cols, y = _ln_drop_args(x, gamma, beta, out)
+    _call("fused_layernorm_relu_dropout", _dtype_code(x), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y),
+          rows, cols, float(eps), float(p), int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1),
+          _stream(x))
+    return y
+
+
+def unfused_layernorm_relu_dropout(x, gamma, beta, p=0.1, seed=0, offset=0, eps=1e-5, out=None,
+                                   workspace=None):
+    """The same as three launches (layer_norm, relu, dropout) through HBM."""
+    rows, cols, y = _ln_drop_args(x, gamma, beta, out)
+    nb = workspace_bytes(OP_LN_RELU_DROPOUT, _dtype_code(x), rows, cols)
+    ws = _workspace(nb, x.device, workspace)
+    _call("unfused_layernorm_relu_dropout", _dtype_code(x), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y),
+          rows, cols, float(eps), float(p), int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1),
+          _ptr(ws), ws.numel() * ws.element_size(), _stream(x))
+    return y
 
 
 # ------------------------------------------------------------------ two-dimensional forms

@@ -254,6 +254,22 @@ mbp_status check_2d(mbp_dtype dtype, std::initializer_list<Operand2d> ins, void*
   return MBP_OK;
 }
 
+// Dropout description of drop probability p: threshold round(p * 2^16) on
+// 16 random bits, scale 1 / (1 - p) (p == 1 drops everything).
+mbp::Drop make_drop(double p, uint64_t seed, uint64_t offset) {
+  mbp::Drop d;
+  d.seed = seed;
+  d.offset = offset;
+  d.thr = (uint32_t)std::llround(p * 65536.0);
+  d.scale = p >= 1.0 ? 0.0f : (float)(1.0 / (1.0 - p));
+  return d;
+}
+
+mbp_status check_dropout_p(double p) {
+  if (!(p >= 0.0 && p <= 1.0)) return fail(MBP_ERR_ARG, "p must be in [0, 1]");
+  return MBP_OK;
+}
+
 }  // namespace
 
 
@@ -285,7 +301,7 @@ mbp_status fused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void* 
   mbp_status st = check_ln(dtype, x, residual, gamma, beta, y, rows, cols, eps, act, true);
   if (st != MBP_OK) return st;
   if (rows == 0) return ok();
-  return from_hip(mbp::launch_layernorm(dtype, x, residual, gamma, beta, y, rows, cols, eps, act,
+  return from_hip(mbp::launch_layernorm(dtype, x, residual, gamma, beta, y, rows, cols, eps, act, nullptr,
                                         as_stream(stream)),
                   "fused_add_layernorm_gelu");
 }
@@ -326,6 +342,48 @@ mbp_status fused_softmax(mbp_dtype dtype, const void* x, void* y, int64_t rows, 
   if (st != MBP_OK) return st;
   if (rows == 0) return ok();
   return from_hip(mbp::launch_softmax(dtype, x, y, rows, cols, as_stream(stream)), "fused_softmax");
+}
+
+mbp_status fused_layernorm_relu_dropout(mbp_dtype dtype, const void* x, const void* gamma,
+                                        const void* beta, void* y, int64_t rows, int64_t cols,
+                                        double eps, double p, uint64_t seed, uint64_t offset,
+                                        void* stream) {
+  mbp_status st = check_ln(dtype, x, nullptr, gamma, beta, y, rows, cols, eps, MBP_ACT_NONE, true);
+  if (st != MBP_OK) return st;
+  st = check_dropout_p(p);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  const mbp::Drop d = make_drop(p, seed, offset);
+  return from_hip(mbp::launch_layernorm(dtype, x, nullptr, gamma, beta, y, rows, cols, eps, mbp::kEpiReluDrop,
+                                        &d, as_stream(stream)),
+                  "fused_layernorm_relu_dropout");
+}
+
+mbp_status unfused_layernorm_relu_dropout(mbp_dtype dtype, const void* x, const void* gamma,
+                                          const void* beta, void* y, int64_t rows, int64_t cols,
+                                          double eps, double p, uint64_t seed, uint64_t offset,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  mbp_status st = check_ln(dtype, x, nullptr, gamma, beta, y, rows, cols, eps, MBP_ACT_NONE, false);
+  if (st != MBP_OK) return st;
+  st = check_dropout_p(p);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  const size_t es = dtype == MBP_BF16 ? 2 : 4;
+  const size_t full = (size_t)rows * cols * es, vec = (size_t)cols * es;
+  Carver c{(char*)workspace};
+  void* ln_out = c.take(full);
+  void* relu_out = c.take(full);
+  st = check_workspace(workspace, workspace_bytes, c.used, {{x, full}, {y, full}, {gamma, vec}, {beta, vec}});
+  if (st != MBP_OK) return st;
+  const mbp::Drop d = make_drop(p, seed, offset);
+  hipStream_t s = as_stream(stream);
+  using namespace mbp;
+  // the three eager launches of [P2] section 2.1: layer_norm, relu, dropout
+  hipError_t e = launch_layernorm(dtype, x, nullptr, gamma, beta, ln_out, rows, cols, eps, kEpiNone, nullptr, s);
+  if (e == hipSuccess) e = launch_ew(EW_RELU, dtype, ln_out, nullptr, 0, nullptr, 0, relu_out, rows, cols, 0.f, s);
+  if (e == hipSuccess)
+    e = launch_ew(EW_DROPOUT, dtype, relu_out, nullptr, 0, nullptr, 0, y, rows, cols, 0.f, s, &d);
+  return from_hip(e, "unfused_layernorm_relu_dropout");
 }
 
 mbp_status unfused_pointwise_chain(const float* x, const float* b1, const float* b2, float* y,
@@ -419,7 +477,7 @@ mbp_status unfused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void
       e = launch_ew(EW_MULADD, D, w.b, gamma, IX_COL, beta, IX_COL, ln_out, rows, cols, 0.f, s);
   } else {
     if (e == hipSuccess)
-      e = launch_layernorm(D, src, nullptr, gamma, beta, ln_out, rows, cols, eps, MBP_ACT_NONE, s);
+      e = launch_layernorm(D, src, nullptr, gamma, beta, ln_out, rows, cols, eps, MBP_ACT_NONE, nullptr, s);
   }
   if (gelu && e == hipSuccess)
     e = launch_ew(EW_GELU, D, w.a, nullptr, 0, nullptr, 0, y, rows, cols, 0.f, s);
@@ -434,6 +492,13 @@ size_t mbp_unfused_workspace_bytes(mbp_op op, mbp_dtype dtype, int64_t rows, int
   switch (op) {
     case MBP_OP_CHAIN: return chain_ws(nullptr, rows * cols, nullptr);
     case MBP_OP_ROW_MEAN: return row_mean_ws(nullptr, rows, cols, nullptr);
+    case MBP_OP_LN_RELU_DROPOUT: {
+      if (dtype != MBP_F32 && dtype != MBP_BF16) return (size_t)-1;
+      Carver c{nullptr};
+      c.take((size_t)rows * cols * (dtype == MBP_BF16 ? 2 : 4));
+      c.take((size_t)rows * cols * (dtype == MBP_BF16 ? 2 : 4));
+      return c.used;
+    }
     case MBP_OP_LAYERNORM:
       if (dtype != MBP_F32 && dtype != MBP_BF16) return (size_t)-1;
       if (granularity != MBP_UNFUSED_PRIMITIVE && granularity != MBP_UNFUSED_EAGER) return (size_t)-1;
@@ -444,8 +509,9 @@ size_t mbp_unfused_workspace_bytes(mbp_op op, mbp_dtype dtype, int64_t rows, int
 }
 
 int mbp_launches_per_call(mbp_op op, int fused, int granularity, int has_residual, mbp_act act) {
-  if (fused) return (op >= MBP_OP_CHAIN && op <= MBP_OP_LAYERNORM) ? 1 : -1;
+  if (fused) return (op >= MBP_OP_CHAIN && op <= MBP_OP_LN_RELU_DROPOUT) ? 1 : -1;
   switch (op) {
+    case MBP_OP_LN_RELU_DROPOUT: return 3;
     case MBP_OP_CHAIN: return 4;
     case MBP_OP_ROW_MEAN: return 10;
     case MBP_OP_LAYERNORM: {

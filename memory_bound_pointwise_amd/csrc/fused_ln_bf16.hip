@@ -7,8 +7,8 @@ namespace mbp {
 
 hipError_t launch_layernorm_bf16(const void* x, const void* residual, const void* gamma,
                                  const void* beta, void* y, int64_t rows, int64_t cols, double eps,
-                                 int act, hipStream_t s) {
-  return ln::launch<BF16IO>(x, residual, gamma, beta, y, rows, cols, eps, act, s);
+                                 int act, const Drop* drop, hipStream_t s) {
+  return ln::launch<BF16IO>(x, residual, gamma, beta, y, rows, cols, eps, act, drop, s);
 }
 
 }  // namespace mbp

@@ -6,13 +6,13 @@ namespace mbp {
 
 hipError_t launch_layernorm_bf16(const void* x, const void* residual, const void* gamma,
                                  const void* beta, void* y, int64_t rows, int64_t cols, double eps,
-                                 int act, hipStream_t s);
+                                 int act, const Drop* drop, hipStream_t s);
 
 hipError_t launch_layernorm(int dtype, const void* x, const void* residual, const void* gamma,
                             const void* beta, void* y, int64_t rows, int64_t cols, double eps,
-                            int act, hipStream_t s) {
-  if (dtype == 1) return launch_layernorm_bf16(x, residual, gamma, beta, y, rows, cols, eps, act, s);
-  return ln::launch<F32IO>(x, residual, gamma, beta, y, rows, cols, eps, act, s);
+                            int act, const Drop* drop, hipStream_t s) {
+  if (dtype == 1) return launch_layernorm_bf16(x, residual, gamma, beta, y, rows, cols, eps, act, drop, s);
+  return ln::launch<F32IO>(x, residual, gamma, beta, y, rows, cols, eps, act, drop, s);
 }
 
 }  // namespace mbp

@@ -101,20 +101,32 @@ __device__ __forceinline__ u32x4 partial_vec(const typename IO::elem* p, int c0,
   return r;
 }
 
-template <class Acc, bool GELU>
+// normalise, affine, then the epilogue: tanh-GeLU, or relu (dropout follows
+// at the store, where the element's index is known)
+template <class Acc, int EPI>
 __device__ __forceinline__ float finish(Acc d, Acc rstd, Acc g, Acc b) {
   const float u = (float)fma_t(d * rstd, g, b);
-  if constexpr (GELU) return gelu_tanh_f32(u);
+  if constexpr (EPI == kEpiGelu) return gelu_tanh_f32(u);
+  if constexpr (EPI == kEpiReluDrop) return (u < 0.0f) ? 0.0f : u;  // relu; NaN passes through
   return u;
+}
+
+// dropout of N outputs with flat indices i0 .. i0 + N - 1
+template <int N, bool ALIGNED>
+__device__ __forceinline__ void apply_dropout(float* o, uint64_t i0, const Drop& drop) {
+  uint32_t h[N];
+  dropout_bits<N, ALIGNED>(i0, drop.seed, drop.offset, h);
+#pragma unroll
+  for (int e = 0; e < N; ++e) o[e] = (h[e] >= drop.thr) ? o[e] * drop.scale : 0.0f;
 }
 
 // ------------------------------------------------------------ aligned rows
 
-template <class IO, int LANES, int VPL, bool RES, bool GELU>
+template <class IO, int LANES, int VPL, bool RES, int EPI>
 __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
     const typename IO::elem* x, const typename IO::elem* res,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
-    typename IO::elem* y, int64_t rows, int cols, double eps_d) {
+    typename IO::elem* y, int64_t rows, int cols, double eps_d, Drop drop) {
   typedef typename Types<IO, RES>::acc Acc;
   typedef typename Types<IO, RES>::val Val;
   constexpr int V = IO::kVec;
@@ -228,10 +240,12 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
       for (int e = 0; e < V; ++e) {
         const Acc d = kInPlace ? (Acc)v[k][e] : (Acc)v[k][e] - mean;
         if constexpr (kPacked)
-          o[e] = finish<Acc, GELU>(d, rstd, (Acc)IO::get(gp[k], e), (Acc)IO::get(bp[k], e));
+          o[e] = finish<Acc, EPI>(d, rstd, (Acc)IO::get(gp[k], e), (Acc)IO::get(bp[k], e));
         else
-          o[e] = finish<Acc, GELU>(d, rstd, (Acc)g[k][e], (Acc)b[k][e]);
+          o[e] = finish<Acc, EPI>(d, rstd, (Acc)g[k][e], (Acc)b[k][e]);
       }
+      if constexpr (EPI == kEpiReluDrop)  // rows start on multiples of V: one aligned group
+        apply_dropout<V, true>(o, (uint64_t)row * (uint64_t)cols + (uint64_t)(vi * V), drop);
       store_nt(reinterpret_cast<u32x4*>(yr) + vi, pack_vec<IO>(o));
     }
   }
@@ -346,7 +360,7 @@ __device__ __forceinline__ u32x4 funnel(const u32x4& lo, const uint32_t* hi, int
 // tensors; the rest (at most the first and last few rows: rows starting
 // within 16 bytes of a tensor's unaligned start or end) take the last
 // `edge_blocks` blocks of the grid, which handle them element by element.
-template <class IO, int LANES, int VPL, bool RES, bool GELU>
+template <class IO, int LANES, int VPL, bool RES, int EPI>
 __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
     const typename IO::elem* x, const typename IO::elem* res,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
@@ -392,7 +406,7 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
     if (live)
       for (int c = lane; c < cols; c += LANES)
         IO::store1(y, e0 + c,
-                   finish<Acc, GELU>((Acc)val(c) - mean, rstd, (Acc)IO::load1(gamma, c), (Acc)IO::load1(beta, c)));
+                   finish<Acc, EPI>((Acc)val(c) - mean, rstd, (Acc)IO::load1(gamma, c), (Acc)IO::load1(beta, c)));
     return;
   }
 
@@ -606,7 +620,7 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const Acc d = kInPlace ? (Acc)v[k][e] : (Acc)v[k][e] - mean;
-        o[e] = finish<Acc, GELU>(d, rstd, (Acc)IO::get(gp[k], e), (Acc)IO::get(bp[k], e));
+        o[e] = finish<Acc, EPI>(d, rstd, (Acc)IO::get(gp[k], e), (Acc)IO::get(bp[k], e));
       }
       const u32x4 ov = pack_vec<IO>(o);
       // window j holds columns V*j - s + e; slot 0 and slot nvec - 1 may
@@ -699,11 +713,11 @@ __device__ __forceinline__ void realign_in(const u32x4 (&c)[VPL + 1], int sb, u3
 #undef MBP_REALIGN_CASE
 }
 
-template <class IO, int LANES, int VPL, bool RES, bool GELU>
+template <class IO, int LANES, int VPL, bool RES, int EPI>
 __global__ __launch_bounds__(block_for(LANES)) void ln_shift_kernel(
     const typename IO::elem* x, const typename IO::elem* res,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
-    typename IO::elem* y, int64_t rows, int cols, double eps_d) {
+    typename IO::elem* y, int64_t rows, int cols, double eps_d, Drop drop) {
   typedef typename IO::elem E;
   typedef typename Types<IO, RES>::acc Acc;
   typedef typename Types<IO, RES>::val Val;
@@ -854,8 +868,10 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_shift_kernel(
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const Acc d = kInPlace ? (Acc)v[k][e] : (Acc)v[k][e] - mean;
-        o[e] = finish<Acc, GELU>(d, rstd, (Acc)IO::get(gp[k], e), (Acc)IO::get(bp[k], e));
+        o[e] = finish<Acc, EPI>(d, rstd, (Acc)IO::get(gp[k], e), (Acc)IO::get(bp[k], e));
       }
+      if constexpr (EPI == kEpiReluDrop)  // slot j holds columns V*j .. V*j + V - 1 of the row
+        apply_dropout<V, false>(o, (uint64_t)(live ? row : 0) * (uint64_t)cols + (uint64_t)(V * slot(k)), drop);
       ov[k] = pack_vec<IO>(o);
     }
     ov[VPL] = ov[VPL - 1];
@@ -937,34 +953,35 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_shift_kernel(
 
 // ------------------------------------------------------------ dispatch
 
-template <class IO, bool RES, bool GELU>
+template <class IO, bool RES, int EPI>
 struct VecSel {
   template <int L, int P>
   struct K {
-    static const void* ptr() { return reinterpret_cast<const void*>(&ln_vec_kernel<IO, L, P, RES, GELU>); }
+    static const void* ptr() { return reinterpret_cast<const void*>(&ln_vec_kernel<IO, L, P, RES, EPI>); }
   };
 };
-template <class IO, bool RES, bool GELU>
+template <class IO, bool RES, int EPI>
 struct ClassSel {
   template <int L, int P>
   struct K {
-    static const void* ptr() { return reinterpret_cast<const void*>(&ln_class_kernel<IO, L, P, RES, GELU>); }
+    static const void* ptr() { return reinterpret_cast<const void*>(&ln_class_kernel<IO, L, P, RES, EPI>); }
   };
 };
-template <class IO, bool RES, bool GELU>
+template <class IO, bool RES, int EPI>
 struct ShiftSel {
   template <int L, int P>
   struct K {
-    static const void* ptr() { return reinterpret_cast<const void*>(&ln_shift_kernel<IO, L, P, RES, GELU>); }
+    static const void* ptr() { return reinterpret_cast<const void*>(&ln_shift_kernel<IO, L, P, RES, EPI>); }
   };
 };
 constexpr int64_t kMaxGrid = 1 << 30;
 constexpr int64_t kShiftGroups = 4;
 constexpr int64_t kClassGroups = 4;
 
-template <class IO, bool RES, bool GELU>
+template <class IO, bool RES, int EPI>
 hipError_t launch_flags(const void* x, const void* res, const void* gamma, const void* beta,
-                        void* y, int64_t rows, int64_t cols, double eps, hipStream_t s) {
+                        void* y, int64_t rows, int64_t cols, double eps, const Drop& drop_in,
+                        hipStream_t s) {
   constexpr int V = IO::kVec;
   const bool aligned = aligned16(x) && aligned16(y) && (!res || aligned16(res)) && aligned16(gamma) &&
                        aligned16(beta) && cols % V == 0;
@@ -976,15 +993,17 @@ hipError_t launch_flags(const void* x, const void* res, const void* gamma, const
   const int64_t groups = (rows + rpb - 1) / rpb;
   const int grid = (int)(groups < kMaxGrid ? groups : kMaxGrid);  // one block per row group
   int icols = (int)cols;
-  void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &eps};
+  Drop drop = drop_in;
+  void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &eps, &drop};
   if (aligned) {
-    const void* k = shape_kernel<VecSel<IO, RES, GELU>::template K>(i);
+    const void* k = shape_kernel<VecSel<IO, RES, EPI>::template K>(i);
     return hipLaunchKernel(k, dim3(grid), dim3(block), args, 0, s);
   }
   const uintptr_t ax = reinterpret_cast<uintptr_t>(x);
   const bool congruent = ((ax ^ reinterpret_cast<uintptr_t>(y)) & 15) == 0 &&
                          (!res || ((ax ^ reinterpret_cast<uintptr_t>(res)) & 15) == 0);
-  if (congruent) {
+  // the class kernel has no dropout epilogue: those rows take the shift kernel
+  if (congruent && EPI != kEpiReluDrop) {
     // Rows whose windows lie inside the tensors: [r_lo, r_hi).  A row
     // starting fewer than 16 - (x mod 16) bytes past an unaligned start, or
     // ending fewer than (end mod 16) bytes before an unaligned end, has a
@@ -1005,25 +1024,31 @@ hipError_t launch_flags(const void* x, const void* res, const void* gamma, const
     const int64_t cgroups = ((r_hi - r_lo + period - 1) / period + rpb - 1) / rpb;
     int64_t nblk = (cgroups + kClassGroups - 1) / kClassGroups;
     if (nblk > kMaxGrid / 16) nblk = kMaxGrid / 16;
-    const void* k = shape_kernel<ClassSel<IO, RES, GELU>::template K>(i);
+    const void* k = shape_kernel<ClassSel<IO, RES, (EPI == kEpiReluDrop ? kEpiNone : EPI)>::template K>(i);
     void* cargs[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &eps, &period, &r_lo, &r_hi, (void*)&edge_blocks};
     return hipLaunchKernel(k, dim3((unsigned)(edge_blocks + period * nblk)), dim3(block), cargs, 0, s);
   }
   // kShiftGroups row groups per block amortise the per-block gamma/beta set-up
-  const void* k = shape_kernel<ShiftSel<IO, RES, GELU>::template K>(i);
+  const void* k = shape_kernel<ShiftSel<IO, RES, EPI>::template K>(i);
   const int sgrid = (int)((groups + kShiftGroups - 1) / kShiftGroups);
   return hipLaunchKernel(k, dim3(sgrid), dim3(block), args, 0, s);
 }
 
+// act: kEpiNone, kEpiGelu, kEpiReluDrop (no residual; `drop` describes it)
 template <class IO>
 hipError_t launch(const void* x, const void* res, const void* gamma, const void* beta, void* y,
-                  int64_t rows, int64_t cols, double eps, int act, hipStream_t s) {
-  const bool gelu = act == 1;
+                  int64_t rows, int64_t cols, double eps, int act, const Drop* drop, hipStream_t s) {
+  const Drop none{0, 0, 0, 1.0f};
+  if (act == kEpiReluDrop) {
+    if (res || !drop) return hipErrorInvalidValue;
+    return launch_flags<IO, false, kEpiReluDrop>(x, res, gamma, beta, y, rows, cols, eps, *drop, s);
+  }
+  const bool gelu = act == kEpiGelu;
   if (res)
-    return gelu ? launch_flags<IO, true, true>(x, res, gamma, beta, y, rows, cols, eps, s)
-                : launch_flags<IO, true, false>(x, res, gamma, beta, y, rows, cols, eps, s);
-  return gelu ? launch_flags<IO, false, true>(x, res, gamma, beta, y, rows, cols, eps, s)
-              : launch_flags<IO, false, false>(x, res, gamma, beta, y, rows, cols, eps, s);
+    return gelu ? launch_flags<IO, true, kEpiGelu>(x, res, gamma, beta, y, rows, cols, eps, none, s)
+                : launch_flags<IO, true, kEpiNone>(x, res, gamma, beta, y, rows, cols, eps, none, s);
+  return gelu ? launch_flags<IO, false, kEpiGelu>(x, res, gamma, beta, y, rows, cols, eps, none, s)
+              : launch_flags<IO, false, kEpiNone>(x, res, gamma, beta, y, rows, cols, eps, none, s);
 }
 
 }  // namespace ln

@@ -139,6 +139,65 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Philox4x32-10 (J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw,
+// "Parallel random numbers: as easy as 1, 2, 3", SC'11): counter
+// (q lo, q hi, offset lo, offset hi), key (seed lo, seed hi); each round
+// multiplies counter words 0 and 2 by 0xD2511F53 and 0xCD9E8D57 into 64-bit
+// products and mixes in words 1 and 3 and the key, which advances by the Weyl
+// constants 0x9E3779B9 and 0xBB67AE85.
+__device__ __forceinline__ void philox4x32_10(uint64_t q, uint64_t seed, uint64_t offset, uint32_t out[4]) {
+  uint32_t c0 = (uint32_t)q, c1 = (uint32_t)(q >> 32), c2 = (uint32_t)offset, c3 = (uint32_t)(offset >> 32);
+  uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+// The 16 random bits of elements i0 .. i0 + N - 1 (N = 1, 4 or 8) of a
+// dropout with (seed, offset): half i mod 8 of block i div 8.  ALIGNED: i0 is
+// a multiple of N, so the elements lie in one block; otherwise they may span two.
+template <int N, bool ALIGNED>
+__device__ __forceinline__ void dropout_bits(uint64_t i0, uint64_t seed, uint64_t offset, uint32_t* h) {
+  uint32_t b0[4];
+  philox4x32_10(i0 >> 3, seed, offset, b0);
+  if constexpr (ALIGNED) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      const int t = N == 8 ? e : (int)(i0 & 7) + e;  // half index within the block
+      const int wi = t >> 1;
+      const uint32_t w = N == 8 ? b0[e >> 1] : (wi == 0 ? b0[0] : wi == 1 ? b0[1] : wi == 2 ? b0[2] : b0[3]);
+      h[e] = (t & 1) ? (w >> 16) : (w & 0xFFFFu);
+    }
+  } else {
+    uint32_t b1[4];
+    philox4x32_10((i0 >> 3) + 1, seed, offset, b1);
+    const int o = (int)(i0 & 7);
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      const int t = o + e;  // half index within the two blocks (0 .. 14)
+      const int wi = (t & 7) >> 1;
+      const uint32_t w0v = wi == 0 ? b0[0] : wi == 1 ? b0[1] : wi == 2 ? b0[2] : b0[3];
+      const uint32_t w1v = wi == 0 ? b1[0] : wi == 1 ? b1[1] : wi == 2 ? b1[2] : b1[3];
+      const uint32_t w = t < 8 ? w0v : w1v;
+      h[e] = (t & 1) ? (w >> 16) : (w & 0xFFFFu);
+    }
+  }
+}
+
 // Sum of v over a group of LANES consecutive lanes (LANES a power of two).
 // Within a wave: xor butterfly.  Because a + b == b + a exactly in IEEE
 // arithmetic, both partners of every exchange compute the same value, so all

@@ -9,6 +9,19 @@
 
 namespace mbp {
 
+// Dropout of one call: element i (flat index) is kept iff its 16 random bits
+// are >= thr; kept values are multiplied by scale.  The bits of element i are
+// half i mod 8 of Philox4x32-10 with key (seed) and counter (i div 8, offset).
+struct Drop {
+  uint64_t seed;
+  uint64_t offset;
+  uint32_t thr;  // round(p * 2^16), 0 .. 65536
+  float scale;   // 1 / (1 - p)
+};
+
+// epilogues of the LayerNorm kernels
+constexpr int kEpiNone = 0, kEpiGelu = 1, kEpiReluDrop = 2;
+
 hipError_t launch_chain(const float* x, const float* b1, const float* b2, float* y, int64_t n,
                         double scale, hipStream_t s);
 // dtype: 0 fp32, 1 bf16, 2 fp16; row strides in elements (0: broadcast row)
@@ -23,9 +36,10 @@ hipError_t launch_row_mean_2d(int dtype, const void* x, int64_t ldx, const void*
 hipError_t launch_row_mean(const float* x, const float* bias, const float* gamma,
                            const float* beta, float* y, int64_t rows, int64_t cols, double alpha,
                            double c, hipStream_t s);
+// act: kEpiNone, kEpiGelu or kEpiReluDrop (then `drop` describes the dropout)
 hipError_t launch_layernorm(int dtype, const void* x, const void* residual, const void* gamma,
                             const void* beta, void* y, int64_t rows, int64_t cols, double eps,
-                            int act, hipStream_t s);
+                            int act, const Drop* drop, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 
 // Unfused primitives (one launch each).
@@ -38,6 +52,7 @@ enum EwOp {
   EW_DIVSD = 5,    // a / sqrt(b + scalar)     (b: per-row variance)
   EW_MULADD = 6,   // a * b + c   (two roundings)
   EW_GELU = 7,     // tanh-GeLU of a
+  EW_DROPOUT = 8,  // keep(i) ? a * drop.scale : 0   (the element's index i picks its random bits)
 };
 // How operand b (and c) is indexed: full tensor, per column (vector of cols),
 // or per row (vector of rows, fp32).
@@ -45,7 +60,7 @@ enum EwIndex { IX_FULL = 0, IX_COL = 1, IX_ROW = 2 };
 
 hipError_t launch_ew(int op, int dtype, const void* a, const void* b, int b_ix, const void* c,
                      int c_ix, void* out, int64_t rows, int64_t cols, float scalar,
-                     hipStream_t s);
+                     hipStream_t s, const Drop* drop = nullptr);
 // Row mean (fp32 out) and biased variance about a given mean (fp32 out) of a
 // [rows, cols] tensor; binary64 accumulation.
 hipError_t launch_row_mean_only(int dtype, const void* a, float* mean, int64_t rows,

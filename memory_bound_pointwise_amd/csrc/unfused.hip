@@ -33,6 +33,7 @@ __device__ __forceinline__ float ew_apply(float a, float b, float c, float scala
   if constexpr (OP == EW_DIVSD) return __fdiv_rn(a, __fsqrt_rn(__fadd_rn(b, scalar)));
   if constexpr (OP == EW_MULADD) return __fadd_rn(__fmul_rn(a, b), c);
   if constexpr (OP == EW_GELU) return gelu_tanh_f32(a);
+  if constexpr (OP == EW_DROPOUT) return a;  // the mask and the scale are applied by the caller
   return 0.0f;
 }
 
@@ -65,7 +66,7 @@ template <class IO, int OP, int VW>
 __global__ __launch_bounds__(kBlock) void ew_kernel(const typename IO::elem* a, const void* b,
                                                     int b_ix, const void* c, int c_ix,
                                                     typename IO::elem* out, int64_t n,
-                                                    int64_t cols, float scalar) {
+                                                    int64_t cols, float scalar, Drop drop) {
   const int64_t nv = n / VW;
   const int64_t items = nv + (n - nv * VW);
   const bool bcast = (b && b_ix != IX_FULL) || (c && c_ix != IX_FULL);
@@ -75,8 +76,13 @@ __global__ __launch_bounds__(kBlock) void ew_kernel(const typename IO::elem* a, 
        it += (int64_t)gridDim.x * kBlock) {
     if (VW == 1 || it >= nv) {
       const int64_t i = VW == 1 ? it : nv * VW + (it - nv);
-      const float r = ew_apply<OP>(IO::load1(a, i), operand<IO>(b, b_ix, i, cols),
-                                   operand<IO>(c, c_ix, i, cols), scalar);
+      float r = ew_apply<OP>(IO::load1(a, i), operand<IO>(b, b_ix, i, cols),
+                             operand<IO>(c, c_ix, i, cols), scalar);
+      if constexpr (OP == EW_DROPOUT) {
+        uint32_t h;
+        dropout_bits<1, true>((uint64_t)i, drop.seed, drop.offset, &h);
+        r = (h >= drop.thr) ? __fmul_rn(r, drop.scale) : 0.0f;
+      }
       IO::store1(out, i, r);
     } else {
       const int64_t i0 = it * VW;
@@ -101,6 +107,12 @@ __global__ __launch_bounds__(kBlock) void ew_kernel(const typename IO::elem* a, 
       for (int e = 0; e < VW; ++e)
         r[e] = ew_apply<OP>(IO::get(av, e), vec_operand<IO, VW>(b, bx, bv, e, row0, col0, cols),
                             vec_operand<IO, VW>(c, cx, cv, e, row0, col0, cols), scalar);
+      if constexpr (OP == EW_DROPOUT) {
+        uint32_t h[VW];
+        dropout_bits<VW, true>((uint64_t)i0, drop.seed, drop.offset, h);
+#pragma unroll
+        for (int e = 0; e < VW; ++e) r[e] = (h[e] >= drop.thr) ? __fmul_rn(r[e], drop.scale) : 0.0f;
+      }
       u32x4 ov;
       if constexpr (VW == 8) {
 #pragma unroll
@@ -209,6 +221,7 @@ const void* ew_ptr(int op) {
     case EW_DIVSD: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_DIVSD, VW>);
     case EW_MULADD: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_MULADD, VW>);
     case EW_GELU: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_GELU, VW>);
+    case EW_DROPOUT: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_DROPOUT, VW>);
     default: return nullptr;
   }
 }
@@ -234,7 +247,7 @@ int64_t stat_grid(int64_t rows, int64_t cols, int es) {
 
 hipError_t launch_ew(int op, int dtype, const void* a, const void* b, int b_ix, const void* c,
                      int c_ix, void* out, int64_t rows, int64_t cols, float scalar,
-                     hipStream_t s) {
+                     hipStream_t s, const Drop* drop) {
   const int64_t n = rows * cols;
   const int vec = dtype == 1 ? 8 : 4;
   // 128-bit form: every full-size operand 16-byte aligned; a broadcast
@@ -250,7 +263,9 @@ hipError_t launch_ew(int op, int dtype, const void* a, const void* b, int b_ix, 
   int64_t grid = (n / vw + n % vw + kBlock - 1) / kBlock;
   if (grid > kMaxGrid) grid = kMaxGrid;
   if (grid < 1) grid = 1;
-  void* args[] = {&a, &b, &b_ix, &c, &c_ix, &out, (void*)&n, &cols, &scalar};
+  Drop dv = drop ? *drop : Drop{0, 0, 0, 1.0f};
+  if (op == EW_DROPOUT && !drop) return hipErrorInvalidValue;
+  void* args[] = {&a, &b, &b_ix, &c, &c_ix, &out, (void*)&n, &cols, &scalar, &dv};
   return hipLaunchKernel(k, dim3((unsigned)grid), dim3(kBlock), args, 0, s);
 }
 

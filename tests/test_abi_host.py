@@ -27,7 +27,8 @@ def mbp():
 def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("fused_pointwise_chain", "fused_row_mean_epilogue", "fused_add_layernorm_gelu",
-                 "fused_pointwise_chain_2d", "fused_row_mean_epilogue_2d",
+                 "fused_pointwise_chain_2d", "fused_row_mean_epilogue_2d", "fused_softmax",
+                 "fused_layernorm_relu_dropout", "unfused_layernorm_relu_dropout",
                  "unfused_pointwise_chain", "unfused_row_mean_epilogue", "unfused_add_layernorm_gelu"):
         assert name in fns
 
@@ -131,6 +132,26 @@ def test_2d_validation(mbp):
     assert st(r2, 1, A, 8, B, B, B, A, 12, 4, 8, 1.1, 0.1, None) == 5             # y == x, other stride
     # fp16 is for the two-dimensional forms only
     assert st("fused_add_layernorm_gelu", 2, A, None, B, B, Y, 4, 8, 1e-5, 0, None) == 3
+
+
+def test_dropout_validation(mbp):
+    global L
+    L = mbp.lib
+    f = "fused_layernorm_relu_dropout"
+    # dtype, x, gamma, beta, y, rows, cols, eps, p, seed, offset, stream
+    assert st(f, 1, A, B, B, Y, 4, 8, 1e-5, 1.5, 0, 0, None) == 8                # p > 1
+    assert st(f, 1, A, B, B, Y, 4, 8, 1e-5, float("nan"), 0, 0, None) == 8       # p NaN
+    assert st(f, 1, A, B, B, Y, 4, 8, 1e-5, -0.1, 0, 0, None) == 8               # p < 0
+    assert st(f, 2, A, B, B, Y, 4, 8, 1e-5, 0.1, 0, 0, None) == 3                # fp16: not here
+    assert st(f, 1, A, B, B, Y, 0, 8, 1e-5, 0.1, 0, 0, None) == 0                # rows == 0
+    assert st(f, 1, A, B, B, A + 2, 4, 8, 1e-5, 0.1, 0, 0, None) == 5            # partial overlap
+    u = "unfused_layernorm_relu_dropout"
+    assert st(u, 1, A, B, B, Y, 4, 8, 1e-5, 0.1, 0, 0, None, 0, None) == 6       # no workspace
+    assert st(u, 1, A, B, B, A, 4, 8, 1e-5, 0.1, 0, 0, Y + 4096, 1 << 20, None) == 5  # in place
+    m = mbp
+    assert m.launches_per_call(m.OP_LN_RELU_DROPOUT, True) == 1
+    assert m.launches_per_call(m.OP_LN_RELU_DROPOUT, False) == 3
+    assert m.workspace_bytes(m.OP_LN_RELU_DROPOUT, m.BF16, 4, 8) == 2 * 256
 
 
 def test_workspace_and_launch_counts(mbp):

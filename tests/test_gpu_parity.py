@@ -404,6 +404,22 @@ def test_next_full_workload(mbp, name):
     d = W.generate(w)
     fmt = w.dtype
     rows = sample_rows(w.rows)
+    if w.kind == "ln_relu_dropout":
+        pr = w.params
+        args = [to_dev(d[k]) for k in ("x", "gamma", "beta")]
+        y1 = mbp.fused_layernorm_relu_dropout(*args, pr["p"], pr["seed"], pr["offset"], pr["eps"])
+        y2 = mbp.fused_layernorm_relu_dropout(*args, pr["p"], pr["seed"], pr["offset"], pr["eps"])
+        assert torch.equal(y1, y2), "not deterministic"
+        # the first 64 rows against the oracle: their element indices (which
+        # pick the random bits) are those of the full tensor
+        exact = oracle.ln_relu_dropout(d["x"][:64], d["gamma"], d["beta"], p=pr["p"], seed=pr["seed"],
+                                       offset=pr["offset"])
+        check_bf16(to_host(y1[:64]), exact, name)
+        assert np.array_equal(as_f64(to_host(y1[:64])) == 0, exact == 0) or \
+            ((as_f64(to_host(y1[:64])) == 0) != (exact == 0)).sum() < 4, "dropout mask differs"
+        frac = (to_host(y1).view(np.uint16) == 0).mean()
+        print(f"{name}: zero fraction {frac:.4f} (p = {pr['p']} plus the relu zeros)")
+        return
     if w.kind == "softmax":
         x = to_dev(d["x"])
         y1 = mbp.fused_softmax(x)
@@ -437,6 +453,68 @@ def test_next_full_workload(mbp, name):
     assert torch.equal(y1.contiguous().view(torch.int16), y2.contiguous().view(torch.int16)), "not deterministic"
     worst, n_off = check_ulp16(bits16(ys), exact, fmt, name)
     print(f"{name}: {len(rows)} sampled rows, max {worst} ulp, {n_off} elements 1 ulp off")
+
+
+# ------------------------------------------------------------------ LayerNorm -> ReLU -> Dropout
+
+def _drop_case(name, rows, cols):
+    w, d, _ = _ln_case(name, rows, cols, residual=False)
+    return w, d
+
+
+def _check_dropout(y_dev, d, w, p, seed, offset, what, mode=oracle.EXACT):
+    """the kept / dropped pattern exactly (where relu(LN) is clearly positive,
+    so that rounding cannot move an element across 0), and the values within
+    the LayerNorm gates"""
+    exact = oracle.ln_relu_dropout(d["x"], d["gamma"], d["beta"], p=p, seed=seed, offset=offset, mode=mode)
+    relu_ln = np.maximum(oracle.add_layernorm_gelu(d["x"], None, d["gamma"], d["beta"], act=oracle.ACT_NONE), 0)
+    y = to_host(y_dev)
+    yf = as_f64(y)
+    clear = relu_ln > 1e-3
+    assert np.array_equal((yf != 0)[clear], (exact != 0)[clear]), f"{what}: dropout mask differs"
+    chk = check_bf16 if w.dtype == "bf16" else check_f32
+    chk(y, exact, what)
+    return (exact == 0)[clear].mean() if clear.any() else 0.0
+
+
+@pytest.mark.parametrize("name", ["ln_8192x4096_f32", "addln_gelu_16384x8192_bf16"])
+@pytest.mark.parametrize("cols", [8, 768, 1001, 1024, 4095, 4096, 8192])
+@pytest.mark.parametrize("p", [0.0, 0.1, 0.5, 1.0])
+def test_ln_relu_dropout(mbp, name, cols, p):
+    w, d = _drop_case(name, 23, cols)
+    seed, offset = 0x5EED0000DEADBEEF, 3
+    args = (to_dev(d["x"]), to_dev(d["gamma"]), to_dev(d["beta"]))
+    y = mbp.fused_layernorm_relu_dropout(*args, p=p, seed=seed, offset=offset)
+    frac = _check_dropout(y, d, w, p, seed, offset, f"ln-relu-dropout {w.dtype} {cols} p={p}")
+    if p in (0.0, 1.0):
+        assert frac == p
+    y2 = mbp.fused_layernorm_relu_dropout(*args, p=p, seed=seed, offset=offset)
+    assert torch.equal(y, y2), "not deterministic"
+
+
+def test_ln_relu_dropout_in_place_offset_misaligned_unfused(mbp):
+    for name in ("ln_8192x4096_f32", "addln_gelu_16384x8192_bf16"):
+        w, d = _drop_case(name, 33, 1024)
+        g, b = to_dev(d["gamma"]), to_dev(d["beta"])
+        x = to_dev(d["x"])
+        y = mbp.fused_layernorm_relu_dropout(x, g, b, p=0.1, seed=9, offset=0)
+        # in place
+        xi = x.clone()
+        mbp.fused_layernorm_relu_dropout(xi, g, b, p=0.1, seed=9, offset=0, out=xi)
+        assert torch.equal(xi, y), "in place differs"
+        # another offset: another mask (of the clearly positive elements, about p(1-p)*2 differ)
+        y3 = mbp.fused_layernorm_relu_dropout(x, g, b, p=0.1, seed=9, offset=1)
+        _check_dropout(y3, d, w, 0.1, 9, 1, f"{name} offset 1")
+        assert not torch.equal(y3, y)
+        # x one element past a 16-byte boundary: the lane-shift kernel, same result
+        buf = torch.zeros(x.numel() + 8, dtype=x.dtype, device="cuda")
+        xs = buf[1:1 + x.numel()].view(x.shape)
+        xs.copy_(x)
+        ys = mbp.fused_layernorm_relu_dropout(xs, g, b, p=0.1, seed=9, offset=0)
+        _check_dropout(ys, d, w, 0.1, 9, 0, f"{name} misaligned")
+        # the three eager launches, against the oracle's three-stage mode
+        yu = mbp.unfused_layernorm_relu_dropout(x, g, b, p=0.1, seed=9, offset=0)
+        _check_dropout(yu, d, w, 0.1, 9, 0, f"{name} unfused", mode=oracle.SEQ3)
 
 
 # ------------------------------------------------------------------ row softmax

@@ -35,6 +35,7 @@ import numpy as np
 class Workload:
     name: str
     kind: str            # "chain" | "row_mean" | "layernorm" | "chain2d" | "row_mean2d" | "softmax"
+    #                      | "ln_relu_dropout"
     seed: int
     sub: int = 0
     n: int = 0           # chain: element count
@@ -64,6 +65,8 @@ class Workload:
             return es * (2 * self.rows * self.cols + 3 * self.cols)    # x in, y out; bias/gamma/beta
         if self.kind == "softmax":
             return es * 2 * self.rows * self.cols                      # x in, y out
+        if self.kind == "ln_relu_dropout":
+            return es * (2 * self.rows * self.cols + 2 * self.cols)    # x in, y out; gamma, beta
         es = 2 if self.dtype == "bf16" else 4
         tensors = 3 if self.residual else 2           # x (+ residual) in, y out
         return es * tensors * self.rows * self.cols + es * 2 * self.cols   # + gamma, beta
@@ -102,6 +105,10 @@ NEXT_WORKLOADS = [
     # operator-fusion practice post, section 4.1 (batch 1, 32 heads,
     # seq_len 4096: probs of 32 x 4096 x 4096, i.e. 131072 rows of 4096)
     Workload("softmax_131072x4096_bf16", "softmax", seed=8, rows=131072, cols=4096, dtype="bf16"),
+    # LayerNorm -> ReLU -> Dropout (p = 0.1 as in "算子融合与 Kernel 优化", section
+    # 2.1) at the residual-LayerNorm workload's shape, without the residual
+    Workload("ln_relu_dropout_16384x8192_bf16", "ln_relu_dropout", seed=4, rows=16384, cols=8192,
+             dtype="bf16", params=dict(eps=1e-5, p=0.1, seed=0x5EED, offset=0)),
 ]
 NEXT_BY_NAME = {w.name: w for w in NEXT_WORKLOADS}
 
@@ -209,6 +216,11 @@ def generate(w: Workload, cols: int | None = None) -> dict:
                     b2=store(_normal_f32((s, u, 2), rows, c), w.dtype))
     if w.kind == "softmax":
         return dict(x=store(_normal_f32((s, u, 0), rows, c), w.dtype))
+    if w.kind == "ln_relu_dropout":
+        g64 = 1.0 + 0.1 * _rng(s, u, 2).standard_normal(c)
+        b64 = 0.1 * _rng(s, u, 3).standard_normal(c)
+        return dict(x=store(_normal_f32((s, u, 0), rows, c), w.dtype),
+                    gamma=store(g64.astype(np.float32), w.dtype), beta=store(b64.astype(np.float32), w.dtype))
     if w.kind == "row_mean2d":
         return dict(x=store(_normal_f32((s, u, 0), rows, c), w.dtype),
                     **{k: store(_rng(s, u, i + 1).standard_normal(c).astype(np.float32), w.dtype)
