@@ -11,13 +11,18 @@ kernel finds its inputs evicted from the 256 MB Infinity Cache by the others
 Printed: one JSON line with
   value        whole-step effective bandwidth: compulsory bytes of all seven
                calls / wall time per step (GB/s, 1e9 B/s);
-  per_workload per kernel: time per call from batches of N back-to-back calls
-               between two HIP events on the launch stream (N such that a
-               batch takes about 1 ms; median, min and p90 over the batches),
-               the calls rotating over B copies of the inputs and outputs with
-               B x working set >= 1 GiB so every call starts cold; effective
-               GB/s, fraction of 8 TB/s; the unfused variant timed the same way
-               (all its launches per call) and the speedup;
+  per_workload per kernel: GPU time per call from batches of N back-to-back
+               calls between two HIP events on the launch stream (N such that
+               a batch takes about 1 ms; median, min and p90 over the
+               batches), the calls rotating over B copies of the inputs and
+               outputs with B x working set >= 1 GiB so every call starts
+               cold.  Each batch is captured once as a HIP graph and replayed,
+               so host work (Python, ctypes, the launch call) stays out of
+               the kernels' time; the same batch issued eagerly from Python
+               is reported beside it (eager_us_median: for the small
+               workloads that one is bound by the host's issue rate).
+               Effective GB/s, fraction of 8 TB/s; the unfused variant timed
+               the same way (all its launches per call) and the speedups;
   roofline     the dominant kernel (largest time per call), its duration from
                HIP events around each of its calls inside the timed region,
                against 8 TB/s;
@@ -26,6 +31,11 @@ Printed: one JSON line with
                row, fp16 10-op graph on padded rows) and the row softmax
                (bf16, attention-probability shape), same batch protocol,
                not part of `value`.
+  launch_study launch cost against bytes: each variant (unfused, TVM's
+               three groups, fused) of small expressions called eagerly
+               through the C ABI, replayed from a graph of one call, and
+               replayed from a graph of many calls (GPU time per call with no
+               host work in between); one set of buffers (cache-warm).
 
 Other modes (for rocprofv3 counter runs): --only NAME runs just one workload's
 fused kernel; --copy-bytes B runs the library's streaming copy of B bytes.
@@ -60,6 +70,7 @@ def parse():
                    help="the oracle runs on 1/K of each workload's rows")
     p.add_argument("--only", default=None, help="run only this workload's fused kernel")
     p.add_argument("--no-next", action="store_true", help="skip the two-dimensional forms")
+    p.add_argument("--no-launch-study", action="store_true", help="skip the eager vs graph study")
     p.add_argument("--unfused-only", default=None, help="run only this workload's unfused variant")
     p.add_argument("--copy-bytes", type=int, default=0, help="run the streaming copy of this size")
     return p.parse_args()
@@ -190,11 +201,16 @@ def main():
         print(json.dumps({"mode": "unfused-only", "workload": names[0], "calls": args.warmup + args.steps}))
         return
 
-    stream = torch.cuda.current_stream(dev)
+    # everything runs on one created stream (graph capture cannot use the
+    # NULL stream); the library calls take the current stream
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.set_stream(stream)
 
-    def batch_times(fns, batches):
-        """Per-call times (us) of `batches` batches of N back-to-back calls
-        rotating over `fns`, each batch between two events on the stream."""
+    def batch_times(fns, batches, eager=None):
+        """Per-call GPU times (us) of `batches` batches of N back-to-back calls
+        rotating over `fns`, each batch replayed from a captured graph between
+        two events on the stream; with eager=list, also the eager per-call
+        times of the same batches issued from Python, appended to it."""
         for f in fns[:3]:
             f()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -205,22 +221,41 @@ def main():
         torch.cuda.synchronize()
         est = e0.elapsed_time(e1) * 1e3 / 3
         n_calls = max(1, min(2000, int(1000.0 / max(est, 1e-3))))
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(batches)]
-        k = 0
+
+        def events():
+            return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for _ in range(batches)]
+
+        if eager is not None:
+            ev = events()
+            k = 0
+            for a, b in ev:
+                a.record(stream)
+                for _ in range(n_calls):
+                    fns[k % len(fns)]()
+                    k += 1
+                b.record(stream)
+            torch.cuda.synchronize()
+            eager.extend(a.elapsed_time(b) * 1e3 / n_calls for a, b in ev)
+        with mbp.capture(stream) as cap:
+            for k in range(n_calls):
+                fns[k % len(fns)]()
+        g = cap.graph
+        g.launch(stream)
+        ev = events()
         for a, b in ev:
             a.record(stream)
-            for _ in range(n_calls):
-                fns[k % len(fns)]()
-                k += 1
+            g.launch(stream)
             b.record(stream)
         torch.cuda.synchronize()
+        g.close()
         return [a.elapsed_time(b) * 1e3 / n_calls for a, b in ev], n_calls
 
     # ---- per-call times, one workload at a time (not the timed region)
-    fused_us, fused_n = {}, {}
+    fused_us, fused_n, fused_eager = {}, {}, {}
     for n in names:
-        fused_us[n], fused_n[n] = batch_times(sets[n], args.batches)
+        fused_eager[n] = []
+        fused_us[n], fused_n[n] = batch_times(sets[n], args.batches, fused_eager[n])
     dominant = max(names, key=lambda n: statistics.median(fused_us[n]))
 
     for _ in range(args.warmup):
@@ -249,9 +284,10 @@ def main():
 
     # ---- unfused variants, same batch protocol
     unf_us = {n: [] for n in names}
+    unf_eager = {n: [] for n in names}
     if args.unfused_reps and not args.only:
         for n in names:
-            unf_us[n], _ = batch_times(usets[n], args.unfused_reps)
+            unf_us[n], _ = batch_times(usets[n], args.unfused_reps, unf_eager[n])
 
     # ---- the two-dimensional forms (16-bit storage, broadcast rows, row
     # strides) and the row softmax: same batch protocol, reported beside the
@@ -306,10 +342,15 @@ def main():
                                                                  pr["eps"], out=y, workspace=ws)
                 uus, _ = batch_times([ufn], args.unfused_reps)
                 um = statistics.median(uus)
+                del ufn
                 nxt[w.name].update({"unfused_us_median": round(um, 3), "launches_unfused": 3,
                                     "speedup_vs_unfused": round(um / med, 3)})
                 del x, g, b, y, ws
         torch.cuda.synchronize()
+
+    study = None
+    if not args.only and not args.no_launch_study:
+        study = launch_study(mbp, W, dev, args.batches)
 
     per = {}
     total_bytes = 0
@@ -324,6 +365,7 @@ def main():
             "fused_us_median": round(med_us, 3),
             "fused_us_min": round(srt[0], 3),
             "fused_us_p90": round(srt[min(len(srt) - 1, int(0.9 * len(srt)))], 3),
+            "eager_us_median": round(statistics.median(fused_eager[n]), 3),
             "calls_per_batch": fused_n[n],
             "input_copies": len(sets[n]),
             "gbps": round(B / (med_us * 1e-6) / 1e9, 1),
@@ -332,8 +374,11 @@ def main():
         }
         if unf_us[n]:
             um = statistics.median(unf_us[n])
+            ue = statistics.median(unf_eager[n])
             rec.update({"unfused_us_median": round(um, 3), "launches_unfused": uinfo[n],
-                        "speedup_vs_unfused": round(um / med_us, 3)})
+                        "speedup_vs_unfused": round(um / med_us, 3),
+                        "unfused_eager_us_median": round(ue, 3),
+                        "speedup_vs_unfused_eager": round(ue / statistics.median(fused_eager[n]), 3)})
         per[n] = rec
 
     dw = W.BY_NAME[dominant]
@@ -369,10 +414,159 @@ def main():
         "cpu_baseline": cpu,
         "per_workload": per,
         "next": nxt,
+        "launch_study": study,
         "library_sha256": sha[:16],
         "setup_s": round(t_gen, 1),
     }
     print(json.dumps(out))
+
+
+def launch_study(mbp, W, dev, batches):
+    """Eager launches against graph replay on small expressions, where the
+    per-launch cost is comparable to the kernels' own time."""
+    import ctypes
+    import functools
+
+    import torch
+
+    L = mbp.lib
+    side = torch.cuda.Stream(dev)
+    sh = side.cuda_stream
+    P = lambda t: t.data_ptr()
+    to_dev = lambda a: W.to_device(a, dev)
+
+    def ws_for(nbytes):
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+    keep = []  # buffers referenced by raw pointers below
+
+    def chain_case(n):
+        d = W.generate(W.scaled(W.BY_NAME["chain_4M_f32"], n=n))
+        x, b1, b2 = (to_dev(d[k]) for k in ("x", "b1", "b2"))
+        y = torch.empty_like(x)
+        ws = ws_for(mbp.workspace_bytes(mbp.OP_CHAIN, mbp.F32, 1, n))
+        keep.extend([x, b1, b2, y, ws])
+        a = (P(x), P(b1), P(b2), P(y), n, 0.5)
+        return 16 * n, {
+            "unfused": (functools.partial(L.unfused_pointwise_chain, *a, P(ws), ws.numel(), sh), 4),
+            "fused": (functools.partial(L.fused_pointwise_chain, *a, sh), 1)}
+
+    def tenop_case(rows, cols):
+        d = W.generate(W.scaled(W.BY_NAME["tenop_1024x1024_f32"], rows=rows), cols=cols)
+        x, bias, g, b = (to_dev(d[k]) for k in ("x", "bias", "gamma", "beta"))
+        y = torch.empty_like(x)
+        wu = ws_for(mbp.workspace_bytes(mbp.OP_ROW_MEAN, mbp.F32, rows, cols))
+        wg = ws_for(mbp.workspace_bytes(mbp.OP_ROW_MEAN, mbp.F32, rows, cols,
+                                        granularity=mbp.UNFUSED_GROUPED))
+        keep.extend([x, bias, g, b, y, wu, wg])
+        a = (P(x), P(bias), P(g), P(b), P(y), rows, cols, 1.1, 0.1)
+        return 8 * rows * cols + 12 * cols, {
+            "unfused": (functools.partial(L.unfused_row_mean_epilogue, *a, P(wu), wu.numel(), sh), 10),
+            "grouped": (functools.partial(L.grouped_row_mean_epilogue, *a, P(wg), wg.numel(), sh), 3),
+            "fused": (functools.partial(L.fused_row_mean_epilogue, *a, sh), 1)}
+
+    def addln_case(rows, cols):
+        w = W.scaled(W.BY_NAME["addln_gelu_16384x8192_bf16"], rows=rows)
+        d = W.generate(w, cols=cols)
+        x, r, g, b = (to_dev(d[k]) for k in ("x", "residual", "gamma", "beta"))
+        y = torch.empty_like(x)
+        wp = ws_for(mbp.workspace_bytes(mbp.OP_LAYERNORM, mbp.BF16, rows, cols, True, "gelu_tanh"))
+        we = ws_for(mbp.workspace_bytes(mbp.OP_LAYERNORM, mbp.BF16, rows, cols, True, "gelu_tanh",
+                                        mbp.UNFUSED_EAGER))
+        keep.extend([x, r, g, b, y, wp, we])
+        a = (mbp.BF16, P(x), P(r), P(g), P(b), P(y), rows, cols, 1e-5, mbp.ACT_GELU_TANH)
+        return 6 * rows * cols + 4 * cols, {
+            "unfused": (functools.partial(L.unfused_add_layernorm_gelu, *a, mbp.UNFUSED_PRIMITIVE, P(wp),
+                                          wp.numel(), sh), 7),
+            "eager_ln": (functools.partial(L.unfused_add_layernorm_gelu, *a, mbp.UNFUSED_EAGER, P(we),
+                                           we.numel(), sh), 3),
+            "fused": (functools.partial(L.fused_add_layernorm_gelu, *a, sh), 1)}
+
+    def lnrd_case(rows, cols):
+        w = W.scaled(W.BY_NAME["addln_gelu_16384x8192_bf16"], rows=rows)
+        d = W.generate(w, cols=cols)
+        x, g, b = (to_dev(d[k]) for k in ("x", "gamma", "beta"))
+        y = torch.empty_like(x)
+        ws = ws_for(mbp.workspace_bytes(mbp.OP_LN_RELU_DROPOUT, mbp.BF16, rows, cols))
+        keep.extend([x, g, b, y, ws])
+        a = (mbp.BF16, P(x), P(g), P(b), P(y), rows, cols, 1e-5, 0.1, 0x5EED, 0)
+        return 4 * rows * cols + 4 * cols, {
+            "unfused": (functools.partial(L.unfused_layernorm_relu_dropout, *a, P(ws), ws.numel(), sh), 3),
+            "fused": (functools.partial(L.fused_layernorm_relu_dropout, *a, sh), 1)}
+
+    cases = {
+        "chain_4M_f32": chain_case(4 * 1024 * 1024),
+        "chain_64K_f32": chain_case(64 * 1024),
+        "tenop_1024x1024_f32": tenop_case(1024, 1024),
+        "tenop_8x1024_f32": tenop_case(8, 1024),
+        "addln_gelu_16x768_bf16": addln_case(16, 768),
+        "ln_relu_dropout_16x768_bf16": lnrd_case(16, 768),
+    }
+
+    def check(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {mbp.STATUS_NAMES.get(st, st)}: {L.mbp_last_error().decode()}")
+
+    def capture(fn, m):
+        check(L.mbp_graph_capture_begin(sh), "capture begin")
+        for _ in range(m):
+            check(fn(), "captured call")
+        h = ctypes.c_void_p()
+        check(L.mbp_graph_capture_end(sh, ctypes.byref(h)), "capture end")
+        return h
+
+    def timed(fn, calls_per_fn):
+        """Median GPU us per call and host us per call over `batches` batches."""
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(side)
+        for _ in range(3):
+            fn()
+        e1.record(side)
+        side.synchronize()
+        est = e0.elapsed_time(e1) * 1e3 / 3
+        n = max(1, min(5000, int(1000.0 / max(est, 1e-3))))
+        gpu, host = [], []
+        for _ in range(batches):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(side)
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            t1 = time.perf_counter()
+            b.record(side)
+            side.synchronize()
+            gpu.append(a.elapsed_time(b) * 1e3 / (n * calls_per_fn))
+            host.append((t1 - t0) * 1e6 / (n * calls_per_fn))
+        return round(statistics.median(gpu), 3), round(statistics.median(host), 3)
+
+    out = {}
+    torch.cuda.synchronize()
+    for cname, (nbytes, variants) in cases.items():
+        rec = {"compulsory_bytes": nbytes}
+        for vname, (fn, launches) in variants.items():
+            check(fn(), f"{cname} {vname}")
+            side.synchronize()
+            eager_gpu, eager_host = timed(fn, 1)
+            g1 = capture(fn, 1)
+            nodes = L.mbp_graph_nodes(g1)
+            g1_gpu, g1_host = timed(functools.partial(L.mbp_graph_launch, g1, sh), 1)
+            m = max(1, 400 // launches)
+            gm = capture(fn, m)
+            gm_gpu, _ = timed(functools.partial(L.mbp_graph_launch, gm, sh), m)
+            side.synchronize()
+            check(L.mbp_graph_destroy(g1), "destroy")
+            check(L.mbp_graph_destroy(gm), "destroy")
+            rec[vname] = {"launches": launches, "graph_nodes": nodes,
+                          "eager_us": eager_gpu, "eager_host_us": eager_host,
+                          "graph1_us": g1_gpu, "graph1_host_us": g1_host,
+                          "graph_batch_us": gm_gpu, "graph_batch_calls": m,
+                          "graph_batch_gbps": round(nbytes / (gm_gpu * 1e-6) / 1e9, 1)}
+        out[cname] = rec
+    torch.cuda.synchronize()
+    del keep
+    return out
 
 
 def cpu_baseline(wl, host, frac):

@@ -5,6 +5,8 @@
  * the given HIP stream and returns at once (asynchronous, like a kernel launch).
  * The caller owns every buffer: the library never allocates or frees device
  * memory and keeps no mutable global state beyond a per-thread error message.
+ * (An instantiated graph, below, holds the HIP runtime's own resources until
+ * the caller destroys it.)
  *
  * Conventions shared by all entry points
  *   - Tensors are dense and row-major (contiguous).  A [rows, cols] tensor has
@@ -43,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MBP_ABI_VERSION 2
+#define MBP_ABI_VERSION 3
 
 /* Largest row length (cols) the row kernels accept: one row lives in registers. */
 #define MBP_MAX_COLS 16384
@@ -76,6 +78,7 @@ typedef enum {
 /* Granularity of the unfused variants. */
 #define MBP_UNFUSED_PRIMITIVE 0 /* one launch per primitive op (4 / 10 / 5 / 7 launches) */
 #define MBP_UNFUSED_EAGER 1     /* LayerNorm as one launch: add, layernorm, gelu (<= 3) */
+#define MBP_UNFUSED_GROUPED 2   /* the 10-op graph in TVM's three groups (MBP_OP_ROW_MEAN only) */
 
 /* ------------------------------------------------------------------------- */
 /* Fused entry points: one launch; only the inputs are read and the output is
@@ -225,6 +228,21 @@ mbp_status unfused_row_mean_epilogue(const float* x, const float* bias, const fl
                                      double alpha, double c, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* The 10-op graph partitioned as TVM's FuseOps rules partition it ([P4]
+ * section 09, Figure 17): three launches, each one kernel of its own group --
+ *   1. s = relu(x*alpha + bias)^2 + relu(x*alpha + bias)*c  (written to the workspace),
+ *   2. m = row mean of s,
+ *   3. y = (s - m)*gamma + beta.
+ * s is written once and read twice.  Every op rounds to fp32 as its eager
+ * kernel does (alpha and c rounded to fp32, no contraction), so y equals the
+ * output of unfused_row_mean_epilogue bit for bit.  Workspace:
+ * mbp_unfused_workspace_bytes(MBP_OP_ROW_MEAN, MBP_F32, rows, cols, 0, 0,
+ * MBP_UNFUSED_GROUPED). */
+mbp_status grouped_row_mean_epilogue(const float* x, const float* bias, const float* gamma,
+                                     const float* beta, float* y, int64_t rows, int64_t cols,
+                                     double alpha, double c, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* [P3] section 4.3 and [P2] section 2.3.  granularity MBP_UNFUSED_PRIMITIVE:
  * [add,] mean, var, sub, div, mul-add[, gelu]  (5 launches for plain
  * LayerNorm, 7 with residual and GeLU).  granularity MBP_UNFUSED_EAGER:
@@ -247,13 +265,43 @@ mbp_status unfused_layernorm_relu_dropout(mbp_dtype dtype, const void* x, const 
 
 /* Workspace the unfused variant of `op` needs (bytes; 0 for a no-op shape).
  * For MBP_OP_CHAIN pass rows = 1, cols = n.  has_residual and act matter only
- * for MBP_OP_LAYERNORM.  Returns (size_t)-1 for invalid arguments. */
+ * for MBP_OP_LAYERNORM; granularity for MBP_OP_LAYERNORM and (GROUPED or not)
+ * MBP_OP_ROW_MEAN.  Returns (size_t)-1 for invalid arguments. */
 size_t mbp_unfused_workspace_bytes(mbp_op op, mbp_dtype dtype, int64_t rows, int64_t cols,
                                    int has_residual, mbp_act act, int granularity);
 
 /* Kernel launches one call makes (fused = 1: the fused entry point; fused = 0:
  * the unfused one at `granularity`).  -1 for invalid arguments. */
 int mbp_launches_per_call(mbp_op op, int fused, int granularity, int has_residual, mbp_act act);
+
+/* ------------------------------------------------------------------------- */
+/* Graph capture ([P2] section 4: capture a fixed sequence of launches once,
+ * instantiate it, then submit it with one call; shapes and addresses are fixed
+ * at capture).  Between mbp_graph_capture_begin and mbp_graph_capture_end,
+ * every launch this thread enqueues on `stream` -- any of the entry points
+ * above -- is recorded, not executed.  The entry points validate their
+ * arguments as usual while recording: one that returns an error records
+ * nothing.  The entry points make no allocation and no memset, so a graph holds
+ * kernel nodes only.
+ *   - stream: a created hipStream_t (the NULL stream cannot be captured).
+ *   - The capture is thread-local (hipStreamCaptureModeThreadLocal): this
+ *     thread may not call hipMalloc or synchronise while it records.
+ *   - mbp_graph_capture_end ends the capture in every case; it instantiates
+ *     the graph and returns a handle the caller owns (MBP_ERR_ARG if nothing
+ *     was captured; MBP_ERR_HIP if the capture was invalidated).
+ *   - mbp_graph_launch enqueues one replay on any stream (NULL allowed); the
+ *     buffers named at capture must still be alive.  Replays of one graph on
+ *     different streams must not overlap in time (they write the same memory).
+ *   - mbp_graph_destroy releases the handle (NULL is a no-op); no replay may
+ *     still be pending. */
+typedef struct mbp_graph_s mbp_graph;
+
+mbp_status mbp_graph_capture_begin(void* stream);
+mbp_status mbp_graph_capture_end(void* stream, mbp_graph** graph);
+mbp_status mbp_graph_launch(const mbp_graph* graph, void* stream);
+/* Number of nodes in the captured graph (-1 for NULL). */
+int64_t mbp_graph_nodes(const mbp_graph* graph);
+mbp_status mbp_graph_destroy(mbp_graph* graph);
 
 /* ------------------------------------------------------------------------- */
 /* Calibration and diagnostics.                                              */

@@ -11,6 +11,7 @@ PyTorch is used for device memory and streams only.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -22,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libmbp.so")
 F32, BF16, F16 = 0, 1, 2
 ACT_NONE, ACT_GELU_TANH = 0, 1
 OP_CHAIN, OP_ROW_MEAN, OP_LAYERNORM, OP_LN_RELU_DROPOUT = 0, 1, 2, 3
-UNFUSED_PRIMITIVE, UNFUSED_EAGER = 0, 1
+UNFUSED_PRIMITIVE, UNFUSED_EAGER, UNFUSED_GROUPED = 0, 1, 2
 MAX_COLS = 16384
 
 STATUS_NAMES = {0: "MBP_OK", 1: "MBP_ERR_NULL", 2: "MBP_ERR_SHAPE", 3: "MBP_ERR_DTYPE",
@@ -43,9 +44,15 @@ SIGNATURES = [
     ("fused_row_mean_epilogue_2d", _I, [_I, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _D, _D, _P]),
     ("unfused_pointwise_chain", _I, [_P, _P, _P, _P, _I64, _D, _P, _SZ, _P]),
     ("unfused_row_mean_epilogue", _I, [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _P, _SZ, _P]),
+    ("grouped_row_mean_epilogue", _I, [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _P, _SZ, _P]),
     ("unfused_add_layernorm_gelu", _I, [_I, _P, _P, _P, _P, _P, _I64, _I64, _D, _I, _I, _P, _SZ, _P]),
     ("mbp_unfused_workspace_bytes", _SZ, [_I, _I, _I64, _I64, _I, _I, _I]),
     ("mbp_launches_per_call", _I, [_I, _I, _I, _I, _I]),
+    ("mbp_graph_capture_begin", _I, [_P]),
+    ("mbp_graph_capture_end", _I, [_P, ctypes.POINTER(_P)]),
+    ("mbp_graph_launch", _I, [_P, _P]),
+    ("mbp_graph_nodes", _I64, [_P]),
+    ("mbp_graph_destroy", _I, [_P]),
     ("mbp_stream_copy", _I, [_P, _P, _SZ, _P]),
     ("mbp_status_string", ctypes.c_char_p, [_I]),
     ("mbp_last_error", ctypes.c_char_p, []),
@@ -361,6 +368,20 @@ def unfused_row_mean_epilogue(x, bias, gamma, beta, alpha=1.1, c=0.1, out=None, 
     return y
 
 
+def grouped_row_mean_epilogue(x, bias, gamma, beta, alpha=1.1, c=0.1, out=None, workspace=None):
+    """The 10-op graph as TVM's three groups: prologue (s written), row mean,
+    epilogue -- three launches, s through HBM."""
+    for t, n in ((x, "x"), (bias, "bias"), (gamma, "gamma"), (beta, "beta"), (out, "out")):
+        _check(t, n, (torch.float32,), x.device)
+    rows, cols = _rows_cols(x)
+    y = torch.empty_like(x) if out is None else out
+    nb = workspace_bytes(OP_ROW_MEAN, F32, rows, cols, granularity=UNFUSED_GROUPED)
+    ws = _workspace(nb, x.device, workspace)
+    _call("grouped_row_mean_epilogue", _ptr(x), _ptr(bias), _ptr(gamma), _ptr(beta), _ptr(y), rows,
+          cols, float(alpha), float(c), _ptr(ws), ws.numel() * ws.element_size(), _stream(x))
+    return y
+
+
 def unfused_add_layernorm_gelu(x, residual, gamma, beta, eps=1e-5, act="gelu_tanh",
                                granularity=UNFUSED_PRIMITIVE, out=None, workspace=None):
     """Residual + LayerNorm + GeLU as one launch per op (granularity 0) or as
@@ -379,6 +400,75 @@ def unfused_add_layernorm_gelu(x, residual, gamma, beta, eps=1e-5, act="gelu_tan
           _ptr(beta), _ptr(y), rows, cols, float(eps), code, granularity, _ptr(ws),
           ws.numel() * ws.element_size(), _stream(x))
     return y
+
+
+# ------------------------------------------------------------------ graphs
+
+def _stream_handle(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+class Graph:
+    """An instantiated HIP graph of library calls (``mbp_graph_*``): replay it
+    with ``launch``; ``close`` (or garbage collection) releases it."""
+
+    def __init__(self, handle: int):
+        self._h = handle
+
+    @property
+    def nodes(self) -> int:
+        return int(lib.mbp_graph_nodes(self._h))
+
+    def launch(self, stream=None) -> None:
+        if self._h is None:
+            raise ValueError("graph has been closed")
+        _call("mbp_graph_launch", self._h, _stream_handle(stream))
+
+    def close(self) -> None:
+        h, self._h = self._h, None
+        if h is not None:
+            _call("mbp_graph_destroy", h)
+
+    def __del__(self):
+        with contextlib.suppress(Exception):
+            self.close()
+
+
+class capture:
+    """Record the library calls made on ``stream`` (a created
+    ``torch.cuda.Stream``, made current inside the block) into a ``Graph``,
+    available as ``.graph`` after the block.  Inside the block nothing may
+    allocate device memory: pass ``out=`` and ``workspace=`` to every call."""
+
+    def __init__(self, stream: torch.cuda.Stream):
+        if not isinstance(stream, torch.cuda.Stream) or stream.cuda_stream == 0:
+            raise ValueError("capture needs a created torch.cuda.Stream")
+        self.stream = stream
+        self.graph = None
+        self._ctx = None
+
+    def __enter__(self):
+        _call("mbp_graph_capture_begin", self.stream.cuda_stream)
+        self._ctx = torch.cuda.stream(self.stream)
+        self._ctx.__enter__()
+        return self
+
+    def __exit__(self, et, ev, tb):
+        self._ctx.__exit__(et, ev, tb)
+        h = _P()
+        st = lib.mbp_graph_capture_end(self.stream.cuda_stream, ctypes.byref(h))
+        if et is not None:  # the capture has ended; report the original error
+            if st == 0:
+                lib.mbp_graph_destroy(h)
+            return False
+        if st != 0:
+            raise MbpError("mbp_graph_capture_end", st, lib.mbp_last_error().decode())
+        self.graph = Graph(h.value)
+        return False
 
 
 def stream_copy(src, dst):

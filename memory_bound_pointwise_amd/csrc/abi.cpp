@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <initializer_list>
+#include <new>
 #include <cstdio>
 #include <string>
 #include <tuple>
@@ -97,6 +98,9 @@ struct ChainWs {
 struct RowMeanWs {
   float *a, *b, *c, *m;
 };
+struct GroupedWs {
+  float *s, *m;
+};
 struct LnWs {
   void *r, *a, *b;
   float *m, *v;
@@ -117,6 +121,15 @@ size_t row_mean_ws(char* base, int64_t rows, int64_t cols, RowMeanWs* w) {
   t.a = (float*)c.take(rows * cols * 4);
   t.b = (float*)c.take(rows * cols * 4);
   t.c = (float*)c.take(rows * cols * 4);
+  t.m = (float*)c.take(rows * 4);
+  if (w) *w = t;
+  return c.used;
+}
+
+size_t grouped_ws(char* base, int64_t rows, int64_t cols, GroupedWs* w) {
+  Carver c{base};
+  GroupedWs t;
+  t.s = (float*)c.take(rows * cols * 4);
   t.m = (float*)c.take(rows * 4);
   if (w) *w = t;
   return c.used;
@@ -439,6 +452,36 @@ mbp_status unfused_row_mean_epilogue(const float* x, const float* bias, const fl
   return from_hip(e, "unfused_row_mean_epilogue");
 }
 
+mbp_status grouped_row_mean_epilogue(const float* x, const float* bias, const float* gamma,
+                                     const float* beta, float* y, int64_t rows, int64_t cols,
+                                     double alpha, double c, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  mbp_status st = check_row_mean(x, bias, gamma, beta, y, rows, cols, alpha, c, false);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  const size_t need = grouped_ws(nullptr, rows, cols, nullptr);
+  const size_t full = (size_t)rows * cols * 4, vec = (size_t)cols * 4;
+  st = check_workspace(workspace, workspace_bytes, need,
+                       {{x, full}, {y, full}, {bias, vec}, {gamma, vec}, {beta, vec}});
+  if (st != MBP_OK) return st;
+  GroupedWs w;
+  grouped_ws((char*)workspace, rows, cols, &w);
+  const float a32 = (float)alpha, c32 = (float)c;
+  hipStream_t s = as_stream(stream);
+  using namespace mbp;
+  const int F = MBP_F32;
+  // group 1: x*alpha + bias, relu, a*a, a*c, p + q  ->  s
+  hipError_t e = launch_ew4(EW_PROLOGUE, F, x, bias, IX_COL, nullptr, 0, nullptr, 0, w.s, rows, cols,
+                            a32, c32, s);
+  // group 2: the row mean of s
+  if (e == hipSuccess) e = launch_row_mean_only(F, w.s, w.m, rows, cols, s);
+  // group 3: (s - m) * gamma + beta
+  if (e == hipSuccess)
+    e = launch_ew4(EW_CENTER_AFFINE, F, w.s, w.m, IX_ROW, gamma, IX_COL, beta, IX_COL, y, rows, cols,
+                   0.0f, 0.0f, s);
+  return from_hip(e, "grouped_row_mean_epilogue");
+}
+
 mbp_status unfused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void* residual,
                                       const void* gamma, const void* beta, void* y, int64_t rows,
                                       int64_t cols, double eps, mbp_act act, int granularity,
@@ -484,6 +527,62 @@ mbp_status unfused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void
   return from_hip(e, "unfused_add_layernorm_gelu");
 }
 
+// ---------------------------------------------------------------- graphs
+
+struct mbp_graph_s {
+  hipGraphExec_t exec;
+  size_t nodes;
+};
+
+mbp_status mbp_graph_capture_begin(void* stream) {
+  if (!stream) return fail(MBP_ERR_ARG, "capture needs a created stream, not the NULL stream");
+  return from_hip(hipStreamBeginCapture(as_stream(stream), hipStreamCaptureModeThreadLocal),
+                  "hipStreamBeginCapture");
+}
+
+mbp_status mbp_graph_capture_end(void* stream, mbp_graph** graph) {
+  if (!graph) return fail(MBP_ERR_NULL, "graph must be non-NULL");
+  *graph = nullptr;
+  if (!stream) return fail(MBP_ERR_ARG, "capture needs a created stream, not the NULL stream");
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(as_stream(stream), &g);
+  if (e != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return from_hip(e, "hipStreamEndCapture");
+  }
+  size_t nodes = 0;
+  e = hipGraphGetNodes(g, nullptr, &nodes);
+  if (e == hipSuccess && nodes == 0) {
+    (void)hipGraphDestroy(g);
+    return fail(MBP_ERR_ARG, "nothing was captured");
+  }
+  hipGraphExec_t exec = nullptr;
+  if (e == hipSuccess) e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);  // the executable graph does not need its template
+  if (e != hipSuccess) return from_hip(e, "hipGraphInstantiate");
+  mbp_graph* h = new (std::nothrow) mbp_graph{exec, nodes};
+  if (!h) {
+    (void)hipGraphExecDestroy(exec);
+    return fail(MBP_ERR_ARG, "out of host memory");
+  }
+  *graph = h;
+  return ok();
+}
+
+mbp_status mbp_graph_launch(const mbp_graph* graph, void* stream) {
+  if (!graph) return fail(MBP_ERR_NULL, "graph must be non-NULL");
+  return from_hip(hipGraphLaunch(graph->exec, as_stream(stream)), "hipGraphLaunch");
+}
+
+int64_t mbp_graph_nodes(const mbp_graph* graph) { return graph ? (int64_t)graph->nodes : -1; }
+
+mbp_status mbp_graph_destroy(mbp_graph* graph) {
+  if (!graph) return ok();
+  const hipError_t e = hipGraphExecDestroy(graph->exec);
+  delete graph;
+  return from_hip(e, "hipGraphExecDestroy");
+}
+
 size_t mbp_unfused_workspace_bytes(mbp_op op, mbp_dtype dtype, int64_t rows, int64_t cols,
                                    int has_residual, mbp_act act, int granularity) {
   if (rows < 0 || cols < 0) return (size_t)-1;
@@ -491,7 +590,9 @@ size_t mbp_unfused_workspace_bytes(mbp_op op, mbp_dtype dtype, int64_t rows, int
   if (rows > kMaxElems / cols) return (size_t)-1;
   switch (op) {
     case MBP_OP_CHAIN: return chain_ws(nullptr, rows * cols, nullptr);
-    case MBP_OP_ROW_MEAN: return row_mean_ws(nullptr, rows, cols, nullptr);
+    case MBP_OP_ROW_MEAN:
+      if (granularity == MBP_UNFUSED_GROUPED) return grouped_ws(nullptr, rows, cols, nullptr);
+      return row_mean_ws(nullptr, rows, cols, nullptr);
     case MBP_OP_LN_RELU_DROPOUT: {
       if (dtype != MBP_F32 && dtype != MBP_BF16) return (size_t)-1;
       Carver c{nullptr};
@@ -513,7 +614,7 @@ int mbp_launches_per_call(mbp_op op, int fused, int granularity, int has_residua
   switch (op) {
     case MBP_OP_LN_RELU_DROPOUT: return 3;
     case MBP_OP_CHAIN: return 4;
-    case MBP_OP_ROW_MEAN: return 10;
+    case MBP_OP_ROW_MEAN: return granularity == MBP_UNFUSED_GROUPED ? 3 : 10;
     case MBP_OP_LAYERNORM: {
       const int extra = (has_residual ? 1 : 0) + (act == MBP_ACT_GELU_TANH ? 1 : 0);
       if (granularity == MBP_UNFUSED_PRIMITIVE) return 5 + extra;

@@ -103,16 +103,6 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
   const int64_t groups = (rows + RPB - 1) / RPB;
   int parity = 0;
   for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x, parity ^= 1) {
-    // the parameters stay fp32 across rows (an empty asm keeps the compiler
-    // from widening them to binary64 once and holding the wide copies)
-#pragma unroll
-    for (int k = 0; k < VPL; ++k)
-#pragma unroll
-      for (int e = 0; e < VW; ++e) {
-        opaque(bi[k][e]);
-        opaque(g[k][e]);
-        opaque(be[k][e]);
-      }
     const int64_t row = grp * RPB + sub;
     const bool live = row < rows;
     // past the last row: reread the last row, store nothing; slots past the
@@ -127,6 +117,18 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
       if constexpr (VW == 1) xv[k][0] = IO::load1(xr, vi);
       else load4_nt<IO>(xr + 4 * vi, xv[k]);
     }
+    // the parameters stay fp32 across rows (an empty asm keeps the compiler
+    // from widening them to binary64 once and holding the wide copies); it
+    // comes after the row's loads are issued, so that on the first row the
+    // parameter loads and the row loads are in flight together
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+#pragma unroll
+      for (int e = 0; e < VW; ++e) {
+        opaque(bi[k][e]);
+        opaque(g[k][e]);
+        opaque(be[k][e]);
+      }
     double s[VPL][VW];
     double sum = 0.0;
 #pragma unroll

@@ -53,6 +53,8 @@ enum EwOp {
   EW_MULADD = 6,   // a * b + c   (two roundings)
   EW_GELU = 7,     // tanh-GeLU of a
   EW_DROPOUT = 8,  // keep(i) ? a * drop.scale : 0   (the element's index i picks its random bits)
+  EW_PROLOGUE = 9,       // r = relu(a * scalar + b); r * r + r * scalar2   (five roundings)
+  EW_CENTER_AFFINE = 10, // (a - b) * c + d   (three roundings)
 };
 // How operand b (and c) is indexed: full tensor, per column (vector of cols),
 // or per row (vector of rows, fp32).
@@ -61,6 +63,11 @@ enum EwIndex { IX_FULL = 0, IX_COL = 1, IX_ROW = 2 };
 hipError_t launch_ew(int op, int dtype, const void* a, const void* b, int b_ix, const void* c,
                      int c_ix, void* out, int64_t rows, int64_t cols, float scalar,
                      hipStream_t s, const Drop* drop = nullptr);
+// launch_ew with a fourth operand d (read by EW_CENTER_AFFINE only) and a
+// second scalar (read by EW_PROLOGUE only).
+hipError_t launch_ew4(int op, int dtype, const void* a, const void* b, int b_ix, const void* c,
+                      int c_ix, const void* d, int d_ix, void* out, int64_t rows, int64_t cols,
+                      float scalar, float scalar2, hipStream_t s, const Drop* drop = nullptr);
 // Row mean (fp32 out) and biased variance about a given mean (fp32 out) of a
 // [rows, cols] tensor; binary64 accumulation.
 hipError_t launch_row_mean_only(int dtype, const void* a, float* mean, int64_t rows,

@@ -24,7 +24,8 @@ constexpr int kBlock = 256;
 constexpr int64_t kMaxGrid = 1 << 30;
 
 template <int OP>
-__device__ __forceinline__ float ew_apply(float a, float b, float c, float scalar) {
+__device__ __forceinline__ float ew_apply(float a, float b, float c, float d, float scalar,
+                                          float scalar2) {
   if constexpr (OP == EW_ADD) return __fadd_rn(a, b);
   if constexpr (OP == EW_SUB) return __fsub_rn(a, b);
   if constexpr (OP == EW_MUL) return __fmul_rn(a, b);
@@ -34,6 +35,14 @@ __device__ __forceinline__ float ew_apply(float a, float b, float c, float scala
   if constexpr (OP == EW_MULADD) return __fadd_rn(__fmul_rn(a, b), c);
   if constexpr (OP == EW_GELU) return gelu_tanh_f32(a);
   if constexpr (OP == EW_DROPOUT) return a;  // the mask and the scale are applied by the caller
+  if constexpr (OP == EW_PROLOGUE) {
+    // the element-wise group of the 10-op graph, each op rounded as its own
+    // eager kernel would round it
+    const float t = __fadd_rn(__fmul_rn(a, scalar), b);
+    const float r = t < 0.0f ? 0.0f : t;
+    return __fadd_rn(__fmul_rn(r, r), __fmul_rn(r, scalar2));
+  }
+  if constexpr (OP == EW_CENTER_AFFINE) return __fadd_rn(__fmul_rn(__fsub_rn(a, b), c), d);
   return 0.0f;
 }
 
@@ -65,19 +74,25 @@ __device__ __forceinline__ float vec_operand(const void* p, int ix, const u32x4&
 template <class IO, int OP, int VW>
 __global__ __launch_bounds__(kBlock) void ew_kernel(const typename IO::elem* a, const void* b,
                                                     int b_ix, const void* c, int c_ix,
+                                                    const void* d, int d_ix,
                                                     typename IO::elem* out, int64_t n,
-                                                    int64_t cols, float scalar, Drop drop) {
+                                                    int64_t cols, float scalar, float scalar2,
+                                                    Drop drop) {
+  // the fourth operand exists for EW_CENTER_AFFINE only
+  constexpr bool kD = OP == EW_CENTER_AFFINE;
   const int64_t nv = n / VW;
   const int64_t items = nv + (n - nv * VW);
-  const bool bcast = (b && b_ix != IX_FULL) || (c && c_ix != IX_FULL);
+  const bool bcast = (b && b_ix != IX_FULL) || (c && c_ix != IX_FULL) || (kD && d && d_ix != IX_FULL);
   const bool col_vec = VW > 1 && cols % VW == 0 && (!b || b_ix != IX_COL || ((uintptr_t)b & 15) == 0) &&
-                       (!c || c_ix != IX_COL || ((uintptr_t)c & 15) == 0);
+                       (!c || c_ix != IX_COL || ((uintptr_t)c & 15) == 0) &&
+                       (!kD || !d || d_ix != IX_COL || ((uintptr_t)d & 15) == 0);
   for (int64_t it = (int64_t)blockIdx.x * kBlock + threadIdx.x; it < items;
        it += (int64_t)gridDim.x * kBlock) {
     if (VW == 1 || it >= nv) {
       const int64_t i = VW == 1 ? it : nv * VW + (it - nv);
+      const float dv = kD ? operand<IO>(d, d_ix, i, cols) : 0.0f;
       float r = ew_apply<OP>(IO::load1(a, i), operand<IO>(b, b_ix, i, cols),
-                             operand<IO>(c, c_ix, i, cols), scalar);
+                             operand<IO>(c, c_ix, i, cols), dv, scalar, scalar2);
       if constexpr (OP == EW_DROPOUT) {
         uint32_t h;
         dropout_bits<1, true>((uint64_t)i, drop.seed, drop.offset, &h);
@@ -94,19 +109,26 @@ __global__ __launch_bounds__(kBlock) void ew_kernel(const typename IO::elem* a, 
       const u32x4 av = reinterpret_cast<const u32x4*>(a)[it];
       // a column-broadcast operand whose vectors line up with the row (cols a
       // multiple of VW, 16-byte aligned) is read as one vector, as if full
-      int bx = b_ix, cx = c_ix;
+      int bx = b_ix, cx = c_ix, dx = d_ix;
       if (bx == IX_COL && col_vec) bx = IX_FULL;
       if (cx == IX_COL && col_vec) cx = IX_FULL;
-      u32x4 bv = {{0u, 0u, 0u, 0u}}, cv = {{0u, 0u, 0u, 0u}};
+      if (dx == IX_COL && col_vec) dx = IX_FULL;
+      u32x4 bv = {{0u, 0u, 0u, 0u}}, cv = {{0u, 0u, 0u, 0u}}, dv = {{0u, 0u, 0u, 0u}};
       if (b && b_ix == IX_FULL) bv = reinterpret_cast<const u32x4*>(b)[it];
       if (b && b_ix == IX_COL && col_vec) bv = reinterpret_cast<const u32x4*>(b)[col0 / VW];
       if (c && c_ix == IX_FULL) cv = reinterpret_cast<const u32x4*>(c)[it];
       if (c && c_ix == IX_COL && col_vec) cv = reinterpret_cast<const u32x4*>(c)[col0 / VW];
+      if constexpr (kD) {
+        if (d && d_ix == IX_FULL) dv = reinterpret_cast<const u32x4*>(d)[it];
+        if (d && d_ix == IX_COL && col_vec) dv = reinterpret_cast<const u32x4*>(d)[col0 / VW];
+      }
       float r[VW];
 #pragma unroll
       for (int e = 0; e < VW; ++e)
         r[e] = ew_apply<OP>(IO::get(av, e), vec_operand<IO, VW>(b, bx, bv, e, row0, col0, cols),
-                            vec_operand<IO, VW>(c, cx, cv, e, row0, col0, cols), scalar);
+                            vec_operand<IO, VW>(c, cx, cv, e, row0, col0, cols),
+                            kD ? vec_operand<IO, VW>(d, dx, dv, e, row0, col0, cols) : 0.0f, scalar,
+                            scalar2);
       if constexpr (OP == EW_DROPOUT) {
         uint32_t h[VW];
         dropout_bits<VW, true>((uint64_t)i0, drop.seed, drop.offset, h);
@@ -222,6 +244,8 @@ const void* ew_ptr(int op) {
     case EW_MULADD: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_MULADD, VW>);
     case EW_GELU: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_GELU, VW>);
     case EW_DROPOUT: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_DROPOUT, VW>);
+    case EW_PROLOGUE: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_PROLOGUE, VW>);
+    case EW_CENTER_AFFINE: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_CENTER_AFFINE, VW>);
     default: return nullptr;
   }
 }
@@ -248,14 +272,23 @@ int64_t stat_grid(int64_t rows, int64_t cols, int es) {
 hipError_t launch_ew(int op, int dtype, const void* a, const void* b, int b_ix, const void* c,
                      int c_ix, void* out, int64_t rows, int64_t cols, float scalar,
                      hipStream_t s, const Drop* drop) {
+  return launch_ew4(op, dtype, a, b, b_ix, c, c_ix, nullptr, IX_FULL, out, rows, cols, scalar, 0.0f, s,
+                    drop);
+}
+
+hipError_t launch_ew4(int op, int dtype, const void* a, const void* b, int b_ix, const void* c,
+                      int c_ix, const void* d, int d_ix, void* out, int64_t rows, int64_t cols,
+                      float scalar, float scalar2, hipStream_t s, const Drop* drop) {
   const int64_t n = rows * cols;
   const int vec = dtype == 1 ? 8 : 4;
+  if (op != EW_CENTER_AFFINE) d = nullptr;
   // 128-bit form: every full-size operand 16-byte aligned; a broadcast
   // operand needs cols >= vec (a vector then wraps into the next row at most once)
-  const bool bcast = (b && b_ix != IX_FULL) || (c && c_ix != IX_FULL);
+  const bool bcast = (b && b_ix != IX_FULL) || (c && c_ix != IX_FULL) || (d && d_ix != IX_FULL);
   bool vector_ok = a16(a) && a16(out) && (!bcast || cols >= vec);
   if (b && b_ix == IX_FULL) vector_ok = vector_ok && a16(b);
   if (c && c_ix == IX_FULL) vector_ok = vector_ok && a16(c);
+  if (d && d_ix == IX_FULL) vector_ok = vector_ok && a16(d);
   const int vw = vector_ok ? vec : 1;
   const void* k = dtype == 1 ? (vector_ok ? ew_ptr<BF16IO, 8>(op) : ew_ptr<BF16IO, 1>(op))
                              : (vector_ok ? ew_ptr<F32IO, 4>(op) : ew_ptr<F32IO, 1>(op));
@@ -265,7 +298,7 @@ hipError_t launch_ew(int op, int dtype, const void* a, const void* b, int b_ix, 
   if (grid < 1) grid = 1;
   Drop dv = drop ? *drop : Drop{0, 0, 0, 1.0f};
   if (op == EW_DROPOUT && !drop) return hipErrorInvalidValue;
-  void* args[] = {&a, &b, &b_ix, &c, &c_ix, &out, (void*)&n, &cols, &scalar, &dv};
+  void* args[] = {&a, &b, &b_ix, &c, &c_ix, &d, &d_ix, &out, (void*)&n, &cols, &scalar, &scalar2, &dv};
   return hipLaunchKernel(k, dim3((unsigned)grid), dim3(kBlock), args, 0, s);
 }
 

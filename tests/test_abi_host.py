@@ -29,7 +29,9 @@ def test_header_declares_the_boundary():
     for name in ("fused_pointwise_chain", "fused_row_mean_epilogue", "fused_add_layernorm_gelu",
                  "fused_pointwise_chain_2d", "fused_row_mean_epilogue_2d", "fused_softmax",
                  "fused_layernorm_relu_dropout", "unfused_layernorm_relu_dropout",
-                 "unfused_pointwise_chain", "unfused_row_mean_epilogue", "unfused_add_layernorm_gelu"):
+                 "unfused_pointwise_chain", "unfused_row_mean_epilogue", "unfused_add_layernorm_gelu",
+                 "grouped_row_mean_epilogue", "mbp_graph_capture_begin", "mbp_graph_capture_end",
+                 "mbp_graph_launch", "mbp_graph_destroy"):
         assert name in fns
 
 
@@ -44,7 +46,7 @@ def test_library_exports_every_declared_symbol(mbp):
 
 
 def test_abi_version_and_strings(mbp):
-    assert mbp.lib.mbp_abi_version() == 2
+    assert mbp.lib.mbp_abi_version() == 3
     for code, name in mbp.STATUS_NAMES.items():
         assert mbp.lib.mbp_status_string(code)
     assert mbp.lib.mbp_status_string(99) == b"unknown status"
@@ -174,6 +176,42 @@ def test_workspace_and_launch_counts(mbp):
     assert m.workspace_bytes(m.OP_LAYERNORM, m.F32, 0, 8) == 0
     with pytest.raises(ValueError):
         m.workspace_bytes(m.OP_LAYERNORM, 5, 4, 8)
+
+
+def test_grouped_validation(mbp):
+    global L
+    L = mbp.lib
+    g = "grouped_row_mean_epilogue"
+    # x, bias, gamma, beta, y, rows, cols, alpha, c, workspace, workspace_bytes, stream
+    ws = Y + 0x100000
+    assert st(g, A, B, B, B, Y, 4, 0, 1.1, 0.1, ws, 1 << 20, None) == 2               # cols == 0
+    assert st(g, A, B, B, B, Y, 0, 8, 1.1, 0.1, None, 0, None) == 0                   # rows == 0
+    assert st(g, A, None, B, B, Y, 4, 8, 1.1, 0.1, ws, 1 << 20, None) == 1            # NULL
+    assert st(g, A, B, B, B, Y, 4, 8, float("inf"), 0.1, ws, 1 << 20, None) == 8      # ARG
+    assert st(g, A, B, B, B, A, 4, 8, 1.1, 0.1, ws, 1 << 20, None) == 5               # y == x
+    assert st(g, A, B, B, B, Y, 4, 8, 1.1, 0.1, None, 0, None) == 6                   # no workspace
+    assert st(g, A, B, B, B, Y, 4, 8, 1.1, 0.1, ws, 16, None) == 6                    # too small
+    assert st(g, A, B, B, B, Y, 4, 8, 1.1, 0.1, A, 1 << 20, None) == 5                # ws over x
+    m = mbp
+    assert m.launches_per_call(m.OP_ROW_MEAN, False, m.UNFUSED_GROUPED) == 3
+    assert m.workspace_bytes(m.OP_ROW_MEAN, m.F32, 1024, 1024, granularity=m.UNFUSED_GROUPED) == \
+        4 * 1024 * 1024 + 4096
+
+
+def test_graph_host_errors(mbp):
+    """Argument errors of the graph entry points, found before any HIP call."""
+    L = mbp.lib
+    h = ctypes.c_void_p(1234)
+    assert L.mbp_graph_capture_begin(None) == 8                       # the NULL stream
+    assert L.mbp_graph_capture_end(None, ctypes.byref(h)) == 8
+    assert h.value is None                                           # cleared on failure
+    assert L.mbp_graph_capture_end(A, None) == 1
+    assert L.mbp_graph_launch(None, None) == 1
+    assert L.mbp_graph_nodes(None) == -1
+    assert L.mbp_graph_destroy(None) == 0
+    import torch
+    with pytest.raises(ValueError):
+        mbp.capture(None)
 
 
 def test_binding_rejects_cpu_tensors(mbp):

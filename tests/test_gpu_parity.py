@@ -593,6 +593,33 @@ def test_unfused_tenop(mbp, rows, cols):
     check_f32(y, ref, f"unfused 10-op {rows}x{cols} vs SEQ")
 
 
+@pytest.mark.parametrize("rows,cols,off", [(1, 1, 0), (3, 7, 1), (5, 3, 0), (33, 1000, 2),
+                                           (1024, 1024, 0), (1024, 1024, 1), (4, 16384, 3), (7, 4093, 0)])
+def test_grouped_tenop(mbp, rows, cols, off):
+    """TVM's three-group partition of the 10-op graph: every op rounds as its
+    eager kernel does, so the output equals the ten-launch variant's bit for
+    bit (and the oracle's sequential fp32 evaluation within the gate); x and y
+    `off` elements past a 16-byte boundary take the element-wise path."""
+    d = W.generate(W.scaled(W.BY_NAME["tenop_1024x1024_f32"], rows=rows), cols=cols)
+
+    def place(a):
+        t = to_dev(a)
+        buf = torch.zeros(t.numel() + 4, dtype=t.dtype, device="cuda")
+        v = buf[off:off + t.numel()].view(t.shape)
+        v.copy_(t)
+        return v
+
+    x = place(d["x"])
+    vecs = [to_dev(d[k]) for k in ("bias", "gamma", "beta")]
+    y = place(np.zeros_like(d["x"]))
+    mbp.grouped_row_mean_epilogue(x, *vecs, out=y)
+    y_g = to_host(y)
+    y_u = to_host(mbp.unfused_row_mean_epilogue(x, *vecs))
+    assert np.array_equal(y_g.view(np.uint32), y_u.view(np.uint32)), "grouped != ten launches"
+    ref = oracle.row_mean_epilogue(d["x"], d["bias"], d["gamma"], d["beta"], mode=oracle.SEQ)
+    check_f32(y_g, ref, f"grouped 10-op {rows}x{cols} offset {off} vs SEQ")
+
+
 @pytest.mark.parametrize("name,rows", [("ln_8192x4096_f32", 64), ("addln_gelu_16384x8192_bf16", 16),
                                        ("addln_gelu_32768x4095_bf16", 16), ("addln_gelu_262144x768_bf16", 64)])
 @pytest.mark.parametrize("gran", [0, 1])
