@@ -21,12 +21,20 @@ Printed: one JSON line with
                the kernels' time; the same batch issued eagerly from Python
                is reported beside it (eager_us_median: for the small
                workloads that one is bound by the host's issue rate).
-               Effective GB/s, fraction of 8 TB/s; the unfused variant timed
-               the same way (all its launches per call) and the speedups;
+               Effective GB/s, fraction of 8 TB/s and of the measured copy
+               ceiling; the same kernel on one set of inputs (cache-warm,
+               labelled warm); the unfused variant timed the same way (all its
+               launches per call) and the speedups;
+  calibration  the library's streaming copy (128-bit loads and stores) of
+               256 MiB, rotating over 4 buffer pairs, same protocol: the
+               attainable read+write bandwidth;
   roofline     the dominant kernel (largest time per call), its duration from
                HIP events around each of its calls inside the timed region,
                against 8 TB/s;
-  cpu_baseline the CPU oracle timed on a bounded sample of the same workloads;
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workloads,
+               on every host core available to the process (row chunks in
+               parallel threads; the oracle's C code releases the GIL) and on
+               one core;
   next         the two-dimensional forms (bf16 chain with a broadcast bias
                row, fp16 10-op graph on padded rows) and the row softmax
                (bf16, attention-probability shape), same batch protocol,
@@ -38,7 +46,9 @@ Printed: one JSON line with
                host work in between); one set of buffers (cache-warm).
 
 Other modes (for rocprofv3 counter runs): --only NAME runs just one workload's
-fused kernel; --copy-bytes B runs the library's streaming copy of B bytes.
+fused kernel; --copy-bytes B runs the library's streaming copy of B bytes;
+--no-graphs times every batch as eager calls (no graph capture, no launch
+study), so that each kernel is an ordinary dispatch.
 """
 from __future__ import annotations
 
@@ -71,6 +81,8 @@ def parse():
     p.add_argument("--only", default=None, help="run only this workload's fused kernel")
     p.add_argument("--no-next", action="store_true", help="skip the two-dimensional forms")
     p.add_argument("--no-launch-study", action="store_true", help="skip the eager vs graph study")
+    p.add_argument("--no-graphs", action="store_true",
+                   help="time the batches as eager calls only (no graph capture; for counter runs)")
     p.add_argument("--unfused-only", default=None, help="run only this workload's unfused variant")
     p.add_argument("--copy-bytes", type=int, default=0, help="run the streaming copy of this size")
     return p.parse_args()
@@ -226,7 +238,7 @@ def main():
             return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                     for _ in range(batches)]
 
-        if eager is not None:
+        if eager is not None or args.no_graphs:
             ev = events()
             k = 0
             for a, b in ev:
@@ -236,7 +248,12 @@ def main():
                     k += 1
                 b.record(stream)
             torch.cuda.synchronize()
-            eager.extend(a.elapsed_time(b) * 1e3 / n_calls for a, b in ev)
+            times = [a.elapsed_time(b) * 1e3 / n_calls for a, b in ev]
+            if args.no_graphs:
+                if eager is not None:
+                    eager.extend(times)
+                return times, n_calls
+            eager.extend(times)
         with mbp.capture(stream) as cap:
             for k in range(n_calls):
                 fns[k % len(fns)]()
@@ -252,10 +269,25 @@ def main():
         return [a.elapsed_time(b) * 1e3 / n_calls for a, b in ev], n_calls
 
     # ---- per-call times, one workload at a time (not the timed region)
-    fused_us, fused_n, fused_eager = {}, {}, {}
+    fused_us, fused_n, fused_eager, fused_warm = {}, {}, {}, {}
     for n in names:
         fused_eager[n] = []
         fused_us[n], fused_n[n] = batch_times(sets[n], args.batches, fused_eager[n])
+        fused_warm[n], _ = batch_times(sets[n][:1], args.batches)
+
+    # ---- calibration: the attainable copy bandwidth, same protocol
+    calibration = None
+    if not args.only:
+        cb = 256 << 20
+        pairs = [(torch.empty(cb // 4, device=dev), torch.empty(cb // 4, device=dev)) for _ in range(4)]
+        for a, _ in pairs:
+            a.fill_(1.0)
+        cus, _ = batch_times([lambda a=a, b=b: mbp.stream_copy(a, b) for a, b in pairs], args.batches)
+        cmed = statistics.median(cus)
+        calibration = {"kernel": "mbp_stream_copy", "bytes_per_call": 2 * cb,
+                       "us_median": round(cmed, 3), "gbps": round(2 * cb / (cmed * 1e-6) / 1e9, 1),
+                       "frac_of_peak": round(2 * cb / (cmed * 1e-6) / 1e9 / PEAK_GBPS, 4)}
+        del pairs
     dominant = max(names, key=lambda n: statistics.median(fused_us[n]))
 
     for _ in range(args.warmup):
@@ -349,7 +381,7 @@ def main():
         torch.cuda.synchronize()
 
     study = None
-    if not args.only and not args.no_launch_study:
+    if not args.only and not args.no_launch_study and not args.no_graphs:
         study = launch_study(mbp, W, dev, args.batches)
 
     per = {}
@@ -370,6 +402,9 @@ def main():
             "input_copies": len(sets[n]),
             "gbps": round(B / (med_us * 1e-6) / 1e9, 1),
             "frac_of_peak": round(B / (med_us * 1e-6) / 1e9 / PEAK_GBPS, 4),
+            "frac_of_copy": (round(B / (med_us * 1e-6) / 1e9 / calibration["gbps"], 4)
+                             if calibration else None),
+            "warm_us_median": round(statistics.median(fused_warm[n]), 3),
             "launches_fused": 1,
         }
         if unf_us[n]:
@@ -411,6 +446,7 @@ def main():
         "config": {"workload": "one call each: " + ", ".join(names), "bytes_per_step": total_bytes,
                    "kernels_per_step": len(names), "frac_of_peak": round(value / PEAK_GBPS, 4)},
         "roofline": roofline,
+        "calibration": calibration,
         "cpu_baseline": cpu,
         "per_workload": per,
         "next": nxt,
@@ -570,36 +606,63 @@ def launch_study(mbp, W, dev, batches):
 
 
 def cpu_baseline(wl, host, frac):
-    """The oracle (plain C, single thread, binary64) on the first 1/frac of each
-    workload's rows (elements for the chain); GB/s on the same compulsory bytes."""
+    """The oracle (plain C, binary64) on the first 1/frac of each workload's
+    rows (elements for the chain); GB/s on the same compulsory bytes.  Timed
+    twice: the rows split into chunks run by one thread per available core
+    (the oracle is called unchanged on each chunk), then on one thread."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     import workloads as W
 
-    t_total = 0.0
-    b_total = 0
-    for w in wl:
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+
+    def jobs(w):
+        """(compulsory bytes, list of zero-argument calls covering the sample)."""
         d = host[w.name]
         if w.kind == "chain":
             n = w.n // frac
-            t = time.perf_counter()
-            oracle.pointwise_chain(d["x"][:n], d["b1"][:n], d["b2"][:n], w.params["scale"])
-            t_total += time.perf_counter() - t
-            b_total += W.scaled(w, n=n).compulsory_bytes
-            continue
+            cuts = [n * i // cores for i in range(cores + 1)]
+            sc = w.params["scale"]
+            return W.scaled(w, n=n).compulsory_bytes, [
+                (lambda a=a, b=b: oracle.pointwise_chain(d["x"][a:b], d["b1"][a:b], d["b2"][a:b], sc))
+                for a, b in zip(cuts, cuts[1:]) if b > a]
         rows = max(1, w.rows // frac)
-        t = time.perf_counter()
+        cuts = [rows * i // cores for i in range(cores + 1)]
+        spans = [(a, b) for a, b in zip(cuts, cuts[1:]) if b > a]
         if w.kind == "row_mean":
-            oracle.row_mean_epilogue(d["x"][:rows], d["bias"], d["gamma"], d["beta"], w.params["alpha"],
-                                     w.params["c"])
+            al, c = w.params["alpha"], w.params["c"]
+            calls = [(lambda a=a, b=b: oracle.row_mean_epilogue(d["x"][a:b], d["bias"], d["gamma"], d["beta"],
+                                                                al, c)) for a, b in spans]
         else:
-            r = None if d["residual"] is None else d["residual"][:rows]
-            oracle.add_layernorm_gelu(d["x"][:rows], r, d["gamma"], d["beta"], w.params["eps"],
-                                      oracle.ACT_GELU_TANH if w.act == "gelu_tanh" else oracle.ACT_NONE)
-        t_total += time.perf_counter() - t
-        b_total += W.scaled(w, rows=rows).compulsory_bytes
-    return {"value": round(b_total / t_total / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            act = oracle.ACT_GELU_TANH if w.act == "gelu_tanh" else oracle.ACT_NONE
+            eps = w.params["eps"]
+            r = d["residual"]
+            calls = [(lambda a=a, b=b: oracle.add_layernorm_gelu(d["x"][a:b], None if r is None else r[a:b],
+                                                                 d["gamma"], d["beta"], eps, act))
+                     for a, b in spans]
+        return W.scaled(w, rows=rows).compulsory_bytes, calls
+
+    t_par = t_one = 0.0
+    b_total = 0
+    with ThreadPoolExecutor(cores) as ex:
+        for w in wl:
+            nbytes, calls = jobs(w)
+            b_total += nbytes
+            t = time.perf_counter()
+            list(ex.map(lambda f: f(), calls))
+            t_par += time.perf_counter() - t
+    for w in wl:
+        _, calls = jobs(w)
+        t = time.perf_counter()
+        for f in calls:
+            f()
+        t_one += time.perf_counter() - t
+    return {"value": round(b_total / t_par / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "single_core_value": round(b_total / t_one / 1e9, 3),
             "sample": f"first 1/{frac} of the rows (elements) of each of the {len(wl)} workloads, "
-                      f"{b_total} compulsory bytes, {t_total:.1f} s, binary64, single thread"}
+                      f"{b_total} compulsory bytes, binary64; {t_par:.1f} s on {cores} threads "
+                      f"(row chunks), {t_one:.1f} s on one thread"}
 
 
 if __name__ == "__main__":
