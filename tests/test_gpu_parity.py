@@ -367,8 +367,11 @@ def test_chain_2d_in_place(mbp):
         _gate_2d(x, oracle.pointwise_chain(xf, b1f, b2f, 0.5), fmt, f"chain 2d in place {fmt}")
 
 
+# 16-bit rows that are whole 16-byte vectors on 16-byte boundaries take the
+# 8-element kernel (1024, 512, 4096, 4000, 16384, 12288 with pads that keep the
+# boundaries); 1020 takes the 4-element one; 1001 and 515 the element one.
 TENOP_2D = [(64, 1024, 0, 0), (33, 1001, 0, 0), (40, 512, 8, 16), (21, 515, 5, 3), (1, 4096, 0, 0),
-            (9, 4000, 0, 8)]
+            (9, 4000, 0, 8), (12, 1020, 4, 4), (3, 16384, 0, 8), (5, 12288, 8, 0), (17, 24, 0, 0)]
 
 
 @pytest.mark.parametrize("fmt,dtype", DT2D, ids=[d[0] for d in DT2D])
