@@ -356,6 +356,65 @@ def test_chain_2d(mbp, fmt, dtype, rows, cols, xpad, ypad, m1, m2):
         assert (ybig[:, cols:].float() == 3.0).all(), "wrote outside the output rows"
 
 
+def _halfway_cases(fmt):
+    """(x, b1, b2, scale) lists whose exact chain result relu(x + b1)*scale + b2
+    lies closer to a halfway point of the 16-bit format than half a binary32
+    ulp, on both sides, for even and odd neighbours, both signs, and (set B,
+    scale 0.5 +- 2^-40 on odd subnormals) below the normal range."""
+    p = 8 if fmt == "bf16" else 11                 # significand bits
+    exps = [-100, -20, -1, 0, 7, 100] if fmt == "bf16" else [1, 5, 10, 15]
+    tiny = (lambda e: 2.0 ** (e - 30)) if fmt == "bf16" else (lambda e: 2.0 ** -24)
+    A = []
+    for e in exps:
+        for k in range(0, 2 ** (p - 1), 1 if fmt == "bf16" else 7):
+            v = (1 + k / 2 ** (p - 1)) * 2.0 ** e
+            h = 2.0 ** (e - p)                      # half an ulp of v
+            for sc in (1.0, -1.0):
+                for t in (tiny(e), -tiny(e)):
+                    A.append((v, h, t, sc))
+    sub_lsb = 2.0 ** -133 if fmt == "bf16" else 2.0 ** -24
+    norm_min = 2.0 ** -126 if fmt == "bf16" else 2.0 ** -14
+    B = [k * sub_lsb for k in range(1, 2 ** (p - 1), 2)]
+    B += [(1 + k / 2 ** (p - 1)) * norm_min for k in range(1, 2 ** (p - 1), 2)]
+    return A, B
+
+
+@pytest.mark.parametrize("fmt,dtype", DT2D[1:], ids=[d[0] for d in DT2D[1:]])
+def test_narrowing_exact_near_halfway(mbp, fmt, dtype):
+    """16-bit results are rounded once from binary64: inputs built so that the
+    exact result sits within a binary32 rounding of a 16-bit halfway point
+    (where rounding first to binary32 and then to 16 bits goes wrong), and odd
+    values halved into the subnormal range; every output must equal the exact
+    result rounded once (0 ulp), not merely lie within the 1-ulp gate."""
+    A, B = _halfway_cases(fmt)
+    cases = [(np.array([a[i] for a in A]) for i in range(4))]
+    xa, b1a, b2a, sca = cases[0]
+    xb = np.array(B)
+    for scale in (1.0, -1.0, 0.5 + 2.0 ** -40, 0.5 - 2.0 ** -40):
+        if abs(scale) == 1.0:
+            sel = sca == scale
+            x, b1, b2 = xa[sel], b1a[sel], b2a[sel]
+        else:
+            x, b1, b2 = xb, np.zeros_like(xb), np.zeros_like(xb)
+        n = x.size
+        cols = 64
+        rows = -(-n // cols)
+        pad = rows * cols - n
+        host = [np.concatenate([a, np.zeros(pad)]).reshape(rows, cols) for a in (x, b1, b2)]
+        dev = [torch.from_numpy(h).to(dtype).cuda() for h in host]
+        stored = [d.float().cpu().numpy() for d in dev]
+        for h, st in zip(host, stored):
+            assert np.array_equal(h.astype(np.float32), st), "a test input is not exact in the 16-bit type"
+        y = mbp.fused_pointwise_chain_2d(*dev, scale)
+        exact = oracle.pointwise_chain(*stored, scale)
+        want = oracle.round_bits(exact, fmt)
+        got = bits16(y)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, (f"{fmt} scale {scale}: {len(bad)} of {n} not rounded once, first at {bad[0]}: "
+                               f"exact {exact[tuple(bad[0])]!r} got {got[tuple(bad[0])]:#06x} "
+                               f"want {want[tuple(bad[0])]:#06x}")
+
+
 def test_chain_2d_in_place(mbp):
     rng = np.random.default_rng(12)
     for dtype, fmt in ((torch.bfloat16, "bf16"), (torch.float16, "f16")):
