@@ -139,6 +139,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// a ^ b ^ c in one instruction: v_bitop3_b32 with the truth table of a
+// three-way XOR (0x96); gfx950 has no v_xor3_b32 and the compiler does not
+// form this from two XORs.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 // Philox4x32-10 (J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw,
 // "Parallel random numbers: as easy as 1, 2, 3", SC'11): counter
 // (q lo, q hi, offset lo, offset hi), key (seed lo, seed hi); each round
@@ -152,8 +159,8 @@ __device__ __forceinline__ void philox4x32_10(uint64_t q, uint64_t seed, uint64_
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+    const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
