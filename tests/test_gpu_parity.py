@@ -88,8 +88,12 @@ def test_chain_full_workload(mbp):
 
 # ------------------------------------------------------------------ 10-op graph
 
+# fp32 rows of up to 256 vectors take one vector per lane in 16- to 256-lane
+# groups (4, 64, 100, 200, 500, 1000, 1024); wider rows the layout table;
+# widths that are not whole vectors the element path
 @pytest.mark.parametrize("rows,cols", [(1, 1), (1, 4), (3, 7), (2, 1024), (5, 1000), (33, 1024),
-                                       (4, 4096), (3, 4093), (2, 16384), (7, 16383), (300, 64)])
+                                       (4, 4096), (3, 4093), (2, 16384), (7, 16383), (300, 64),
+                                       (9, 100), (17, 200), (5, 500), (40, 1020)])
 def test_tenop_shapes(mbp, rows, cols):
     w = W.scaled(W.BY_NAME["tenop_1024x1024_f32"], rows=rows)
     d = W.generate(w, cols=cols)
