@@ -299,6 +299,16 @@ def test_ln_full_workload(mbp, name):
     assert torch.isfinite(y1.float()).all()
 
 
+def test_ln_f32_two_groups_per_block(mbp):
+    """fp32 rows with thousands of row groups run two groups per block (a
+    grid-stride loop); an odd count leaves the last block one group."""
+    w, d, act = _ln_case("ln_8192x4096_f32", 4097, 4096, residual=True, act="gelu_tanh")
+    y = mbp.fused_add_layernorm_gelu(to_dev(d["x"]), to_dev(d["residual"]), to_dev(d["gamma"]),
+                                     to_dev(d["beta"]), eps=1e-5, act=act)
+    rows = np.unique(np.concatenate([sample_rows(4097), [2047, 2048, 2049, 4095, 4096]]))
+    check_f32(to_host(y)[rows], _ln_ref(d, act, rows), "fp32 LN 4097 x 4096, two groups per block")
+
+
 # ------------------------------------------------------------------ two-dimensional forms
 
 DT2D = [("f32", torch.float32), ("bf16", torch.bfloat16), ("f16", torch.float16)]
