@@ -1,5 +1,5 @@
 // fused_tenop.hip -- the 10-op graph of "TorchInductor Pipeline 与算子融合" (the
-// model at the top of the post) as one persistent row kernel:
+// model at the top of the post) as one row kernel:
 //
 //   t = x*alpha + bias;  a = relu(t);  s = a*a + a*c;
 //   m = (row sum of s) / cols   (section 6.4: a sum, then the division);
@@ -14,7 +14,8 @@
 // (fp32 in and out), so the result is the exactly rounded value up to a few
 // binary64 roundings.  Rows that do not start on 16-byte boundaries take the
 // same kernel with one element per load.  The same kernel serves bf16 and fp16
-// storage and row-strided x / y (each result rounded once to the storage type).
+// storage and row-strided x / y (each result rounded once to the storage type);
+// 16-bit rows on 16-byte boundaries take tenop8_kernel (16-byte accesses).
 #include "mbp_internal.hpp"
 #include "row_common.hpp"
 

@@ -7,9 +7,10 @@
 // row (VPL of them), so each load instruction of the group covers a contiguous
 // stretch of the row (coalesced).  A vector is 16 bytes (4 fp32 / 8 bf16).
 // Groups of up to 256 lanes run in 256-lane blocks (several rows per block);
-// wider groups are one block.  Blocks are persistent (no more than can be
-// resident) and stride over the row groups, so the per-column vectors (gamma,
-// beta, bias) are loaded once per block.
+// wider groups are one block.  The kernels loop over row groups with a grid
+// stride, loading the per-column vectors (gamma, beta, bias) once per block;
+// the launchers mostly give each block one row group (the hardware dispatcher
+// then keeps the most loads in flight).
 #pragma once
 
 #include "mbp_device.hpp"
