@@ -101,23 +101,25 @@ __device__ __forceinline__ u32x4 partial_vec(const typename IO::elem* p, int c0,
   return r;
 }
 
-// normalise, affine, then the epilogue: tanh-GeLU, or relu (dropout follows
+// normalise, affine, then the epilogue: tanh-GeLU (relu and dropout follow
 // at the store, where the element's index is known)
 template <class Acc, int EPI>
 __device__ __forceinline__ float finish(Acc d, Acc rstd, Acc g, Acc b) {
   const float u = (float)fma_t(d * rstd, g, b);
   if constexpr (EPI == kEpiGelu) return gelu_tanh_f32(u);
-  if constexpr (EPI == kEpiReluDrop) return (u < 0.0f) ? 0.0f : u;  // relu; NaN passes through
   return u;
 }
 
-// dropout of N outputs with flat indices i0 .. i0 + N - 1
+// relu, then dropout, of N outputs with flat indices i0 .. i0 + N - 1, as one
+// select: an element survives if it is kept and not below 0 (relu maps u < 0
+// to 0, and 0 * scale is 0; -0 and NaN pass through relu unchanged and are
+// scaled when kept)
 template <int N, bool ALIGNED>
-__device__ __forceinline__ void apply_dropout(float* o, uint64_t i0, const Drop& drop) {
+__device__ __forceinline__ void relu_dropout(float* o, uint64_t i0, const Drop& drop) {
   uint32_t h[N];
   dropout_bits<N, ALIGNED>(i0, drop.seed, drop.offset, h);
 #pragma unroll
-  for (int e = 0; e < N; ++e) o[e] = (h[e] >= drop.thr) ? o[e] * drop.scale : 0.0f;
+  for (int e = 0; e < N; ++e) o[e] = (h[e] >= drop.thr && !(o[e] < 0.0f)) ? o[e] * drop.scale : 0.0f;
 }
 
 // ------------------------------------------------------------ aligned rows
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
           o[e] = finish<Acc, EPI>(d, rstd, (Acc)g[k][e], (Acc)b[k][e]);
       }
       if constexpr (EPI == kEpiReluDrop)  // rows start on multiples of V: one aligned group
-        apply_dropout<V, true>(o, (uint64_t)row * (uint64_t)cols + (uint64_t)(vi * V), drop);
+        relu_dropout<V, true>(o, (uint64_t)row * (uint64_t)cols + (uint64_t)(vi * V), drop);
       store_nt(reinterpret_cast<u32x4*>(yr) + vi, pack_vec<IO>(o));
     }
   }
@@ -871,7 +873,7 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_shift_kernel(
         o[e] = finish<Acc, EPI>(d, rstd, (Acc)IO::get(gp[k], e), (Acc)IO::get(bp[k], e));
       }
       if constexpr (EPI == kEpiReluDrop)  // slot j holds columns V*j .. V*j + V - 1 of the row
-        apply_dropout<V, false>(o, (uint64_t)(live ? row : 0) * (uint64_t)cols + (uint64_t)(V * slot(k)), drop);
+        relu_dropout<V, false>(o, (uint64_t)(live ? row : 0) * (uint64_t)cols + (uint64_t)(V * slot(k)), drop);
       ov[k] = pack_vec<IO>(o);
     }
     ov[VPL] = ov[VPL - 1];
