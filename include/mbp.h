@@ -313,6 +313,13 @@ mbp_status mbp_graph_destroy(mbp_graph* graph);
  * multiple of 16. */
 mbp_status mbp_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
 
+/* y[i] = x[i] rounded to bfloat16 (nearest even; NaN stays NaN with its sign),
+ * with the binary32 -> bfloat16 conversion that every kernel storing bf16 uses
+ * (v_cvt_pk_bf16_f32), exposed so that it can be checked over every binary32
+ * bit pattern.  x: device fp32 [n], 4-byte aligned; y: device [n] bf16 bit
+ * patterns, 2-byte aligned, not overlapping x.  n == 0 is a no-op. */
+mbp_status mbp_convert_f32_to_bf16(const float* x, uint16_t* y, int64_t n, void* stream);
+
 /* Static description of a status code. */
 const char* mbp_status_string(mbp_status s);
 

@@ -54,6 +54,7 @@ SIGNATURES = [
     ("mbp_graph_nodes", _I64, [_P]),
     ("mbp_graph_destroy", _I, [_P]),
     ("mbp_stream_copy", _I, [_P, _P, _SZ, _P]),
+    ("mbp_convert_f32_to_bf16", _I, [_P, _P, _I64, _P]),
     ("mbp_status_string", ctypes.c_char_p, [_I]),
     ("mbp_last_error", ctypes.c_char_p, []),
     ("mbp_abi_version", _I, []),
@@ -469,6 +470,17 @@ class capture:
             raise MbpError("mbp_graph_capture_end", st, lib.mbp_last_error().decode())
         self.graph = Graph(h.value)
         return False
+
+
+def convert_f32_to_bf16(x, out=None):
+    """fp32 -> bf16 with the kernels' store conversion (round to nearest even)."""
+    _check(x, "x", (torch.float32,))
+    _check(out, "out", (torch.bfloat16,), x.device)
+    y = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device) if out is None else out
+    if y.numel() != x.numel():
+        raise ValueError("out has the wrong size")
+    _call("mbp_convert_f32_to_bf16", _ptr(x), _ptr(y), x.numel(), _stream(x))
+    return y
 
 
 def stream_copy(src, dst):

@@ -634,6 +634,16 @@ mbp_status mbp_stream_copy(const void* src, void* dst, size_t bytes, void* strea
   return from_hip(mbp::launch_copy(src, dst, bytes, as_stream(stream)), "mbp_stream_copy");
 }
 
+mbp_status mbp_convert_f32_to_bf16(const float* x, uint16_t* y, int64_t n, void* stream) {
+  if (n < 0) return fail(MBP_ERR_SHAPE, "n must be >= 0 (got %lld)", (long long)n);
+  if (n == 0) return ok();
+  if (n > kMaxElems) return fail(MBP_ERR_SHAPE, "n is too large");
+  if (!x || !y) return fail(MBP_ERR_NULL, "x and y must be non-NULL");
+  if (misaligned(x, 4) || misaligned(y, 2)) return fail(MBP_ERR_ALIGN, "x must be 4-byte and y 2-byte aligned");
+  if (overlaps(Span{x, (size_t)n * 4}, Span{y, (size_t)n * 2})) return fail(MBP_ERR_OVERLAP, "y overlaps x");
+  return from_hip(mbp::launch_to_bf16(x, y, n, as_stream(stream)), "mbp_convert_f32_to_bf16");
+}
+
 const char* mbp_status_string(mbp_status s) {
   switch (s) {
     case MBP_OK: return "ok";

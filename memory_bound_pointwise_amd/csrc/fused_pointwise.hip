@@ -146,7 +146,43 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(const u32x4* src, u32x4* d
 }
 
 
+// binary32 -> bfloat16 with the conversion every bf16-storing kernel uses
+// (pack_bf16x2 / f32_to_bf16: v_cvt_pk_bf16_f32, round to nearest even), for
+// checking it over every binary32 bit pattern.  Eight values per item when x
+// and y are 16-byte aligned, then the n % 8 tail one at a time.
+__global__ __launch_bounds__(kBlock) void to_bf16_kernel(const float* x, uint16_t* y, int64_t n,
+                                                       int vec) {
+  const int64_t n8 = vec ? n / 8 : 0;
+  const int64_t items = n8 + (n - 8 * n8);
+  for (int64_t it = (int64_t)blockIdx.x * kBlock + threadIdx.x; it < items;
+       it += (int64_t)gridDim.x * kBlock) {
+    if (it < n8) {
+      const u32x4 a = load_nt(reinterpret_cast<const u32x4*>(x) + 2 * it);
+      const u32x4 b = load_nt(reinterpret_cast<const u32x4*>(x) + 2 * it + 1);
+      u32x4 o;
+      o.w[0] = pack_bf16x2(__uint_as_float(a.w[0]), __uint_as_float(a.w[1]));
+      o.w[1] = pack_bf16x2(__uint_as_float(a.w[2]), __uint_as_float(a.w[3]));
+      o.w[2] = pack_bf16x2(__uint_as_float(b.w[0]), __uint_as_float(b.w[1]));
+      o.w[3] = pack_bf16x2(__uint_as_float(b.w[2]), __uint_as_float(b.w[3]));
+      store_nt(reinterpret_cast<u32x4*>(y) + it, o);
+    } else {
+      const int64_t i = 8 * n8 + (it - n8);
+      y[i] = f32_to_bf16(x[i]);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s) {
+  const int vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) == 0;
+  const int64_t items = vec ? n / 8 + n % 8 : n;
+  int64_t grid = (items + kBlock - 1) / kBlock;
+  if (grid > kMaxGrid) grid = kMaxGrid;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)grid), dim3(kBlock), 0, s, x, y, n, vec);
+  return hipGetLastError();
+}
 
 hipError_t launch_chain(const float* x, const float* b1, const float* b2, float* y, int64_t n,
                         double scale, hipStream_t s) {

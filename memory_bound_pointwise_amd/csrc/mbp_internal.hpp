@@ -41,6 +41,7 @@ hipError_t launch_layernorm(int dtype, const void* x, const void* residual, cons
                             const void* beta, void* y, int64_t rows, int64_t cols, double eps,
                             int act, const Drop* drop, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
 
 // Unfused primitives (one launch each).
 enum EwOp {

@@ -214,6 +214,17 @@ def test_graph_host_errors(mbp):
         mbp.capture(None)
 
 
+def test_convert_validation(mbp):
+    L = mbp.lib
+    f = L.mbp_convert_f32_to_bf16
+    assert f(A, Y, -1, None) == 2                 # SHAPE
+    assert f(None, None, 0, None) == 0            # n == 0: no-op
+    assert f(None, Y, 8, None) == 1               # NULL
+    assert f(A + 2, Y, 8, None) == 4              # x not 4-byte aligned
+    assert f(A, Y + 1, 8, None) == 4              # y not 2-byte aligned
+    assert f(A, A + 16, 8, None) == 5             # y overlaps x
+
+
 def test_binding_rejects_cpu_tensors(mbp):
     import torch
     x = torch.zeros(8)

@@ -746,6 +746,32 @@ def test_empty_inputs(mbp):
     assert mbp.fused_add_layernorm_gelu(x, None, v, v).numel() == 0
 
 
+def test_bf16_store_conversion_exhaustive(mbp):
+    """Every binary32 bit pattern through the bf16 store conversion that the
+    kernels use, against round-to-nearest-even written in integer arithmetic
+    (torch int64 operations on the GPU, no float conversion involved): a
+    non-NaN input u gives (u + 0x7FFF + bit 16 of u) >> 16 -- carries move a
+    rounded-up mantissa into the exponent and past the largest finite value
+    to infinity, subnormals included; a NaN gives a NaN of the same sign."""
+    chunk = 1 << 28
+    x = torch.empty(chunk, dtype=torch.float32, device="cuda")
+    y = torch.empty(chunk, dtype=torch.bfloat16, device="cuda")
+    for c in range(1 << 4):
+        u = torch.arange(c * chunk, (c + 1) * chunk, dtype=torch.int64, device="cuda")
+        x.view(torch.int32).copy_(torch.where(u >= 1 << 31, u - (1 << 32), u).to(torch.int32))
+        mbp.convert_f32_to_bf16(x, out=y)
+        got = y.view(torch.int16).to(torch.int64) & 0xFFFF
+        nan = (u & 0x7FFFFFFF) > 0x7F800000
+        rne = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+        bad = (got != rne) & ~nan
+        assert not bad.any(), f"chunk {c}: {int(bad.sum())} patterns not rounded to nearest even, " \
+                              f"first input {int(u[bad][0]):#010x} -> {int(got[bad][0]):#06x}"
+        gn, un = got[nan], u[nan]
+        assert (((gn & 0x7F80) == 0x7F80) & ((gn & 0x7F) != 0) & ((gn >> 15) == (un >> 31))).all(), \
+            f"chunk {c}: a NaN input did not give a NaN of the same sign"
+        del u, got, nan, rne, bad, gn, un
+
+
 def test_stream_copy(mbp):
     src = torch.arange(1 << 20, dtype=torch.float32, device="cuda")
     dst = torch.zeros_like(src)
