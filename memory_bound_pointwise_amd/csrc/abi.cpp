@@ -552,12 +552,12 @@ mbp_status mbp_graph_capture_end(void* stream, mbp_graph** graph) {
   }
   size_t nodes = 0;
   e = hipGraphGetNodes(g, nullptr, &nodes);
-  if (e == hipSuccess && nodes == 0) {
+  if (e != hipSuccess || nodes == 0) {
     (void)hipGraphDestroy(g);
-    return fail(MBP_ERR_ARG, "nothing was captured");
+    return e != hipSuccess ? from_hip(e, "hipGraphGetNodes") : fail(MBP_ERR_ARG, "nothing was captured");
   }
   hipGraphExec_t exec = nullptr;
-  if (e == hipSuccess) e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+  e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
   (void)hipGraphDestroy(g);  // the executable graph does not need its template
   if (e != hipSuccess) return from_hip(e, "hipGraphInstantiate");
   mbp_graph* h = new (std::nothrow) mbp_graph{exec, nodes};
