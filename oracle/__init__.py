@@ -71,6 +71,8 @@ def _bind(lib):
     lib.oracle_round_to_bf16.restype = None
     lib.oracle_softmax.argtypes = [P, I64, I64, P]
     lib.oracle_softmax.restype = I
+    lib.oracle_softmax_mode.argtypes = [I, P, I64, I64, I, P]
+    lib.oracle_softmax_mode.restype = I
     lib.oracle_philox4x32_10.argtypes = [P, P, I64, P]
     lib.oracle_philox4x32_10.restype = None
     U32, U64 = ctypes.c_uint32, ctypes.c_uint64
@@ -170,15 +172,17 @@ def round_bits(x, fmt, lib=None):
     return out
 
 
-def softmax(x, lib=None):
+def softmax(x, mode=EXACT, dtype="f32", lib=None):
     """Row softmax over the last dimension of a 2-D array of stored values
-    (float32; 16-bit inputs widened to float32 first)."""
+    (float32; 16-bit inputs widened to float32 first).  mode SEQ: as eager
+    one-op kernels storing `dtype` ("f32" or "bf16") evaluate it."""
     lib = lib or load()
     x = _f32(x)
     if x.ndim != 2:
         raise ValueError("x must be 2-D")
     y = np.empty(x.shape, dtype=np.float64)
-    _check(lib.oracle_softmax(_ptr(x), x.shape[0], x.shape[1], _ptr(y)), "softmax")
+    dt = {"f32": F32, "bf16": BF16}[dtype]
+    _check(lib.oracle_softmax_mode(dt, _ptr(x), x.shape[0], x.shape[1], mode, _ptr(y)), "softmax")
     return y
 
 

@@ -375,10 +375,20 @@ int oracle_add_layernorm_gelu(int dtype, const void* x, const void* residual, co
  * pages' running-max update (a new maximum rescales the partial sum by
  * exp(m_old - m_new)) reaches the same values in exact arithmetic; this is
  * the plain definition.  A NaN anywhere in a row makes its sum NaN, so the row
- * is NaN; a row of -inf only is 0/0 = NaN (both as torch.softmax). */
-int oracle_softmax(const float* x, int64_t rows, int64_t cols, double* y) {
+ * is NaN; a row of -inf only is 0/0 = NaN (both as torch.softmax).
+ * ORACLE_SEQ: the same four ops as eager one-op kernels evaluate them ([P3]
+ * section 4.2 names softmax as the reduce + element-wise pattern that fusion
+ * targets): the difference x - m, the exponential and the quotient are each
+ * rounded as such a kernel stores its result -- to binary32, then to the I/O
+ * type (dtype ORACLE_BF16: bfloat16, nearest even) -- and the row sum is
+ * accumulated in binary64 and stored as binary32.  ORACLE_EXACT ignores
+ * dtype. */
+int oracle_softmax_mode(int dtype, const float* x, int64_t rows, int64_t cols, int mode, double* y) {
+  if (mode != ORACLE_EXACT && mode != ORACLE_SEQ) return -2;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -3;
   if (rows < 0 || (rows > 0 && cols <= 0)) return -1;
   if (rows == 0) return 0;
+  const int seq = mode == ORACLE_SEQ;
   const int64_t n = rows * cols;
   double* m = alloc_d(rows);
   double* e = alloc_d(n);
@@ -393,20 +403,33 @@ int oracle_softmax(const float* x, int64_t rows, int64_t cols, double* y) {
     }
     m[i] = mi;
   }
-  /* op 2: shifted exponentials */
+  /* op 2: shifted exponentials (SEQ: the difference and the exponential are
+   * two eager ops, each result stored in the I/O type) */
   for (int64_t i = 0; i < rows; ++i)
-    for (int64_t j = 0; j < cols; ++j) e[i * cols + j] = exp((double)x[i * cols + j] - m[i]);
-  /* op 3: row sum */
+    for (int64_t j = 0; j < cols; ++j) {
+      double d = (double)x[i * cols + j] - m[i];
+      if (seq) d = rstore(dtype, d);
+      const double ev = exp(d);
+      e[i * cols + j] = seq ? rstore(dtype, ev) : ev;
+    }
+  /* op 3: row sum (SEQ: accumulated in binary64, stored as binary32) */
   for (int64_t i = 0; i < rows; ++i) {
     double acc = 0.0;
     for (int64_t j = 0; j < cols; ++j) acc += e[i * cols + j];
-    l[i] = acc;
+    l[i] = seq ? r32(acc) : acc;
   }
   /* op 4: divide */
   for (int64_t i = 0; i < rows; ++i)
-    for (int64_t j = 0; j < cols; ++j) y[i * cols + j] = e[i * cols + j] / l[i];
+    for (int64_t j = 0; j < cols; ++j) {
+      const double q = e[i * cols + j] / l[i];
+      y[i * cols + j] = seq ? rstore(dtype, q) : q;
+    }
   free(m); free(e); free(l);
   return 0;
+}
+
+int oracle_softmax(const float* x, int64_t rows, int64_t cols, double* y) {
+  return oracle_softmax_mode(ORACLE_F32, x, rows, cols, ORACLE_EXACT, y);
 }
 
 /* ---- counter-based random numbers: Philox4x32-10 ---------------------------

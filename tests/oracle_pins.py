@@ -538,6 +538,65 @@ def pin_softmax_torch(lib):
     assert np.all(np.abs(s - 1) < 1e-13), "rows sum to 1"
 
 
+def _f32_ordered(a):
+    i = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    return np.where(i < 0, -(i & 0x7FFFFFFF), i)
+
+
+def pin_softmax_seq(lib):
+    """The eager (SEQ) softmax against the same op sequence evaluated by
+    independent libraries -- numpy float32 operations for binary32 storage,
+    torch CPU bfloat16 tensors for bfloat16 storage (each op's result stored
+    in the I/O type, the row sum taken in float64 and kept as float32) --
+    which may differ only where their exponentials round differently; and
+    rows whose every intermediate is exact."""
+    import torch
+
+    def rn(v, dt):
+        v32 = np.float32(v)
+        return float(torch.tensor(v32).to(torch.bfloat16).float()) if dt == "bf16" else float(v32)
+
+    for dt in ("f32", "bf16"):
+        x = np.full((3, 9), -np.inf, np.float32)
+        x[0, 4] = 2.5                      # one finite entry: 1 there, 0 elsewhere
+        x[1, [1, 3, 7]] = -1.0             # three equal maxima: 1/3 rounded to the I/O type
+        x[2, :] = 0.75                     # nine equal entries
+        y = oracle.softmax(x, mode=oracle.SEQ, dtype=dt, lib=lib)
+        assert np.array_equal(y[0], np.eye(9)[4]), f"{dt}: one-hot row {y[0]}"
+        assert np.all(y[1, [1, 3, 7]] == rn(1 / 3, dt)) and np.all(np.delete(y[1], [1, 3, 7]) == 0), \
+            f"{dt}: three maxima {y[1]}"
+        assert np.all(y[2] == rn(1 / 9, dt)), f"{dt}: uniform row {y[2]}"
+
+    r = _rng(33)
+    x = (r.standard_normal((64, 257)) * np.exp2(r.integers(0, 5, (64, 1)))).astype(np.float32)
+    # binary32 storage: numpy float32
+    y = oracle.softmax(x, mode=oracle.SEQ, dtype="f32", lib=lib)
+    assert np.array_equal(y, y.astype(np.float32).astype(np.float64)), "f32 SEQ results must be binary32 values"
+    d = (x - x.max(axis=1, keepdims=True)).astype(np.float32)
+    e = np.exp(d).astype(np.float32)
+    l = e.astype(np.float64).sum(axis=1, keepdims=True).astype(np.float32)
+    want = (e / l).astype(np.float32)
+    # numpy's float32 exp is itself up to 2 ulp from the correctly rounded value
+    ulp = np.abs(_f32_ordered(y) - _f32_ordered(want))
+    assert ulp.max() <= 4 and (ulp > 2).mean() <= 0.01, \
+        f"f32 SEQ vs numpy float32: max {ulp.max()} ulp, {(ulp > 2).mean():.3%} beyond 2 ulp"
+    # bfloat16 storage: torch CPU bfloat16 tensors
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    y = oracle.softmax(xb.float().numpy(), mode=oracle.SEQ, dtype="bf16", lib=lib)
+    yb = torch.from_numpy(y).to(torch.bfloat16)
+    assert np.array_equal(yb.double().numpy(), y), "bf16 SEQ results must be bfloat16 values"
+    eb = torch.exp(xb - xb.max(dim=1, keepdim=True).values)
+    lb = eb.double().sum(dim=1, keepdim=True).float()
+    wb = (eb.float() / lb).to(torch.bfloat16)
+    o = lambda t: (lambda i: np.where(i < 0, -(i & 0x7FFF), i))(t.view(torch.int16).numpy().astype(np.int64))
+    ulp = np.abs(o(yb) - o(wb))
+    assert ulp.max() <= 1 and (ulp > 0).mean() <= 0.05, \
+        f"bf16 SEQ vs torch bfloat16: max {ulp.max()} ulp, {(ulp > 0).mean():.2%} differ"
+    # a large common offset: no overflow
+    y = oracle.softmax(x[:4] + np.float32(1000), mode=oracle.SEQ, dtype="f32", lib=lib)
+    assert np.all(np.isfinite(y)) and np.all(np.abs(y.sum(axis=1) - 1) < 1e-4), "SEQ with an offset of 1000"
+
+
 def pin_philox_kat(lib):
     g = read("philox_kat.txt")
     for k in range(3):
@@ -597,6 +656,6 @@ ALL_PINS = [
     pin_tenop_worked, pin_tenop_bruteforce, pin_tenop_invariants, pin_tenop_seq,
     pin_ln_worked, pin_ln_closed_forms, pin_ln_bruteforce, pin_ln_torch, pin_gelu,
     pin_residual_zero, pin_bf16_encode, pin_ln_seq, pin_round_f16, pin_round_bf16,
-    pin_softmax_worked, pin_softmax_closed_forms, pin_softmax_bruteforce, pin_softmax_torch,
+    pin_softmax_worked, pin_softmax_closed_forms, pin_softmax_bruteforce, pin_softmax_torch, pin_softmax_seq,
     pin_philox_kat, pin_dropout,
 ]

@@ -42,10 +42,13 @@ MUTANTS = [
     ("round: no overflow to infinity", "if (r > maxf) r = INFINITY;", ""),
     ("f16 encode: exponent bias off by one", "(uint16_t)((e - 1 + 15) << 10)", "(uint16_t)((e + 15) << 10)"),
     ("f16 encode: subnormal scale", "(uint16_t)ldexp(a, 24)); /* zero or subnormal */", "(uint16_t)ldexp(a, 23)); /* zero or subnormal */"),
-    ("softmax: maximum not subtracted", "e[i * cols + j] = exp((double)x[i * cols + j] - m[i]);", "e[i * cols + j] = exp((double)x[i * cols + j]);"),
+    ("softmax: maximum not subtracted", "double d = (double)x[i * cols + j] - m[i];", "double d = (double)x[i * cols + j];"),
     ("softmax: minimum for maximum", "if (v > mi) mi = v;", "if (v < mi || mi == -INFINITY) mi = v;"),
     ("softmax: sum skips the last column", "for (int64_t j = 0; j < cols; ++j) acc += e[i * cols + j];", "for (int64_t j = 0; j + 1 < cols; ++j) acc += e[i * cols + j];"),
-    ("softmax: divide by cols", "y[i * cols + j] = e[i * cols + j] / l[i];", "y[i * cols + j] = e[i * cols + j] / (double)cols;"),
+    ("softmax: divide by cols", "const double q = e[i * cols + j] / l[i];", "const double q = e[i * cols + j] / (double)cols;"),
+    ("softmax SEQ: difference not rounded", "if (seq) d = rstore(dtype, d);", ""),
+    ("softmax SEQ: exponential not rounded", "e[i * cols + j] = seq ? rstore(dtype, ev) : ev;", "e[i * cols + j] = ev;"),
+    ("softmax SEQ: quotient not rounded", "y[i * cols + j] = seq ? rstore(dtype, q) : q;", "y[i * cols + j] = q;"),
     ("philox: nine rounds", "for (int r = 0; r < 10; ++r) {", "for (int r = 0; r < 9; ++r) {"),
     ("philox: no key bump", "k0 += 0x9E3779B9u;", ""),
     ("philox: c1 and c3 swapped", "uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;", "uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[3] ^ k0;"),
