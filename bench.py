@@ -363,6 +363,19 @@ def main():
                            "gbps": round(w.compulsory_bytes / (med * 1e-6) / 1e9, 1),
                            "frac_of_peak": round(w.compulsory_bytes / (med * 1e-6) / 1e9 / PEAK_GBPS, 4)}
             del fns
+            if w.kind == "softmax" and args.unfused_reps:
+                # the five eager launches: max, x - m, exp, sum, divide
+                x = to_dev(d["x"])
+                y = torch.empty_like(x)
+                ws = torch.empty(mbp.workspace_bytes(mbp.OP_SOFTMAX, mbp.BF16, w.rows, w.cols),
+                                 dtype=torch.uint8, device=dev)
+                ufn = lambda: mbp.unfused_softmax(x, out=y, workspace=ws)
+                uus, _ = batch_times([ufn], args.unfused_reps)
+                um = statistics.median(uus)
+                del ufn
+                nxt[w.name].update({"unfused_us_median": round(um, 3), "launches_unfused": 5,
+                                    "speedup_vs_unfused": round(um / med, 3)})
+                del x, y, ws
             if w.kind == "ln_relu_dropout" and args.unfused_reps:
                 # the three eager launches of the same expression
                 x, g, b = (to_dev(d[k]) for k in ("x", "gamma", "beta"))

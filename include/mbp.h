@@ -72,7 +72,8 @@ typedef enum {
   MBP_OP_CHAIN = 0,
   MBP_OP_ROW_MEAN = 1,
   MBP_OP_LAYERNORM = 2,
-  MBP_OP_LN_RELU_DROPOUT = 3
+  MBP_OP_LN_RELU_DROPOUT = 3,
+  MBP_OP_SOFTMAX = 4
 } mbp_op;
 
 /* Granularity of the unfused variants. */
@@ -262,6 +263,19 @@ mbp_status unfused_layernorm_relu_dropout(mbp_dtype dtype, const void* x, const 
                                           const void* beta, void* y, int64_t rows, int64_t cols,
                                           double eps, double p, uint64_t seed, uint64_t offset,
                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The row softmax of fused_softmax as the eager sequence of five launches
+ * ([P3] section 4.2 names softmax as the reduce + element-wise pattern that
+ * fusion collapses): row max m; d = x - m; e = exp(d); row sum l; y = e / l.
+ * d and e are stored in `dtype` (MBP_F32 or MBP_BF16) in the workspace, m and
+ * l as fp32; each element-wise op computes in fp32 (expf for the exponential)
+ * and rounds once to `dtype`; the row sum accumulates in binary64.
+ * Workspace: mbp_unfused_workspace_bytes(MBP_OP_SOFTMAX, dtype, rows, cols,
+ * 0, 0, 0).  y may not alias x.
+ */
+mbp_status unfused_softmax(mbp_dtype dtype, const void* x, void* y, int64_t rows, int64_t cols,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace the unfused variant of `op` needs (bytes; 0 for a no-op shape).
  * For MBP_OP_CHAIN pass rows = 1, cols = n.  has_residual and act matter only

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libmbp.so")
 
 F32, BF16, F16 = 0, 1, 2
 ACT_NONE, ACT_GELU_TANH = 0, 1
-OP_CHAIN, OP_ROW_MEAN, OP_LAYERNORM, OP_LN_RELU_DROPOUT = 0, 1, 2, 3
+OP_CHAIN, OP_ROW_MEAN, OP_LAYERNORM, OP_LN_RELU_DROPOUT, OP_SOFTMAX = 0, 1, 2, 3, 4
 UNFUSED_PRIMITIVE, UNFUSED_EAGER, UNFUSED_GROUPED = 0, 1, 2
 MAX_COLS = 16384
 
@@ -40,6 +40,7 @@ SIGNATURES = [
     ("fused_softmax", _I, [_I, _P, _P, _I64, _I64, _P]),
     ("fused_layernorm_relu_dropout", _I, [_I, _P, _P, _P, _P, _I64, _I64, _D, _D, _U64, _U64, _P]),
     ("unfused_layernorm_relu_dropout", _I, [_I, _P, _P, _P, _P, _I64, _I64, _D, _D, _U64, _U64, _P, _SZ, _P]),
+    ("unfused_softmax", _I, [_I, _P, _P, _I64, _I64, _P, _SZ, _P]),
     ("fused_pointwise_chain_2d", _I, [_I, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _D, _P]),
     ("fused_row_mean_epilogue_2d", _I, [_I, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _D, _D, _P]),
     ("unfused_pointwise_chain", _I, [_P, _P, _P, _P, _I64, _D, _P, _SZ, _P]),
@@ -380,6 +381,23 @@ def grouped_row_mean_epilogue(x, bias, gamma, beta, alpha=1.1, c=0.1, out=None, 
     ws = _workspace(nb, x.device, workspace)
     _call("grouped_row_mean_epilogue", _ptr(x), _ptr(bias), _ptr(gamma), _ptr(beta), _ptr(y), rows,
           cols, float(alpha), float(c), _ptr(ws), ws.numel() * ws.element_size(), _stream(x))
+    return y
+
+
+def unfused_softmax(x, out=None, workspace=None):
+    """Row softmax as five eager launches (max, subtract, exp, sum, divide)
+    through HBM temporaries; fp32 or bf16."""
+    _check(x, "x", (torch.float32, torch.bfloat16))
+    _check(out, "out", (x.dtype,), x.device)
+    rows, cols = _rows_cols(x)
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape:
+        raise ValueError("out has the wrong shape")
+    code = _dtype_code(x)
+    nb = workspace_bytes(OP_SOFTMAX, code, rows, cols)
+    ws = _workspace(nb, x.device, workspace)
+    _call("unfused_softmax", code, _ptr(x), _ptr(y), rows, cols, _ptr(ws), ws.numel() * ws.element_size(),
+          _stream(x))
     return y
 
 

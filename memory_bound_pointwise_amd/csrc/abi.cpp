@@ -126,6 +126,26 @@ size_t row_mean_ws(char* base, int64_t rows, int64_t cols, RowMeanWs* w) {
   return c.used;
 }
 
+// softmax as eager ops: m [rows], d = x - m, e = exp(d) [rows, cols] in the
+// I/O type, l [rows]
+struct SoftmaxWs {
+  float* m;
+  void *d, *e;
+  float* l;
+};
+
+size_t softmax_ws(char* base, int dtype, int64_t rows, int64_t cols, SoftmaxWs* w) {
+  Carver c{base};
+  const size_t full = (size_t)rows * cols * (dtype == MBP_BF16 ? 2 : 4);
+  SoftmaxWs t;
+  t.m = (float*)c.take(rows * 4);
+  t.d = c.take(full);
+  t.e = c.take(full);
+  t.l = (float*)c.take(rows * 4);
+  if (w) *w = t;
+  return c.used;
+}
+
 size_t grouped_ws(char* base, int64_t rows, int64_t cols, GroupedWs* w) {
   Carver c{base};
   GroupedWs t;
@@ -372,6 +392,30 @@ mbp_status fused_layernorm_relu_dropout(mbp_dtype dtype, const void* x, const vo
                   "fused_layernorm_relu_dropout");
 }
 
+mbp_status unfused_softmax(mbp_dtype dtype, const void* x, void* y, int64_t rows, int64_t cols,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != MBP_F32 && dtype != MBP_BF16) return fail(MBP_ERR_DTYPE, "unfused_softmax takes fp32 or bf16");
+  mbp_status st = check_2d(dtype, {{x, cols}}, y, cols, rows, cols, MBP_MAX_COLS, nullptr);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  const size_t need = softmax_ws(nullptr, dtype, rows, cols, nullptr);
+  const size_t full = (size_t)rows * cols * dtype_size(dtype);
+  st = check_workspace(workspace, workspace_bytes, need, {{x, full}, {y, full}});
+  if (st != MBP_OK) return st;
+  SoftmaxWs w;
+  softmax_ws((char*)workspace, dtype, rows, cols, &w);
+  hipStream_t s = as_stream(stream);
+  using namespace mbp;
+  const int D = dtype;
+  // the eager sequence: row max, x - m, exp, row sum, divide
+  hipError_t e = launch_row_max(D, x, w.m, rows, cols, s);
+  if (e == hipSuccess) e = launch_ew(EW_SUB, D, x, w.m, IX_ROW, nullptr, 0, w.d, rows, cols, 0.f, s);
+  if (e == hipSuccess) e = launch_ew(EW_EXP, D, w.d, nullptr, 0, nullptr, 0, w.e, rows, cols, 0.f, s);
+  if (e == hipSuccess) e = launch_row_sum(D, w.e, w.l, rows, cols, s);
+  if (e == hipSuccess) e = launch_ew(EW_DIV, D, w.e, w.l, IX_ROW, nullptr, 0, y, rows, cols, 0.f, s);
+  return from_hip(e, "unfused_softmax");
+}
+
 mbp_status unfused_layernorm_relu_dropout(mbp_dtype dtype, const void* x, const void* gamma,
                                           const void* beta, void* y, int64_t rows, int64_t cols,
                                           double eps, double p, uint64_t seed, uint64_t offset,
@@ -593,6 +637,9 @@ size_t mbp_unfused_workspace_bytes(mbp_op op, mbp_dtype dtype, int64_t rows, int
     case MBP_OP_ROW_MEAN:
       if (granularity == MBP_UNFUSED_GROUPED) return grouped_ws(nullptr, rows, cols, nullptr);
       return row_mean_ws(nullptr, rows, cols, nullptr);
+    case MBP_OP_SOFTMAX:
+      if (dtype != MBP_F32 && dtype != MBP_BF16) return (size_t)-1;
+      return softmax_ws(nullptr, dtype, rows, cols, nullptr);
     case MBP_OP_LN_RELU_DROPOUT: {
       if (dtype != MBP_F32 && dtype != MBP_BF16) return (size_t)-1;
       Carver c{nullptr};
@@ -610,8 +657,9 @@ size_t mbp_unfused_workspace_bytes(mbp_op op, mbp_dtype dtype, int64_t rows, int
 }
 
 int mbp_launches_per_call(mbp_op op, int fused, int granularity, int has_residual, mbp_act act) {
-  if (fused) return (op >= MBP_OP_CHAIN && op <= MBP_OP_LN_RELU_DROPOUT) ? 1 : -1;
+  if (fused) return (op >= MBP_OP_CHAIN && op <= MBP_OP_SOFTMAX) ? 1 : -1;
   switch (op) {
+    case MBP_OP_SOFTMAX: return 5;
     case MBP_OP_LN_RELU_DROPOUT: return 3;
     case MBP_OP_CHAIN: return 4;
     case MBP_OP_ROW_MEAN: return granularity == MBP_UNFUSED_GROUPED ? 3 : 10;

@@ -234,4 +234,33 @@ __device__ __forceinline__ T group_sum(T v, T* lds) {
   }
 }
 
+// Maximum of v over a group of LANES consecutive lanes, laid out as for
+// group_sum.  The maximum is exact and independent of the combine order, so
+// every lane ends with the same value.  Comparisons with `>` never select a
+// NaN: callers keep NaN out of v (a NaN element propagates later, as in the
+// sum of exponentials).
+template <int LANES, int BLOCK, typename T>
+__device__ __forceinline__ T group_max(T v, T* lds) {
+  constexpr int kIn = LANES < 64 ? LANES : 64;
+#pragma unroll
+  for (int m = 1; m < kIn; m <<= 1) {
+    const T o = __shfl_xor(v, m);
+    v = o > v ? o : v;
+  }
+  if constexpr (LANES <= 64) {
+    return v;
+  } else {
+    static_assert(LANES % 64 == 0 && BLOCK % LANES == 0, "wave-multiple groups");
+    constexpr int kWaves = LANES / 64;
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[wave] = v;
+    lds_barrier();
+    const int first = (threadIdx.x / LANES) * kWaves;
+    T s = lds[first];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) s = lds[first + w] > s ? lds[first + w] : s;
+    return s;
+  }
+}
+
 }  // namespace mbp

@@ -56,6 +56,8 @@ enum EwOp {
   EW_DROPOUT = 8,  // keep(i) ? a * drop.scale : 0   (the element's index i picks its random bits)
   EW_PROLOGUE = 9,       // r = relu(a * scalar + b); r * r + r * scalar2   (five roundings)
   EW_CENTER_AFFINE = 10, // (a - b) * c + d   (three roundings)
+  EW_EXP = 11,           // exp(a)   (fp32 expf)
+  EW_DIV = 12,           // a / b
 };
 // How operand b (and c) is indexed: full tensor, per column (vector of cols),
 // or per row (vector of rows, fp32).
@@ -69,6 +71,10 @@ hipError_t launch_ew(int op, int dtype, const void* a, const void* b, int b_ix, 
 hipError_t launch_ew4(int op, int dtype, const void* a, const void* b, int b_ix, const void* c,
                       int c_ix, const void* d, int d_ix, void* out, int64_t rows, int64_t cols,
                       float scalar, float scalar2, hipStream_t s, const Drop* drop = nullptr);
+// Row maximum (NaN skipped) and row sum (binary64 accumulation) of a
+// [rows, cols] tensor, stored as fp32 [rows].
+hipError_t launch_row_max(int dtype, const void* a, float* out, int64_t rows, int64_t cols, hipStream_t s);
+hipError_t launch_row_sum(int dtype, const void* a, float* out, int64_t rows, int64_t cols, hipStream_t s);
 // Row mean (fp32 out) and biased variance about a given mean (fp32 out) of a
 // [rows, cols] tensor; binary64 accumulation.
 hipError_t launch_row_mean_only(int dtype, const void* a, float* mean, int64_t rows,

@@ -43,6 +43,8 @@ __device__ __forceinline__ float ew_apply(float a, float b, float c, float d, fl
     return __fadd_rn(__fmul_rn(r, r), __fmul_rn(r, scalar2));
   }
   if constexpr (OP == EW_CENTER_AFFINE) return __fadd_rn(__fmul_rn(__fsub_rn(a, b), c), d);
+  if constexpr (OP == EW_EXP) return expf(a);
+  if constexpr (OP == EW_DIV) return __fdiv_rn(a, b);
   return 0.0f;
 }
 
@@ -148,13 +150,15 @@ __global__ __launch_bounds__(kBlock) void ew_kernel(const typename IO::elem* a, 
   }
 }
 
-// Row statistics: one 256-lane block per row, binary64 accumulation, then a
-// fixed-order block reduction.  MODE 0: mean; MODE 1: biased variance about
-// `mean`.  The row is read in aligned 16-byte windows (window q: bytes
-// [16q, 16q + 16) above the 16-byte boundary at or below `a`), kU windows per
-// lane in flight; elements of a window outside the row are skipped, and a
-// window reaching outside the tensor (at its first or last row only) is read
-// element by element.
+// Row statistics: a lane group per row (one wave for rows of up to 4 KiB,
+// the 256-lane block otherwise), binary64 accumulation, then a fixed-order
+// group reduction.  MODE 0: mean; MODE 1: biased variance about
+// `mean`; MODE 2: maximum (NaN elements skipped; -inf for a row without a
+// larger value); MODE 3: sum.  The row is read in aligned 16-byte windows
+// (window q: bytes [16q, 16q + 16) above the 16-byte boundary at or below
+// `a`), kU windows per lane in flight; elements of a window outside the row
+// are skipped, and a window reaching outside the tensor (at its first or last
+// row only) is read element by element.
 constexpr int kU = 4;
 
 template <class IO>
@@ -200,7 +204,7 @@ __global__ __launch_bounds__(kBlock) void row_stat_kernel(const typename IO::ele
     const int64_t lo = mb + (int64_t)ES * (live ? row : 0) * cols, hi = live ? lo + (int64_t)ES * cols : lo;
     const int64_t q_end = (hi + 15) >> 4;
     const double mu = MODE == 1 && live ? (double)mean[row] : 0.0;
-    double acc = 0.0;
+    double acc = MODE == 2 ? -__builtin_inf() : 0.0;
     for (int64_t q0 = (lo >> 4) + lane; q0 < q_end; q0 += kU * LANES) {
       u32x4 w[kU];
 #pragma unroll
@@ -217,8 +221,10 @@ __global__ __launch_bounds__(kBlock) void row_stat_kernel(const typename IO::ele
           const int64_t bb = wb + ES * e;
           if (inner || (bb >= lo && bb < hi)) {
             const double v = (double)IO::get(w[u], e);
-            if constexpr (MODE == 0) {
+            if constexpr (MODE == 0 || MODE == 3) {
               acc += v;
+            } else if constexpr (MODE == 2) {
+              acc = v > acc ? v : acc;
             } else {
               const double d = v - mu;
               acc += d * d;
@@ -227,8 +233,10 @@ __global__ __launch_bounds__(kBlock) void row_stat_kernel(const typename IO::ele
         }
       }
     }
-    const double tot = group_sum<LANES, kBlock>(acc, red[parity]);
-    if (live && lane == 0) out[row] = (float)(tot / (double)cols);
+    double tot;
+    if constexpr (MODE == 2) tot = group_max<LANES, kBlock>(acc, red[parity]);
+    else tot = group_sum<LANES, kBlock>(acc, red[parity]);
+    if (live && lane == 0) out[row] = (float)(MODE >= 2 ? tot : tot / (double)cols);
   }
 }
 
@@ -246,6 +254,8 @@ const void* ew_ptr(int op) {
     case EW_DROPOUT: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_DROPOUT, VW>);
     case EW_PROLOGUE: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_PROLOGUE, VW>);
     case EW_CENTER_AFFINE: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_CENTER_AFFINE, VW>);
+    case EW_EXP: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_EXP, VW>);
+    case EW_DIV: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_DIV, VW>);
     default: return nullptr;
   }
 }
@@ -308,6 +318,22 @@ hipError_t launch_row_mean_only(int dtype, const void* a, float* mean, int64_t r
   const float* none = nullptr;
   const int grid = (int)stat_grid(rows, cols, dtype == 1 ? 2 : 4);
   void* args[] = {&a, &none, &mean, &rows, &cols};
+  return hipLaunchKernel(k, dim3(grid), dim3(kBlock), args, 0, s);
+}
+
+hipError_t launch_row_max(int dtype, const void* a, float* out, int64_t rows, int64_t cols, hipStream_t s) {
+  const void* k = dtype == 1 ? stat_ptr<BF16IO, 2>(cols) : stat_ptr<F32IO, 2>(cols);
+  const float* none = nullptr;
+  const int grid = (int)stat_grid(rows, cols, dtype == 1 ? 2 : 4);
+  void* args[] = {&a, &none, &out, &rows, &cols};
+  return hipLaunchKernel(k, dim3(grid), dim3(kBlock), args, 0, s);
+}
+
+hipError_t launch_row_sum(int dtype, const void* a, float* out, int64_t rows, int64_t cols, hipStream_t s) {
+  const void* k = dtype == 1 ? stat_ptr<BF16IO, 3>(cols) : stat_ptr<F32IO, 3>(cols);
+  const float* none = nullptr;
+  const int grid = (int)stat_grid(rows, cols, dtype == 1 ? 2 : 4);
+  void* args[] = {&a, &none, &out, &rows, &cols};
   return hipLaunchKernel(k, dim3(grid), dim3(kBlock), args, 0, s);
 }
 

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
                  "fused_pointwise_chain_2d", "fused_row_mean_epilogue_2d", "fused_softmax",
                  "fused_layernorm_relu_dropout", "unfused_layernorm_relu_dropout",
                  "unfused_pointwise_chain", "unfused_row_mean_epilogue", "unfused_add_layernorm_gelu",
-                 "grouped_row_mean_epilogue", "mbp_graph_capture_begin", "mbp_graph_capture_end",
+                 "grouped_row_mean_epilogue", "unfused_softmax", "mbp_graph_capture_begin", "mbp_graph_capture_end",
                  "mbp_graph_launch", "mbp_graph_destroy"):
         assert name in fns
 
@@ -212,6 +212,26 @@ def test_graph_host_errors(mbp):
     import torch
     with pytest.raises(ValueError):
         mbp.capture(None)
+
+
+def test_unfused_softmax_validation(mbp):
+    global L
+    L = mbp.lib
+    u = "unfused_softmax"
+    ws = Y + 0x100000
+    # dtype, x, y, rows, cols, workspace, workspace_bytes, stream
+    assert st(u, 2, A, Y, 4, 8, ws, 1 << 20, None) == 3                 # fp16: fused only
+    assert st(u, 1, A, Y, 4, 0, ws, 1 << 20, None) == 2                 # cols == 0
+    assert st(u, 1, A, Y, 0, 8, None, 0, None) == 0                     # rows == 0
+    assert st(u, 1, A, A, 4, 8, ws, 1 << 20, None) == 5                 # y == x
+    assert st(u, 1, A, Y, 4, 8, None, 0, None) == 6                     # no workspace
+    assert st(u, 0, A, Y, 4, 8, ws, 16, None) == 6                      # too small
+    m = mbp
+    assert m.launches_per_call(m.OP_SOFTMAX, True) == 1
+    assert m.launches_per_call(m.OP_SOFTMAX, False) == 5
+    assert m.workspace_bytes(m.OP_SOFTMAX, m.BF16, 4, 8) == 4 * 256
+    with pytest.raises(ValueError):
+        m.workspace_bytes(m.OP_SOFTMAX, m.F16, 4, 8)
 
 
 def test_convert_validation(mbp):

@@ -73,11 +73,15 @@ def _case(mbp, name):
     if name == "softmax":
         x = torch.randn(257, 1000, device="cuda", dtype=torch.bfloat16)
         return x, lambda y, ws: m.fused_softmax(x, out=y), 0, 1
+    if name == "softmax_unfused":
+        x = torch.randn(257, 1000, device="cuda", dtype=torch.bfloat16)
+        nb = m.workspace_bytes(m.OP_SOFTMAX, m.BF16, 257, 1000)
+        return x, lambda y, ws: m.unfused_softmax(x, out=y, workspace=ws), nb, 5
     raise KeyError(name)
 
 
 CASES = ["chain_unfused", "chain_fused", "tenop_unfused", "tenop_grouped", "tenop_fused",
-         "ln_unfused", "ln_fused", "lnrd_unfused", "lnrd_fused", "softmax"]
+         "ln_unfused", "ln_fused", "lnrd_unfused", "lnrd_fused", "softmax", "softmax_unfused"]
 
 
 @pytest.mark.parametrize("name", CASES)

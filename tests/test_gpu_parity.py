@@ -14,7 +14,7 @@ import torch
 import oracle
 import workloads as W
 from parity_util import (as_f64, check_bf16, check_chain, check_f32, sample_rows, to_dev,
-                         to_host, bits16, check_ulp16)
+                         to_host, bits16, check_ulp16, ordered)
 
 pytestmark = pytest.mark.gpu
 
@@ -733,6 +733,46 @@ def test_unfused_layernorm_shapes(mbp, name, cols, rows, off, gran):
     ref = _ln_ref(d, act, mode=oracle.SEQ if gran == 0 else oracle.SEQ3)
     chk = check_bf16 if w.dtype == "bf16" else check_f32
     chk(to_host(y), ref, f"unfused {name} {rows}x{cols} offset {off} granularity {gran}")
+
+
+SM_UNFUSED = [(3, 1), (5, 7), (33, 1000), (7, 4096), (2, 16384), (64, 768), (9, 4095)]
+
+
+@pytest.mark.parametrize("fmt,dtype", DT2D[:2], ids=[d[0] for d in DT2D[:2]])
+@pytest.mark.parametrize("rows,cols", SM_UNFUSED)
+def test_unfused_softmax(mbp, fmt, dtype, rows, cols):
+    """The five eager launches (max, x - m, exp, sum, divide) against the
+    oracle's SEQ softmax (each element-wise result rounded to binary32 and to
+    the I/O type, the row sum kept as binary32).  The GPU's expf is within an
+    ulp of the exact exponential the oracle rounds, so bf16 results may differ
+    by 1 ulp where a rounding flips and fp32 results by a few ulps.  Masked
+    entries (-inf) give exactly 0; an all-masked row gives NaN."""
+    rng = np.random.default_rng([17, rows, cols])
+    xh = torch.from_numpy(rng.standard_normal((rows, cols)) * 3).to(dtype)
+    xh[torch.from_numpy(rng.random((rows, cols)) < 0.1)] = float("-inf")
+    xh[:, 0] = torch.from_numpy(rng.standard_normal(rows)).to(dtype)
+    if rows > 2:
+        xh[2, :] = float("-inf")
+    xf = xh.float().numpy()
+    y = mbp.unfused_softmax(xh.cuda())
+    want = oracle.softmax(xf, mode=oracle.SEQ, dtype=fmt)
+    what = f"unfused softmax {fmt} {rows}x{cols}"
+    if fmt == "bf16":
+        check_ulp16(bits16(y), want, fmt, what)
+    else:
+        got = to_host(y)
+        assert np.array_equal(np.isnan(got), np.isnan(want)), f"{what}: NaN mismatch"
+        d = np.where(np.isnan(want), 0, np.abs(ordered(got) - ordered(want.astype(np.float32))))
+        assert d.max(initial=0) <= 4, f"{what}: max {d.max()} ulp"
+    masked = np.isneginf(xf) & ~np.isnan(want)
+    assert np.all(to_host(y.float())[masked] == 0), f"{what}: masked entries must be exactly 0"
+    # the same result from a misaligned input (element paths of every launch)
+    buf = torch.zeros(rows * cols + 1, dtype=dtype, device="cuda")
+    xm = buf[1:].view(rows, cols)
+    xm.copy_(xh.cuda())
+    ym = mbp.unfused_softmax(xm)
+    assert torch.equal(ym.view(torch.int16 if fmt == "bf16" else torch.int32),
+                       y.view(torch.int16 if fmt == "bf16" else torch.int32)), f"{what}: misaligned differs"
 
 
 # ------------------------------------------------------------------ misc
