@@ -778,12 +778,27 @@ def test_unfused_softmax(mbp, fmt, dtype, rows, cols):
 # ------------------------------------------------------------------ misc
 
 def test_empty_inputs(mbp):
+    """rows == 0 (n == 0) is a no-op for every entry point, fused and unfused."""
     e = torch.empty(0, device="cuda")
     assert mbp.fused_pointwise_chain(e, e, e).numel() == 0
+    assert mbp.unfused_pointwise_chain(e, e, e).numel() == 0
+    assert mbp.convert_f32_to_bf16(e).numel() == 0
     x = torch.empty(0, 64, device="cuda")
     v = torch.zeros(64, device="cuda")
-    assert mbp.fused_row_mean_epilogue(x, v, v, v).numel() == 0
+    for f in (mbp.fused_row_mean_epilogue, mbp.unfused_row_mean_epilogue, mbp.grouped_row_mean_epilogue):
+        assert f(x, v, v, v).numel() == 0
     assert mbp.fused_add_layernorm_gelu(x, None, v, v).numel() == 0
+    assert mbp.unfused_add_layernorm_gelu(x, None, v, v).numel() == 0
+    assert mbp.fused_layernorm_relu_dropout(x, v, v).numel() == 0
+    assert mbp.unfused_layernorm_relu_dropout(x, v, v).numel() == 0
+    for dt in (torch.float32, torch.bfloat16, torch.float16):
+        xd = torch.empty(0, 64, dtype=dt, device="cuda")
+        vd = torch.zeros(64, dtype=dt, device="cuda")
+        assert mbp.fused_softmax(xd).numel() == 0
+        assert mbp.fused_pointwise_chain_2d(xd, vd, vd).numel() == 0
+        assert mbp.fused_row_mean_epilogue_2d(xd, vd, vd, vd).numel() == 0
+    assert mbp.unfused_softmax(torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")).numel() == 0
+    torch.cuda.synchronize()
 
 
 def test_bf16_store_conversion_exhaustive(mbp):
