@@ -351,19 +351,23 @@ __device__ __forceinline__ u32x4 funnel(const u32x4& lo, const uint32_t* hi, int
 
 // Rows off 16-byte boundaries whose x, residual and y share one alignment
 // (the usual case: e.g. bf16 rows of 4095 elements in freshly allocated
-// tensors).  The byte offset of row r in its first 16-byte window is then
-// (base + r * row_bytes) mod 16, which repeats with period P = 16 / gcd(16,
-// row_bytes) rows; the rows with one offset form a class.  A block serves
-// one class, so the offset s (in elements) is uniform over the block, and the
-// row is processed directly in window space: slot j of the ln_vec_kernel
-// layout holds window j of the row, element e of it being column
-// V*j + e - s.  gamma and beta are gathered once per block into that layout.
+// tensors).  The byte offset of row r in its line, (base + r * row_bytes) mod
+// line, with line = 128 bytes when the three tensors agree modulo 128 (else
+// 16), repeats with period P = line / gcd(line, row_bytes) rows; the rows with
+// one offset form a class.  A block serves one class, so the offset is
+// uniform over the block: d whole windows and s elements past the line.  The
+// row is processed directly in window space: relative slot j holds window j of
+// the row, element e of it being column V*j + e - s, and relative slot j sits
+// at slot (j + d) mod nvec of the ln_vec_kernel layout, so every load and
+// store instruction covers whole 128-byte lines (runs that straddle lines cost
+// 10% of the bandwidth).  gamma and beta are gathered once per block into that
+// layout.
 //
 // A row spans nvec = ceil(cols / V) windows, or one more when its offset
 // pushes its tail into window nvec.  In that case the tail (fewer than s
 // elements) is moved into the unused head of slot 0 (whose first s elements
 // belong to the previous row), so VPL is the same as for aligned rows.  Only
-// slot 0 and slot nvec - 1 hold elements outside the row: they are zeroed in
+// relative slots 0 and nvec - 1 hold elements outside the row: they are zeroed in
 // the packed inputs, their (0 - mean)^2 terms are taken out of the variance
 // sum again, and their windows (and the folded one) are stored element by
 // element.
@@ -372,11 +376,19 @@ __device__ __forceinline__ u32x4 funnel(const u32x4& lo, const uint32_t* hi, int
 // tensors; the rest (at most the first and last few rows: rows starting
 // within 16 bytes of a tensor's unaligned start or end) take the last
 // `edge_blocks` blocks of the grid, which handle them element by element.
+// Layouts whose gamma / beta fit in 32 KB of LDS park them there, which
+// leaves the 16-bit row loop within 128 registers: four waves per SIMD (the
+// binary64 fp32 loop would spill at that bound).
+constexpr bool class_lds_gb(int lanes, int vpl) { return block_for(lanes) * vpl * 32 <= 32768; }
+constexpr int class_min_waves(int lanes, int vpl, int es) {
+  return es == 2 && class_lds_gb(lanes, vpl) ? 4 : 1;
+}
+
 template <class IO, int LANES, int VPL, bool RES, int EPI>
-__global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
+__global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_eu(class_min_waves(LANES, VPL, (int)sizeof(typename IO::elem))))) void ln_class_kernel(
     const typename IO::elem* x, const typename IO::elem* res,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
-    typename IO::elem* y, int64_t rows, int cols, double eps_d, int period, int64_t r_lo,
+    typename IO::elem* y, int64_t rows, int cols, double eps_d, int period, int line, int64_t r_lo,
     int64_t r_hi, int edge_blocks) {
   typedef typename IO::elem E;
   typedef typename Types<IO, RES>::acc Acc;
@@ -386,6 +398,7 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
   constexpr int BLOCK = block_for(LANES);
   constexpr int RPB = BLOCK / LANES;
   constexpr bool kInPlace = std::is_same<Acc, Val>::value;
+  constexpr bool kLdsGB = class_lds_gb(LANES, VPL);
   __shared__ Acc red[2][BLOCK / 64];
 
   const int lane = threadIdx.x % LANES;
@@ -438,9 +451,22 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
   const int64_t last_row = first + ((crows - 1) << lp);
 
   const int mb = (int)(reinterpret_cast<uintptr_t>(x) & 15);
-  const int sb = (int)((mb + (int64_t)ES * first * cols) & 15);  // the class's byte offset
+  // the class's byte offset in its line (line = 128 or 16 bytes): window
+  // offset d, byte offset sb in that window
+  const int sl = (int)((reinterpret_cast<uintptr_t>(x) + (uint64_t)((int64_t)ES * first * cols)) & (unsigned)(line - 1));
+  const int d = sl >> 4;
+  const int sb = sl & 15;
   const int s = sb / ES;
   const int nvec = (cols + V - 1) / V;
+  // Slot p = lane + k*LANES holds window rel(p) = (p - d) mod nvec of the
+  // row, so the run of slots a load or store instruction covers starts on a
+  // line: relative slot 0 sits at slot d and the last d windows wrap round to
+  // slots 0 .. d-1 (the host ensures d < min(nvec, LANES)).  Slots p >= nvec
+  // are unused and clamped.
+  auto rel = [&](int k) -> int {
+    const int p = min(lane + k * LANES, nvec - 1);
+    return p < d ? p - d + nvec : p - d;
+  };
   const int nv = (sb + ES * cols + 15) >> 4;
   const bool fold = nv > nvec;
   const int klast = (nvec - 1) / LANES;
@@ -489,7 +515,7 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
     const int q = ((16 - sb) & 15) >> 2, bb = (16 - sb) & 3;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int jc = min(lane + k * LANES, nvec - 1);
+      const int jc = rel(k);
       const int jp = jc == 0 ? nvec - 1 : jc - 1;
       u32x4 ga = pg, gb = pg, ba = pb, bv = pb;
       if (jfull >= 0) {
@@ -517,14 +543,14 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
     // element gather; clamped unconditional loads, so they issue together
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int j = lane + k * LANES;
+      const int j = rel(k);
       u32x4 gv = {{0u, 0u, 0u, 0u}}, bv = {{0u, 0u, 0u, 0u}};
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const int c = col_of(j, e);
         const int cc = min(max(c, 0), cols - 1);
         const E ge = gamma[cc], be = beta[cc];
-        if (j < nvec && c >= 0 && c < cols) {
+        if (c >= 0 && c < cols) {
           set_elem<IO>(gv, e, ge);
           set_elem<IO>(bv, e, be);
         }
@@ -534,11 +560,31 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
     }
   }
 
-  for (int64_t grp = blk; grp < cgroups; grp += nblk) {
+  int jr[VPL];
+  bool used[VPL];
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    jr[k] = rel(k);
+    used[k] = lane + k * LANES < nvec;
+  }
+  // gamma / beta of this lane's slots parked in LDS (each lane reads back
+  // only what it wrote, so no barrier): 32 fewer registers in the row loop
+  __shared__ u32x4 lg[kLdsGB ? BLOCK * VPL : 1], lb[kLdsGB ? BLOCK * VPL : 1];
+  if constexpr (kLdsGB) {
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      opaque(gp[k]);
-      opaque(bp[k]);
+      lg[k * BLOCK + threadIdx.x] = gp[k];
+      lb[k * BLOCK + threadIdx.x] = bp[k];
+    }
+  }
+
+  for (int64_t grp = blk; grp < cgroups; grp += nblk) {
+    if constexpr (!kLdsGB) {
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) {
+        opaque(gp[k]);
+        opaque(bp[k]);
+      }
     }
     const int64_t row = first + (int64_t)period * (grp * RPB + sub);
     const bool live = row <= last_row;
@@ -552,11 +598,10 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
     u32x4 xw[VPL], rw[VPL];
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int j = min(lane + k * LANES, nvec - 1);
-      xw[k] = load_nt(sx + j);
-      if constexpr (RES) rw[k] = load_nt(sr + j);
+      xw[k] = load_nt(sx + jr[k]);
+      if constexpr (RES) rw[k] = load_nt(sr + jr[k]);
     }
-    if (fold && lane == 0) {  // slot 0 takes the row's last window into its bytes [0, sb)
+    if (fold && lane == d) {  // relative slot 0 takes the row's last window into its bytes [0, sb)
       int sbv = sb;
       opaque(sbv);
       const u32x4 xf = load_nt(sx + nvec);
@@ -573,8 +618,8 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
     // zero the elements outside the row (slot 0 and slot nvec - 1 only)
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      if (k != 0 && k != klast) continue;
-      const int j = lane + k * LANES;
+      if (k != 0 && k != klast) continue;  // relative slots 0 and nvec - 1 sit in these rounds
+      const int j = jr[k];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const uint32_t m = (j == 0 ? mk0[t] : 0xffffffffu) & (j == nvec - 1 ? mkl[t] : 0xffffffffu);
@@ -587,7 +632,6 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
     Acc sum = 0;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int j = lane + k * LANES;
       Acc part = 0;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
@@ -596,20 +640,20 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
         v[k][e] = t;
         part += (Acc)t;
       }
-      if (j < nvec) sum += part;
+      if (used[k]) sum += part;
     }
     const Acc mean = group_sum<LANES, BLOCK>(sum, red[0]) / (Acc)cols;
 
     Acc m2 = 0;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int j = lane + k * LANES;
+      const int j = jr[k];
       Acc part = 0;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        const Acc d = (Acc)v[k][e] - mean;
-        if constexpr (kInPlace) v[k][e] = d;
-        part = fma_t(d, d, part);
+        const Acc dv = (Acc)v[k][e] - mean;
+        if constexpr (kInPlace) v[k][e] = dv;
+        part = fma_t(dv, dv, part);
       }
       if (k == 0 || k == klast) {
         // a zeroed element contributed (0 - mean)^2 to this slot's
@@ -617,7 +661,7 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
         const int nout = (j == 0 ? n0 : 0) + (j == nvec - 1 && j != 0 ? nl : 0);
         part -= (Acc)nout * (mean * mean);
       }
-      if (j < nvec) m2 += part;
+      if (used[k]) m2 += part;
     }
     const Acc rstd = inv_sqrt(group_sum<LANES, BLOCK>(m2, red[1]) / (Acc)cols + eps);
 
@@ -626,13 +670,15 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_class_kernel(
     E* yrow = y + row * (int64_t)cols;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const int j = lane + k * LANES;
-      if (j >= nvec) continue;
+      const int j = jr[k];
+      if (!used[k]) continue;
       float o[V];
+      const u32x4 gk = kLdsGB ? lg[k * BLOCK + threadIdx.x] : gp[k];
+      const u32x4 bk = kLdsGB ? lb[k * BLOCK + threadIdx.x] : bp[k];
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        const Acc d = kInPlace ? (Acc)v[k][e] : (Acc)v[k][e] - mean;
-        o[e] = finish<Acc, EPI>(d, rstd, (Acc)IO::get(gp[k], e), (Acc)IO::get(bp[k], e));
+        const Acc dv = kInPlace ? (Acc)v[k][e] : (Acc)v[k][e] - mean;
+        o[e] = finish<Acc, EPI>(dv, rstd, (Acc)IO::get(gk, e), (Acc)IO::get(bk, e));
       }
       const u32x4 ov = pack_vec<IO>(o);
       // window j holds columns V*j - s + e; slot 0 and slot nvec - 1 may
@@ -1034,15 +1080,25 @@ hipError_t launch_flags(const void* x, const void* res, const void* gamma, const
     if (r_hi < r_lo) r_hi = r_lo;
     const int64_t n_edge = r_lo + (rows - r_hi);
     const int edge_blocks = (int)((n_edge + rpb - 1) / rpb);
-    // P classes of rows with one offset; each block takes up to kClassGroups
-    // row groups of its class.
-    int period = 16;
-    while (period > 1 && (rb * (period / 2)) % 16 == 0) period /= 2;
+    // Classes are taken modulo a 128-byte line when x, residual and y agree
+    // modulo 128 and a row spans at least a wave of windows: the kernel then
+    // starts every wave's loads and stores on a line (a 4095-wide bf16 row
+    // stream measured 150 us with runs straddling lines, 136 us with runs on
+    // lines, 136 us for 4096-wide rows).  Otherwise modulo 16 bytes.
+    const int nvec = (int)((cols + V - 1) / V);
+    const bool same_line = ((ax ^ reinterpret_cast<uintptr_t>(y)) & 127) == 0 &&
+                           (!res || ((ax ^ reinterpret_cast<uintptr_t>(res)) & 127) == 0);
+    int line = same_line && nvec >= 64 ? 128 : 16;
+    // P classes of rows with one offset in the line; each block takes up to
+    // kClassGroups row groups of its class.
+    int period = line;
+    while (period > 1 && (rb * (period / 2)) % line == 0) period /= 2;
     const int64_t cgroups = ((r_hi - r_lo + period - 1) / period + rpb - 1) / rpb;
     int64_t nblk = (cgroups + kClassGroups - 1) / kClassGroups;
-    if (nblk > kMaxGrid / 16) nblk = kMaxGrid / 16;
+    if (nblk > kMaxGrid / 128) nblk = kMaxGrid / 128;
     const void* k = shape_kernel<ClassSel<IO, RES, (EPI == kEpiReluDrop ? kEpiNone : EPI)>::template K>(i);
-    void* cargs[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &eps, &period, &r_lo, &r_hi, (void*)&edge_blocks};
+    void* cargs[] = {&x,      &res,   &gamma, &beta, &y,    &rows,
+                     &icols,  &eps,   &period, &line, &r_lo, &r_hi, (void*)&edge_blocks};
     return hipLaunchKernel(k, dim3((unsigned)(edge_blocks + period * nblk)), dim3(block), cargs, 0, s);
   }
   // kShiftGroups row groups per block amortise the per-block gamma/beta set-up
