@@ -360,15 +360,15 @@ __device__ __forceinline__ u32x4 funnel(const u32x4& lo, const uint32_t* hi, int
 // the row, element e of it being column V*j + e - s, and relative slot j sits
 // at slot (j + d) mod nvec of the ln_vec_kernel layout, so every load and
 // store instruction covers whole 128-byte lines (runs that straddle lines cost
-// 10% of the bandwidth).  gamma and beta are gathered once per block into that
-// layout.
+// 10% of the bandwidth).  gamma and beta are laid out once per block to
+// match (an LDS ring for layouts up to 2048 slots, registers beyond).
 //
 // A row spans nvec = ceil(cols / V) windows, or one more when its offset
 // pushes its tail into window nvec.  In that case the tail (fewer than s
-// elements) is moved into the unused head of slot 0 (whose first s elements
-// belong to the previous row), so VPL is the same as for aligned rows.  Only
-// relative slots 0 and nvec - 1 hold elements outside the row: they are zeroed in
-// the packed inputs, their (0 - mean)^2 terms are taken out of the variance
+// elements) is moved into the unused head of relative slot 0 (whose first s
+// elements belong to the previous row), so VPL is the same as for aligned
+// rows.  Only relative slots 0 and nvec - 1 hold elements outside the row:
+// they are zeroed in the packed inputs, their (0 - mean)^2 terms are taken out of the variance
 // sum again, and their windows (and the folded one) are stored element by
 // element.
 //
@@ -376,12 +376,12 @@ __device__ __forceinline__ u32x4 funnel(const u32x4& lo, const uint32_t* hi, int
 // tensors; the rest (at most the first and last few rows: rows starting
 // within 16 bytes of a tensor's unaligned start or end) take the last
 // `edge_blocks` blocks of the grid, which handle them element by element.
-// Layouts whose gamma / beta fit in 32 KB of LDS park them there, which
-// leaves the 16-bit row loop within 128 registers: four waves per SIMD (the
-// binary64 fp32 loop would spill at that bound).
-constexpr bool class_lds_gb(int lanes, int vpl) { return block_for(lanes) * vpl * 32 <= 32768; }
+// Layouts of up to 2048 slots keep gamma / beta in LDS (at most 64 KB per
+// block), which leaves the 16-bit row loop of up to 4 vectors per lane within
+// 128 registers: four waves per SIMD.
+constexpr bool class_raw_gb(int lanes, int vpl) { return lanes * vpl <= 2048; }
 constexpr int class_min_waves(int lanes, int vpl, int es) {
-  return es == 2 && class_lds_gb(lanes, vpl) ? 4 : 1;
+  return es == 2 && vpl <= 4 && class_raw_gb(lanes, vpl) ? 4 : 1;
 }
 
 template <class IO, int LANES, int VPL, bool RES, int EPI>
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
   constexpr int BLOCK = block_for(LANES);
   constexpr int RPB = BLOCK / LANES;
   constexpr bool kInPlace = std::is_same<Acc, Val>::value;
-  constexpr bool kLdsGB = class_lds_gb(LANES, VPL);
+  constexpr bool kRaw = class_raw_gb(LANES, VPL);
   __shared__ Acc red[2][BLOCK / 64];
 
   const int lane = threadIdx.x % LANES;
@@ -497,14 +497,59 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
     }
   }
 
-  // gamma / beta in the class's window layout: slot j holds columns
+  // gamma / beta in the class's window layout: relative slot j holds columns
   // V*j - s + e, i.e. bytes [16 - sb, 32 - sb) of vectors j-1 || j; slot 0
   // takes vector nvec - 1 as its "j-1", which yields exactly the folded tail
-  // columns V*nvec - s + e, e < s.  Whole vectors are loaded with clamped
-  // indices; a partial last vector is read once element by element (zero
-  // past the end, no byte past gamma or beta) and selected where needed.
-  u32x4 gp[VPL], bp[VPL];
-  if (((reinterpret_cast<uintptr_t>(gamma) | reinterpret_cast<uintptr_t>(beta)) & 15) == 0) {
+  // columns V*nvec - s + e, e < s.  A partial last vector is read element by
+  // element (zero past the end, no byte past gamma or beta).
+  //
+  // Layouts of up to 2048 slots (kRaw) write gamma and beta into an LDS ring
+  // of nvec vectors, column c at element (c + s) mod V*nvec, so that relative
+  // slot j reads its vector at ring vector j, aligned (the V*nvec - cols gap
+  // elements are zero).  The set-up is one coalesced pass and a barrier,
+  // shared by the block's row groups.  Wider layouts funnel once per block
+  // into registers.
+  const bool gb_aligned = ((reinterpret_cast<uintptr_t>(gamma) | reinterpret_cast<uintptr_t>(beta)) & 15) == 0;
+  __shared__ u32x4 ringg[kRaw ? LANES * VPL : 1], ringb[kRaw ? LANES * VPL : 1];
+  u32x4 gp[kRaw ? 1 : VPL], bp[kRaw ? 1 : VPL];
+  if constexpr (kRaw) {
+    E* rg = reinterpret_cast<E*>(ringg);
+    E* rb = reinterpret_cast<E*>(ringb);
+    const int ring = V * nvec;
+    if ((int)threadIdx.x < ring - cols) {
+      const int pos = (cols + s + (int)threadIdx.x) % ring;
+      rg[pos] = (E)0;
+      rb[pos] = (E)0;
+    }
+    constexpr int kIt = (LANES * VPL + BLOCK - 1) / BLOCK;
+    u32x4 tg[kIt], tb[kIt];
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int v = min((int)threadIdx.x + i * BLOCK, nvec - 1);
+      if (gb_aligned && V * (v + 1) <= cols) {
+        tg[i] = load_vec<IO>(gamma, v);
+        tb[i] = load_vec<IO>(beta, v);
+      } else {
+        tg[i] = partial_vec<IO>(gamma, V * v, cols);
+        tb[i] = partial_vec<IO>(beta, V * v, cols);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int v = (int)threadIdx.x + i * BLOCK;
+      if (v >= nvec) continue;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const int c = V * v + e;
+        if (c >= cols) continue;
+        const int pos = c + s < ring ? c + s : c + s - ring;
+        rg[pos] = elem_bits<IO>(tg[i], e);
+        rb[pos] = elem_bits<IO>(tb[i], e);
+      }
+    }
+    lds_barrier();
+  } else if (gb_aligned) {
+    const int q = ((16 - sb) & 15) >> 2, bb = (16 - sb) & 3;
     const bool partial = (cols % V) != 0;
     const int jfull = partial ? nvec - 2 : nvec - 1;  // last whole vector (-1: none)
     u32x4 pg = {{0u, 0u, 0u, 0u}}, pb = {{0u, 0u, 0u, 0u}};
@@ -512,7 +557,6 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
       pg = partial_vec<IO>(gamma, V * (nvec - 1), cols);
       pb = partial_vec<IO>(beta, V * (nvec - 1), cols);
     }
-    const int q = ((16 - sb) & 15) >> 2, bb = (16 - sb) & 3;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       const int jc = rel(k);
@@ -567,19 +611,9 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
     jr[k] = rel(k);
     used[k] = lane + k * LANES < nvec;
   }
-  // gamma / beta of this lane's slots parked in LDS (each lane reads back
-  // only what it wrote, so no barrier): 32 fewer registers in the row loop
-  __shared__ u32x4 lg[kLdsGB ? BLOCK * VPL : 1], lb[kLdsGB ? BLOCK * VPL : 1];
-  if constexpr (kLdsGB) {
-#pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-      lg[k * BLOCK + threadIdx.x] = gp[k];
-      lb[k * BLOCK + threadIdx.x] = bp[k];
-    }
-  }
 
   for (int64_t grp = blk; grp < cgroups; grp += nblk) {
-    if constexpr (!kLdsGB) {
+    if constexpr (!kRaw) {
 #pragma unroll
       for (int k = 0; k < VPL; ++k) {
         opaque(gp[k]);
@@ -673,8 +707,14 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
       const int j = jr[k];
       if (!used[k]) continue;
       float o[V];
-      const u32x4 gk = kLdsGB ? lg[k * BLOCK + threadIdx.x] : gp[k];
-      const u32x4 bk = kLdsGB ? lb[k * BLOCK + threadIdx.x] : bp[k];
+      u32x4 gk, bk;
+      if constexpr (kRaw) {
+        gk = ringg[j];
+        bk = ringb[j];
+      } else {
+        gk = gp[k];
+        bk = bp[k];
+      }
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const Acc dv = kInPlace ? (Acc)v[k][e] : (Acc)v[k][e] - mean;
