@@ -503,55 +503,55 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
   // columns V*nvec - s + e, e < s.  A partial last vector is read element by
   // element (zero past the end, no byte past gamma or beta).
   //
-  // Layouts of up to 2048 slots (kRaw) write gamma and beta into an LDS ring
-  // of nvec vectors, column c at element (c + s) mod V*nvec, so that relative
-  // slot j reads its vector at ring vector j, aligned (the V*nvec - cols gap
-  // elements are zero).  The set-up is one coalesced pass and a barrier,
-  // shared by the block's row groups.  Wider layouts funnel once per block
-  // into registers.
+  // Layouts of up to 2048 slots (kRaw) keep gamma and beta in an LDS ring of
+  // nvec vectors: ring vector j is relative slot j's vector, funnelled from
+  // vectors j-1 and j, so each slot reads its gamma / beta aligned in the row
+  // loop.  One thread builds each ring vector (consecutive lanes, consecutive
+  // 16 bytes: no bank conflicts), then one barrier.  Wider layouts funnel
+  // once per block into registers.
   const bool gb_aligned = ((reinterpret_cast<uintptr_t>(gamma) | reinterpret_cast<uintptr_t>(beta)) & 15) == 0;
+  const bool partial = (cols % V) != 0;
+  const int jfull = partial ? nvec - 2 : nvec - 1;  // last whole vector (-1: none)
+  const int q = ((16 - sb) & 15) >> 2, bb = (16 - sb) & 3;
   __shared__ u32x4 ringg[kRaw ? LANES * VPL : 1], ringb[kRaw ? LANES * VPL : 1];
   u32x4 gp[kRaw ? 1 : VPL], bp[kRaw ? 1 : VPL];
   if constexpr (kRaw) {
-    E* rg = reinterpret_cast<E*>(ringg);
-    E* rb = reinterpret_cast<E*>(ringb);
-    const int ring = V * nvec;
-    if ((int)threadIdx.x < ring - cols) {
-      const int pos = (cols + s + (int)threadIdx.x) % ring;
-      rg[pos] = (E)0;
-      rb[pos] = (E)0;
-    }
     constexpr int kIt = (LANES * VPL + BLOCK - 1) / BLOCK;
+    auto fetch = [&](int vi, u32x4& g, u32x4& b) {
+      if (gb_aligned && vi <= jfull) {
+        g = load_vec<IO>(gamma, vi);
+        b = load_vec<IO>(beta, vi);
+      } else {  // the partial last vector, or gamma / beta off 16-byte boundaries
+        g = partial_vec<IO>(gamma, V * vi, cols);
+        b = partial_vec<IO>(beta, V * vi, cols);
+      }
+    };
     u32x4 tg[kIt], tb[kIt];
 #pragma unroll
     for (int i = 0; i < kIt; ++i) {
-      const int v = min((int)threadIdx.x + i * BLOCK, nvec - 1);
-      if (gb_aligned && V * (v + 1) <= cols) {
-        tg[i] = load_vec<IO>(gamma, v);
-        tb[i] = load_vec<IO>(beta, v);
-      } else {
-        tg[i] = partial_vec<IO>(gamma, V * v, cols);
-        tb[i] = partial_vec<IO>(beta, V * v, cols);
+      const int jc = min((int)threadIdx.x + i * BLOCK, nvec - 1);
+      const int jp = jc == 0 ? nvec - 1 : jc - 1;
+      u32x4 gc, bc, ga = {{0u, 0u, 0u, 0u}}, ba = {{0u, 0u, 0u, 0u}};
+      fetch(jc, gc, bc);
+      if (sb != 0) fetch(jp, ga, ba);
+      switch (sb == 0 ? -1 : q) {
+        case -1: tg[i] = gc; tb[i] = bc; break;
+        case 0: tg[i] = funnel<ES, 0>(ga, gc.w, bb); tb[i] = funnel<ES, 0>(ba, bc.w, bb); break;
+        case 1: tg[i] = funnel<ES, 1>(ga, gc.w, bb); tb[i] = funnel<ES, 1>(ba, bc.w, bb); break;
+        case 2: tg[i] = funnel<ES, 2>(ga, gc.w, bb); tb[i] = funnel<ES, 2>(ba, bc.w, bb); break;
+        default: tg[i] = funnel<ES, 3>(ga, gc.w, bb); tb[i] = funnel<ES, 3>(ba, bc.w, bb); break;
       }
     }
 #pragma unroll
     for (int i = 0; i < kIt; ++i) {
       const int v = (int)threadIdx.x + i * BLOCK;
-      if (v >= nvec) continue;
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        const int c = V * v + e;
-        if (c >= cols) continue;
-        const int pos = c + s < ring ? c + s : c + s - ring;
-        rg[pos] = elem_bits<IO>(tg[i], e);
-        rb[pos] = elem_bits<IO>(tb[i], e);
+      if (v < nvec) {
+        ringg[v] = tg[i];
+        ringb[v] = tb[i];
       }
     }
     lds_barrier();
   } else if (gb_aligned) {
-    const int q = ((16 - sb) & 15) >> 2, bb = (16 - sb) & 3;
-    const bool partial = (cols % V) != 0;
-    const int jfull = partial ? nvec - 2 : nvec - 1;  // last whole vector (-1: none)
     u32x4 pg = {{0u, 0u, 0u, 0u}}, pb = {{0u, 0u, 0u, 0u}};
     if (partial) {
       pg = partial_vec<IO>(gamma, V * (nvec - 1), cols);

@@ -268,23 +268,28 @@ def test_ln_independent_misalignment(mbp, dtype_name, cols, offs, rows):
 
 
 
-@pytest.mark.parametrize("cols,rows", [(4095, 130), (768 + 1, 70), (1023, 33), (12290, 9)])
-@pytest.mark.parametrize("bytes_off", [(2, 2, 2), (18, 18, 18), (126, 126, 126), (64, 64, 64),
-                                       (2, 18, 2), (6, 6, 118)])
-def test_ln_line_classes(mbp, cols, rows, bytes_off):
-    """bf16 rows off 16-byte boundaries, x, residual and y starting
-    `bytes_off` bytes past a 128-byte line.  Equal offsets take the per-class
-    window path with classes modulo a line (every window offset in the line
-    appears among the rows); offsets equal only modulo 16 take it with classes
-    modulo 16 bytes."""
-    w, d, act = _ln_case("addln_gelu_16384x8192_bf16", rows, cols, residual=True)
+@pytest.mark.parametrize("name,cols,rows", [
+    ("addln_gelu_16384x8192_bf16", 4095, 130), ("addln_gelu_16384x8192_bf16", 768 + 1, 70),
+    ("addln_gelu_16384x8192_bf16", 1023, 33), ("addln_gelu_16384x8192_bf16", 12290, 9),
+    ("ln_8192x4096_f32", 4093, 70), ("ln_8192x4096_f32", 1021, 40)])
+@pytest.mark.parametrize("bytes_off", [(4, 4, 4), (20, 20, 20), (124, 124, 124), (64, 64, 64),
+                                       (4, 20, 4), (12, 12, 124)])
+def test_ln_line_classes(mbp, name, cols, rows, bytes_off):
+    """Rows off 16-byte boundaries, x, residual and y starting `bytes_off`
+    bytes past a 128-byte line.  Equal offsets take the per-class window path
+    with classes modulo a line (the rows cover every class, so every window
+    offset in the line and every ring shift of gamma / beta appears); offsets
+    equal only modulo 16 take it with classes modulo 16 bytes."""
+    w, d, act = _ln_case(name, rows, cols, residual=True)
     ref = _ln_ref(d, act)
+    chk = check_bf16 if w.dtype == "bf16" else check_f32
+    es = 2 if w.dtype == "bf16" else 4
 
     def place(a, off_b, fill=0.0):
         t = to_dev(a)
         buf = torch.full((t.numel() + 128,), fill, dtype=t.dtype, device="cuda")
         assert buf.data_ptr() % 128 == 0
-        v = buf[off_b // 2:off_b // 2 + t.numel()].view(t.shape)
+        v = buf[off_b // es:off_b // es + t.numel()].view(t.shape)
         v.copy_(t)
         return v, buf
 
@@ -292,9 +297,9 @@ def test_ln_line_classes(mbp, cols, rows, bytes_off):
     r, _ = place(d["residual"], bytes_off[1])
     y, yb = place(np.zeros_like(d["x"]), bytes_off[2], fill=3.0)
     mbp.fused_add_layernorm_gelu(x, r, to_dev(d["gamma"]), to_dev(d["beta"]), act=act, out=y)
-    check_bf16(to_host(y), ref, f"{rows}x{cols} byte offsets {bytes_off}")
-    host = as_f64(to_host(yb))
-    o = bytes_off[2] // 2
+    chk(to_host(y), ref, f"{name} {rows}x{cols} byte offsets {bytes_off}")
+    host = to_host(yb).astype(np.float64) if yb.dtype != torch.bfloat16 else as_f64(to_host(yb))
+    o = bytes_off[2] // es
     assert (host[:o] == 3.0).all() and (host[o + x.numel():] == 3.0).all(), "wrote outside y"
 
 def test_ln_constant_rows_give_beta(mbp):
