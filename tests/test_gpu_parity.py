@@ -686,6 +686,52 @@ def test_softmax_masks_in_place_and_misaligned(mbp, fmt, dtype):
     _softmax_gate(y2[torch.from_numpy(ok).cuda()], exact[ok], fmt, f"softmax misaligned {fmt}")
 
 
+
+@pytest.mark.parametrize("fmt,dtype", DT2D, ids=[d[0] for d in DT2D])
+@pytest.mark.parametrize("cols,rows", [(4095, 70), (4088, 20), (1000, 40), (769, 70), (33, 90), (16383, 5)])
+@pytest.mark.parametrize("offs", [(0, 0), (4, 4), (20, 20), (124, 124), (4, 20), (12, 124), (0, 16)])
+def test_softmax_windows(mbp, fmt, dtype, cols, rows, offs):
+    """x and y starting offs[0] and offs[1] bytes past a 128-byte line.  Equal
+    offsets modulo 16 take the windowed path (rows off 16-byte boundaries, or
+    on them but not on lines), rotated onto lines when the offsets agree
+    modulo 128, with the rows at an unaligned start or end done element by
+    element; masked (-inf) entries fall in the shared and folded windows too."""
+    es = torch.empty(0, dtype=dtype).element_size()
+    if offs[0] % es or offs[1] % es:
+        pytest.skip("offset not a whole element")
+    rng = np.random.default_rng([23, cols, rows, offs[0], offs[1]])
+    xh, _ = _stored(rng, (rows, cols), dtype, 4.0)
+    mask = rng.random((rows, cols)) < 0.05
+    mask[:, 0] = mask[:, -1] = True    # the first and last column of every row
+    mask[1, :] = True                  # a fully masked row: NaN
+    xh[torch.from_numpy(mask)] = float("-inf")
+    xf = xh.float().numpy()
+    exact = oracle.softmax(xf)
+
+    def place(t, off_b, fill):
+        buf = torch.full((t.numel() + 256 // es,), fill, dtype=dtype, device="cuda")
+        assert buf.data_ptr() % 128 == 0
+        v = buf[off_b // es:off_b // es + t.numel()].view(t.shape)
+        v.copy_(t)
+        return v, buf
+
+    x, _ = place(xh.cuda(), offs[0], 0.0)
+    y, yb = place(torch.zeros_like(xh).cuda(), offs[1], 3.0)
+    mbp.fused_softmax(x, out=y)
+    yh = y.float().cpu().numpy()
+    assert np.isnan(yh[1]).all(), "a fully masked row must be NaN"
+    ok = np.ones(rows, bool)
+    ok[1] = False
+    assert (yh[ok][mask[ok]] == 0).all(), "masked entries must be exactly 0"
+    _softmax_gate(y[torch.from_numpy(ok).cuda()], exact[ok], fmt, f"softmax {fmt} {rows}x{cols} offsets {offs}")
+    host = yb.float().cpu().numpy()
+    o = offs[1] // es
+    assert (host[:o] == 3.0).all() and (host[o + x.numel():] == 3.0).all(), "wrote outside y"
+    if offs[0] == offs[1]:  # in place: a shared window may already hold a neighbour's outputs, in elements the row masks
+        mbp.fused_softmax(x, out=x)
+        iv = torch.int32 if es == 4 else torch.int16
+        assert torch.equal(x.view(iv), y.view(iv)), "in place differs"
+
 # ------------------------------------------------------------------ unfused variants
 
 def test_unfused_chain_bit_exact(mbp):
