@@ -70,8 +70,10 @@ def test_layernorm_bf16_past_2_31(mbp, cols):
     check_bf16(to_host(y[ti]), ref, f"residual+LN+GeLU {rows}x{cols} bf16, rows around element 2^31")
 
 
-def test_softmax_bf16_past_2_31(mbp):
-    rows, cols = BIG // 4096 + 3, 4096
+@pytest.mark.parametrize("cols", [4096, 4095])
+def test_softmax_bf16_past_2_31(mbp, cols):
+    """4096: 16-byte accesses; 4095: the windowed path (rows off 16-byte boundaries)"""
+    rows = BIG // cols + 3
     x = _randn((rows, cols), torch.bfloat16, 21, std=3.0)
     y = mbp.fused_softmax(x)
     rs = _rows_around(rows, cols)
