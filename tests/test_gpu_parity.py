@@ -603,6 +603,37 @@ def test_ln_relu_dropout(mbp, name, cols, p):
     assert torch.equal(y, y2), "not deterministic"
 
 
+
+@pytest.mark.parametrize("name", ["ln_8192x4096_f32", "addln_gelu_16384x8192_bf16"])
+@pytest.mark.parametrize("cols,rows", [(4095, 70), (1001, 40), (7, 50)])
+@pytest.mark.parametrize("off_b", [0, 4, 20, 124])
+def test_ln_relu_dropout_windows(mbp, name, cols, rows, off_b):
+    """x and y both `off_b` bytes past a 128-byte line, rows off 16-byte
+    boundaries: the relu + dropout epilogue on vectors that straddle two
+    generator blocks, the rows at an unaligned start, and in place."""
+    w, d = _drop_case(name, rows, cols)
+    es = 4 if w.dtype == "f32" else 2
+    seed, offset, p = 0x0123456789ABCDEF, 5, 0.25
+
+    def place(t, fill):
+        buf = torch.full((t.numel() + 256 // es,), fill, dtype=t.dtype, device="cuda")
+        assert buf.data_ptr() % 128 == 0
+        v = buf[off_b // es:off_b // es + t.numel()].view(t.shape)
+        v.copy_(t)
+        return v, buf
+
+    x, _ = place(to_dev(d["x"]), 0.0)
+    y, yb = place(torch.zeros_like(to_dev(d["x"])), 3.0)
+    g, b = to_dev(d["gamma"]), to_dev(d["beta"])
+    mbp.fused_layernorm_relu_dropout(x, g, b, p=p, seed=seed, offset=offset, out=y)
+    _check_dropout(y, d, w, p, seed, offset, f"ln-relu-dropout {w.dtype} {rows}x{cols} at +{off_b} bytes")
+    host = yb.float().cpu().numpy()
+    o = off_b // es
+    assert (host[:o] == 3.0).all() and (host[o + x.numel():] == 3.0).all(), "wrote outside y"
+    mbp.fused_layernorm_relu_dropout(x, g, b, p=p, seed=seed, offset=offset, out=x)
+    iv = torch.int32 if es == 4 else torch.int16
+    assert torch.equal(x.view(iv), y.view(iv)), "in place differs"
+
 def test_ln_relu_dropout_in_place_offset_misaligned_unfused(mbp):
     for name in ("ln_8192x4096_f32", "addln_gelu_16384x8192_bf16"):
         w, d = _drop_case(name, 33, 1024)
