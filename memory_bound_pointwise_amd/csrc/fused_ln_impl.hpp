@@ -122,6 +122,40 @@ __device__ __forceinline__ void relu_dropout(float* o, uint64_t i0, const Drop& 
   for (int e = 0; e < N; ++e) o[e] = (h[e] >= drop.thr && !(o[e] < 0.0f)) ? o[e] * drop.scale : 0.0f;
 }
 
+// The 16-bit halves o .. o + 7 of the two generator blocks w0 || w1 (o in
+// 0 .. 7, uniform over the wave: a scalar branch, then one v_alignbyte_b32
+// per output word).
+__device__ __forceinline__ void halves_at(const u32x4& w0, const u32x4& w1, int o, uint32_t* h) {
+  uint32_t w[8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    w[t] = w0.w[t];
+    w[4 + t] = w1.w[t];
+  }
+  const int bb = (o & 1) * 2;
+  uint32_t r[4];
+  switch (o >> 1) {
+    case 0:
+#pragma unroll
+      for (int t = 0; t < 4; ++t) r[t] = __builtin_amdgcn_alignbyte(w[t + 1], w[t], bb);
+      break;
+    case 1:
+#pragma unroll
+      for (int t = 0; t < 4; ++t) r[t] = __builtin_amdgcn_alignbyte(w[t + 2], w[t + 1], bb);
+      break;
+    case 2:
+#pragma unroll
+      for (int t = 0; t < 4; ++t) r[t] = __builtin_amdgcn_alignbyte(w[t + 3], w[t + 2], bb);
+      break;
+    default:
+#pragma unroll
+      for (int t = 0; t < 4; ++t) r[t] = __builtin_amdgcn_alignbyte(w[t + 4], w[t + 3], bb);
+      break;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = (e & 1) ? (r[e >> 1] >> 16) : (r[e >> 1] & 0xFFFFu);
+}
+
 // ------------------------------------------------------------ aligned rows
 
 template <class IO, int LANES, int VPL, bool RES, int EPI>
@@ -378,18 +412,19 @@ __device__ __forceinline__ u32x4 funnel(const u32x4& lo, const uint32_t* hi, int
 // `edge_blocks` blocks of the grid, which handle them element by element.
 // Layouts of up to 2048 slots keep gamma / beta in LDS (at most 64 KB per
 // block), which leaves the 16-bit row loop of up to 4 vectors per lane within
-// 128 registers: four waves per SIMD.
+// 128 registers: four waves per SIMD (not with the dropout epilogue, whose
+// generator blocks take more LDS).
 constexpr bool class_raw_gb(int lanes, int vpl) { return lanes * vpl <= 2048; }
-constexpr int class_min_waves(int lanes, int vpl, int es) {
-  return es == 2 && vpl <= 4 && class_raw_gb(lanes, vpl) ? 4 : 1;
+constexpr int class_min_waves(int lanes, int vpl, int es, int epi) {
+  return es == 2 && vpl <= 4 && epi != kEpiReluDrop && class_raw_gb(lanes, vpl) ? 4 : 1;
 }
 
 template <class IO, int LANES, int VPL, bool RES, int EPI>
-__global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_eu(class_min_waves(LANES, VPL, (int)sizeof(typename IO::elem))))) void ln_class_kernel(
+__global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_eu(class_min_waves(LANES, VPL, (int)sizeof(typename IO::elem), EPI)))) void ln_class_kernel(
     const typename IO::elem* x, const typename IO::elem* res,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
     typename IO::elem* y, int64_t rows, int cols, double eps_d, int period, int line, int64_t r_lo,
-    int64_t r_hi, int edge_blocks) {
+    int64_t r_hi, int edge_blocks, Drop drop) {
   typedef typename IO::elem E;
   typedef typename Types<IO, RES>::acc Acc;
   typedef typename Types<IO, RES>::val Val;
@@ -399,6 +434,15 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
   constexpr int RPB = BLOCK / LANES;
   constexpr bool kInPlace = std::is_same<Acc, Val>::value;
   constexpr bool kRaw = class_raw_gb(LANES, VPL);
+  // Dropout: a row's elements lie off the generator's 8-element blocks, so
+  // each slot straddles two blocks.  Where LDS allows, every block of the row
+  // is computed once, by one lane, into LDS (two buffers, alternating by row
+  // group, so a wave may run ahead by one row) and each slot reads its two;
+  // otherwise each slot computes both.
+  constexpr int kPB = (LANES * VPL * V) / 8 + 2;  // blocks of a row, at most
+  constexpr bool kDrop = EPI == kEpiReluDrop;
+  constexpr bool kPhLds =
+      kDrop && 2 * RPB * kPB * 16 + (kRaw ? 2 * LANES * VPL * 16 : 0) <= 60 * 1024;
   __shared__ Acc red[2][BLOCK / 64];
 
   const int lane = threadIdx.x % LANES;
@@ -429,9 +473,11 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
     }
     const Acc rstd = inv_sqrt(group_sum<LANES, BLOCK>(m2, red[1]) / (Acc)cols + eps);
     if (live)
-      for (int c = lane; c < cols; c += LANES)
-        IO::store1(y, e0 + c,
-                   finish<Acc, EPI>((Acc)val(c) - mean, rstd, (Acc)IO::load1(gamma, c), (Acc)IO::load1(beta, c)));
+      for (int c = lane; c < cols; c += LANES) {
+        float o = finish<Acc, EPI>((Acc)val(c) - mean, rstd, (Acc)IO::load1(gamma, c), (Acc)IO::load1(beta, c));
+        if constexpr (EPI == kEpiReluDrop) relu_dropout<1, true>(&o, (uint64_t)(e0 + c), drop);
+        IO::store1(y, e0 + c, o);
+      }
     return;
   }
 
@@ -612,7 +658,9 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
     used[k] = lane + k * LANES < nvec;
   }
 
-  for (int64_t grp = blk; grp < cgroups; grp += nblk) {
+  __shared__ u32x4 pblk[kPhLds ? 2 * RPB * kPB : 1];
+  int parity = 0;
+  for (int64_t grp = blk; grp < cgroups; grp += nblk, parity ^= 1) {
     if constexpr (!kRaw) {
 #pragma unroll
       for (int k = 0; k < VPL; ++k) {
@@ -647,6 +695,24 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
         const uint32_t keep = sh == 4 ? 0u : 0xffffffffu << (8 * sh);
         xw[0].w[t] = (xw[0].w[t] & keep) | (xf.w[t] & ~keep);
         if constexpr (RES) rw[0].w[t] = (rw[0].w[t] & keep) | (rf.w[t] & ~keep);
+      }
+    }
+    // dropout: the row's generator blocks bfirst .. bfirst + nb_row - 1,
+    // each computed once into this group's buffer (while the loads are in
+    // flight)
+    uint64_t rc = 0, bfirst = 0;
+    int nb_row = 0;
+    if constexpr (kDrop) {
+      rc = (uint64_t)(live ? row : last_row) * (uint64_t)cols;
+      bfirst = rc >> 3;
+      nb_row = (int)(((rc + (uint64_t)cols - 1) >> 3) - bfirst) + 1;
+      if constexpr (kPhLds) {
+        u32x4* pb = pblk + (parity * RPB + sub) * kPB;
+        for (int i = lane; i < nb_row; i += LANES) {
+          uint32_t w[4];
+          philox4x32_10(bfirst + (uint64_t)i, drop.seed, drop.offset, w);
+          pb[i] = u32x4{{w[0], w[1], w[2], w[3]}};
+        }
       }
     }
     // zero the elements outside the row (slot 0 and slot nvec - 1 only)
@@ -698,6 +764,7 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
       if (used[k]) m2 += part;
     }
     const Acc rstd = inv_sqrt(group_sum<LANES, BLOCK>(m2, red[1]) / (Acc)cols + eps);
+    if constexpr (kPhLds) lds_barrier();  // the generator blocks are in LDS
 
     if (!live) continue;
     u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(y) - mb) + q0;
@@ -719,6 +786,35 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
       for (int e = 0; e < V; ++e) {
         const Acc dv = kInPlace ? (Acc)v[k][e] : (Acc)v[k][e] - mean;
         o[e] = finish<Acc, EPI>(dv, rstd, (Acc)IO::get(gk, e), (Acc)IO::get(bk, e));
+      }
+      if constexpr (kDrop) {
+        // element e of relative slot j has flat index rc + V*j - s + e; the
+        // folded tail of relative slot 0 (e < s) has rc + V*nvec - s + e
+        uint32_t h[8];
+        auto bits = [&](uint64_t i0, uint32_t* hh) {
+          if constexpr (kPhLds) {
+            const u32x4* pb = pblk + (parity * RPB + sub) * kPB;
+            const int64_t b = (int64_t)((i0 >> 3) - bfirst);  // -1: the previous row's block
+            const u32x4 w0 = pb[min(max(b, (int64_t)0), (int64_t)nb_row - 1)];
+            const u32x4 w1 = pb[min(max(b + 1, (int64_t)0), (int64_t)nb_row - 1)];
+            int o8 = (int)(i0 & 7);
+            // one row per wave and V*j a multiple of 8: the same for the whole wave
+            if constexpr (LANES >= 64 && V == 8) o8 = __builtin_amdgcn_readfirstlane(o8);
+            halves_at(w0, w1, o8, hh);
+          } else {
+            dropout_bits<V, false>(i0, drop.seed, drop.offset, hh);
+          }
+        };
+        bits(rc + (uint64_t)(V * j) - (uint64_t)s, h);
+        if (fold && j == 0) {
+          uint32_t ht[8];
+          bits(rc + (uint64_t)(V * nvec) - (uint64_t)s, ht);
+#pragma unroll
+          for (int e = 0; e < V; ++e)
+            if (e < s) h[e] = ht[e];
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) o[e] = (h[e] >= drop.thr && !(o[e] < 0.0f)) ? o[e] * drop.scale : 0.0f;
       }
       const u32x4 ov = pack_vec<IO>(o);
       // window j holds columns V*j - s + e; slot 0 and slot nvec - 1 may
@@ -1105,8 +1201,7 @@ hipError_t launch_flags(const void* x, const void* res, const void* gamma, const
   const uintptr_t ax = reinterpret_cast<uintptr_t>(x);
   const bool congruent = ((ax ^ reinterpret_cast<uintptr_t>(y)) & 15) == 0 &&
                          (!res || ((ax ^ reinterpret_cast<uintptr_t>(res)) & 15) == 0);
-  // the class kernel has no dropout epilogue: those rows take the shift kernel
-  if (congruent && EPI != kEpiReluDrop) {
+  if (congruent) {
     // Rows whose windows lie inside the tensors: [r_lo, r_hi).  A row
     // starting fewer than 16 - (x mod 16) bytes past an unaligned start, or
     // ending fewer than (end mod 16) bytes before an unaligned end, has a
@@ -1136,9 +1231,9 @@ hipError_t launch_flags(const void* x, const void* res, const void* gamma, const
     const int64_t cgroups = ((r_hi - r_lo + period - 1) / period + rpb - 1) / rpb;
     int64_t nblk = (cgroups + kClassGroups - 1) / kClassGroups;
     if (nblk > kMaxGrid / 128) nblk = kMaxGrid / 128;
-    const void* k = shape_kernel<ClassSel<IO, RES, (EPI == kEpiReluDrop ? kEpiNone : EPI)>::template K>(i);
-    void* cargs[] = {&x,      &res,   &gamma, &beta, &y,    &rows,
-                     &icols,  &eps,   &period, &line, &r_lo, &r_hi, (void*)&edge_blocks};
+    const void* k = shape_kernel<ClassSel<IO, RES, EPI>::template K>(i);
+    void* cargs[] = {&x,   &res,    &gamma, &beta, &y,    &rows, &icols,
+                     &eps, &period, &line,  &r_lo, &r_hi, (void*)&edge_blocks, &drop};
     return hipLaunchKernel(k, dim3((unsigned)(edge_blocks + period * nblk)), dim3(block), cargs, 0, s);
   }
   // kShiftGroups row groups per block amortise the per-block gamma/beta set-up
