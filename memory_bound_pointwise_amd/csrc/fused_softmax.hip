@@ -22,6 +22,8 @@
 #include "mbp_internal.hpp"
 #include "row_common.hpp"
 
+#include <type_traits>
+
 namespace mbp {
 namespace {
 
@@ -289,7 +291,11 @@ __global__ __launch_bounds__(block_for(LANES)) void softmax_win_kernel(const typ
 
   char* yb = reinterpret_cast<char*>(y) + (int64_t)ES * row * cols;
   u32x4* dst = reinterpret_cast<u32x4*>(yb - sb);  // y agrees with x modulo 16
-  E* yrow = reinterpret_cast<E*>(yb);
+  // fp32: element stores through a volatile pointer, so that the compiler
+  // keeps the whole-window store one dwordx4 instead of sinking its last dword
+  // into a tail shared with the element stores; 16-bit: plain stores
+  typedef typename std::conditional<ES == 4, volatile E, E>::type VE;
+  VE* vrow = reinterpret_cast<E*>(yb);
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
     if (lane + k * LANES >= nvec) continue;
@@ -321,13 +327,13 @@ __global__ __launch_bounds__(block_for(LANES)) void softmax_win_kernel(const typ
       opaque(eb);
 #pragma unroll
       for (int e = 0; e < V; ++e)
-        if (e >= ea && e < eb) yrow[V * j - s + e] = stored_elem<IO>(ov, e);
+        if (e >= ea && e < eb) vrow[V * j - s + e] = stored_elem<IO>(ov, e);
       if (fold && j == 0) {  // the folded tail: columns V*nvec - s + e
         int fb = cols - (V * nvec - s);
         opaque(fb);
 #pragma unroll
         for (int e = 0; e < V; ++e)
-          if (e < fb) yrow[V * nvec - s + e] = stored_elem<IO>(ov, e);
+          if (e < fb) vrow[V * nvec - s + e] = stored_elem<IO>(ov, e);
       }
     }
   }
