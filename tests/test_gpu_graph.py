@@ -60,9 +60,9 @@ def _case(mbp, name):
             return x, (lambda y, ws: m.unfused_add_layernorm_gelu(x, r, g, b, act="gelu_tanh", out=y,
                                                                   workspace=ws)), nb, 7
         return x, lambda y, ws: m.fused_add_layernorm_gelu(x, r, g, b, act="gelu_tanh", out=y), 0, 1
-    if name in ("lnrd_unfused", "lnrd_fused"):
+    if name in ("lnrd_unfused", "lnrd_fused", "lnrd_fused_4095"):
         w = W.scaled(W.BY_NAME["addln_gelu_16384x8192_bf16"], rows=32)
-        d = W.generate(w, cols=8192)
+        d = W.generate(w, cols=4095 if name == "lnrd_fused_4095" else 8192)
         x, g, b = (to_dev(d[k]) for k in ("x", "gamma", "beta"))
         kw = dict(p=0.1, seed=0x5EED, offset=12345)
         if name == "lnrd_unfused":
@@ -81,7 +81,7 @@ def _case(mbp, name):
 
 
 CASES = ["chain_unfused", "chain_fused", "tenop_unfused", "tenop_grouped", "tenop_fused",
-         "ln_unfused", "ln_fused", "lnrd_unfused", "lnrd_fused", "softmax", "softmax_unfused"]
+         "ln_unfused", "ln_fused", "lnrd_unfused", "lnrd_fused", "lnrd_fused_4095", "softmax", "softmax_unfused"]
 
 
 @pytest.mark.parametrize("name", CASES)
