@@ -605,12 +605,13 @@ def test_ln_relu_dropout(mbp, name, cols, p):
 
 
 @pytest.mark.parametrize("name", ["ln_8192x4096_f32", "addln_gelu_16384x8192_bf16"])
-@pytest.mark.parametrize("cols,rows", [(4095, 70), (1001, 40), (7, 50)])
+@pytest.mark.parametrize("cols,rows", [(4095, 70), (1001, 40), (7, 50), (8191, 9), (12287, 5)])
 @pytest.mark.parametrize("off_b", [0, 4, 20, 124])
 def test_ln_relu_dropout_windows(mbp, name, cols, rows, off_b):
     """x and y both `off_b` bytes past a 128-byte line, rows off 16-byte
     boundaries: the relu + dropout epilogue on vectors that straddle two
-    generator blocks, the rows at an unaligned start, and in place."""
+    generator blocks (the blocks shared through LDS, and for the widest rows
+    computed in every slot), the rows at an unaligned start, and in place."""
     w, d = _drop_case(name, rows, cols)
     es = 4 if w.dtype == "f32" else 2
     seed, offset, p = 0x0123456789ABCDEF, 5, 0.25
