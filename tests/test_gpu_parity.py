@@ -271,7 +271,8 @@ def test_ln_independent_misalignment(mbp, dtype_name, cols, offs, rows):
 @pytest.mark.parametrize("name,cols,rows", [
     ("addln_gelu_16384x8192_bf16", 4095, 130), ("addln_gelu_16384x8192_bf16", 768 + 1, 70),
     ("addln_gelu_16384x8192_bf16", 1023, 33), ("addln_gelu_16384x8192_bf16", 12290, 9),
-    ("ln_8192x4096_f32", 4093, 70), ("ln_8192x4096_f32", 1021, 40)])
+    ("ln_8192x4096_f32", 4093, 70), ("ln_8192x4096_f32", 1021, 40), ("ln_8192x4096_f32", 12289, 9),
+    ("addln_gelu_16384x8192_bf16", 16383, 5)])
 @pytest.mark.parametrize("bytes_off", [(4, 4, 4), (20, 20, 20), (124, 124, 124), (64, 64, 64),
                                        (4, 20, 4), (12, 12, 124)])
 def test_ln_line_classes(mbp, name, cols, rows, bytes_off):
@@ -279,7 +280,9 @@ def test_ln_line_classes(mbp, name, cols, rows, bytes_off):
     bytes past a 128-byte line.  Equal offsets take the per-class window path
     with classes modulo a line (the rows cover every class, so every window
     offset in the line and every ring shift of gamma / beta appears); offsets
-    equal only modulo 16 take it with classes modulo 16 bytes."""
+    equal only modulo 16 take it with classes modulo 16 bytes.  fp32 rows of
+    12289 (over 2048 slots) take gamma / beta funnelled into registers instead
+    of the LDS ring."""
     w, d, act = _ln_case(name, rows, cols, residual=True)
     ref = _ln_ref(d, act)
     chk = check_bf16 if w.dtype == "bf16" else check_f32
