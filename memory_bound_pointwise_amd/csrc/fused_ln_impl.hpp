@@ -437,12 +437,17 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
   // Dropout: a row's elements lie off the generator's 8-element blocks, so
   // each slot straddles two blocks.  Where LDS allows, every block of the row
   // is computed once, by one lane, into LDS (two buffers, alternating by row
-  // group, so a wave may run ahead by one row) and each slot reads its two;
-  // otherwise each slot computes both.
+  // group, so a wave may run ahead by one row; one buffer and a barrier before
+  // each refill where two do not fit) and each slot reads its two; otherwise
+  // each slot computes both.
   constexpr int kPB = (LANES * VPL * V) / 8 + 2;  // blocks of a row, at most
   constexpr bool kDrop = EPI == kEpiReluDrop;
-  constexpr bool kPhLds =
-      kDrop && 2 * RPB * kPB * 16 + (kRaw ? 2 * LANES * VPL * 16 : 0) <= 60 * 1024;
+  constexpr int kRingB = kRaw ? 2 * LANES * VPL * 16 : 0;
+  // two buffers where they fit, else one (and a barrier before each refill)
+  constexpr int kPhBuf = !kDrop ? 0 : 2 * RPB * kPB * 16 + kRingB <= 60 * 1024 ? 2
+                                    : RPB * kPB * 16 + kRingB <= 60 * 1024       ? 1
+                                                                                 : 0;
+  constexpr bool kPhLds = kPhBuf > 0;
   __shared__ Acc red[2][BLOCK / 64];
 
   const int lane = threadIdx.x % LANES;
@@ -658,7 +663,7 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
     used[k] = lane + k * LANES < nvec;
   }
 
-  __shared__ u32x4 pblk[kPhLds ? 2 * RPB * kPB : 1];
+  __shared__ u32x4 pblk[kPhLds ? kPhBuf * RPB * kPB : 1];
   int parity = 0;
   for (int64_t grp = blk; grp < cgroups; grp += nblk, parity ^= 1) {
     if constexpr (!kRaw) {
@@ -707,7 +712,10 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
       bfirst = rc >> 3;
       nb_row = (int)(((rc + (uint64_t)cols - 1) >> 3) - bfirst) + 1;
       if constexpr (kPhLds) {
-        u32x4* pb = pblk + (parity * RPB + sub) * kPB;
+        if constexpr (kPhBuf == 1) {
+          if (grp != blk) lds_barrier();  // every lane has read the previous row's blocks
+        }
+        u32x4* pb = pblk + ((kPhBuf == 2 ? parity : 0) * RPB + sub) * kPB;
         for (int i = lane; i < nb_row; i += LANES) {
           uint32_t w[4];
           philox4x32_10(bfirst + (uint64_t)i, drop.seed, drop.offset, w);
@@ -800,7 +808,7 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
         uint32_t h[8];
         auto bits = [&](uint64_t i0, uint32_t* hh) {
           if constexpr (kPhLds) {
-            const u32x4* pb = pblk + (parity * RPB + sub) * kPB;
+            const u32x4* pb = pblk + ((kPhBuf == 2 ? parity : 0) * RPB + sub) * kPB;
             const int64_t b = (int64_t)((i0 >> 3) - bfirst);  // -1: the previous row's block
             const u32x4 w0 = pb[min(max(b, (int64_t)0), (int64_t)nb_row - 1)];
             const u32x4 w1 = pb[min(max(b + 1, (int64_t)0), (int64_t)nb_row - 1)];
