@@ -305,6 +305,25 @@ def test_ln_line_classes(mbp, name, cols, rows, bytes_off):
     o = bytes_off[2] // es
     assert (host[:o] == 3.0).all() and (host[o + x.numel():] == 3.0).all(), "wrote outside y"
 
+
+@pytest.mark.parametrize("name", ["ln_8192x4096_f32", "addln_gelu_16384x8192_bf16"])
+@pytest.mark.parametrize("cols", [4096, 4095])
+@pytest.mark.parametrize("eps", [0.0, 1e-12, 1.0, 100.0])
+def test_ln_eps(mbp, name, cols, eps):
+    """eps from 0 to far above the row variance (the output tends to beta),
+    on the aligned and the per-class window kernels; rows of small spread
+    (1e-3 around 5) where eps = 1e-12 and eps = 0 still differ from 1e-5"""
+    w, d, act = _ln_case(name, 17, cols, residual=False)
+    rng = np.random.default_rng([31, cols, int(eps * 1000)])
+    x = d["x"]
+    if w.dtype == "f32":
+        x[3] = (5.0 + 1e-3 * rng.standard_normal(cols)).astype(np.float32)
+    y = mbp.fused_add_layernorm_gelu(to_dev(x), None, to_dev(d["gamma"]), to_dev(d["beta"]), eps=eps, act=act)
+    ref = oracle.add_layernorm_gelu(x, None, d["gamma"], d["beta"], eps=eps, act=(
+        oracle.ACT_GELU_TANH if act == "gelu_tanh" else oracle.ACT_NONE))
+    chk = check_bf16 if w.dtype == "bf16" else check_f32
+    chk(to_host(y), ref, f"{name} {cols} eps={eps}")
+
 def test_ln_constant_rows_give_beta(mbp):
     for name in ("ln_8192x4096_f32", "addln_gelu_16384x8192_bf16"):
         w, d, _ = _ln_case(name, 4, 4096, residual=False)
