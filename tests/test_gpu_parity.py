@@ -704,6 +704,22 @@ def test_softmax_shapes(mbp, fmt, dtype, cols, scale):
     _softmax_gate(y, oracle.softmax(xf), fmt, f"softmax {fmt} {rows}x{cols} scale {scale}")
 
 
+
+@pytest.mark.parametrize("fmt,dtype", DT2D, ids=[d[0] for d in DT2D])
+@pytest.mark.parametrize("shift", [-3.0e4, 3.0e4, -60000.0])
+def test_softmax_large_offsets(mbp, fmt, dtype, shift):
+    """rows far from 0 (exp(x) alone would overflow or underflow): the
+    running maximum keeps every exponent <= 0; aligned and windowed rows"""
+    if fmt == "f16" and abs(shift) > 6.0e4:
+        pytest.skip("beyond the fp16 range")
+    rng = np.random.default_rng([24, abs(int(shift)), int(shift < 0)])
+    for cols in (4096, 4095):
+        xh, _ = _stored(rng, (9, cols), dtype, 3.0)
+        xh = (xh.float() + shift).to(dtype)
+        xf = xh.float().numpy()
+        y = mbp.fused_softmax(xh.cuda())
+        _softmax_gate(y, oracle.softmax(xf), fmt, f"softmax {fmt} 9x{cols} shifted by {shift}")
+
 @pytest.mark.parametrize("fmt,dtype", DT2D, ids=[d[0] for d in DT2D])
 def test_softmax_masks_in_place_and_misaligned(mbp, fmt, dtype):
     rng = np.random.default_rng(22)
