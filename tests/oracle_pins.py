@@ -389,6 +389,110 @@ def pin_ln_seq(lib):
     assert np.array_equal(y, ref.astype(np.float64)), "LN SEQ (fp32) must match op-by-op emulation"
 
 
+def _rb(a):
+    """float32 -> bfloat16 (nearest even, torch's conversion) -> float32."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def _gelu_mp(u):
+    """tanh-GeLU with the printed constants, each value evaluated in 40-digit
+    mpmath and rounded once to binary64 (an evaluation independent of the
+    oracle's C code)."""
+    mpmath.mp.dps = 40
+    out = []
+    for t in np.asarray(u, np.float64).ravel():
+        m = mpmath.mpf(float(t))
+        z = mpmath.mpf("0.7978845608") * (m + mpmath.mpf("0.044715") * m ** 3)
+        out.append(float(mpmath.mpf("0.5") * m * (1 + mpmath.tanh(z))))
+    return np.array(out, np.float64).reshape(np.shape(u))
+
+
+def _ln_f64_torch(v, gamma, beta, eps=1e-5):
+    """LayerNorm rows in float64 with torch's CPU layer_norm (library code)."""
+    import torch
+    import torch.nn.functional as F
+    t = torch.from_numpy(np.asarray(v, np.float64))
+    g = torch.from_numpy(np.asarray(gamma, np.float64))
+    b = torch.from_numpy(np.asarray(beta, np.float64))
+    return F.layer_norm(t, (t.shape[1],), g, b, eps=eps).numpy()
+
+
+def pin_ln_seq_gelu(lib):
+    """SEQ mode with the residual and the tanh-GeLU: the seven eager launches of
+    [P2] section 2.3's chain (add, mean, var, sub, div, mul-add, gelu), every
+    element-wise result stored in the I/O type.  Emulated op by op with numpy
+    float32 arithmetic, torch's bfloat16 rounding and a 40-digit GeLU rounded
+    to the storage type at its store."""
+    r = _rng(43)
+    rows, cols = 5, 48
+    x = _rb(r.standard_normal((rows, cols)).astype(np.float32) * 2)
+    res = _rb(r.standard_normal((rows, cols)).astype(np.float32) * 2)
+    gamma = _rb((1 + 0.1 * r.standard_normal(cols)).astype(np.float32))
+    beta = _rb((0.1 * r.standard_normal(cols)).astype(np.float32))
+    v = _rb(x + res)
+    mu = np.array([np.float32(math.fsum(map(float, row)) / cols) for row in v], np.float32)[:, None]
+    var = np.array([np.float32(math.fsum((float(t) - float(m)) ** 2 for t in row) / cols)
+                    for row, m in zip(v, mu[:, 0])], np.float32)[:, None]
+    nrm = _rb(_rb(v - mu) / np.sqrt(var + np.float32(1e-5)))
+    u = _rb(nrm * gamma + beta)
+    want = _rb(_gelu_mp(u).astype(np.float32)).astype(np.float64)
+    bits = _torch_bf16_bits
+    y = oracle.add_layernorm_gelu(bits(x), bits(res), bits(gamma), bits(beta), act=oracle.ACT_GELU_TANH,
+                                  mode=oracle.SEQ, lib=lib)
+    assert np.array_equal(y, want), \
+        f"LN+GeLU SEQ (bf16): {int((y != want).sum())} of {y.size} differ from the op-by-op emulation"
+    # fp32 I/O: the same seven ops, each stored as binary32
+    x32 = r.standard_normal((rows, cols)).astype(np.float32)
+    r32 = r.standard_normal((rows, cols)).astype(np.float32)
+    g32 = (1 + 0.1 * r.standard_normal(cols)).astype(np.float32)
+    b32 = (0.1 * r.standard_normal(cols)).astype(np.float32)
+    v = x32 + r32
+    mu = np.array([np.float32(math.fsum(map(float, row)) / cols) for row in v], np.float32)[:, None]
+    var = np.array([np.float32(math.fsum((float(t) - float(m)) ** 2 for t in row) / cols)
+                    for row, m in zip(v, mu[:, 0])], np.float32)[:, None]
+    u = ((v - mu) / np.sqrt(var + np.float32(1e-5))) * g32 + b32
+    want = _gelu_mp(u).astype(np.float32).astype(np.float64)
+    y = oracle.add_layernorm_gelu(x32, r32, g32, b32, act=oracle.ACT_GELU_TANH, mode=oracle.SEQ, lib=lib)
+    assert np.array_equal(y, want), \
+        f"LN+GeLU SEQ (fp32): {int((y != want).sum())} of {y.size} differ from the op-by-op emulation"
+
+
+def pin_ln_seq3(lib):
+    """SEQ3 mode: the three eager launches of [P2] section 2.3's chain -- the
+    residual add, one LayerNorm kernel, the GeLU -- each result stored in the
+    I/O type; the LayerNorm launch itself computes in binary64.  Emulated with
+    numpy float32 for the add, torch's float64 layer_norm for the middle launch,
+    torch's rounding to the storage type and a 40-digit GeLU."""
+    r = _rng(44)
+    rows, cols = 5, 56
+    x = _rb(r.standard_normal((rows, cols)).astype(np.float32) * 2 + 0.5)
+    res = _rb(r.standard_normal((rows, cols)).astype(np.float32) * 2)
+    gamma = _rb((1 + 0.1 * r.standard_normal(cols)).astype(np.float32))
+    beta = _rb((0.1 * r.standard_normal(cols)).astype(np.float32))
+    v = _rb(x + res)
+    u = _rb(_ln_f64_torch(v, gamma, beta).astype(np.float32))
+    bits = _torch_bf16_bits
+    y = oracle.add_layernorm_gelu(bits(x), bits(res), bits(gamma), bits(beta), act=oracle.ACT_NONE,
+                                  mode=oracle.SEQ3, lib=lib)
+    assert np.array_equal(y, u.astype(np.float64)), \
+        f"LN SEQ3 (bf16): {int((y != u).sum())} of {y.size} differ from add -> layer_norm, each stored"
+    want = _rb(_gelu_mp(u).astype(np.float32)).astype(np.float64)
+    y = oracle.add_layernorm_gelu(bits(x), bits(res), bits(gamma), bits(beta), act=oracle.ACT_GELU_TANH,
+                                  mode=oracle.SEQ3, lib=lib)
+    assert np.array_equal(y, want), \
+        f"LN+GeLU SEQ3 (bf16): {int((y != want).sum())} of {y.size} differ from add -> layer_norm -> gelu"
+    x32 = r.standard_normal((rows, cols)).astype(np.float32)
+    r32 = r.standard_normal((rows, cols)).astype(np.float32)
+    g32 = (1 + 0.1 * r.standard_normal(cols)).astype(np.float32)
+    b32 = (0.1 * r.standard_normal(cols)).astype(np.float32)
+    u = _ln_f64_torch(x32 + r32, g32, b32).astype(np.float32)
+    want = _gelu_mp(u).astype(np.float32).astype(np.float64)
+    y = oracle.add_layernorm_gelu(x32, r32, g32, b32, act=oracle.ACT_GELU_TANH, mode=oracle.SEQ3, lib=lib)
+    assert np.array_equal(y, want), \
+        f"LN+GeLU SEQ3 (fp32): {int((y != want).sum())} of {y.size} differ from the three launches"
+
+
 def _nearest_even_bits(x, table_vals, table_bits, max_bits, inf_bits):
     """Brute force: the bit pattern of the value in `table_vals` (all finite
     non-negative values of a format, ascending, with their patterns) nearest to
@@ -651,11 +755,54 @@ def pin_dropout(lib):
         assert abs(agree - (p * p + (1 - p) ** 2)) < 0.02, f"masks of other (seed, offset) agree {agree}"
 
 
+def _dropout_keep(shape, p, seed, offset, lib):
+    """Kept-element mask of [P2] section 2.1's dropout under the Philox
+    reading: half k mod 8 of block (k div 8, offset) keyed by seed, kept iff
+    it is >= round(p 2^16).  Blocks from the oracle's generator, which the
+    published known answers pin."""
+    n = int(np.prod(shape))
+    q = np.arange((n + 7) // 8, dtype=np.uint64)
+    ctr = np.stack([q & 0xFFFFFFFF, q >> 32, np.full_like(q, offset & 0xFFFFFFFF),
+                    np.full_like(q, offset >> 32)], axis=1).astype(np.uint32)
+    key = np.tile(np.array([seed & 0xFFFFFFFF, seed >> 32], np.uint32), (len(q), 1))
+    words = oracle.philox4x32_10(ctr, key, lib=lib).reshape(-1)
+    halves = np.stack([words & 0xFFFF, words >> 16], axis=1).reshape(-1)[:n].reshape(shape)
+    return halves >= round(p * 65536)
+
+
+def pin_dropout_seq3(lib):
+    """SEQ3 mode of LayerNorm -> ReLU -> Dropout: the three eager launches of
+    [P2] section 2.1 (layer_norm, relu, dropout), each result stored in the I/O
+    type.  The layer_norm launch: torch's float64 layer_norm, stored; relu of a
+    stored value is exact; the dropout launch an fp32 kernel: the kept value
+    times the scale 1/(1 - p) rounded to binary32 (numpy float32 product),
+    stored; dropped elements 0."""
+    r = _rng(45)
+    p, seed, offset = 0.1, 0x2545F4914F6CDD1D, 3
+    for dt in ("f32", "bf16"):
+        x, g, b = _ln_case_pin(r, 12, 200, dtype=dt)
+        if dt == "bf16":
+            xv, gv, bv = ((a.astype(np.uint32) << 16).view(np.float32) for a in (x, g, b))
+            store = _rb
+        else:
+            xv, gv, bv = x, g, b
+            store = lambda a: np.asarray(a, np.float32)
+        u = store(_ln_f64_torch(xv, gv, bv).astype(np.float32))
+        relu = np.maximum(u, np.float32(0))
+        keep = _dropout_keep(x.shape, p, seed, offset, lib)
+        kept = store(relu * np.float32(1.0 / (1.0 - p)))
+        want = np.where(keep, kept, np.float32(0)).astype(np.float64)
+        y = oracle.ln_relu_dropout(x, g, b, p=p, seed=seed, offset=offset, mode=oracle.SEQ3, lib=lib)
+        assert np.array_equal(y, want), \
+            f"LN-ReLU-dropout SEQ3 ({dt}): {int((y != want).sum())} of {y.size} differ from the three launches"
+
+
 ALL_PINS = [
     pin_chain_worked, pin_chain_bruteforce, pin_chain_invariants, pin_chain_numpy,
     pin_tenop_worked, pin_tenop_bruteforce, pin_tenop_invariants, pin_tenop_seq,
     pin_ln_worked, pin_ln_closed_forms, pin_ln_bruteforce, pin_ln_torch, pin_gelu,
-    pin_residual_zero, pin_bf16_encode, pin_ln_seq, pin_round_f16, pin_round_bf16,
+    pin_residual_zero, pin_bf16_encode, pin_ln_seq, pin_ln_seq_gelu, pin_ln_seq3,
+    pin_round_f16, pin_round_bf16,
     pin_softmax_worked, pin_softmax_closed_forms, pin_softmax_bruteforce, pin_softmax_torch, pin_softmax_seq,
-    pin_philox_kat, pin_dropout,
+    pin_philox_kat, pin_dropout, pin_dropout_seq3,
 ]

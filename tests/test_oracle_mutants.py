@@ -55,8 +55,17 @@ MUTANTS = [
     ("dropout: word 0 for every element", "const uint32_t w = out[(i & 7) >> 1];", "const uint32_t w = out[0];"),
     ("dropout: low half for every element", "return (i & 1) ? (w >> 16) : (w & 0xFFFFu);", "return w & 0xFFFFu;"),
     ("dropout: keep below the threshold", "const int keep = w >= threshold;", "const int keep = w < threshold;"),
-    ("dropout: no rescale", "double v = keep ? y[k] * scale : 0.0;", "double v = keep ? y[k] : 0.0;"),
+    ("dropout: no rescale", "double v = keep ? y[k] * sc : 0.0;", "double v = keep ? y[k] : 0.0;"),
     ("dropout: relu dropped", "for (int64_t k = 0; k < n; ++k) y[k] = (y[k] < 0.0) ? 0.0 : y[k];", ""),
+    ("LN SEQ/SEQ3: GeLU output not rounded", "if (seq || seq3) o = rstore(dtype, o);", ""),
+    ("LN SEQ: GeLU output not rounded (SEQ3 still rounds)", "if (seq || seq3) o = rstore(dtype, o);",
+     "if (seq3) o = rstore(dtype, o);"),
+    ("LN SEQ3: u not rounded", "if (seq3) uv = rstore(dtype, uv);", ""),
+    ("LN SEQ3: residual sum not rounded", "if (seq || seq3) xv = rstore(dtype, xv);",
+     "if (seq) xv = rstore(dtype, xv);"),
+    ("dropout SEQ3: output not rounded", "if (seq3) v = rstore(dtype, v);", ""),
+    ("dropout SEQ3: scale kept in binary64", "const double sc = seq3 ? r32(scale) : scale;",
+     "const double sc = scale;"),
 ]
 
 
