@@ -6,7 +6,8 @@
  * The caller owns every buffer: the library never allocates or frees device
  * memory and keeps no mutable global state beyond a per-thread error message.
  * (An instantiated graph, below, holds the HIP runtime's own resources until
- * the caller destroys it.)
+ * the caller destroys it; grouped_row_mean_epilogue_noalloc keeps its
+ * intermediates in a static device array compiled into the library.)
  *
  * Conventions shared by all entry points
  *   - Tensors are dense and row-major (contiguous).  A [rows, cols] tensor has
@@ -45,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MBP_ABI_VERSION 3
+#define MBP_ABI_VERSION 4
 
 /* Largest row length (cols) the row kernels accept: one row lives in registers. */
 #define MBP_MAX_COLS 16384
@@ -243,6 +244,31 @@ mbp_status grouped_row_mean_epilogue(const float* x, const float* bias, const fl
                                      const float* beta, float* y, int64_t rows, int64_t cols,
                                      double alpha, double c, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/* Bytes of the library's static scratch array (one per GPU). */
+#define MBP_STATIC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * grouped_row_mean_epilogue for callers that cannot allocate device memory
+ * (code recorded by graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same three launches and the same result bit for bit, with s
+ * and m kept in a static array of MBP_STATIC_SCRATCH_BYTES compiled into the
+ * library instead of a caller's workspace.  No workspace argument; the call
+ * allocates nothing and issues no memset (every byte of s and m it reads it
+ * has written first).  Limit: rows * cols * 4 plus rows * 4 (each rounded up
+ * to 256 bytes) must fit the array -- about 4 M elements, e.g. 1024 x 1024 --
+ * else MBP_ERR_WORKSPACE.  Each GPU has its own copy of the array, held from
+ * the first call on that GPU until the process ends; the first call on a GPU
+ * looks the copy up (make it outside a capture).  `stream` must belong to the
+ * current device (else MBP_ERR_ARG).  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (different streams, or threads
+ * without ordering) race on it and must not be made; calls in one stream are
+ * ordered and safe.  Arguments and errors otherwise as
+ * grouped_row_mean_epilogue.
+ */
+mbp_status grouped_row_mean_epilogue_noalloc(const float* x, const float* bias, const float* gamma,
+                                             const float* beta, float* y, int64_t rows, int64_t cols,
+                                             double alpha, double c, void* stream);
 
 /* [P3] section 4.3 and [P2] section 2.3.  granularity MBP_UNFUSED_PRIMITIVE:
  * [add,] mean, var, sub, div, mul-add[, gelu]  (5 launches for plain

@@ -46,6 +46,7 @@ SIGNATURES = [
     ("unfused_pointwise_chain", _I, [_P, _P, _P, _P, _I64, _D, _P, _SZ, _P]),
     ("unfused_row_mean_epilogue", _I, [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _P, _SZ, _P]),
     ("grouped_row_mean_epilogue", _I, [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _P, _SZ, _P]),
+    ("grouped_row_mean_epilogue_noalloc", _I, [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _P]),
     ("unfused_add_layernorm_gelu", _I, [_I, _P, _P, _P, _P, _P, _I64, _I64, _D, _I, _I, _P, _SZ, _P]),
     ("mbp_unfused_workspace_bytes", _SZ, [_I, _I, _I64, _I64, _I, _I, _I]),
     ("mbp_launches_per_call", _I, [_I, _I, _I, _I, _I]),
@@ -381,6 +382,19 @@ def grouped_row_mean_epilogue(x, bias, gamma, beta, alpha=1.1, c=0.1, out=None, 
     ws = _workspace(nb, x.device, workspace)
     _call("grouped_row_mean_epilogue", _ptr(x), _ptr(bias), _ptr(gamma), _ptr(beta), _ptr(y), rows,
           cols, float(alpha), float(c), _ptr(ws), ws.numel() * ws.element_size(), _stream(x))
+    return y
+
+
+def grouped_row_mean_epilogue_noalloc(x, bias, gamma, beta, alpha=1.1, c=0.1, out=None):
+    """grouped_row_mean_epilogue with s and m in the library's static scratch
+    array (no workspace; the C call allocates nothing).  Pass ``out=`` to keep
+    the whole call allocation-free."""
+    for t, n in ((x, "x"), (bias, "bias"), (gamma, "gamma"), (beta, "beta"), (out, "out")):
+        _check(t, n, (torch.float32,), x.device)
+    rows, cols = _rows_cols(x)
+    y = torch.empty_like(x) if out is None else out
+    _call("grouped_row_mean_epilogue_noalloc", _ptr(x), _ptr(bias), _ptr(gamma), _ptr(beta), _ptr(y),
+          rows, cols, float(alpha), float(c), _stream(x))
     return y
 
 

@@ -303,6 +303,25 @@ mbp_status check_dropout_p(double p) {
   return MBP_OK;
 }
 
+// The 10-op graph as TVM's three groups, s and m in the buffers `w`.
+hipError_t launch_grouped(const float* x, const float* bias, const float* gamma, const float* beta,
+                          float* y, int64_t rows, int64_t cols, double alpha, double c,
+                          const GroupedWs& w, hipStream_t s) {
+  const float a32 = (float)alpha, c32 = (float)c;
+  using namespace mbp;
+  const int F = MBP_F32;
+  // group 1: x*alpha + bias, relu, a*a, a*c, p + q  ->  s
+  hipError_t e = launch_ew4(EW_PROLOGUE, F, x, bias, IX_COL, nullptr, 0, nullptr, 0, w.s, rows, cols,
+                            a32, c32, s);
+  // group 2: the row mean of s
+  if (e == hipSuccess) e = launch_row_mean_only(F, w.s, w.m, rows, cols, s);
+  // group 3: (s - m) * gamma + beta
+  if (e == hipSuccess)
+    e = launch_ew4(EW_CENTER_AFFINE, F, w.s, w.m, IX_ROW, gamma, IX_COL, beta, IX_COL, y, rows, cols,
+                   0.0f, 0.0f, s);
+  return e;
+}
+
 }  // namespace
 
 
@@ -510,20 +529,40 @@ mbp_status grouped_row_mean_epilogue(const float* x, const float* bias, const fl
   if (st != MBP_OK) return st;
   GroupedWs w;
   grouped_ws((char*)workspace, rows, cols, &w);
-  const float a32 = (float)alpha, c32 = (float)c;
+  return from_hip(launch_grouped(x, bias, gamma, beta, y, rows, cols, alpha, c, w, as_stream(stream)),
+                  "grouped_row_mean_epilogue");
+}
+
+mbp_status grouped_row_mean_epilogue_noalloc(const float* x, const float* bias, const float* gamma,
+                                             const float* beta, float* y, int64_t rows, int64_t cols,
+                                             double alpha, double c, void* stream) {
+  mbp_status st = check_row_mean(x, bias, gamma, beta, y, rows, cols, alpha, c, false);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  const size_t need = grouped_ws(nullptr, rows, cols, nullptr);
+  if (need > (size_t)MBP_STATIC_SCRATCH_BYTES)
+    return fail(MBP_ERR_WORKSPACE,
+                "%lld x %lld needs %zu bytes of scratch; the static scratch holds %zu (rows * cols "
+                "must stay below about %zu elements)",
+                (long long)rows, (long long)cols, need, (size_t)MBP_STATIC_SCRATCH_BYTES,
+                (size_t)MBP_STATIC_SCRATCH_BYTES / 4);
   hipStream_t s = as_stream(stream);
-  using namespace mbp;
-  const int F = MBP_F32;
-  // group 1: x*alpha + bias, relu, a*a, a*c, p + q  ->  s
-  hipError_t e = launch_ew4(EW_PROLOGUE, F, x, bias, IX_COL, nullptr, 0, nullptr, 0, w.s, rows, cols,
-                            a32, c32, s);
-  // group 2: the row mean of s
-  if (e == hipSuccess) e = launch_row_mean_only(F, w.s, w.m, rows, cols, s);
-  // group 3: (s - m) * gamma + beta
-  if (e == hipSuccess)
-    e = launch_ew4(EW_CENTER_AFFINE, F, w.s, w.m, IX_ROW, gamma, IX_COL, beta, IX_COL, y, rows, cols,
-                   0.0f, 0.0f, s);
-  return from_hip(e, "grouped_row_mean_epilogue");
+  // the scratch looked up below is the current GPU's copy: the work must run there
+  int cur = -1, sdev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e == hipSuccess && s) e = hipStreamGetDevice(s, &sdev);
+  if (e != hipSuccess) return from_hip(e, "grouped_row_mean_epilogue_noalloc");
+  if (s && sdev != cur)
+    return fail(MBP_ERR_ARG, "the stream belongs to device %d but device %d is current", sdev, cur);
+  void* base = nullptr;
+  size_t have = 0;
+  e = mbp::static_scratch(&base, &have);
+  if (e != hipSuccess) return from_hip(e, "grouped_row_mean_epilogue_noalloc: scratch lookup");
+  if (have < need) return fail(MBP_ERR_WORKSPACE, "static scratch is smaller than %zu bytes", need);
+  GroupedWs w;
+  grouped_ws((char*)base, rows, cols, &w);
+  return from_hip(launch_grouped(x, bias, gamma, beta, y, rows, cols, alpha, c, w, s),
+                  "grouped_row_mean_epilogue_noalloc");
 }
 
 mbp_status unfused_add_layernorm_gelu(mbp_dtype dtype, const void* x, const void* residual,

@@ -82,4 +82,9 @@ hipError_t launch_row_mean_only(int dtype, const void* a, float* mean, int64_t r
 hipError_t launch_row_var(int dtype, const void* a, const float* mean, float* var, int64_t rows,
                           int64_t cols, hipStream_t s);
 
+// The current GPU's copy of the library's static scratch array (its device
+// address, found once per GPU with hipGetSymbolAddress and kept) and its size
+// in bytes.  Allocates nothing.
+hipError_t static_scratch(void** ptr, size_t* bytes);
+
 }  // namespace mbp

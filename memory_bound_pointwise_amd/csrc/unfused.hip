@@ -14,11 +14,27 @@
 // per element), and the row reductions read aligned 16-byte windows, so the
 // comparison with the fused kernels is one of bytes and launches, not of load
 // width.
+#include <atomic>
+#include <mutex>
+
+#include "mbp.h"
 #include "mbp_device.hpp"
 #include "mbp_internal.hpp"
 
+// Scratch memory for the entry point that allocates nothing
+// (grouped_row_mean_epilogue_noalloc): one copy of this array per GPU, in that
+// GPU's memory from the first use until the process ends.  In host code the
+// name `scratch` is only a host-side stand-in, not a device address: host code
+// reaches the array through the pointer static_scratch() looks up for the
+// current device, never through the name.
+static __device__ __align__(256) unsigned char scratch[MBP_STATIC_SCRATCH_BYTES];
+
 namespace mbp {
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
 
 constexpr int kBlock = 256;
 constexpr int64_t kMaxGrid = 1 << 30;
@@ -278,6 +294,30 @@ int64_t stat_grid(int64_t rows, int64_t cols, int es) {
 }
 
 }  // namespace
+
+hipError_t static_scratch(void** ptr, size_t* bytes) {
+  *ptr = nullptr;
+  *bytes = 0;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      // with `dev` current: this GPU's copy of the array
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  *bytes = sizeof scratch;
+  return hipSuccess;
+}
 
 hipError_t launch_ew(int op, int dtype, const void* a, const void* b, int b_ix, const void* c,
                      int c_ix, void* out, int64_t rows, int64_t cols, float scalar,
