@@ -76,7 +76,7 @@ def _bind(lib):
     lib.oracle_philox4x32_10.argtypes = [P, P, I64, P]
     lib.oracle_philox4x32_10.restype = None
     U32, U64 = ctypes.c_uint32, ctypes.c_uint64
-    lib.oracle_ln_relu_dropout.argtypes = [I, P, P, P, I64, I64, D, U32, D, U64, U64, I, P]
+    lib.oracle_ln_relu_dropout.argtypes = [I, P, P, P, I64, I64, D, U32, D, U64, U64, I64, I, P]
     lib.oracle_ln_relu_dropout.restype = I
     return lib
 
@@ -207,8 +207,10 @@ def dropout_threshold(p):
     return t, scale
 
 
-def ln_relu_dropout(x, gamma, beta, p=0.1, seed=0, offset=0, eps=1e-5, mode=EXACT, lib=None):
-    """LayerNorm -> ReLU -> Dropout (training semantics) over the last dimension."""
+def ln_relu_dropout(x, gamma, beta, p=0.1, seed=0, offset=0, eps=1e-5, mode=EXACT, first_row=0, lib=None):
+    """LayerNorm -> ReLU -> Dropout (training semantics) over the last dimension.
+    x may be rows [first_row, first_row + len(x)) of a larger tensor: the
+    element indices that pick the random bits are those of that tensor."""
     lib = lib or load()
     if x.dtype == np.uint16:
         dtype, cast = BF16, (lambda a: np.ascontiguousarray(a, dtype=np.uint16))
@@ -223,5 +225,5 @@ def ln_relu_dropout(x, gamma, beta, p=0.1, seed=0, offset=0, eps=1e-5, mode=EXAC
     t, scale = dropout_threshold(p)
     y = np.empty((rows, cols), dtype=np.float64)
     _check(lib.oracle_ln_relu_dropout(dtype, _ptr(x), _ptr(gamma), _ptr(beta), rows, cols, eps, t,
-                                      scale, seed, offset, mode, _ptr(y)), "ln_relu_dropout")
+                                      scale, seed, offset, first_row, mode, _ptr(y)), "ln_relu_dropout")
     return y

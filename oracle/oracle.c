@@ -492,15 +492,20 @@ static uint32_t dropout_bits(uint64_t seed, uint64_t offset, uint64_t i) {
  * are >= threshold; threshold = round(p * 2^16) in [0, 65536], so an element
  * is dropped with probability threshold / 2^16 = p to within 2^-17 (65536
  * drops everything); scale = 1 / (1 - p).  The caller passes threshold and
- * scale.  Modes: ORACLE_EXACT, binary64 throughout; ORACLE_SEQ3 stores u, r
+ * scale.  x holds rows [first_row, first_row + rows) of a larger [*, cols]
+ * tensor (first_row 0: the whole tensor): element (i, j) of x has the index
+ * (first_row + i) * cols + j there, which picks its random bits, so a tensor
+ * can be evaluated in row chunks with the same result.
+ * Modes: ORACLE_EXACT, binary64 throughout; ORACLE_SEQ3 stores u, r
  * and y in the I/O type (three eager launches), the dropout launch being an
  * fp32 kernel: its scale is rounded to binary32 first, like every constant in
  * the SEQ modes, and the product is rounded as it is stored.  dtype
  * ORACLE_F32 / ORACLE_BF16 as for the LayerNorm oracle. */
 int oracle_ln_relu_dropout(int dtype, const void* x, const void* gamma, const void* beta, int64_t rows,
                            int64_t cols, double eps, uint32_t threshold, double scale, uint64_t seed,
-                           uint64_t offset, int mode, double* y) {
+                           uint64_t offset, int64_t first_row, int mode, double* y) {
   if (mode != ORACLE_EXACT && mode != ORACLE_SEQ3) return -1;
+  if (first_row < 0) return -1;
   const int seq3 = mode == ORACLE_SEQ3;
   const double sc = seq3 ? r32(scale) : scale;
   int rc = oracle_add_layernorm_gelu(dtype, x, NULL, gamma, beta, rows, cols, eps, ORACLE_ACT_NONE,
@@ -511,7 +516,7 @@ int oracle_ln_relu_dropout(int dtype, const void* x, const void* gamma, const vo
   for (int64_t k = 0; k < n; ++k) y[k] = (y[k] < 0.0) ? 0.0 : y[k];
   /* op: dropout */
   for (int64_t k = 0; k < n; ++k) {
-    const uint32_t w = dropout_bits(seed, offset, (uint64_t)k);
+    const uint32_t w = dropout_bits(seed, offset, (uint64_t)(first_row * cols + k));
     const int keep = w >= threshold;
     double v = keep ? y[k] * sc : 0.0;
     if (seq3) v = rstore(dtype, v);

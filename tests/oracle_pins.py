@@ -749,6 +749,10 @@ def pin_dropout(lib):
     y2 = oracle.ln_relu_dropout(x2, g, b, p=p, seed=seed, offset=offset, lib=lib)
     pos = (relu_ln > 0) & (np.maximum(oracle.add_layernorm_gelu(x2, None, g, b, act=oracle.ACT_NONE, lib=lib), 0) > 0)
     assert np.array_equal((y != 0)[pos], (y2 != 0)[pos]), "mask independent of the data"
+    # rows [r0, r1) evaluated on their own with first_row = r0: those rows of the whole call
+    for r0, r1 in ((0, 5), (17, 40), (63, 64)):
+        part = oracle.ln_relu_dropout(x[r0:r1], g, b, p=p, seed=seed, offset=offset, first_row=r0, lib=lib)
+        assert np.array_equal(part, y[r0:r1]), f"rows {r0}..{r1} evaluated with first_row"
     for s2, o2 in ((seed, offset + 1), (seed + 1, offset)):
         y3 = oracle.ln_relu_dropout(x, g, b, p=p, seed=s2, offset=o2, lib=lib)
         agree = ((y3 != 0) == (y != 0))[relu_ln > 0].mean()

@@ -63,6 +63,8 @@ MUTANTS = [
     ("LN SEQ3: u not rounded", "if (seq3) uv = rstore(dtype, uv);", ""),
     ("LN SEQ3: residual sum not rounded", "if (seq || seq3) xv = rstore(dtype, xv);",
      "if (seq) xv = rstore(dtype, xv);"),
+    ("dropout: first_row ignored", "dropout_bits(seed, offset, (uint64_t)(first_row * cols + k));",
+     "dropout_bits(seed, offset, (uint64_t)k);"),
     ("dropout SEQ3: output not rounded", "if (seq3) v = rstore(dtype, v);", ""),
     ("dropout SEQ3: scale kept in binary64", "const double sc = seq3 ? r32(scale) : scale;",
      "const double sc = scale;"),
