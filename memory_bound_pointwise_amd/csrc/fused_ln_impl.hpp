@@ -534,7 +534,6 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
   auto low = [](int n) -> uint32_t { return n <= 0 ? 0u : (1u << n) - 1u; };
   const uint32_t in0 = (low(min(V, s + cols)) & ~low(s)) | (fold ? low(cols - (V * nvec - s)) : 0u);
   const uint32_t inl = nvec == 1 ? in0 : low(min(V, cols - V * (nvec - 1) + s));
-  const int n0 = V - __builtin_popcount(in0), nl = V - __builtin_popcount(inl);
   // the same as masks of the packed words (all ones: inside)
   uint32_t mk0[4], mkl[4];
 #pragma unroll
@@ -756,18 +755,19 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       const int j = jr[k];
+      // elements outside the row (relative slots 0 and nvec - 1, which sit in
+      // rounds 0 and klast) add nothing to the centred sum of squares: their
+      // deviation is set to 0 rather than (0 - mean)^2 taken out again, which
+      // in fp32 would cancel badly for rows far from 0
+      const bool edge = k == 0 || k == klast;
+      const uint32_t inb = !edge ? ~0u : (j == 0 ? in0 : ~0u) & (j == nvec - 1 ? inl : ~0u);
       Acc part = 0;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        const Acc dv = (Acc)v[k][e] - mean;
+        Acc dv = (Acc)v[k][e] - mean;
+        if (edge) dv = ((inb >> e) & 1u) ? dv : (Acc)0;
         if constexpr (kInPlace) v[k][e] = dv;
         part = fma_t(dv, dv, part);
-      }
-      if (k == 0 || k == klast) {
-        // a zeroed element contributed (0 - mean)^2 to this slot's
-        // eight-term partial; take it out again
-        const int nout = (j == 0 ? n0 : 0) + (j == nvec - 1 && j != 0 ? nl : 0);
-        part -= (Acc)nout * (mean * mean);
       }
       if (used[k]) m2 += part;
     }

@@ -8,7 +8,9 @@ Gates (fused kernels against the oracle's binary64 result):
 * bf16 row kernels: |y - exact| <= max(2e-2, half a bf16 ulp of exact);
 * 16-bit outputs of the two-dimensional forms (binary64 inside, one rounding
   at the store): at most 1 ulp, on the ordered bit line, from the exact result
-  rounded once to the format by the oracle.
+  rounded once to the format by the oracle;
+* fp32 softmax: relative to the exact probability, with a bound derived from
+  the kernel's fp32 arithmetic and the row's input range (check_softmax_f32).
 The half-ulp term only matters where no output of the storage type can be
 within 1e-5 (|exact| >= 256 in fp32) or 2e-2 (|exact| >= 8 in bf16) of the
 exact value; those elements are counted and reported.
@@ -104,6 +106,37 @@ def check_ulp16(bits, exact, fmt, what=""):
     d = np.where(nan_e, 0, np.abs(ordered16(bits) - ordered16(want)))
     assert d.max(initial=0) <= 1, f"{what}: max {d.max()} ulp at {np.unravel_index(np.argmax(d), d.shape)}"
     return int(d.max(initial=0)), int((d > 0).sum())
+
+
+def check_softmax_f32(y, exact, x, what=""):
+    """fp32 softmax: |y - e| <= (192 + 8 R) 2^-24 e + 2^-125 per element, R the
+    range (max - min) of the row's finite inputs.  The kernel's output is
+    exp2((x - m_lane) log2e) * (exp2((m_lane - m) log2e) / l) in fp32: rounding
+    the difference and its product with log2e moves each exponential by at
+    most 3 2^-24 times its argument, and along any term's chain of rescalings
+    the arguments add up to m - x <= R (6 R for the element and for l
+    together); each v_exp_f32 adds 2 ulp, the per-lane sum at most 64
+    roundings, the (at most 21) merges 4 each, the divide and the product 2.
+    Subnormal results may flush: the 2^-125 floor.  Returns the largest error
+    in units of 2^-24 e and the largest error / bound."""
+    yh = np.asarray(y, np.float64)
+    x = np.asarray(x, np.float64)
+    assert yh.shape == exact.shape == x.shape
+    nan_e = np.isnan(exact)
+    assert (np.isnan(yh) == nan_e).all(), f"{what}: NaN mismatch"
+    fin = np.where(np.isfinite(x), x, np.nan)
+    with np.errstate(all="ignore"):
+        rng_ = np.nanmax(fin, axis=1, keepdims=True) - np.nanmin(fin, axis=1, keepdims=True)
+    rng_ = np.where(np.isnan(rng_), 0.0, rng_)
+    u = 2.0 ** -24
+    err = np.where(nan_e, 0.0, np.abs(yh - exact))
+    bound = (192.0 + 8.0 * rng_) * u * np.abs(np.where(nan_e, 0.0, exact)) + 2.0 ** -125
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements over the gate, first at "
+                           f"{np.argwhere(bad)[:3].tolist()}: err {err[bad][:3]}, bound {bound[bad][:3]}")
+    with np.errstate(all="ignore"):
+        rel = np.where(exact > 0, err / (u * np.abs(exact)), 0.0)
+    return float(np.nanmax(rel, initial=0.0)), float(np.max(err / bound, initial=0.0))
 
 
 def sample_rows(rows, k=48, seed=7):
