@@ -326,7 +326,20 @@ def main():
     # step, not in `value`
     nxt = {}
     if not args.only and not args.no_next:
+        def padded(a, ld):
+            """a [rows, cols] view of a device copy of `a` inside rows of ld elements"""
+            t = to_dev(a)
+            buf = torch.zeros((t.shape[0], ld), dtype=t.dtype, device=dev)
+            v = buf[:, :t.shape[1]]
+            v.copy_(t)
+            return v
+
         def build_next(w, d):
+            if w.kind == "layernorm2d":
+                ld = w.params["ld"]
+                x, r, y = padded(d["x"], ld), padded(d["residual"], ld), padded(np.zeros_like(d["x"]), ld)
+                g, b = to_dev(d["gamma"]), to_dev(d["beta"])
+                return lambda: mbp.fused_add_layernorm_gelu(x, r, g, b, w.params["eps"], w.act, out=y)
             if w.kind == "ln_relu_dropout":
                 x, g, b = (to_dev(d[k]) for k in ("x", "gamma", "beta"))
                 y = torch.empty_like(x)

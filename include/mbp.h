@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MBP_ABI_VERSION 4
+#define MBP_ABI_VERSION 5
 
 /* Largest row length (cols) the row kernels accept: one row lives in registers. */
 #define MBP_MAX_COLS 16384
@@ -207,6 +207,46 @@ mbp_status fused_row_mean_epilogue_2d(mbp_dtype dtype, const void* x, int64_t ld
                                       const void* bias, const void* gamma, const void* beta,
                                       void* y, int64_t ldy, int64_t rows, int64_t cols,
                                       double alpha, double c, void* stream);
+
+/*
+ * fused_add_layernorm_gelu with row strides: row i of x starts at element
+ * i*ldx, of the residual at i*ldr, of y at i*ldy (unit stride along a row),
+ * so padded or sliced activations (x[:, :cols] of a wider buffer) are read
+ * and written in place, without the hidden .contiguous() copy [P1] section
+ * 6.2 warns about.  dtype MBP_F32 or MBP_BF16; gamma, beta: dense [cols].
+ * residual may be NULL (ldr ignored).  ldx and ldr: 0 (one row used for
+ * every row) or >= cols; ldy >= cols (any value when rows == 1).  y may be
+ * exactly x (y == x, ldy == ldx) or exactly the residual; any other overlap
+ * of y's extent with an input's returns MBP_ERR_OVERLAP.  Results equal
+ * those of fused_add_layernorm_gelu on the same rows bit for bit.  The
+ * fastest paths need rows on 16-byte boundaries (16-byte aligned bases and
+ * strides of whole 16-byte vectors), or x, residual and y sharing one stride
+ * and one alignment modulo 16 bytes.
+ */
+mbp_status fused_add_layernorm_gelu_2d(mbp_dtype dtype, const void* x, int64_t ldx, const void* residual,
+                                       int64_t ldr, const void* gamma, const void* beta, void* y,
+                                       int64_t ldy, int64_t rows, int64_t cols, double eps, mbp_act act,
+                                       void* stream);
+
+/*
+ * fused_layernorm_relu_dropout with row strides ldx and ldy (as above; y may
+ * be exactly x).  The dropout mask still follows the element's position in
+ * the [rows, cols] result, k = i*cols + j, not its address, so it is the
+ * dense call's mask.
+ */
+mbp_status fused_layernorm_relu_dropout_2d(mbp_dtype dtype, const void* x, int64_t ldx, const void* gamma,
+                                           const void* beta, void* y, int64_t ldy, int64_t rows, int64_t cols,
+                                           double eps, double p, uint64_t seed, uint64_t offset,
+                                           void* stream);
+
+/*
+ * fused_softmax with row strides ldx (0 or >= cols) and ldy (>= cols);
+ * fp32, bf16 or fp16; y may be exactly x.  Rows of x and y that agree
+ * modulo 16 bytes (equal alignment and strides that differ by a multiple of
+ * 16 bytes) keep the 16-byte window path.
+ */
+mbp_status fused_softmax_2d(mbp_dtype dtype, const void* x, int64_t ldx, void* y, int64_t ldy,
+                            int64_t rows, int64_t cols, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Unfused "before" variants: one launch per op, every intermediate written to

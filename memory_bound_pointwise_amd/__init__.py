@@ -38,6 +38,9 @@ SIGNATURES = [
     ("fused_row_mean_epilogue", _I, [_P, _P, _P, _P, _P, _I64, _I64, _D, _D, _P]),
     ("fused_add_layernorm_gelu", _I, [_I, _P, _P, _P, _P, _P, _I64, _I64, _D, _I, _P]),
     ("fused_softmax", _I, [_I, _P, _P, _I64, _I64, _P]),
+    ("fused_softmax_2d", _I, [_I, _P, _I64, _P, _I64, _I64, _I64, _P]),
+    ("fused_add_layernorm_gelu_2d", _I, [_I, _P, _I64, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _D, _I, _P]),
+    ("fused_layernorm_relu_dropout_2d", _I, [_I, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _D, _D, _U64, _U64, _P]),
     ("fused_layernorm_relu_dropout", _I, [_I, _P, _P, _P, _P, _I64, _I64, _D, _D, _U64, _U64, _P]),
     ("unfused_layernorm_relu_dropout", _I, [_I, _P, _P, _P, _P, _I64, _I64, _D, _D, _U64, _U64, _P, _SZ, _P]),
     ("unfused_softmax", _I, [_I, _P, _P, _I64, _I64, _P, _SZ, _P]),
@@ -99,7 +102,9 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _check(t, name, dtypes, device=None):
+def _check(t, name, dtypes, device=None, strided=False):
+    """type, device and dtype checks; dense unless `strided` (then any tensor
+    _row_view accepts)"""
     if t is None:
         return
     if not isinstance(t, torch.Tensor):
@@ -110,7 +115,7 @@ def _check(t, name, dtypes, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
-    if not t.is_contiguous():
+    if not strided and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
@@ -132,6 +137,35 @@ def _rows_cols(x):
     cols = x.shape[-1]
     rows = x.numel() // cols if cols else 0
     return rows, cols
+
+
+def _row_view(t, name):
+    """(rows, cols, ld) of a tensor seen as [rows, cols] rows of its last
+    dimension: the last dimension must be contiguous and the leading ones must
+    collapse to one row stride ld (elements; 0 for a row expanded over the
+    others).  A dense tensor has ld == cols."""
+    if t.dim() < 1:
+        raise ValueError(f"{name} must have at least one dimension")
+    rows, cols = _rows_cols(t)
+    if cols > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the elements of a row must be contiguous (last stride 1)")
+    if t.dim() == 1 or rows <= 1:
+        return rows, cols, cols
+    sizes, strides = t.shape[:-1], t.stride()[:-1]
+    ld = None
+    for i in range(len(sizes) - 1, -1, -1):  # innermost leading dimension first
+        if sizes[i] == 1:
+            continue
+        if ld is None:
+            ld = strides[i]
+            span = ld * sizes[i]
+        elif strides[i] != span:
+            raise ValueError(f"{name}: the leading dimensions do not collapse to one row stride")
+        else:
+            span *= sizes[i]
+    if ld != 0 and ld < cols:
+        raise ValueError(f"{name}: rows overlap (row stride {ld} < {cols})")
+    return rows, cols, ld
 
 
 # ------------------------------------------------------------------ fused
@@ -170,22 +204,35 @@ def fused_add_layernorm_gelu(x, residual, gamma, beta, eps=1e-5, act="gelu_tanh"
     """gelu_tanh(LayerNorm(x + residual) * gamma + beta) over the last dimension.
 
     fp32 or bf16 (all tensors one dtype); residual may be None; act "none"
-    gives plain LayerNorm."""
+    gives plain LayerNorm.  x, residual and out may be strided views whose
+    rows are contiguous (e.g. x[:, :cols] of a wider buffer, or an expanded
+    residual row): they are read and written in place through the row
+    strides, never copied."""
     dts = (torch.float32, torch.bfloat16)
-    _check(x, "x", dts)
-    for t, n in ((residual, "residual"), (gamma, "gamma"), (beta, "beta"), (out, "out")):
+    _check(x, "x", dts, strided=True)
+    for t, n in ((residual, "residual"), (out, "out")):
+        _check(t, n, (x.dtype,), x.device, strided=True)
+    for t, n in ((gamma, "gamma"), (beta, "beta")):
         _check(t, n, (x.dtype,), x.device)
-    rows, cols = _rows_cols(x)
-    if residual is not None and residual.shape != x.shape:
-        raise ValueError("residual must have x's shape")
+    rows, cols, ldx = _row_view(x, "x")
+    ldr = cols
+    if residual is not None:
+        if residual.shape != x.shape:
+            raise ValueError("residual must have x's shape")
+        ldr = _row_view(residual, "residual")[2]
     for t, n in ((gamma, "gamma"), (beta, "beta")):
         if t.numel() != cols:
             raise ValueError(f"{n} must have {cols} elements")
-    y = torch.empty_like(x) if out is None else out
+    y = torch.empty(x.shape, dtype=x.dtype, device=x.device) if out is None else out
     if y.shape != x.shape:
         raise ValueError("out has the wrong shape")
-    _call("fused_add_layernorm_gelu", _dtype_code(x), _ptr(x), _ptr(residual), _ptr(gamma),
-          _ptr(beta), _ptr(y), rows, cols, float(eps), _act_code(act), _stream(x))
+    ldy = _row_view(y, "out")[2]
+    if ldx == ldr == ldy == cols:
+        _call("fused_add_layernorm_gelu", _dtype_code(x), _ptr(x), _ptr(residual), _ptr(gamma),
+              _ptr(beta), _ptr(y), rows, cols, float(eps), _act_code(act), _stream(x))
+    else:
+        _call("fused_add_layernorm_gelu_2d", _dtype_code(x), _ptr(x), ldx, _ptr(residual), ldr, _ptr(gamma),
+              _ptr(beta), _ptr(y), ldy, rows, cols, float(eps), _act_code(act), _stream(x))
     return y
 
 
@@ -212,11 +259,29 @@ def _ln_drop_args(x, gamma, beta, out):
 def fused_layernorm_relu_dropout(x, gamma, beta, p=0.1, seed=0, offset=0, eps=1e-5, out=None):
     """dropout(relu(LayerNorm(x) * gamma + beta), p) over the last dimension,
     training semantics, one launch.  The mask is a function of (seed, offset,
-    element index): Philox4x32-10, 16 bits per element."""
-    rows, cols, y = _ln_drop_args(x, gamma, beta, out)
-    _call("fused_layernorm_relu_dropout", _dtype_code(x), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y),
-          rows, cols, float(eps), float(p), int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1),
-          _stream(x))
+    element index): Philox4x32-10, 16 bits per element.  x and out may be
+    strided views whose rows are contiguous (the mask follows the element's
+    position in the result, not its address)."""
+    dts = (torch.float32, torch.bfloat16)
+    _check(x, "x", dts, strided=True)
+    _check(out, "out", (x.dtype,), x.device, strided=True)
+    for t, n in ((gamma, "gamma"), (beta, "beta")):
+        _check(t, n, (x.dtype,), x.device)
+    rows, cols, ldx = _row_view(x, "x")
+    for t, n in ((gamma, "gamma"), (beta, "beta")):
+        if t.numel() != cols:
+            raise ValueError(f"{n} must have {cols} elements")
+    y = torch.empty(x.shape, dtype=x.dtype, device=x.device) if out is None else out
+    if y.shape != x.shape:
+        raise ValueError("out has the wrong shape")
+    ldy = _row_view(y, "out")[2]
+    seed, offset = int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1)
+    if ldx == ldy == cols:
+        _call("fused_layernorm_relu_dropout", _dtype_code(x), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y),
+              rows, cols, float(eps), float(p), seed, offset, _stream(x))
+    else:
+        _call("fused_layernorm_relu_dropout_2d", _dtype_code(x), _ptr(x), ldx, _ptr(gamma), _ptr(beta), _ptr(y),
+              ldy, rows, cols, float(eps), float(p), seed, offset, _stream(x))
     return y
 
 
@@ -309,18 +374,23 @@ def fused_row_mean_epilogue_2d(x, bias, gamma, beta, alpha=1.1, c=0.1, out=None)
 
 
 def fused_softmax(x, out=None):
-    """Row softmax over the last dimension (fp32, bf16 or fp16; one launch)."""
+    """Row softmax over the last dimension (fp32, bf16 or fp16; one launch).
+    x and out may be strided views whose rows are contiguous."""
     if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
         raise ValueError("x must be a GPU tensor")
     if x.dtype not in _DTYPES_2D:
         raise TypeError(f"unsupported dtype {x.dtype}")
-    _check(x, "x", (x.dtype,))
-    _check(out, "out", (x.dtype,), x.device)
-    rows, cols = _rows_cols(x)
-    y = torch.empty_like(x) if out is None else out
+    _check(x, "x", (x.dtype,), strided=True)
+    _check(out, "out", (x.dtype,), x.device, strided=True)
+    rows, cols, ldx = _row_view(x, "x")
+    y = torch.empty(x.shape, dtype=x.dtype, device=x.device) if out is None else out
     if y.shape != x.shape:
         raise ValueError("out has the wrong shape")
-    _call("fused_softmax", _DTYPES_2D[x.dtype], _ptr(x), _ptr(y), rows, cols, _stream(x))
+    ldy = _row_view(y, "out")[2]
+    if ldx == ldy == cols:
+        _call("fused_softmax", _DTYPES_2D[x.dtype], _ptr(x), _ptr(y), rows, cols, _stream(x))
+    else:
+        _call("fused_softmax_2d", _DTYPES_2D[x.dtype], _ptr(x), ldx, _ptr(y), ldy, rows, cols, _stream(x))
     return y
 
 

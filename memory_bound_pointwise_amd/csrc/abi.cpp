@@ -393,7 +393,52 @@ mbp_status fused_softmax(mbp_dtype dtype, const void* x, void* y, int64_t rows, 
   mbp_status st = check_2d(dtype, {{x, cols}}, y, cols, rows, cols, MBP_MAX_COLS, x);
   if (st != MBP_OK) return st;
   if (rows == 0) return ok();
-  return from_hip(mbp::launch_softmax(dtype, x, y, rows, cols, as_stream(stream)), "fused_softmax");
+  return from_hip(mbp::launch_softmax(dtype, x, cols, y, cols, rows, cols, as_stream(stream)), "fused_softmax");
+}
+
+mbp_status fused_softmax_2d(mbp_dtype dtype, const void* x, int64_t ldx, void* y, int64_t ldy,
+                            int64_t rows, int64_t cols, void* stream) {
+  mbp_status st = check_2d(dtype, {{x, ldx}}, y, ldy, rows, cols, MBP_MAX_COLS, x);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  return from_hip(mbp::launch_softmax(dtype, x, ldx, y, ldy, rows, cols, as_stream(stream)), "fused_softmax_2d");
+}
+
+mbp_status fused_add_layernorm_gelu_2d(mbp_dtype dtype, const void* x, int64_t ldx, const void* residual,
+                                       int64_t ldr, const void* gamma, const void* beta, void* y,
+                                       int64_t ldy, int64_t rows, int64_t cols, double eps, mbp_act act,
+                                       void* stream) {
+  if (dtype != MBP_F32 && dtype != MBP_BF16) return fail(MBP_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (act != MBP_ACT_NONE && act != MBP_ACT_GELU_TANH) return fail(MBP_ERR_DTYPE, "unknown act %d", (int)act);
+  if (!std::isfinite(eps) || eps < 0) return fail(MBP_ERR_ARG, "eps must be finite and >= 0");
+  // y may be exactly x or exactly the residual (same pointer, same stride)
+  const void* inplace = y == x ? x : (residual && y == residual ? residual : nullptr);
+  mbp_status st = residual ? check_2d(dtype, {{x, ldx}, {residual, ldr}, {gamma, 0}, {beta, 0}}, y, ldy, rows,
+                                      cols, MBP_MAX_COLS, inplace)
+                           : check_2d(dtype, {{x, ldx}, {gamma, 0}, {beta, 0}}, y, ldy, rows, cols,
+                                      MBP_MAX_COLS, inplace);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  return from_hip(mbp::launch_layernorm_2d(dtype, x, ldx, residual, ldr, gamma, beta, y, ldy, rows, cols, eps,
+                                           act, nullptr, as_stream(stream)),
+                  "fused_add_layernorm_gelu_2d");
+}
+
+mbp_status fused_layernorm_relu_dropout_2d(mbp_dtype dtype, const void* x, int64_t ldx, const void* gamma,
+                                           const void* beta, void* y, int64_t ldy, int64_t rows, int64_t cols,
+                                           double eps, double p, uint64_t seed, uint64_t offset,
+                                           void* stream) {
+  if (dtype != MBP_F32 && dtype != MBP_BF16) return fail(MBP_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (!std::isfinite(eps) || eps < 0) return fail(MBP_ERR_ARG, "eps must be finite and >= 0");
+  mbp_status st = check_dropout_p(p);
+  if (st != MBP_OK) return st;
+  st = check_2d(dtype, {{x, ldx}, {gamma, 0}, {beta, 0}}, y, ldy, rows, cols, MBP_MAX_COLS, x);
+  if (st != MBP_OK) return st;
+  if (rows == 0) return ok();
+  const mbp::Drop d = make_drop(p, seed, offset);
+  return from_hip(mbp::launch_layernorm_2d(dtype, x, ldx, nullptr, 0, gamma, beta, y, ldy, rows, cols, eps,
+                                           mbp::kEpiReluDrop, &d, as_stream(stream)),
+                  "fused_layernorm_relu_dropout_2d");
 }
 
 mbp_status fused_layernorm_relu_dropout(mbp_dtype dtype, const void* x, const void* gamma,

@@ -162,7 +162,8 @@ template <class IO, int LANES, int VPL, bool RES, int EPI>
 __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
     const typename IO::elem* x, const typename IO::elem* res,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
-    typename IO::elem* y, int64_t rows, int cols, double eps_d, Drop drop) {
+    typename IO::elem* y, int64_t rows, int cols, int64_t ldx, int64_t ldr, int64_t ldy, double eps_d,
+    Drop drop) {
   typedef typename Types<IO, RES>::acc Acc;
   typedef typename Types<IO, RES>::val Val;
   constexpr int V = IO::kVec;
@@ -235,9 +236,9 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
     // past the row's last vector reads that vector and is left out of the
     // sums.  Every load is in bounds and none needs a branch or a zero fill.
     const int64_t lrow = live ? row : rows - 1;
-    const typename IO::elem* xr = x + lrow * (int64_t)cols;
-    const typename IO::elem* rr = RES ? res + lrow * (int64_t)cols : nullptr;
-    typename IO::elem* yr = y + row * (int64_t)cols;
+    const typename IO::elem* xr = x + lrow * ldx;
+    const typename IO::elem* rr = RES ? res + lrow * ldr : nullptr;
+    typename IO::elem* yr = y + row * ldy;
 
     // issue every load of the row first
     u32x4 xv[VPL], rv[VPL];
@@ -385,10 +386,11 @@ __device__ __forceinline__ u32x4 funnel(const u32x4& lo, const uint32_t* hi, int
 
 // Rows off 16-byte boundaries whose x, residual and y share one alignment
 // (the usual case: e.g. bf16 rows of 4095 elements in freshly allocated
-// tensors).  The byte offset of row r in its line, (base + r * row_bytes) mod
-// line, with line = 128 bytes when the three tensors agree modulo 128 (else
-// 16), repeats with period P = line / gcd(line, row_bytes) rows; the rows with
-// one offset form a class.  A block serves one class, so the offset is
+// tensors, or rows of one padded buffer: the three share one row stride).
+// The byte offset of row r in its line, (base + r * pitch) mod line (pitch:
+// the row stride in bytes), with line = 128 bytes when the three tensors agree
+// modulo 128 (else 16), repeats with period P = line / gcd(line, pitch) rows;
+// the rows with one offset form a class.  A block serves one class, so the offset is
 // uniform over the block: d whole windows and s elements past the line.  The
 // row is processed directly in window space: relative slot j holds window j of
 // the row, element e of it being column V*j + e - s, and relative slot j sits
@@ -402,9 +404,9 @@ __device__ __forceinline__ u32x4 funnel(const u32x4& lo, const uint32_t* hi, int
 // elements) is moved into the unused head of relative slot 0 (whose first s
 // elements belong to the previous row), so VPL is the same as for aligned
 // rows.  Only relative slots 0 and nvec - 1 hold elements outside the row:
-// they are zeroed in the packed inputs, their (0 - mean)^2 terms are taken out of the variance
-// sum again, and their windows (and the folded one) are stored element by
-// element.
+// they are zeroed in the packed inputs, their deviations are set to 0 before
+// the variance sum, and their windows (and the folded one) are stored element
+// by element.
 //
 // The host passes [r_lo, r_hi), the rows whose windows lie inside the
 // tensors; the rest (at most the first and last few rows: rows starting
@@ -423,8 +425,8 @@ template <class IO, int LANES, int VPL, bool RES, int EPI>
 __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_eu(class_min_waves(LANES, VPL, (int)sizeof(typename IO::elem), EPI)))) void ln_class_kernel(
     const typename IO::elem* x, const typename IO::elem* res,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
-    typename IO::elem* y, int64_t rows, int cols, double eps_d, int period, int line, int64_t r_lo,
-    int64_t r_hi, int edge_blocks, Drop drop) {
+    typename IO::elem* y, int64_t rows, int cols, int64_t ld, double eps_d, int period, int line,
+    int64_t r_lo, int64_t r_hi, int edge_blocks, Drop drop) {
   typedef typename IO::elem E;
   typedef typename Types<IO, RES>::acc Acc;
   typedef typename Types<IO, RES>::val Val;
@@ -462,7 +464,7 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
     const int64_t n_edge = r_lo + (rows - r_hi);
     const bool live = i < n_edge;
     const int64_t row = !live ? 0 : (i < r_lo ? i : r_hi + (i - r_lo));
-    const int64_t e0 = row * (int64_t)cols;
+    const int64_t e0 = row * ld;  // the row in memory (x, residual and y share the row stride)
     auto val = [&](int c) -> Val {
       Val t = (Val)IO::load1(x, e0 + c);
       if constexpr (RES) t += (Val)IO::load1(res, e0 + c);
@@ -480,7 +482,7 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
     if (live)
       for (int c = lane; c < cols; c += LANES) {
         float o = finish<Acc, EPI>((Acc)val(c) - mean, rstd, (Acc)IO::load1(gamma, c), (Acc)IO::load1(beta, c));
-        if constexpr (EPI == kEpiReluDrop) relu_dropout<1, true>(&o, (uint64_t)(e0 + c), drop);
+        if constexpr (EPI == kEpiReluDrop) relu_dropout<1, true>(&o, (uint64_t)(row * cols + c), drop);
         IO::store1(y, e0 + c, o);
       }
     return;
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
   const int mb = (int)(reinterpret_cast<uintptr_t>(x) & 15);
   // the class's byte offset in its line (line = 128 or 16 bytes): window
   // offset d, byte offset sb in that window
-  const int sl = (int)((reinterpret_cast<uintptr_t>(x) + (uint64_t)((int64_t)ES * first * cols)) & (unsigned)(line - 1));
+  const int sl = (int)((reinterpret_cast<uintptr_t>(x) + (uint64_t)((int64_t)ES * first * ld)) & (unsigned)(line - 1));
   const int d = sl >> 4;
   const int sb = sl & 15;
   const int s = sb / ES;
@@ -674,7 +676,7 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
     }
     const int64_t row = first + (int64_t)period * (grp * RPB + sub);
     const bool live = row <= last_row;
-    const int64_t e0 = (live ? row : last_row) * (int64_t)cols;
+    const int64_t e0 = (live ? row : last_row) * ld;  // memory offset of the row
     const int64_t q0 = (mb + (int64_t)ES * e0) >> 4;
 
     // every window of the row lies inside the tensors (rows in [r_lo, r_hi))
@@ -755,19 +757,29 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       const int j = jr[k];
+      Acc dv[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) dv[e] = (Acc)v[k][e] - mean;
       // elements outside the row (relative slots 0 and nvec - 1, which sit in
       // rounds 0 and klast) add nothing to the centred sum of squares: their
       // deviation is set to 0 rather than (0 - mean)^2 taken out again, which
-      // in fp32 would cancel badly for rows far from 0
-      const bool edge = k == 0 || k == klast;
-      const uint32_t inb = !edge ? ~0u : (j == 0 ? in0 : ~0u) & (j == nvec - 1 ? inl : ~0u);
+      // in fp32 would cancel badly for rows far from 0.  Only the one or two
+      // lanes holding those slots need it: with fp32 statistics a wave-uniform
+      // branch skips the selects in every other wave (16384 x 4095 bf16: -0.9%,
+      // with dropout at 8191: -5.2%); with binary64 statistics the selects cost
+      // nothing measurable and the branch cost 17% (8192 x 4093 fp32).
+      if (k == 0 || k == klast) {
+        const uint32_t inb = (j == 0 ? in0 : ~0u) & (j == nvec - 1 ? inl : ~0u);
+        if (sizeof(Acc) == 8 || __builtin_amdgcn_ballot_w64(inb != ~0u) != 0) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) dv[e] = ((inb >> e) & 1u) ? dv[e] : (Acc)0;
+        }
+      }
       Acc part = 0;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        Acc dv = (Acc)v[k][e] - mean;
-        if (edge) dv = ((inb >> e) & 1u) ? dv : (Acc)0;
-        if constexpr (kInPlace) v[k][e] = dv;
-        part = fma_t(dv, dv, part);
+        if constexpr (kInPlace) v[k][e] = dv[e];
+        part = fma_t(dv[e], dv[e], part);
       }
       if (used[k]) m2 += part;
     }
@@ -776,7 +788,7 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
 
     if (!live) continue;
     u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(y) - mb) + q0;
-    E* yrow = y + row * (int64_t)cols;
+    E* yrow = y + row * ld;
     // fp32: element stores of the windows shared with a neighbouring row go
     // through a volatile pointer; otherwise the compiler sinks the last one
     // into a common tail with the whole-window store, which then splits into
@@ -926,7 +938,8 @@ template <class IO, int LANES, int VPL, bool RES, int EPI>
 __global__ __launch_bounds__(block_for(LANES)) void ln_shift_kernel(
     const typename IO::elem* x, const typename IO::elem* res,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
-    typename IO::elem* y, int64_t rows, int cols, double eps_d, Drop drop) {
+    typename IO::elem* y, int64_t rows, int cols, int64_t ldx, int64_t ldr, int64_t ldy, double eps_d,
+    Drop drop) {
   typedef typename IO::elem E;
   typedef typename Types<IO, RES>::acc Acc;
   typedef typename Types<IO, RES>::val Val;
@@ -944,10 +957,10 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_shift_kernel(
   const int nvec = (cols + V - 1) / V;  // the last vector may be partial
   const int rem = cols - V * (nvec - 1);  // its elements inside the row (1 .. V)
   const Acc eps = (Acc)eps_d;
-  const int64_t total = rows * (int64_t)cols;
-  const Win wx = make_win<IO>(x, total);
-  const Win wr = RES ? make_win<IO>(res, total) : wx;
-  const Win wy = make_win<IO>(y, total);
+  // each tensor's extent: its last row ends (rows - 1) * ld + cols elements in
+  const Win wx = make_win<IO>(x, (rows - 1) * ldx + cols);
+  const Win wr = RES ? make_win<IO>(res, (rows - 1) * ldr + cols) : wx;
+  const Win wy = make_win<IO>(y, (rows - 1) * ldy + cols);
   auto slot = [&](int k) -> int {
     return LANES >= 64 ? (lane / 64) * 64 * VPL + k * 64 + wl : k * LANES + lane;
   };
@@ -979,12 +992,13 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_shift_kernel(
     }
     const int64_t row = grp * RPB + sub;
     const bool live = row < rows;
-    const int64_t e0 = (live ? row : rows - 1) * (int64_t)cols;
+    const int64_t lrow = live ? row : rows - 1;
+    const int64_t ex = lrow * ldx, er = lrow * ldr;  // the row in x and in the residual
 
     // row vectors of x and residual
     u32x4 xa[VPL], ra[VPL];
     {
-      const int64_t offx = wx.mb + (int64_t)ES * e0, offr = wr.mb + (int64_t)ES * e0;
+      const int64_t offx = wx.mb + (int64_t)ES * ex, offr = wr.mb + (int64_t)ES * er;
       const int64_t qx = offx >> 4, qr = offr >> 4;
       const int nvx = (int)(((offx & 15) + (int64_t)ES * cols + 15) >> 4);
       const int nvr = (int)(((offr & 15) + (int64_t)ES * cols + 15) >> 4);
@@ -1018,8 +1032,8 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_shift_kernel(
 #pragma unroll
           for (int e = 0; e < V; ++e)
             if (e < lim) {
-              set_elem<IO>(xa[k], e, x[e0 + V * slot(k) + e]);
-              if constexpr (RES) set_elem<IO>(ra[k], e, res[e0 + V * slot(k) + e]);
+              set_elem<IO>(xa[k], e, x[ex + V * slot(k) + e]);
+              if constexpr (RES) set_elem<IO>(ra[k], e, res[er + V * slot(k) + e]);
             }
         }
       }
@@ -1090,11 +1104,11 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_shift_kernel(
     // j-1 only where that vector is known here (not in the first slot of a
     // wave or group), and the slot after the last one (k == VPL, lane 0 of
     // the wave or group) writes the bytes of the last slot's vector.
-    const int64_t offy = wy.mb + (int64_t)ES * (row * (int64_t)cols);
+    const int64_t offy = wy.mb + (int64_t)ES * (row * ldy);
     const int sb = (int)(offy & 15);
     const int nvy = (int)((sb + (int64_t)ES * cols + 15) >> 4);
     u32x4* dy = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(y) - wy.mb) + (offy >> 4);
-    E* yrow = y + row * (int64_t)cols;
+    E* yrow = y + row * ldy;
     const int rbytes = ES * cols;
     // window of each round (k == VPL: the slot after the last)
     u32x4 win[VPL + 1];
@@ -1188,12 +1202,15 @@ constexpr int64_t kShiftGroups = 4;
 constexpr int64_t kClassGroups = 4;
 
 template <class IO, bool RES, int EPI>
-hipError_t launch_flags(const void* x, const void* res, const void* gamma, const void* beta,
-                        void* y, int64_t rows, int64_t cols, double eps, const Drop& drop_in,
-                        hipStream_t s) {
+hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr, const void* gamma,
+                        const void* beta, void* y, int64_t ldy, int64_t rows, int64_t cols, double eps,
+                        const Drop& drop_in, hipStream_t s) {
   constexpr int V = IO::kVec;
+  constexpr int64_t ES = (int64_t)sizeof(typename IO::elem);
+  // rows on 16-byte boundaries: aligned bases and row strides of whole 16-byte vectors
   const bool aligned = aligned16(x) && aligned16(y) && (!res || aligned16(res)) && aligned16(gamma) &&
-                       aligned16(beta) && cols % V == 0;
+                       aligned16(beta) && cols % V == 0 && (ES * ldx) % 16 == 0 && (ES * ldy) % 16 == 0 &&
+                       (!res || (ES * ldr) % 16 == 0);
   const int i = pick_shape((cols + V - 1) / V);
   if (i < 0) return hipErrorInvalidValue;
   const int lanes = kShapes[i].lanes;
@@ -1203,7 +1220,7 @@ hipError_t launch_flags(const void* x, const void* res, const void* gamma, const
   const int grid = (int)(groups < kMaxGrid ? groups : kMaxGrid);  // one block per row group
   int icols = (int)cols;
   Drop drop = drop_in;
-  void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &eps, &drop};
+  void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &ldx, &ldr, &ldy, &eps, &drop};
   if (aligned) {
     const void* k = shape_kernel<VecSel<IO, RES, EPI>::template K>(i);
     // fp32 rows, when there are thousands of row groups: two per block
@@ -1214,18 +1231,22 @@ hipError_t launch_flags(const void* x, const void* res, const void* gamma, const
     return hipLaunchKernel(k, dim3(vgrid), dim3(block), args, 0, s);
   }
   const uintptr_t ax = reinterpret_cast<uintptr_t>(x);
+  // x, residual and y agree modulo 16 bytes in every row: congruent bases and
+  // one row stride
   const bool congruent = ((ax ^ reinterpret_cast<uintptr_t>(y)) & 15) == 0 &&
-                         (!res || ((ax ^ reinterpret_cast<uintptr_t>(res)) & 15) == 0);
+                         (!res || ((ax ^ reinterpret_cast<uintptr_t>(res)) & 15) == 0) && ldx > 0 &&
+                         ldy == ldx && (!res || ldr == ldx);
   if (congruent) {
-    // Rows whose windows lie inside the tensors: [r_lo, r_hi).  A row
-    // starting fewer than 16 - (x mod 16) bytes past an unaligned start, or
-    // ending fewer than (end mod 16) bytes before an unaligned end, has a
-    // window that reaches outside.
-    const int64_t rb = (int64_t)sizeof(typename IO::elem) * cols;
+    // Rows whose windows lie inside the tensors: [r_lo, r_hi).  With the row
+    // pitch pb (bytes), a row starting fewer than 16 - (x mod 16) bytes past an
+    // unaligned start, or ending fewer than (end mod 16) bytes before an
+    // unaligned end, has a window that reaches outside; that is the first
+    // ceil((16 - x mod 16) / pb) and the last ceil((end mod 16) / pb) rows.
+    const int64_t pb = ES * ldx;
     const int64_t mb = (int64_t)(ax & 15);
-    const int64_t me = (int64_t)((ax + (uintptr_t)(rb * rows)) & 15);
-    int64_t r_lo = mb == 0 ? 0 : (16 - mb + rb - 1) / rb;
-    int64_t r_hi = me == 0 ? rows : rows - (me + rb - 1) / rb;
+    const int64_t me = (int64_t)((ax + (uintptr_t)(ES * ((rows - 1) * ldx + cols))) & 15);
+    int64_t r_lo = mb == 0 ? 0 : (16 - mb + pb - 1) / pb;
+    int64_t r_hi = me == 0 ? rows : rows - (me + pb - 1) / pb;
     if (r_lo > rows) r_lo = rows;
     if (r_hi < r_lo) r_hi = r_lo;
     const int64_t n_edge = r_lo + (rows - r_hi);
@@ -1242,12 +1263,12 @@ hipError_t launch_flags(const void* x, const void* res, const void* gamma, const
     // P classes of rows with one offset in the line; each block takes up to
     // kClassGroups row groups of its class.
     int period = line;
-    while (period > 1 && (rb * (period / 2)) % line == 0) period /= 2;
+    while (period > 1 && (pb * (period / 2)) % line == 0) period /= 2;
     const int64_t cgroups = ((r_hi - r_lo + period - 1) / period + rpb - 1) / rpb;
     int64_t nblk = (cgroups + kClassGroups - 1) / kClassGroups;
     if (nblk > kMaxGrid / 128) nblk = kMaxGrid / 128;
     const void* k = shape_kernel<ClassSel<IO, RES, EPI>::template K>(i);
-    void* cargs[] = {&x,   &res,    &gamma, &beta, &y,    &rows, &icols,
+    void* cargs[] = {&x,   &res,    &gamma, &beta, &y,    &rows, &icols, &ldx,
                      &eps, &period, &line,  &r_lo, &r_hi, (void*)&edge_blocks, &drop};
     return hipLaunchKernel(k, dim3((unsigned)(edge_blocks + period * nblk)), dim3(block), cargs, 0, s);
   }
@@ -1257,21 +1278,24 @@ hipError_t launch_flags(const void* x, const void* res, const void* gamma, const
   return hipLaunchKernel(k, dim3(sgrid), dim3(block), args, 0, s);
 }
 
-// act: kEpiNone, kEpiGelu, kEpiReluDrop (no residual; `drop` describes it)
+// act: kEpiNone, kEpiGelu, kEpiReluDrop (no residual; `drop` describes it).
+// Row strides in elements: row i of x, residual and y starts at i * ld.
 template <class IO>
-hipError_t launch(const void* x, const void* res, const void* gamma, const void* beta, void* y,
-                  int64_t rows, int64_t cols, double eps, int act, const Drop* drop, hipStream_t s) {
+hipError_t launch(const void* x, int64_t ldx, const void* res, int64_t ldr, const void* gamma,
+                  const void* beta, void* y, int64_t ldy, int64_t rows, int64_t cols, double eps, int act,
+                  const Drop* drop, hipStream_t s) {
   const Drop none{0, 0, 0, 1.0f};
+  if (rows == 1) ldx = ldr = ldy = cols;  // one row: its stride is never used
   if (act == kEpiReluDrop) {
     if (res || !drop) return hipErrorInvalidValue;
-    return launch_flags<IO, false, kEpiReluDrop>(x, res, gamma, beta, y, rows, cols, eps, *drop, s);
+    return launch_flags<IO, false, kEpiReluDrop>(x, ldx, res, ldr, gamma, beta, y, ldy, rows, cols, eps, *drop, s);
   }
   const bool gelu = act == kEpiGelu;
   if (res)
-    return gelu ? launch_flags<IO, true, kEpiGelu>(x, res, gamma, beta, y, rows, cols, eps, none, s)
-                : launch_flags<IO, true, kEpiNone>(x, res, gamma, beta, y, rows, cols, eps, none, s);
-  return gelu ? launch_flags<IO, false, kEpiGelu>(x, res, gamma, beta, y, rows, cols, eps, none, s)
-              : launch_flags<IO, false, kEpiNone>(x, res, gamma, beta, y, rows, cols, eps, none, s);
+    return gelu ? launch_flags<IO, true, kEpiGelu>(x, ldx, res, ldr, gamma, beta, y, ldy, rows, cols, eps, none, s)
+                : launch_flags<IO, true, kEpiNone>(x, ldx, res, ldr, gamma, beta, y, ldy, rows, cols, eps, none, s);
+  return gelu ? launch_flags<IO, false, kEpiGelu>(x, ldx, res, ldr, gamma, beta, y, ldy, rows, cols, eps, none, s)
+              : launch_flags<IO, false, kEpiNone>(x, ldx, res, ldr, gamma, beta, y, ldy, rows, cols, eps, none, s);
 }
 
 }  // namespace ln

@@ -71,7 +71,7 @@ __device__ __forceinline__ void group_merge(float& m, float& l, float* lds_m, fl
 template <class IO, int LANES, int VPL, int VW>
 __global__ __launch_bounds__(block_for(LANES)) void softmax_kernel(const typename IO::elem* x,
                                                                    typename IO::elem* y, int64_t rows,
-                                                                   int cols) {
+                                                                   int cols, int64_t ldx, int64_t ldy) {
   typedef typename IO::elem E;
   constexpr int BLOCK = block_for(LANES);
   constexpr int RPB = BLOCK / LANES;
@@ -82,8 +82,8 @@ __global__ __launch_bounds__(block_for(LANES)) void softmax_kernel(const typenam
   const bool live = row < rows;
   const int nvec = (cols + VW - 1) / VW;
   // past the last row: reread the last row, store nothing
-  const E* xr = x + (live ? row : rows - 1) * (int64_t)cols;
-  E* yr = y + row * (int64_t)cols;
+  const E* xr = x + (live ? row : rows - 1) * ldx;
+  E* yr = y + row * ldy;
 
   float v[VPL][VW];
 #pragma unroll
@@ -177,7 +177,8 @@ __device__ __forceinline__ typename IO::elem stored_elem(const u32x4& v, int e) 
 template <class IO, int LANES, int VPL>
 __global__ __launch_bounds__(block_for(LANES)) void softmax_win_kernel(const typename IO::elem* x,
                                                                        typename IO::elem* y, int64_t rows,
-                                                                       int cols, int line, int64_t r_lo,
+                                                                       int cols, int64_t ldx, int64_t ldy,
+                                                                       int line, int64_t r_lo,
                                                                        int64_t r_hi, int edge_blocks) {
   typedef typename IO::elem E;
   constexpr int ES = (int)sizeof(E);
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(block_for(LANES)) void softmax_win_kernel(const typ
     const int64_t n_edge = r_lo + (rows - r_hi);
     const bool live = i < n_edge;
     const int64_t row = !live ? 0 : (i < r_lo ? i : r_hi + (i - r_lo));
-    const E* xr = x + row * (int64_t)cols;
+    const E* xr = x + row * ldx;
     float m = kNegInf;
     for (int c = lane; c < cols; c += LANES) m = __builtin_fmaxf(m, IO::load1(xr, c));
     const float mm = (m == kNegInf) ? 0.0f : m;
@@ -211,14 +212,14 @@ __global__ __launch_bounds__(block_for(LANES)) void softmax_win_kernel(const typ
     else if (m_lane == kNegInf) f = 0.0f;
     else f = exp_f(m_lane - m) / l;
     if (live)
-      for (int c = lane; c < cols; c += LANES) IO::store1(y + row * (int64_t)cols, c, exp_f(IO::load1(xr, c) - mm) * f);
+      for (int c = lane; c < cols; c += LANES) IO::store1(y + row * ldy, c, exp_f(IO::load1(xr, c) - mm) * f);
     return;
   }
 
   const int64_t row = r_lo + (int64_t)blockIdx.x * RPB + sub;
   const bool live = row < r_hi;
   const int64_t lrow = live ? row : r_hi - 1;  // past the last row: reread it, store nothing
-  const char* xb = reinterpret_cast<const char*>(x) + (int64_t)ES * lrow * cols;
+  const char* xb = reinterpret_cast<const char*>(x) + (int64_t)ES * lrow * ldx;
   const int sl = (int)(reinterpret_cast<uintptr_t>(xb) & (unsigned)(line - 1));
   const int d = sl >> 4, sb = sl & 15, s = sb / ES;
   const int nvec = (cols + V - 1) / V;
@@ -289,8 +290,8 @@ __global__ __launch_bounds__(block_for(LANES)) void softmax_win_kernel(const typ
   else f = exp_f(m_lane - m) / l;
   if (!live) return;
 
-  char* yb = reinterpret_cast<char*>(y) + (int64_t)ES * row * cols;
-  u32x4* dst = reinterpret_cast<u32x4*>(yb - sb);  // y agrees with x modulo 16
+  char* yb = reinterpret_cast<char*>(y) + (int64_t)ES * row * ldy;
+  u32x4* dst = reinterpret_cast<u32x4*>(yb - sb);  // the row of y agrees with the row of x modulo 16
   // fp32: element stores through a volatile pointer, so that the compiler
   // keeps the whole-window store one dwordx4 instead of sinking its last dword
   // into a tail shared with the element stores; 16-bit: plain stores
@@ -359,9 +360,12 @@ struct SoftmaxSel {
 };
 
 template <class IO>
-hipError_t launch_softmax_io(const void* x, void* y, int64_t rows, int64_t cols, hipStream_t s) {
+hipError_t launch_softmax_io(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t cols,
+                             hipStream_t s) {
   typedef typename IO::elem E;
   constexpr int V = IO::kVec;
+  constexpr int64_t ES = (int64_t)sizeof(E);
+  if (rows == 1) ldx = ldy = cols;  // one row: its stride is never used
   const int64_t nvec = (cols + V - 1) / V;
   const int shape = pick_shape(nvec);
   if (shape < 0) return hipErrorInvalidValue;
@@ -371,23 +375,28 @@ hipError_t launch_softmax_io(const void* x, void* y, int64_t rows, int64_t cols,
   E* ye = static_cast<E*>(y);
   int icols = (int)cols;
   const uintptr_t ax = reinterpret_cast<uintptr_t>(x), ay = reinterpret_cast<uintptr_t>(y);
-  const int64_t rb = (int64_t)sizeof(E) * cols;
-  const bool vec = cols % V == 0 && aligned16(x) && aligned16(y);
-  // windows on 128-byte lines need x and y to agree modulo 128 and rows of a
-  // wave's worth of windows; rows on 16-byte boundaries whose length is a
-  // multiple of 128 bytes are on lines already (a 4088-wide bf16 row stream
-  // measured 386 us against 342 for 4096 before the windows were rotated onto
-  // lines)
-  const bool line_ok = ((ax ^ ay) & 127) == 0 && nvec >= 64;
-  if (((ax ^ ay) & 15) == 0 && !(vec && (rb % 128 == 0 || !line_ok))) {
+  const int64_t px = ES * ldx, py = ES * ldy;  // row pitches (bytes)
+  // rows on 16-byte boundaries: aligned bases, pitches of whole vectors
+  const bool vec = cols % V == 0 && aligned16(x) && aligned16(y) && px % 16 == 0 && py % 16 == 0;
+  // windows on 128-byte lines need every row of x and y to agree modulo 128
+  // and rows of a wave's worth of windows; rows on 16-byte boundaries whose
+  // pitches are multiples of 128 bytes are on lines already (a 4088-wide bf16
+  // row stream measured 386 us against 342 for 4096 before the windows were
+  // rotated onto lines)
+  const bool line_ok = ((ax ^ ay) & 127) == 0 && (px - py) % 128 == 0 && nvec >= 64;
+  const bool win_ok = ((ax ^ ay) & 15) == 0 && (px - py) % 16 == 0 && ldx > 0;
+  if (win_ok && !(vec && ((px % 128 == 0 && py % 128 == 0) || !line_ok))) {
     // Rows whose windows lie inside both tensors: [r_lo, r_hi).  A row
     // starting fewer than 16 - (x mod 16) bytes past an unaligned start, or
     // ending fewer than (end mod 16) bytes before an unaligned end, has a
-    // window that reaches outside.
+    // window that reaches outside: the first ceil((16 - x mod 16) / pitch)
+    // and the last ceil((end mod 16) / pitch) rows (x and y end alike modulo
+    // 16; the smaller pitch counts).
+    const int64_t pmin = px < py ? px : py;
     const int64_t mb = (int64_t)(ax & 15);
-    const int64_t me = (int64_t)((ax + (uintptr_t)(rb * rows)) & 15);
-    int64_t r_lo = mb == 0 ? 0 : (16 - mb + rb - 1) / rb;
-    int64_t r_hi = me == 0 ? rows : rows - (me + rb - 1) / rb;
+    const int64_t me = (int64_t)((ax + (uintptr_t)(ES * ((rows - 1) * ldx + cols))) & 15);
+    int64_t r_lo = mb == 0 ? 0 : (16 - mb + pmin - 1) / pmin;
+    int64_t r_hi = me == 0 ? rows : rows - (me + pmin - 1) / pmin;
     if (r_lo > rows) r_lo = rows;
     if (r_hi < r_lo) r_hi = r_lo;
     const int64_t n_edge = r_lo + (rows - r_hi);
@@ -397,7 +406,7 @@ hipError_t launch_softmax_io(const void* x, void* y, int64_t rows, int64_t cols,
     int line = line_ok ? 128 : 16;
     int eb = (int)edge_blocks;
     const void* k = shape_kernel<SoftmaxWinSel<IO>::template K>(shape);
-    void* args[] = {&xe, &ye, &rows, &icols, &line, &r_lo, &r_hi, &eb};
+    void* args[] = {&xe, &ye, &rows, &icols, &ldx, &ldy, &line, &r_lo, &r_hi, &eb};
     return hipLaunchKernel(k, dim3((unsigned)(main_blocks + edge_blocks)), dim3(block), args, 0, s);
   }
   const void* k = vec ? shape_kernel<SoftmaxSel<IO, true>::template K>(shape)
@@ -405,16 +414,17 @@ hipError_t launch_softmax_io(const void* x, void* y, int64_t rows, int64_t cols,
   const int64_t groups = (rows + rpb - 1) / rpb;
   const int grid = (int)(groups < (1 << 30) ? groups : (1 << 30));
   if (groups > grid) return hipErrorInvalidValue;  // one block per row group
-  void* args[] = {&xe, &ye, &rows, &icols};
+  void* args[] = {&xe, &ye, &rows, &icols, &ldx, &ldy};
   return hipLaunchKernel(k, dim3(grid), dim3(block), args, 0, s);
 }
 
 }  // namespace
 
-hipError_t launch_softmax(int dtype, const void* x, void* y, int64_t rows, int64_t cols, hipStream_t s) {
-  if (dtype == 0) return launch_softmax_io<F32IO>(x, y, rows, cols, s);
-  if (dtype == 1) return launch_softmax_io<BF16IO>(x, y, rows, cols, s);
-  return launch_softmax_io<F16IO>(x, y, rows, cols, s);
+hipError_t launch_softmax(int dtype, const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows,
+                          int64_t cols, hipStream_t s) {
+  if (dtype == 0) return launch_softmax_io<F32IO>(x, ldx, y, ldy, rows, cols, s);
+  if (dtype == 1) return launch_softmax_io<BF16IO>(x, ldx, y, ldy, rows, cols, s);
+  return launch_softmax_io<F16IO>(x, ldx, y, ldy, rows, cols, s);
 }
 
 }  // namespace mbp

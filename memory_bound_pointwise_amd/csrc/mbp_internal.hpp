@@ -28,8 +28,10 @@ hipError_t launch_chain(const float* x, const float* b1, const float* b2, float*
 hipError_t launch_chain_2d(int dtype, const void* x, int64_t ldx, const void* b1, int64_t ldb1,
                           const void* b2, int64_t ldb2, void* y, int64_t ldy, int64_t rows, int64_t cols,
                           double scale, hipStream_t s);
-// row softmax over the last dimension (dtype 0 fp32, 1 bf16, 2 fp16)
-hipError_t launch_softmax(int dtype, const void* x, void* y, int64_t rows, int64_t cols, hipStream_t s);
+// row softmax over the last dimension (dtype 0 fp32, 1 bf16, 2 fp16); row i
+// of x at i * ldx, of y at i * ldy (elements)
+hipError_t launch_softmax(int dtype, const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows,
+                          int64_t cols, hipStream_t s);
 hipError_t launch_row_mean_2d(int dtype, const void* x, int64_t ldx, const void* bias, const void* gamma,
                               const void* beta, void* y, int64_t ldy, int64_t rows, int64_t cols,
                               double alpha, double c, hipStream_t s);
@@ -40,6 +42,11 @@ hipError_t launch_row_mean(const float* x, const float* bias, const float* gamma
 hipError_t launch_layernorm(int dtype, const void* x, const void* residual, const void* gamma,
                             const void* beta, void* y, int64_t rows, int64_t cols, double eps,
                             int act, const Drop* drop, hipStream_t s);
+// the same with row strides (elements): row i of x, residual and y at i * ld
+// (an input stride of 0: one row used for every row)
+hipError_t launch_layernorm_2d(int dtype, const void* x, int64_t ldx, const void* residual, int64_t ldr,
+                               const void* gamma, const void* beta, void* y, int64_t ldy, int64_t rows,
+                               int64_t cols, double eps, int act, const Drop* drop, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
 

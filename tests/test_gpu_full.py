@@ -219,6 +219,34 @@ def test_unfused_ln_full_output(mbp, name, gran):
     assert same >= 0.999 * n, f"only {same / n:.4%} of the elements are the oracle's stored value"
 
 
+@pytest.mark.parametrize("name", ["addln_gelu_16384x8192_bf16_ld8320", "addln_gelu_16384x8192_bf16_ld8195"])
+def test_ln_strided_full_output(mbp, name):
+    """The padded-row workloads the bench times: x, residual and y are views
+    into buffers of rows of `ld` elements; every element vs EXACT, and the
+    padding left untouched."""
+    w = W.NEXT_BY_NAME[name]
+    d = W.generate(w)
+    ld = w.params["ld"]
+
+    def padded(a, fill):
+        t = to_dev(a)
+        buf = torch.full((w.rows, ld), fill, dtype=t.dtype, device="cuda")
+        v = buf[:, :w.cols]
+        v.copy_(t)
+        return v, buf
+
+    x, _ = padded(d["x"], 0.0)
+    r, _ = padded(d["residual"], 0.0)
+    y, yb = padded(np.zeros_like(d["x"]), 3.0)
+    print(f"{name}: fused on rows of {ld} elements, every element vs EXACT", flush=True)
+    mbp.fused_add_layernorm_gelu(x, r, to_dev(d["gamma"]), to_dev(d["beta"]), eps=1e-5, act=w.act, out=y)
+    assert bool((yb[:, w.cols:].float() == 3.0).all()), "wrote into the row padding"
+    yh = to_host(y.contiguous())
+    res, n = compare_rows(w.rows, w.cols, _ln_ref_fn(d, w.act, oracle.EXACT),
+                          lambda a, b, ref: check_bf16(yh[a:b], ref, f"{name} rows {a}..{b}"))
+    print(f"{name}: compared {n} elements, max abs err {max(r_[0] for r_ in res):.3g}")
+
+
 # ------------------------------------------------------------------ LayerNorm -> ReLU -> Dropout
 
 def _dropout_gate(y, d, dtype, p, seed, offset, mode, what):

@@ -376,6 +376,135 @@ def test_ln_f32_two_groups_per_block(mbp):
     check_f32(to_host(y)[rows], _ln_ref(d, act, rows), "fp32 LN 4097 x 4096, two groups per block")
 
 
+# ------------------------------------------------------------------ row strides of the row kernels
+
+# (rows, cols, x (pad, offset), residual (pad, offset) or None, y (pad, offset) or "x")
+# pads and offsets in elements: row i of an operand starts at offset + i * (cols + pad)
+LN_STRIDED = [
+    (37, 4096, (64, 0), (64, 0), (64, 0)),        # pitches of whole 16-byte vectors: aligned kernel
+    (37, 4096, (3, 0), (3, 0), (3, 0)),           # one pitch off 16 bytes: per-class windows
+    (37, 4096, (3, 5), (3, 5), (3, 5)),           # the same, bases off 16 bytes (sliced columns)
+    (37, 4096, (3, 0), (5, 0), (0, 0)),           # different pitches: lane-shift kernel
+    (40, 4095, (1, 0), (1, 0), "x"),              # in place on a padded buffer
+    (41, 768, (8, 2), None, (9, 1)),              # narrow rows, sub-wave groups
+    (9, 12288, (16, 0), (7, 3), (16, 0)),
+    (5, 16384, (2, 1), (2, 1), (2, 1)),           # the widest rows, per-class windows
+    (300, 64, (4, 0), (4, 0), (4, 0)),
+    (33, 1000, (24, 8), (24, 8), (24, 8)),
+]
+
+
+def _strided(host, pad, off, fill):
+    """a [rows, cols] view into a padded buffer (rows at offset + i * (cols + pad)),
+    the padding holding `fill`; returns (view, whole buffer)"""
+    rows, cols = host.shape
+    ld = cols + pad
+    buf = torch.full((off + rows * ld + 8,), fill, dtype=host.dtype, device="cuda")
+    v = buf[off:off + rows * ld].view(rows, ld)[:, :cols]
+    v.copy_(host.cuda())
+    return v, buf
+
+
+def _outside(buf, view, fill):
+    """elements of buf outside the view still equal to fill"""
+    mask = torch.ones(buf.numel(), dtype=torch.bool, device="cuda")
+    idx = (torch.arange(view.shape[0], device="cuda")[:, None] * view.stride(0) +
+           torch.arange(view.shape[1], device="cuda")[None, :] + view.storage_offset())
+    mask[idx.reshape(-1)] = False
+    return bool((buf[mask].float() == fill).all())
+
+
+@pytest.mark.parametrize("fmt,dtype", [("f32", torch.float32), ("bf16", torch.bfloat16)], ids=["f32", "bf16"])
+@pytest.mark.parametrize("rows,cols,xs,rs,ys", LN_STRIDED)
+def test_ln_strided(mbp, fmt, dtype, rows, cols, xs, rs, ys):
+    """Residual + LayerNorm + GeLU (and plain LayerNorm, and dropout) on
+    padded and sliced rows through the row strides ([P1] section 6.2: no
+    hidden .contiguous() copy): the result equals the oracle on the rows'
+    values and nothing outside the output rows is written."""
+    rng = np.random.default_rng([51, rows, cols, xs[0], xs[1]])
+    xh = torch.from_numpy(rng.standard_normal((rows, cols)) * 2 + 0.5).to(dtype)
+    rh = torch.from_numpy(rng.standard_normal((rows, cols)) * 2).to(dtype)
+    g = torch.from_numpy(1 + 0.1 * rng.standard_normal(cols)).to(dtype)
+    b = torch.from_numpy(0.1 * rng.standard_normal(cols)).to(dtype)
+    host = (lambda t: t.view(torch.int16).numpy().view(np.uint16)) if fmt == "bf16" else (lambda t: t.numpy())
+    chk = check_bf16 if fmt == "bf16" else check_f32
+    fill = 7.0
+    x, xbuf = _strided(xh, *xs, fill)
+    r, rbuf = _strided(rh, *rs, fill) if rs is not None else (None, None)
+    if ys == "x":
+        y, ybuf = x, xbuf
+    else:
+        y, ybuf = _strided(torch.zeros_like(xh), *ys, fill)
+    ref = oracle.add_layernorm_gelu(host(xh), None if r is None else host(rh), host(g), host(b),
+                                    act=oracle.ACT_GELU_TANH)
+    mbp.fused_add_layernorm_gelu(x, r, g.cuda(), b.cuda(), act="gelu_tanh", out=y)
+    what = f"{fmt} {rows}x{cols} x{xs} r{rs} y{ys}"
+    chk(to_host(y.contiguous()), ref, f"strided LN+GeLU {what}")
+    assert _outside(ybuf, y, fill), f"{what}: wrote outside the output rows"
+    if ys != "x":
+        # plain LayerNorm and LN-ReLU-dropout on the same strided views
+        ref = oracle.add_layernorm_gelu(host(xh), None, host(g), host(b), act=oracle.ACT_NONE)
+        mbp.fused_add_layernorm_gelu(x, None, g.cuda(), b.cuda(), act="none", out=y)
+        chk(to_host(y.contiguous()), ref, f"strided LN {what}")
+        d = {"x": host(xh), "gamma": host(g), "beta": host(b)}
+        w = W.scaled(W.BY_NAME["ln_8192x4096_f32" if fmt == "f32" else "addln_gelu_16384x8192_bf16"], rows=rows)
+        mbp.fused_layernorm_relu_dropout(x, g.cuda(), b.cuda(), p=0.25, seed=77, offset=2, out=y)
+        _check_dropout(y.contiguous(), d, w, 0.25, 77, 2, f"strided LN-ReLU-dropout {what}")
+        assert _outside(ybuf, y, fill), f"{what}: dropout wrote outside the output rows"
+
+
+def test_ln_strided_views(mbp):
+    """Views the binding accepts (a 3-D slice whose leading dimensions collapse
+    to one row stride, a residual row expanded over the rows) and one it must
+    refuse (leading dimensions that do not collapse)."""
+    rng = np.random.default_rng(52)
+    B, S, W_, H = 3, 5, 800, 768
+    big = torch.from_numpy(rng.standard_normal((B, S, W_))).to(torch.bfloat16).cuda()
+    x = big[:, :, 16:16 + H]                       # strides (S*W, W, 1): row stride W
+    rrow = torch.from_numpy(rng.standard_normal(H)).to(torch.bfloat16).cuda()
+    r = rrow.expand(B, S, H)                       # row stride 0
+    g = torch.ones(H, dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(H, dtype=torch.bfloat16, device="cuda")
+    y = mbp.fused_add_layernorm_gelu(x, r, g, b, act="gelu_tanh")
+    assert y.shape == x.shape and y.is_contiguous()
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1, H)
+    vbits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.add_layernorm_gelu(bits(x), bits(r), vbits(g), vbits(b), act=oracle.ACT_GELU_TANH)
+    check_bf16(bits(y), ref, "3-D slice with an expanded residual row")
+    with pytest.raises(ValueError):
+        mbp.fused_add_layernorm_gelu(big[:, :S - 1, :H], None, g, b)   # strides (S*W, W) over sizes (B, S-1)
+    with pytest.raises(ValueError):
+        mbp.fused_softmax(big[:, :S - 1, :H])
+
+
+SM_STRIDED = [  # rows, cols, x (pad, off), y (pad, off) or "x"
+    (37, 4096, (64, 0), (0, 0)),      # padded x, dense y: both on 16-byte boundaries
+    (37, 4096, (3, 0), (3, 0)),       # one pitch off 16 bytes: windows
+    (37, 4096, (3, 0), (11, 0)),      # pitches 16 bytes apart (bf16/fp16: 8 elements): windows
+    (37, 4095, (2, 1), (7, 4)),       # rows that never agree modulo 16: element path
+    (30, 4095, (1, 0), "x"),          # in place on a padded buffer
+    (64, 768, (8, 2), (8, 2)),
+    (5, 16384, (2, 0), (2, 0)),
+]
+
+
+@pytest.mark.parametrize("fmt,dtype", [("f32", torch.float32), ("bf16", torch.bfloat16), ("f16", torch.float16)],
+                         ids=["f32", "bf16", "f16"])
+@pytest.mark.parametrize("rows,cols,xs,ys", SM_STRIDED)
+def test_softmax_strided(mbp, fmt, dtype, rows, cols, xs, ys):
+    rng = np.random.default_rng([53, rows, cols, xs[0]])
+    xh, xf = _stored(rng, (rows, cols), dtype, 3.0)
+    fill = 5.0
+    x, xbuf = _strided(xh, *xs, fill)
+    if ys == "x":
+        y, ybuf = x, xbuf
+    else:
+        y, ybuf = _strided(torch.zeros_like(xh), *ys, fill)
+    mbp.fused_softmax(x, out=y)
+    _softmax_gate(y.contiguous(), oracle.softmax(xf), fmt, f"strided softmax {fmt} {rows}x{cols} x{xs} y{ys}", xf)
+    assert _outside(ybuf, y, fill), "wrote outside the output rows"
+
+
 # ------------------------------------------------------------------ two-dimensional forms
 
 DT2D = [("f32", torch.float32), ("bf16", torch.bfloat16), ("f16", torch.float16)]

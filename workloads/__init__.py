@@ -35,7 +35,7 @@ import numpy as np
 class Workload:
     name: str
     kind: str            # "chain" | "row_mean" | "layernorm" | "chain2d" | "row_mean2d" | "softmax"
-    #                      | "ln_relu_dropout"
+    #                      | "ln_relu_dropout" | "layernorm2d" (layernorm on padded rows)
     seed: int
     sub: int = 0
     n: int = 0           # chain: element count
@@ -109,6 +109,16 @@ NEXT_WORKLOADS = [
     # 2.1) at the residual-LayerNorm workload's shape, without the residual
     Workload("ln_relu_dropout_16384x8192_bf16", "ln_relu_dropout", seed=4, rows=16384, cols=8192,
              dtype="bf16", params=dict(eps=1e-5, p=0.1, seed=0x5EED, offset=0)),
+    # residual + LayerNorm + GeLU on padded rows, read and written through
+    # the row strides (the PyTorch operator-fusion practice post, section 6.2:
+    # no hidden .contiguous() copy): the residual-LayerNorm workload's inputs
+    # with x, residual and y each a [16384, 8192] view into a buffer of rows of
+    # params["ld"] elements -- 8320 keeps every row on a 128-byte line, 8195
+    # puts them off 16-byte boundaries (one stride for the three)
+    Workload("addln_gelu_16384x8192_bf16_ld8320", "layernorm2d", seed=4, rows=16384, cols=8192,
+             dtype="bf16", residual=True, act="gelu_tanh", params=dict(eps=1e-5, ld=8320)),
+    Workload("addln_gelu_16384x8192_bf16_ld8195", "layernorm2d", seed=4, rows=16384, cols=8192,
+             dtype="bf16", residual=True, act="gelu_tanh", params=dict(eps=1e-5, ld=8195)),
 ]
 NEXT_BY_NAME = {w.name: w for w in NEXT_WORKLOADS}
 
