@@ -80,6 +80,7 @@ def parse():
                    help="the oracle runs on 1/K of each workload's rows")
     p.add_argument("--only", default=None, help="run only this workload's fused kernel")
     p.add_argument("--no-next", action="store_true", help="skip the two-dimensional forms")
+    p.add_argument("--no-floors", action="store_true", help="skip the per-workload bare-stream floors")
     p.add_argument("--no-launch-study", action="store_true", help="skip the eager vs graph study")
     p.add_argument("--no-graphs", action="store_true",
                    help="time the batches as eager calls only (no graph capture; for counter runs)")
@@ -288,6 +289,34 @@ def main():
                        "us_median": round(cmed, 3), "gbps": round(2 * cb / (cmed * 1e-6) / 1e9, 1),
                        "frac_of_peak": round(2 * cb / (cmed * 1e-6) / 1e9 / PEAK_GBPS, 4)}
         del pairs
+    # ---- like-for-like floors: the bare stream of each workload's own reads
+    # and write (mbp_stream_rw: nsrc inputs, one output, the tensors' sizes, no
+    # arithmetic), same rotation over input copies and the same batches
+    def floor_spec(w):
+        """(tensors read, bytes per tensor) of the workload's streams (the
+        per-column vectors, at most 48 KiB, left out)"""
+        es = 4 if w.dtype == "f32" else 2
+        if w.kind == "chain":
+            return 3, 4 * w.n
+        if w.kind == "chain2d":
+            return 2, es * w.rows * w.cols
+        if w.kind in ("layernorm", "layernorm2d"):
+            return (2 if w.residual else 1), es * w.rows * w.cols
+        return 1, es * w.rows * w.cols       # row_mean, row_mean2d, softmax, ln_relu_dropout
+
+    def copy_floor(w):
+        nsrc, nb = floor_spec(w)
+        nb = -(-nb // 16) * 16
+        sets = [([torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(nsrc)],
+                 torch.empty(nb, dtype=torch.uint8, device=dev)) for _ in range(n_sets(w))]
+        us, _ = batch_times([lambda s=s, d=d: mbp.stream_rw(s, d) for s, d in sets], args.batches)
+        del sets
+        return {"copy_floor_us": round(statistics.median(us), 3), "copy_floor_reads": nsrc}
+
+    floors = {}
+    if not args.only and not args.no_floors:
+        for n in names:
+            floors[n] = copy_floor(W.BY_NAME[n])
     dominant = max(names, key=lambda n: statistics.median(fused_us[n]))
 
     for _ in range(args.warmup):
@@ -376,6 +405,10 @@ def main():
                            "gbps": round(w.compulsory_bytes / (med * 1e-6) / 1e9, 1),
                            "frac_of_peak": round(w.compulsory_bytes / (med * 1e-6) / 1e9 / PEAK_GBPS, 4)}
             del fns
+            if not args.no_floors:
+                fl = copy_floor(w)
+                nxt[w.name].update(fl)
+                nxt[w.name]["frac_of_copy_floor"] = round(fl["copy_floor_us"] / med, 4)
             if w.kind == "softmax" and args.unfused_reps:
                 # the five eager launches: max, x - m, exp, sum, divide
                 x = to_dev(d["x"])
@@ -433,6 +466,9 @@ def main():
             "warm_us_median": round(statistics.median(fused_warm[n]), 3),
             "launches_fused": 1,
         }
+        if n in floors:
+            rec.update(floors[n])
+            rec["frac_of_copy_floor"] = round(floors[n]["copy_floor_us"] / med_us, 4)
         if unf_us[n]:
             um = statistics.median(unf_us[n])
             ue = statistics.median(unf_eager[n])

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MBP_ABI_VERSION 5
+#define MBP_ABI_VERSION 6
 
 /* Largest row length (cols) the row kernels accept: one row lives in registers. */
 #define MBP_MAX_COLS 16384
@@ -392,6 +392,15 @@ mbp_status mbp_graph_destroy(mbp_graph* graph);
  * src and dst: device pointers, 16-byte aligned, not overlapping; bytes a
  * multiple of 16. */
 mbp_status mbp_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+/* The same streaming pattern with nsrc (1 .. 4) inputs of `bytes` bytes each:
+ * dst = srcs[0] ^ srcs[1] ^ ... (bitwise), so every load is used.  The bare
+ * stream of a kernel that reads nsrc tensors and writes one, with no
+ * arithmetic: the like-for-like floor of each fused kernel ([P1] section 6.3:
+ * confirm a gain with the profiler and the bandwidth arithmetic).  srcs: host
+ * array of nsrc device pointers, each 16-byte aligned and not overlapping
+ * dst; dst 16-byte aligned; bytes a multiple of 16 (0: no-op). */
+mbp_status mbp_stream_rw(const void* const* srcs, int nsrc, void* dst, size_t bytes, void* stream);
 
 /* y[i] = x[i] rounded to bfloat16 (nearest even; NaN stays NaN with its sign),
  * with the binary32 -> bfloat16 conversion that every kernel storing bf16 uses

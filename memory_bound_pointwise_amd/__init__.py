@@ -59,6 +59,7 @@ SIGNATURES = [
     ("mbp_graph_nodes", _I64, [_P]),
     ("mbp_graph_destroy", _I, [_P]),
     ("mbp_stream_copy", _I, [_P, _P, _SZ, _P]),
+    ("mbp_stream_rw", _I, [ctypes.POINTER(_P), _I, _P, _SZ, _P]),
     ("mbp_convert_f32_to_bf16", _I, [_P, _P, _I64, _P]),
     ("mbp_status_string", ctypes.c_char_p, [_I]),
     ("mbp_last_error", ctypes.c_char_p, []),
@@ -583,6 +584,20 @@ def convert_f32_to_bf16(x, out=None):
         raise ValueError("out has the wrong size")
     _call("mbp_convert_f32_to_bf16", _ptr(x), _ptr(y), x.numel(), _stream(x))
     return y
+
+
+def stream_rw(srcs, dst):
+    """dst = srcs[0] ^ srcs[1] ^ ... over dst's bytes: the bare stream of a
+    kernel reading len(srcs) tensors and writing one (bandwidth floors)."""
+    nbytes = dst.numel() * dst.element_size()
+    for i, t in enumerate(srcs):
+        _check(t, f"srcs[{i}]", (t.dtype,), dst.device)
+        if t.numel() * t.element_size() < nbytes:
+            raise ValueError(f"srcs[{i}] is smaller than dst")
+    _check(dst, "dst", (dst.dtype,))
+    arr = (_P * len(srcs))(*[t.data_ptr() for t in srcs])
+    _call("mbp_stream_rw", arr, len(srcs), _ptr(dst), nbytes, _stream(dst))
+    return dst
 
 
 def stream_copy(src, dst):

@@ -766,6 +766,19 @@ mbp_status mbp_stream_copy(const void* src, void* dst, size_t bytes, void* strea
   return from_hip(mbp::launch_copy(src, dst, bytes, as_stream(stream)), "mbp_stream_copy");
 }
 
+mbp_status mbp_stream_rw(const void* const* srcs, int nsrc, void* dst, size_t bytes, void* stream) {
+  if (nsrc < 1 || nsrc > 4) return fail(MBP_ERR_ARG, "nsrc must be 1 .. 4 (got %d)", nsrc);
+  if (bytes == 0) return ok();
+  if (!srcs || !dst) return fail(MBP_ERR_NULL, "srcs and dst must be non-NULL");
+  if (misaligned(dst, 16) || bytes % 16) return fail(MBP_ERR_ALIGN, "dst and bytes must be multiples of 16");
+  for (int k = 0; k < nsrc; ++k) {
+    if (!srcs[k]) return fail(MBP_ERR_NULL, "srcs[%d] is NULL", k);
+    if (misaligned(srcs[k], 16)) return fail(MBP_ERR_ALIGN, "srcs[%d] must be 16-byte aligned", k);
+    if (overlaps(Span{srcs[k], bytes}, Span{dst, bytes})) return fail(MBP_ERR_OVERLAP, "dst overlaps srcs[%d]", k);
+  }
+  return from_hip(mbp::launch_stream(srcs, nsrc, dst, bytes, as_stream(stream)), "mbp_stream_rw");
+}
+
 mbp_status mbp_convert_f32_to_bf16(const float* x, uint16_t* y, int64_t n, void* stream) {
   if (n < 0) return fail(MBP_ERR_SHAPE, "n must be >= 0 (got %lld)", (long long)n);
   if (n == 0) return ok();

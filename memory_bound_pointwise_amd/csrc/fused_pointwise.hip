@@ -145,6 +145,28 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(const u32x4* src, u32x4* d
     store_nt(dst + i, load_nt(src + i));
 }
 
+// The copy's access pattern with NSRC inputs: dst = src0 ^ src1 ^ ..., so
+// every load is used -- the bare stream of a kernel that reads NSRC tensors
+// and writes one, with no arithmetic.
+struct Srcs {
+  const u32x4* p[4];
+};
+template <int NSRC>
+__global__ __launch_bounds__(kBlock) void stream_kernel(Srcs src, u32x4* dst, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * kBlock) {
+    u32x4 v[NSRC];
+#pragma unroll
+    for (int k = 0; k < NSRC; ++k) v[k] = load_nt(src.p[k] + i);
+    u32x4 o = v[0];
+#pragma unroll
+    for (int k = 1; k < NSRC; ++k)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o.w[w] ^= v[k].w[w];
+    store_nt(dst + i, o);
+  }
+}
+
 
 // binary32 -> bfloat16 with the conversion every bf16-storing kernel uses
 // (pack_bf16x2 / f32_to_bf16: v_cvt_pk_bf16_f32, round to nearest even), for
@@ -218,6 +240,24 @@ hipError_t launch_chain_2d(int dtype, const void* x, int64_t ldx, const void* b1
   if (dtype == 0) return launch_chain2d_io<F32IO>(x, ldx, b1, ldb1, b2, ldb2, y, ldy, rows, cols, scale, s);
   if (dtype == 1) return launch_chain2d_io<BF16IO>(x, ldx, b1, ldb1, b2, ldb2, y, ldy, rows, cols, scale, s);
   return launch_chain2d_io<F16IO>(x, ldx, b1, ldb1, b2, ldb2, y, ldy, rows, cols, scale, s);
+}
+
+hipError_t launch_stream(const void* const* srcs, int nsrc, void* dst, size_t bytes, hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  int64_t grid = (n16 + kBlock - 1) / kBlock;
+  if (grid > kMaxGrid) grid = kMaxGrid;
+  Srcs p = {{nullptr, nullptr, nullptr, nullptr}};
+  for (int k = 0; k < nsrc; ++k) p.p[k] = static_cast<const u32x4*>(srcs[k]);
+  u32x4* d = static_cast<u32x4*>(dst);
+  const dim3 g((unsigned)grid), b(kBlock);
+  switch (nsrc) {
+    case 1: hipLaunchKernelGGL(stream_kernel<1>, g, b, 0, s, p, d, n16); break;
+    case 2: hipLaunchKernelGGL(stream_kernel<2>, g, b, 0, s, p, d, n16); break;
+    case 3: hipLaunchKernelGGL(stream_kernel<3>, g, b, 0, s, p, d, n16); break;
+    case 4: hipLaunchKernelGGL(stream_kernel<4>, g, b, 0, s, p, d, n16); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {

@@ -48,6 +48,8 @@ hipError_t launch_layernorm_2d(int dtype, const void* x, int64_t ldx, const void
                                const void* gamma, const void* beta, void* y, int64_t ldy, int64_t rows,
                                int64_t cols, double eps, int act, const Drop* drop, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+// dst = srcs[0] ^ ... ^ srcs[nsrc - 1] (nsrc 1 .. 4), 16-byte accesses
+hipError_t launch_stream(const void* const* srcs, int nsrc, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
 
 // Unfused primitives (one launch each).

@@ -31,6 +31,8 @@ def test_header_declares_the_boundary():
                  "fused_layernorm_relu_dropout", "unfused_layernorm_relu_dropout",
                  "unfused_pointwise_chain", "unfused_row_mean_epilogue", "unfused_add_layernorm_gelu",
                  "grouped_row_mean_epilogue", "unfused_softmax", "mbp_graph_capture_begin", "mbp_graph_capture_end",
+                 "fused_add_layernorm_gelu_2d", "fused_layernorm_relu_dropout_2d", "fused_softmax_2d",
+                 "grouped_row_mean_epilogue_noalloc", "mbp_stream_rw",
                  "mbp_graph_launch", "mbp_graph_destroy"):
         assert name in fns
 
@@ -46,7 +48,7 @@ def test_library_exports_every_declared_symbol(mbp):
 
 
 def test_abi_version_and_strings(mbp):
-    assert mbp.lib.mbp_abi_version() == 5
+    assert mbp.lib.mbp_abi_version() == 6
     for code, name in mbp.STATUS_NAMES.items():
         assert mbp.lib.mbp_status_string(code)
     assert mbp.lib.mbp_status_string(99) == b"unknown status"
@@ -232,6 +234,56 @@ def test_unfused_softmax_validation(mbp):
     assert m.workspace_bytes(m.OP_SOFTMAX, m.BF16, 4, 8) == 4 * 256
     with pytest.raises(ValueError):
         m.workspace_bytes(m.OP_SOFTMAX, m.F16, 4, 8)
+
+
+def test_row_2d_validation(mbp):
+    """The strided forms of residual + LayerNorm + GeLU, LayerNorm-ReLU-dropout
+    and softmax: stride rules, in-place only with the same stride, gamma and
+    beta never overlapped."""
+    global L
+    L = mbp.lib
+    f = "fused_add_layernorm_gelu_2d"
+    # dtype, x, ldx, residual, ldr, gamma, beta, y, ldy, rows, cols, eps, act, stream
+    assert st(f, 2, A, 8, None, 0, B, B, Y, 8, 4, 8, 1e-5, 0, None) == 3          # fp16: not here
+    assert st(f, 1, A, 8, None, 0, B, B, Y, 8, 4, 8, 1e-5, 5, None) == 3          # unknown act
+    assert st(f, 1, A, 8, None, 0, B, B, Y, 8, 4, 8, -1.0, 0, None) == 8          # eps < 0
+    assert st(f, 1, A, 8, None, 0, B, B, Y, 8, 0, 8, 1e-5, 0, None) == 0          # rows == 0
+    assert st(f, 1, A, 6, None, 0, B, B, Y, 8, 4, 8, 1e-5, 0, None) == 2          # 0 < ldx < cols
+    assert st(f, 1, A, 8, B, 6, B + 64, B + 64, Y, 8, 4, 8, 1e-5, 0, None) == 2   # 0 < ldr < cols
+    assert st(f, 1, A, 8, None, 0, B, B, Y, 6, 4, 8, 1e-5, 0, None) == 2          # ldy < cols
+    assert st(f, 1, A, 8, None, 0, B, B, Y, 8, 4, mbp.MAX_COLS + 1, 1e-5, 0, None) == 2
+    assert st(f, 1, A, 8, None, 0, B, B, A, 16, 4, 8, 1e-5, 0, None) == 5         # y == x, other stride
+    assert st(f, 1, A, 8, None, 0, B, B, A + 2, 8, 4, 8, 1e-5, 0, None) == 5       # partial overlap
+    assert st(f, 1, A, 8, None, 0, Y + 4, B, Y, 8, 4, 8, 1e-5, 0, None) == 5       # y over gamma
+    assert st(f, 1, A, 8, None, 0, B, B, Y + 1, 8, 4, 8, 1e-5, 0, None) == 4       # y misaligned
+    assert st(f, 1, None, 8, None, 0, B, B, Y, 8, 4, 8, 1e-5, 0, None) == 1        # NULL x
+    d = "fused_layernorm_relu_dropout_2d"
+    # dtype, x, ldx, gamma, beta, y, ldy, rows, cols, eps, p, seed, offset, stream
+    assert st(d, 1, A, 8, B, B, Y, 8, 4, 8, 1e-5, 1.5, 0, 0, None) == 8           # p > 1
+    assert st(d, 1, A, 8, B, B, A, 12, 4, 8, 1e-5, 0.1, 0, 0, None) == 5          # y == x, other stride
+    assert st(d, 1, A, 5, B, B, Y, 8, 4, 8, 1e-5, 0.1, 0, 0, None) == 2           # 0 < ldx < cols
+    sm = "fused_softmax_2d"
+    # dtype, x, ldx, y, ldy, rows, cols, stream
+    assert st(sm, 3, A, 8, Y, 8, 4, 8, None) == 3                                  # DTYPE
+    assert st(sm, 1, A, 7, Y, 8, 4, 8, None) == 2                                  # 0 < ldx < cols
+    assert st(sm, 1, A, 8, A, 9, 4, 8, None) == 5                                  # y == x, other stride
+    assert st(sm, 1, A, 8, Y, 8, 0, 8, None) == 0                                  # rows == 0
+    assert st(sm, 1, A, 8, Y, 8, 4, mbp.MAX_COLS + 1, None) == 2
+
+
+def test_stream_rw_validation(mbp):
+    import ctypes
+    L = mbp.lib
+    arr = lambda *p: (ctypes.c_void_p * len(p))(*p)
+    f = L.mbp_stream_rw
+    assert f(arr(A), 0, Y, 64, None) == 8                 # nsrc < 1
+    assert f(arr(A, A, A, A, A), 5, Y, 64, None) == 8     # nsrc > 4
+    assert f(arr(A), 1, Y, 0, None) == 0                  # bytes == 0: no-op
+    assert f(arr(A, None), 2, Y, 64, None) == 1           # a NULL source
+    assert f(arr(A), 1, None, 64, None) == 1              # NULL dst
+    assert f(arr(A + 8), 1, Y, 64, None) == 4             # source off 16 bytes
+    assert f(arr(A), 1, Y, 24, None) == 4                 # bytes not a multiple of 16
+    assert f(arr(A, B), 2, B + 32, 64, None) == 5         # dst overlaps a source
 
 
 def test_convert_validation(mbp):

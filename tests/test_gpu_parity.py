@@ -1016,6 +1016,20 @@ def test_unfused_softmax(mbp, fmt, dtype, rows, cols):
 
 # ------------------------------------------------------------------ misc
 
+@pytest.mark.parametrize("nsrc", [1, 2, 3, 4])
+def test_stream_rw(mbp, nsrc):
+    """The calibration stream: dst = the bytewise XOR of its sources."""
+    rng = np.random.default_rng([61, nsrc])
+    n = (1 << 20) + 48
+    srcs = [rng.integers(0, 256, n, dtype=np.uint8) for _ in range(nsrc)]
+    dst = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    mbp.stream_rw([torch.from_numpy(a).cuda() for a in srcs], dst)
+    want = srcs[0].copy()
+    for a in srcs[1:]:
+        want ^= a
+    assert np.array_equal(dst.cpu().numpy(), want)
+
+
 def test_empty_inputs(mbp):
     """rows == 0 (n == 0) is a no-op for every entry point, fused and unfused."""
     e = torch.empty(0, device="cuda")
