@@ -262,7 +262,7 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
       }
       if (lane + k * LANES < nvec) sum += part;
     }
-    const Acc mean = group_sum<LANES, BLOCK>(sum, red[0]) / (Acc)cols;
+    const Acc mean = mean_cols(group_sum<LANES, BLOCK>(sum, red[0]), cols);
 
     Acc m2 = 0;
 #pragma unroll
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
       }
       if (lane + k * LANES < nvec) m2 += part;
     }
-    const Acc rstd = inv_sqrt(group_sum<LANES, BLOCK>(m2, red[1]) / (Acc)cols + eps);
+    const Acc rstd = inv_sqrt(div_cols(group_sum<LANES, BLOCK>(m2, red[1]), cols) + eps);
 
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
@@ -472,13 +472,13 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
     };
     Acc sum = 0;
     for (int c = lane; c < cols; c += LANES) sum += (Acc)val(c);
-    const Acc mean = group_sum<LANES, BLOCK>(sum, red[0]) / (Acc)cols;
+    const Acc mean = mean_cols(group_sum<LANES, BLOCK>(sum, red[0]), cols);
     Acc m2 = 0;
     for (int c = lane; c < cols; c += LANES) {
       const Acc d = (Acc)val(c) - mean;
       m2 = fma_t(d, d, m2);
     }
-    const Acc rstd = inv_sqrt(group_sum<LANES, BLOCK>(m2, red[1]) / (Acc)cols + eps);
+    const Acc rstd = inv_sqrt(div_cols(group_sum<LANES, BLOCK>(m2, red[1]), cols) + eps);
     if (live)
       for (int c = lane; c < cols; c += LANES) {
         float o = finish<Acc, EPI>((Acc)val(c) - mean, rstd, (Acc)IO::load1(gamma, c), (Acc)IO::load1(beta, c));
@@ -751,7 +751,7 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
       }
       if (used[k]) sum += part;
     }
-    const Acc mean = group_sum<LANES, BLOCK>(sum, red[0]) / (Acc)cols;
+    const Acc mean = mean_cols(group_sum<LANES, BLOCK>(sum, red[0]), cols);
 
     Acc m2 = 0;
 #pragma unroll
@@ -783,7 +783,7 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
       }
       if (used[k]) m2 += part;
     }
-    const Acc rstd = inv_sqrt(group_sum<LANES, BLOCK>(m2, red[1]) / (Acc)cols + eps);
+    const Acc rstd = inv_sqrt(div_cols(group_sum<LANES, BLOCK>(m2, red[1]), cols) + eps);
     if constexpr (kPhLds) lds_barrier();  // the generator blocks are in LDS
 
     if (!live) continue;
@@ -1060,7 +1060,7 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_shift_kernel(
       for (int e = 0; e < V; ++e) part += (Acc)v[k][e];
       if (j < nvec) sum += part;
     }
-    const Acc mean = group_sum<LANES, BLOCK>(sum, red[0]) / (Acc)cols;
+    const Acc mean = mean_cols(group_sum<LANES, BLOCK>(sum, red[0]), cols);
 
     Acc m2 = 0;
 #pragma unroll
@@ -1082,7 +1082,7 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_shift_kernel(
       for (int e = 0; e < V; ++e) part = fma_t(dd[e], dd[e], part);
       if (j < nvec) m2 += part;
     }
-    const Acc rstd = inv_sqrt(group_sum<LANES, BLOCK>(m2, red[1]) / (Acc)cols + eps);
+    const Acc rstd = inv_sqrt(div_cols(group_sum<LANES, BLOCK>(m2, red[1]), cols) + eps);
 
     u32x4 ov[VPL + 1];
 #pragma unroll
@@ -1223,11 +1223,14 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &ldx, &ldr, &ldy, &eps, &drop};
   if (aligned) {
     const void* k = shape_kernel<VecSel<IO, RES, EPI>::template K>(i);
-    // fp32 rows, when there are thousands of row groups: two per block
+    // two row groups per block, when there are thousands: fp32 rows
     // (measured at 8192 x 4096: 46.2 us against 47.5 for one; 4 or 8 per
-    // block no better; bf16 rows gain nothing)
+    // block no better) and the dropout epilogue, whose per-block set-up is
+    // then paid once for two rows (16384 x 8192 bf16: 96.8 -> 91.9 us; 4 or 8
+    // per block no better; 512 x 2 and 1024 x 1 layouts 23% and 33% slower);
+    // the other bf16 rows gain nothing
     int vgrid = grid;
-    if (sizeof(typename IO::elem) == 4 && groups >= 4096) vgrid = (int)((groups + 1) / 2);
+    if ((sizeof(typename IO::elem) == 4 || EPI == kEpiReluDrop) && groups >= 4096) vgrid = (int)((groups + 1) / 2);
     return hipLaunchKernel(k, dim3(vgrid), dim3(block), args, 0, s);
   }
   const uintptr_t ax = reinterpret_cast<uintptr_t>(x);

@@ -42,14 +42,26 @@ __device__ __forceinline__ void ms_merge(float& m, float& l, float om, float ol)
   l = a + b;
 }
 
+template <int S>
+__device__ __forceinline__ void merge_stage(float& m, float& l) {
+  float ma, mb, la, lb;
+  lane_pair<S>(m, ma, mb);
+  lane_pair<S>(l, la, lb);
+  m = ma;
+  l = la;
+  ms_merge(m, l, mb, lb);
+}
+
 template <int LANES, int BLOCK>
 __device__ __forceinline__ void group_merge(float& m, float& l, float* lds_m, float* lds_l) {
   constexpr int kIn = LANES < 64 ? LANES : 64;
-#pragma unroll
-  for (int k = 1; k < kIn; k <<= 1) {
-    const float om = __shfl_xor(m, k), ol = __shfl_xor(l, k);
-    ms_merge(m, l, om, ol);
-  }
+  // butterfly stages as in wave_reduce; ms_merge is symmetric in its two pairs
+  if constexpr (kIn > 1) merge_stage<1>(m, l);
+  if constexpr (kIn > 2) merge_stage<2>(m, l);
+  if constexpr (kIn > 4) merge_stage<4>(m, l);
+  if constexpr (kIn > 8) merge_stage<8>(m, l);
+  if constexpr (kIn > 16) merge_stage<16>(m, l);
+  if constexpr (kIn > 32) merge_stage<32>(m, l);
   if constexpr (LANES > 64) {
     constexpr int kWaves = LANES / 64;
     const int wave = threadIdx.x >> 6;

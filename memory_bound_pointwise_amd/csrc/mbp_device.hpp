@@ -1,6 +1,6 @@
 // mbp_device.hpp -- device-side building blocks shared by the HIP kernels of
 // libmbp: 128-bit vector types, bfloat16 unpack/pack, and the deterministic
-// lane-group sum used by every row reduction.
+// lane-group reductions used by every row reduction.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -205,19 +205,86 @@ __device__ __forceinline__ void dropout_bits(uint64_t i0, uint64_t seed, uint64_
   }
 }
 
-// Sum of v over a group of LANES consecutive lanes (LANES a power of two).
-// Within a wave: xor butterfly.  Because a + b == b + a exactly in IEEE
-// arithmetic, both partners of every exchange compute the same value, so all
-// lanes of the group end with bitwise the same sum, independent of timing.
-// Groups wider than a wave: each wave writes its partial to LDS, one barrier,
-// and every lane adds the group's partials in wave order.  `lds` must hold one
-// slot per wave of the block and must not be rewritten by any lane before all
-// lanes have read it (callers alternate between slots).
-template <int LANES, int BLOCK, typename T>
-__device__ __forceinline__ T group_sum(T v, T* lds) {
-  constexpr int kIn = LANES < 64 ? LANES : 64;
-#pragma unroll
-  for (int m = 1; m < kIn; m <<= 1) v += __shfl_xor(v, m);
+// Butterfly exchange within a wave, without LDS traffic.  lane_pair<S>(v, a, b)
+// (S = 1, 2, 4, 8, 16, 32) hands each lane the values {a, b} of itself and of
+// its partner at stage S of an all-reduce; both lanes of a pair get the same
+// two values, so a symmetric combine (a + b, max) leaves them bitwise equal.
+// Stages 1 and 2 pair lane i with i ^ 1 and i ^ 2 (DPP quad permutations).
+// Stages 4 and 8 pair it with 7 - i and 15 - i within its 8 and 16 lanes (DPP
+// row_half_mirror, row_mirror): like i ^ 4 and i ^ 8 these pair whole blocks of
+// 4 and 8 lanes, and once each block holds a single value, as it does after the
+// earlier stages, they combine the same values.  Stages 16 and 32 swap rows of
+// 16 lanes and the halves of the wave (gfx950's v_permlane16_swap and
+// v_permlane32_swap), which give both lanes {lower one's value, upper one's}.
+template <int S>
+__device__ __forceinline__ void lane_pair(uint32_t v, uint32_t& a, uint32_t& b) {
+  if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  } else if constexpr (S == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  } else {
+    static_assert(S == 1 || S == 2 || S == 4 || S == 8, "stage");
+    constexpr int kCtrl = S == 1 ? 0xB1 : S == 2 ? 0x4E : S == 4 ? 0x141 : 0x140;
+    a = v;
+    b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xf, 0xf, false);
+  }
+}
+template <int S>
+__device__ __forceinline__ void lane_pair(float v, float& a, float& b) {
+  uint32_t ua, ub;
+  lane_pair<S>(__builtin_bit_cast(uint32_t, v), ua, ub);
+  a = __builtin_bit_cast(float, ua);
+  b = __builtin_bit_cast(float, ub);
+}
+template <int S>
+__device__ __forceinline__ void lane_pair(double v, double& a, double& b) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  uint32_t la, lb, ha, hb;
+  lane_pair<S>((uint32_t)u, la, lb);
+  lane_pair<S>((uint32_t)(u >> 32), ha, hb);
+  a = __builtin_bit_cast(double, ((uint64_t)ha << 32) | la);
+  b = __builtin_bit_cast(double, ((uint64_t)hb << 32) | lb);
+}
+
+struct SumOp {
+  template <typename T>
+  __device__ __forceinline__ T operator()(T a, T b) const { return a + b; }
+};
+// `>` never selects a NaN: callers keep NaN out of the operands.
+struct MaxOp {
+  template <typename T>
+  __device__ __forceinline__ T operator()(T a, T b) const { return b > a ? b : a; }
+};
+
+// All-reduce of v with op over groups of N consecutive lanes (N a power of
+// two, at most 64) inside a wave; every lane of a group ends with bitwise the
+// same value.
+template <int N, typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  T a, b;
+  if constexpr (N > 1) { lane_pair<1>(v, a, b); v = op(a, b); }
+  if constexpr (N > 2) { lane_pair<2>(v, a, b); v = op(a, b); }
+  if constexpr (N > 4) { lane_pair<4>(v, a, b); v = op(a, b); }
+  if constexpr (N > 8) { lane_pair<8>(v, a, b); v = op(a, b); }
+  if constexpr (N > 16) { lane_pair<16>(v, a, b); v = op(a, b); }
+  if constexpr (N > 32) { lane_pair<32>(v, a, b); v = op(a, b); }
+  return v;
+}
+
+// op over a group of LANES consecutive lanes (LANES a power of two), every
+// lane of the group ending with bitwise the same value, independent of timing.
+// Within a wave: wave_reduce.  Groups wider than a wave: each wave writes its
+// result to LDS, one barrier, and every lane combines the group's partials in
+// wave order.  `lds` must hold one slot per wave of the block and must not be
+// rewritten by any lane before all lanes have read it (callers alternate
+// between slots).
+template <int LANES, int BLOCK, typename T, typename Op>
+__device__ __forceinline__ T group_reduce(T v, T* lds, Op op) {
+  v = wave_reduce<(LANES < 64 ? LANES : 64)>(v, op);
   if constexpr (LANES <= 64) {
     return v;
   } else {
@@ -229,38 +296,23 @@ __device__ __forceinline__ T group_sum(T v, T* lds) {
     const int first = (threadIdx.x / LANES) * kWaves;
     T s = lds[first];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) s += lds[first + w];
+    for (int w = 1; w < kWaves; ++w) s = op(s, lds[first + w]);
     return s;
   }
 }
 
-// Maximum of v over a group of LANES consecutive lanes, laid out as for
-// group_sum.  The maximum is exact and independent of the combine order, so
-// every lane ends with the same value.  Comparisons with `>` never select a
-// NaN: callers keep NaN out of v (a NaN element propagates later, as in the
-// sum of exponentials).
+// Sum of v over a group of LANES consecutive lanes, as group_reduce.
+template <int LANES, int BLOCK, typename T>
+__device__ __forceinline__ T group_sum(T v, T* lds) {
+  return group_reduce<LANES, BLOCK>(v, lds, SumOp());
+}
+
+// Maximum of v over a group of LANES consecutive lanes, as group_reduce.  The
+// maximum is exact and independent of the combine order.  Callers keep NaN out
+// of v (a NaN element propagates later, as in the sum of exponentials).
 template <int LANES, int BLOCK, typename T>
 __device__ __forceinline__ T group_max(T v, T* lds) {
-  constexpr int kIn = LANES < 64 ? LANES : 64;
-#pragma unroll
-  for (int m = 1; m < kIn; m <<= 1) {
-    const T o = __shfl_xor(v, m);
-    v = o > v ? o : v;
-  }
-  if constexpr (LANES <= 64) {
-    return v;
-  } else {
-    static_assert(LANES % 64 == 0 && BLOCK % LANES == 0, "wave-multiple groups");
-    constexpr int kWaves = LANES / 64;
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) lds[wave] = v;
-    lds_barrier();
-    const int first = (threadIdx.x / LANES) * kWaves;
-    T s = lds[first];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) s = lds[first + w] > s ? lds[first + w] : s;
-    return s;
-  }
+  return group_reduce<LANES, BLOCK>(v, lds, MaxOp());
 }
 
 }  // namespace mbp

@@ -38,8 +38,32 @@ __device__ __forceinline__ void opaque(u32x4& v) {
 __device__ __forceinline__ float fma_t(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
 __device__ __forceinline__ double fma_t(double a, double b, double c) { return __builtin_fma(a, b, c); }
 
-__device__ __forceinline__ float inv_sqrt(float a) { return 1.0f / __builtin_sqrtf(a); }
+// 1 / sqrt(a).  fp32 statistics (16-bit I/O): v_rsq_f32, within about an
+// ulp, where a correctly rounded square root and an IEEE division would cost
+// some twenty instructions per row in every wave; binary64 statistics keep
+// the correctly rounded root and division.
+__device__ __forceinline__ float inv_sqrt(float a) { return __builtin_amdgcn_rsqf(a); }
 __device__ __forceinline__ double inv_sqrt(double a) { return 1.0 / __builtin_sqrt(a); }
+
+// v / n for a row length n: fp32 statistics multiply by v_rcp_f32(n) (within
+// about an ulp of the quotient, exact for powers of two) instead of an IEEE
+// division sequence; binary64 statistics divide.
+__device__ __forceinline__ float div_cols(float v, int n) { return v * __builtin_amdgcn_rcpf((float)n); }
+__device__ __forceinline__ double div_cols(double v, int n) { return v / (double)n; }
+
+// The row mean s / n.  fp32: the quotient q = s * rcp(n) corrected once with
+// its residual s - q n (exact in an fma), which lands within half an ulp but
+// for rare ties and returns c exactly when s = n c exactly (a row of equal
+// values), where q alone can be an ulp off, and that ulp, divided by the
+// row's zero spread, would be scaled up by 1 / sqrt(eps); the mean's error
+// counts |mean| / sigma times in the output, so it gets the two extra
+// instructions the spread's quotient does not need.  binary64: division.
+__device__ __forceinline__ float mean_cols(float s, int n) {
+  const float nf = (float)n, r = __builtin_amdgcn_rcpf(nf);
+  const float q = s * r;
+  return __builtin_fmaf(__builtin_fmaf(-q, nf, s), r, q);
+}
+__device__ __forceinline__ double mean_cols(double s, int n) { return s / (double)n; }
 
 // (LANES, VPL) layouts.  The first layout whose LANES * VPL vectors cover the
 // row is used.  At most 5 vectors (40 bf16 / 20 fp32 values) per lane keeps the

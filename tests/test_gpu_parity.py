@@ -358,12 +358,24 @@ def test_ln_bf16_rows_far_from_zero(mbp, cols, offset):
         print(f"bf16 {rows}x{cols} rows around {offset}, element offsets {offs}: max abs err {err:.3g}")
 
 
-def test_ln_constant_rows_give_beta(mbp):
+@pytest.mark.parametrize("cols", [4096, 4095, 1001, 768, 12287])
+def test_ln_constant_rows_give_beta(mbp, cols):
+    """A row of equal values has mean exactly that value and variance 0, so the
+    output is beta exactly.  Row lengths that are not powers of two catch a
+    mean taken as sum * (1 / cols) without correction: one ulp off, and that
+    ulp over a zero spread is scaled up by 1 / sqrt(eps).  Values of several
+    magnitudes (x 1, x 1000) in every row layout kernel."""
     for name in ("ln_8192x4096_f32", "addln_gelu_16384x8192_bf16"):
-        w, d, _ = _ln_case(name, 4, 4096, residual=False)
-        d["x"] = np.repeat(d["x"][:, :1], 4096, axis=1)
+        w, d, _ = _ln_case(name, 6, cols, residual=False)
+        col = d["x"][:, :1]
+        if w.dtype == "bf16":
+            f = W.bf16_bits_to_f32(col)
+            col = np.concatenate([col[:3], W.f32_to_bf16_bits(f[3:] * np.float32(1000.0))])
+        else:
+            col = np.concatenate([col[:3], col[3:] * np.float32(1000.0)]).astype(np.float32)
+        d["x"] = np.ascontiguousarray(np.repeat(col, cols, axis=1))
         y = to_host(_ln_run(mbp, d, "none"))
-        assert np.array_equal(y, np.broadcast_to(d["beta"], y.shape)), f"{name}: constant row != beta"
+        assert np.array_equal(y, np.broadcast_to(d["beta"], y.shape)), f"{name} {cols}: constant row != beta"
 
 
 def test_ln_f32_two_groups_per_block(mbp):
