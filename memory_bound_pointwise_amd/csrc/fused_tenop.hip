@@ -2,7 +2,8 @@
 // model at the top of the post) as one row kernel:
 //
 //   t = x*alpha + bias;  a = relu(t);  s = a*a + a*c;
-//   m = (row sum of s) / cols   (section 6.4: a sum, then the division);
+//   m = (row sum of s) / cols   (section 6.4: a sum, then the division; here
+//                                the sum times 1/cols, within a binary64 ulp);
 //   y = (s - m)*gamma + beta
 //
 // Section 8 of that post describes the fused kernel Inductor generates: one
@@ -74,7 +75,7 @@ template <class IO, int LANES, int VPL, int VW>
 __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
     const typename IO::elem* x, int64_t ldx, const typename IO::elem* __restrict__ bias,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
-    typename IO::elem* y, int64_t ldy, int64_t rows, int cols, double alpha, double c) {
+    typename IO::elem* y, int64_t ldy, int64_t rows, int cols, double alpha, double c, double inv_cols) {
   typedef typename IO::elem E;
   constexpr int BLOCK = block_for(LANES);
   constexpr int RPB = BLOCK / LANES;
@@ -144,7 +145,18 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
       }
       if (lane + k * LANES < nvec) sum += part;
     }
-    const double m = group_sum<LANES, BLOCK>(sum, red[parity]) / (double)cols;
+    // gamma and beta widened while the reduction's exchanges are in flight
+    double gd[VPL][VW], bd[VPL][VW];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+#pragma unroll
+      for (int e = 0; e < VW; ++e) {
+        gd[k][e] = (double)g[k][e];
+        bd[k][e] = (double)be[k][e];
+        opaque(gd[k][e]);
+        opaque(bd[k][e]);
+      }
+    const double m = group_sum<LANES, BLOCK>(sum, red[parity]) * inv_cols;
 
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
@@ -153,7 +165,7 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
       uint32_t o[VW];
 #pragma unroll
       for (int e = 0; e < VW; ++e)
-        o[e] = narrow_bits<IO>(__builtin_fma(s[k][e] - m, (double)g[k][e], (double)be[k][e]));
+        o[e] = narrow_bits<IO>(__builtin_fma(s[k][e] - m, gd[k][e], bd[k][e]));
       if constexpr (VW == 1) {
         if constexpr (sizeof(E) == 4) yr[vi] = __uint_as_float(o[0]);
         else yr[vi] = (uint16_t)o[0];
@@ -175,7 +187,7 @@ template <class IO, int LANES, int VPL, bool KEEP>
 __global__ __launch_bounds__(block_for(LANES)) void tenop8_kernel(
     const typename IO::elem* x, int64_t ldx, const typename IO::elem* __restrict__ bias,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
-    typename IO::elem* y, int64_t ldy, int64_t rows, int cols, double alpha, double c) {
+    typename IO::elem* y, int64_t ldy, int64_t rows, int cols, double alpha, double c, double inv_cols) {
   typedef typename IO::elem E;
   static_assert(sizeof(E) == 2, "16-bit storage only");
   constexpr int BLOCK = block_for(LANES);
@@ -224,7 +236,7 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop8_kernel(
       }
       if (lane + k * LANES < nvec) sum += part;
     }
-    const double m = group_sum<LANES, BLOCK>(sum, red[parity]) / (double)cols;
+    const double m = group_sum<LANES, BLOCK>(sum, red[parity]) * inv_cols;
 
     if constexpr (!KEEP) {
       // new values as far as the compiler knows: s is evaluated again below,
@@ -308,6 +320,13 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
   int lanes = kShapes[shape].lanes;
   if constexpr (sizeof(E) == 2) {
     if (vector8_ok) k = shape_kernel<Tenop8Sel<IO>::template K>(shape);
+    // rows of 65-128 vectors: 64 lanes x 2 rather than the table's 32 x 4
+    // (8192 x 1024 fp16, row stride 1056: 10.26 against 10.57 us; 128 x 1:
+    // 10.63)
+    if (vector8_ok && cols / 8 > 64 && cols / 8 <= 128) {
+      lanes = 64;
+      k = reinterpret_cast<const void*>(&tenop8_kernel<IO, 64, 2, true>);
+    }
   } else {
     // fp32 rows of at most 256 vectors: one vector per lane (measured at
     // 1024 x 1024: 3.67 us against 3.80 for 64 lanes x 4; 8192 x 1024: 14.1
@@ -330,7 +349,8 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
   const E *xe = static_cast<const E*>(x), *bie = static_cast<const E*>(bias);
   const E *ge = static_cast<const E*>(gamma), *bee = static_cast<const E*>(beta);
   E* ye = static_cast<E*>(y);
-  void* args[] = {&xe, &ldx, &bie, &ge, &bee, &ye, &ldy, &rows, &icols, &alpha, &c};
+  double inv_cols = 1.0 / (double)cols;  // the mean is the row sum times this
+  void* args[] = {&xe, &ldx, &bie, &ge, &bee, &ye, &ldy, &rows, &icols, &alpha, &c, &inv_cols};
   return hipLaunchKernel(k, dim3(grid), dim3(block), args, 0, s);
 }
 

@@ -28,6 +28,7 @@ constexpr int block_for(int lanes) { return lanes > kMinBlock ? lanes : kMinBloc
 // a loop-invariant value from being widened once and held wide across a loop).
 __device__ __forceinline__ void opaque(float& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(double& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void opaque(u32x4& v) {
 #pragma unroll
