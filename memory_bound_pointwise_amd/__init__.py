@@ -24,7 +24,7 @@ F32, BF16, F16 = 0, 1, 2
 ACT_NONE, ACT_GELU_TANH = 0, 1
 OP_CHAIN, OP_ROW_MEAN, OP_LAYERNORM, OP_LN_RELU_DROPOUT, OP_SOFTMAX = 0, 1, 2, 3, 4
 UNFUSED_PRIMITIVE, UNFUSED_EAGER, UNFUSED_GROUPED = 0, 1, 2
-MAX_COLS = 16384
+MAX_COLS = 32768
 
 STATUS_NAMES = {0: "MBP_OK", 1: "MBP_ERR_NULL", 2: "MBP_ERR_SHAPE", 3: "MBP_ERR_DTYPE",
                 4: "MBP_ERR_ALIGN", 5: "MBP_ERR_OVERLAP", 6: "MBP_ERR_WORKSPACE",

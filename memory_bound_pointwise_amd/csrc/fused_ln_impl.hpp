@@ -156,6 +156,57 @@ __device__ __forceinline__ void halves_at(const u32x4& w0, const u32x4& w1, int 
   for (int e = 0; e < 8; ++e) h[e] = (e & 1) ? (r[e >> 1] >> 16) : (r[e >> 1] & 0xFFFFu);
 }
 
+// ------------------------------------------------------------ wide rows
+
+// Rows of more than kRegCols columns: one 1024-lane block per row, three
+// passes over it -- the sum, the squared deviations about the mean, the
+// output -- the second and third rereading x (and the residual) from the
+// caches.  Column c is lane c mod 1024's; any width, alignment and row
+// strides.  The statistics are those of the register-resident kernels.
+template <class IO, bool RES, int EPI>
+__global__ __launch_bounds__(1024) void ln_wide_kernel(
+    const typename IO::elem* x, const typename IO::elem* res,
+    const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
+    typename IO::elem* y, int64_t rows, int cols, int64_t ldx, int64_t ldr, int64_t ldy, double eps_d,
+    Drop drop) {
+  typedef typename Types<IO, RES>::acc Acc;
+  typedef typename Types<IO, RES>::val Val;
+  constexpr int LANES = 1024;
+  __shared__ Acc red[2][LANES / 64];
+  const int lane = threadIdx.x;
+  const Acc eps = (Acc)eps_d;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const typename IO::elem* xr = x + row * ldx;
+    const typename IO::elem* rr = RES ? res + row * ldr : nullptr;
+    typename IO::elem* yr = y + row * ldy;
+    Acc sum = 0;
+#pragma unroll 4
+    for (int c = lane; c < cols; c += LANES) {
+      Val t = (Val)IO::load1(xr, c);
+      if constexpr (RES) t += (Val)IO::load1(rr, c);
+      sum += (Acc)t;
+    }
+    const Acc mean = mean_cols(group_sum<LANES, LANES>(sum, red[0]), cols);
+    Acc m2 = 0;
+#pragma unroll 4
+    for (int c = lane; c < cols; c += LANES) {
+      Val t = (Val)IO::load1(xr, c);
+      if constexpr (RES) t += (Val)IO::load1(rr, c);
+      const Acc d = (Acc)t - mean;
+      m2 = fma_t(d, d, m2);
+    }
+    const Acc rstd = inv_sqrt(div_cols(group_sum<LANES, LANES>(m2, red[1]), cols) + eps);
+#pragma unroll 4
+    for (int c = lane; c < cols; c += LANES) {
+      Val t = (Val)IO::load1(xr, c);
+      if constexpr (RES) t += (Val)IO::load1(rr, c);
+      float o = finish<Acc, EPI>((Acc)t - mean, rstd, (Acc)IO::load1(gamma, c), (Acc)IO::load1(beta, c));
+      if constexpr (EPI == kEpiReluDrop) relu_dropout<1, true>(&o, (uint64_t)row * (uint64_t)cols + (uint64_t)c, drop);
+      IO::store1(yr, c, o);
+    }
+  }
+}
+
 // ------------------------------------------------------------ aligned rows
 
 template <class IO, int LANES, int VPL, bool RES, int EPI>
@@ -1211,6 +1262,14 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   const bool aligned = aligned16(x) && aligned16(y) && (!res || aligned16(res)) && aligned16(gamma) &&
                        aligned16(beta) && cols % V == 0 && (ES * ldx) % 16 == 0 && (ES * ldy) % 16 == 0 &&
                        (!res || (ES * ldr) % 16 == 0);
+  if (cols > kRegCols) {  // rows wider than the register-resident layouts
+    const int wgrid = (int)(rows < 4096 ? rows : 4096);
+    int wcols = (int)cols;
+    Drop wdrop = drop_in;
+    void* wargs[] = {&x, &res, &gamma, &beta, &y, &rows, &wcols, &ldx, &ldr, &ldy, &eps, &wdrop};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&ln_wide_kernel<IO, RES, EPI>), dim3(wgrid),
+                           dim3(1024), wargs, 0, s);
+  }
   const int i = pick_shape((cols + V - 1) / V);
   if (i < 0) return hipErrorInvalidValue;
   const int lanes = kShapes[i].lanes;

@@ -164,6 +164,37 @@ __global__ __launch_bounds__(block_for(LANES)) void softmax_kernel(const typenam
   }
 }
 
+// Rows of more than kRegCols columns: one 1024-lane block per row, three
+// passes -- the row maximum M, then L = sum of exp(x - M), then the output
+// exp(x - M) / L -- the later two rereading x from the caches; any width,
+// alignment and row strides.  -inf entries give exactly 0, a row of -inf
+// only gives NaN (0 / 0) and a NaN makes its row NaN, as in softmax_kernel.
+template <class IO>
+__global__ __launch_bounds__(1024) void softmax_wide_kernel(const typename IO::elem* x, typename IO::elem* y,
+                                                            int64_t rows, int cols, int64_t ldx, int64_t ldy) {
+  constexpr int LANES = 1024;
+  __shared__ float red[2][LANES / 64];
+  const int lane = threadIdx.x;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const typename IO::elem* xr = x + row * ldx;
+    typename IO::elem* yr = y + row * ldy;
+    float m = -__builtin_inff();
+#pragma unroll 4
+    for (int c = lane; c < cols; c += LANES) m = __builtin_fmaxf(m, IO::load1(xr, c));
+    m = group_max<LANES, LANES>(m, red[0]);
+    const float mm = (m == -__builtin_inff()) ? 0.0f : m;
+    float l = 0.0f;
+#pragma unroll 4
+    for (int c = lane; c < cols; c += LANES) l += exp_f(IO::load1(xr, c) - mm);
+    l = group_sum<LANES, LANES>(l, red[1]);
+    const float inv_l = 1.0f / l;
+#pragma unroll 4
+    for (int c = lane; c < cols; c += LANES) IO::store1(yr, c, exp_f(IO::load1(xr, c) - mm) * inv_l);
+    // red[0] is written again by the next row's maximum only after every lane
+    // has passed this row's second barrier (red[1])
+  }
+}
+
 // Element e of a packed output vector, as stored bits.
 template <class IO>
 __device__ __forceinline__ typename IO::elem stored_elem(const u32x4& v, int e) {
@@ -379,6 +410,12 @@ hipError_t launch_softmax_io(const void* x, int64_t ldx, void* y, int64_t ldy, i
   constexpr int64_t ES = (int64_t)sizeof(E);
   if (rows == 1) ldx = ldy = cols;  // one row: its stride is never used
   const int64_t nvec = (cols + V - 1) / V;
+  if (cols > kRegCols) {  // rows wider than the register-resident layouts
+    const int wgrid = (int)(rows < 4096 ? rows : 4096);
+    hipLaunchKernelGGL(softmax_wide_kernel<IO>, dim3(wgrid), dim3(1024), 0, s, static_cast<const E*>(x),
+                       static_cast<E*>(y), rows, (int)cols, ldx, ldy);
+    return hipGetLastError();
+  }
   const int shape = pick_shape(nvec);
   if (shape < 0) return hipErrorInvalidValue;
   const int block = block_for(kShapes[shape].lanes);

@@ -176,6 +176,44 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
   }
 }
 
+// s = relu(x * alpha + bias) * (relu(...) + c) as the 10-op kernels form it
+__device__ __forceinline__ double tenop_s(float xv, float bv, double alpha, double c) {
+  const double t = __builtin_fma((double)xv, alpha, (double)bv);
+  const double a = (t < 0.0) ? 0.0 : t;  // relu; NaN passes through
+  return __builtin_fma(a, a, a * c);
+}
+
+// Rows of more than kRegCols columns: one 1024-lane block per row, two
+// passes -- s and its row sum, then s again (the same binary64 operations)
+// and the output -- the second rereading x from the caches; any width,
+// alignment and row strides.
+template <class IO>
+__global__ __launch_bounds__(1024) void tenop_wide_kernel(
+    const typename IO::elem* x, int64_t ldx, const typename IO::elem* __restrict__ bias,
+    const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
+    typename IO::elem* y, int64_t ldy, int64_t rows, int cols, double alpha, double c, double inv_cols) {
+  constexpr int LANES = 1024;
+  __shared__ double red[2][LANES / 64];  // alternating by row
+  const int lane = threadIdx.x;
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x, parity ^= 1) {
+    const typename IO::elem* xr = x + row * ldx;
+    typename IO::elem* yr = y + row * ldy;
+    double sum = 0.0;
+#pragma unroll 4
+    for (int j = lane; j < cols; j += LANES) sum += tenop_s(IO::load1(xr, j), IO::load1(bias, j), alpha, c);
+    const double m = group_sum<LANES, LANES>(sum, red[parity]) * inv_cols;
+#pragma unroll 4
+    for (int j = lane; j < cols; j += LANES) {
+      const double sv = tenop_s(IO::load1(xr, j), IO::load1(bias, j), alpha, c);
+      const uint32_t o =
+          narrow_bits<IO>(__builtin_fma(sv - m, (double)IO::load1(gamma, j), (double)IO::load1(beta, j)));
+      if constexpr (sizeof(typename IO::elem) == 4) yr[j] = __uint_as_float(o);
+      else yr[j] = (uint16_t)o;
+    }
+  }
+}
+
 // 16-bit storage on 16-byte boundaries: 8 elements per access (one 16-byte
 // load or store per vector).  The row and the parameters stay in storage form.
 // KEEP: s is held in binary64 registers from the row sum to the epilogue (two
@@ -313,6 +351,13 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
   const bool vector8_ok = sizeof(E) == 2 && (cols % 8) == 0 && aligned16(x) && aligned16(y) &&
                           aligned16(bias) && aligned16(gamma) && aligned16(beta) && ldx % 8 == 0 &&
                           ldy % 8 == 0;
+  if (cols > kRegCols) {  // rows wider than the register-resident layouts
+    const int wgrid = (int)(rows < 4096 ? rows : 4096);
+    hipLaunchKernelGGL(tenop_wide_kernel<IO>, dim3(wgrid), dim3(1024), 0, s, static_cast<const E*>(x), ldx,
+                       static_cast<const E*>(bias), static_cast<const E*>(gamma), static_cast<const E*>(beta),
+                       static_cast<E*>(y), ldy, rows, (int)cols, alpha, c, 1.0 / (double)cols);
+    return hipGetLastError();
+  }
   const int shape = vector8_ok ? pick_shape(cols / 8) : pick_shape((cols + 3) / 4);
   if (shape < 0) return hipErrorInvalidValue;
   const void* k = vector_ok ? shape_kernel<TenopSel<IO, true>::template K>(shape)

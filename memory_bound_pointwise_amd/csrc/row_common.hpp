@@ -66,6 +66,11 @@ __device__ __forceinline__ float mean_cols(float s, int n) {
 }
 __device__ __forceinline__ double mean_cols(double s, int n) { return s / (double)n; }
 
+// Rows of more than kRegCols columns are not held in registers: they take
+// the three-pass row kernels (one 1024-lane block per row, the later passes
+// rereading the row from the caches), which hold nothing per element.
+constexpr int64_t kRegCols = 16384;
+
 // (LANES, VPL) layouts.  The first layout whose LANES * VPL vectors cover the
 // row is used.  At most 5 vectors (40 bf16 / 20 fp32 values) per lane keeps the
 // kernels free of register spills; wider rows take wider groups.

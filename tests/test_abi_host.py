@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(mbp):
 
 
 def test_abi_version_and_strings(mbp):
-    assert mbp.lib.mbp_abi_version() == 6
+    assert mbp.lib.mbp_abi_version() == 7
     for code, name in mbp.STATUS_NAMES.items():
         assert mbp.lib.mbp_status_string(code)
     assert mbp.lib.mbp_status_string(99) == b"unknown status"
