@@ -48,7 +48,10 @@ Printed: one JSON line with
 Other modes (for rocprofv3 counter runs): --only NAME runs just one workload's
 fused kernel; --copy-bytes B runs the library's streaming copy of B bytes;
 --no-graphs times every batch as eager calls (no graph capture, no launch
-study), so that each kernel is an ordinary dispatch.
+study), so that each kernel is an ordinary dispatch; --element-check runs the
+fp32 two-dimensional chain on rows one element off 16-byte boundaries (its
+element path: 4-byte accesses), whose bytes are known, to check the HBM
+counters' scale on a request mix other than the copy's.
 """
 from __future__ import annotations
 
@@ -86,6 +89,9 @@ def parse():
                    help="time the batches as eager calls only (no graph capture; for counter runs)")
     p.add_argument("--unfused-only", default=None, help="run only this workload's unfused variant")
     p.add_argument("--copy-bytes", type=int, default=0, help="run the streaming copy of this size")
+    p.add_argument("--element-check", action="store_true",
+                   help="run the fp32 chain on rows off 16-byte boundaries (one element per access), "
+                        "for checking the HBM counters' scale on that request mix")
     return p.parse_args()
 
 
@@ -146,6 +152,20 @@ def main():
             mbp.stream_copy(src, dst)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes": n * 4, "launches": args.warmup + args.steps}))
+        return
+
+    if args.element_check:
+        # [8192, 4095] fp32 operands in rows of 4096, one element past a
+        # 16-byte boundary: the two-dimensional chain takes its element path
+        rows, cols, ld = 8192, 4095, 4096
+        bufs = [torch.randn(rows * ld + 4, device=dev) for _ in range(4)]
+        x, b1, b2, y = (b[1:1 + rows * ld].view(rows, ld)[:, :cols] for b in bufs)
+        for _ in range(args.warmup + args.steps):
+            mbp.fused_pointwise_chain_2d(x, b1, b2, 0.5, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "element-check", "rows": rows, "cols": cols, "row_stride": ld,
+                          "bytes_read_per_call": 3 * rows * cols * 4, "bytes_written_per_call": rows * cols * 4,
+                          "launches": args.warmup + args.steps}))
         return
 
     names = [w.name for w in W.WORKLOADS]
