@@ -559,7 +559,8 @@ def _gate_2d(y, exact, fmt, what, row_kernel=False):
 CHAIN_2D = [  # rows, cols, x pad, y pad, b1, b2
     (37, 1000, 0, 0, "full", "full"), (37, 1003, 0, 0, "full", "full"),
     (19, 512, 8, 24, "row", "full"), (19, 515, 3, 5, "expand", "row"),
-    (1, 4099, 0, 0, "row", "row"), (64, 8, 0, 0, "expand", "expand"), (300, 24, 8, 0, "row", "expand")]
+    (1, 4099, 0, 0, "row", "row"), (64, 8, 0, 0, "expand", "expand"), (300, 24, 8, 0, "row", "expand"),
+    (23, 4095, 1, 3, "full", "row"), (9, 1024, 5, 0, "expand", "full"), (5, 20001, 3, 1, "row", "full")]
 
 
 @pytest.mark.parametrize("fmt,dtype", DT2D, ids=[d[0] for d in DT2D])
