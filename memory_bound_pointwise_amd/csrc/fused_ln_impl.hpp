@@ -1323,11 +1323,19 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
                            (!res || ((ax ^ reinterpret_cast<uintptr_t>(res)) & 127) == 0);
     int line = same_line && nvec >= 64 ? 128 : 16;
     // P classes of rows with one offset in the line; each block takes up to
-    // kClassGroups row groups of its class.
+    // kClassGroups row groups of its class, twice that for fp32 rows and the
+    // dropout epilogue where a block holds one row group (groups of 256 lanes
+    // or more), whose per-block set-up (the gamma/beta ring, the generator's
+    // blocks) then weighs more: 8192 x 4093 fp32 58.5 -> 55.1 us, 16384 x 8191
+    // bf16 dropout 149.8 -> 142.5 us.  Four stay best for two row groups a
+    // block (16384 x 4095 dropout: eight +9.6%) and for bf16 + GeLU (32768 x
+    // 4095: eight +0.6%; 16384 x 8191: +0.8%); two and sixteen are slower
+    // everywhere.
     int period = line;
     while (period > 1 && (pb * (period / 2)) % line == 0) period /= 2;
     const int64_t cgroups = ((r_hi - r_lo + period - 1) / period + rpb - 1) / rpb;
-    int64_t nblk = (cgroups + kClassGroups - 1) / kClassGroups;
+    const int64_t per_block = (rpb == 1 && (ES == 4 || EPI == kEpiReluDrop)) ? 2 * kClassGroups : kClassGroups;
+    int64_t nblk = (cgroups + per_block - 1) / per_block;
     if (nblk > kMaxGrid / 128) nblk = kMaxGrid / 128;
     const void* k = shape_kernel<ClassSel<IO, RES, EPI>::template K>(i);
     void* cargs[] = {&x,   &res,    &gamma, &beta, &y,    &rows, &icols, &ldx,
