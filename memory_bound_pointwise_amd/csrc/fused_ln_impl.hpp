@@ -1298,7 +1298,17 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   const bool congruent = ((ax ^ reinterpret_cast<uintptr_t>(y)) & 15) == 0 &&
                          (!res || ((ax ^ reinterpret_cast<uintptr_t>(res)) & 15) == 0) && ldx > 0 &&
                          ldy == ldx && (!res || ldr == ldx);
-  if (congruent) {
+  // fp32 rows of up to 2048 vectors (LayerNorm, + residual, + GeLU) take the
+  // shift kernel even when congruent:
+  // measured faster than the class kernel there (8192 x 4093: 55.0 -> 53.2 us;
+  // 8192 x 1001: 21.4 -> 17.9; with residual and GeLU 76.7 -> 75.3 and
+  // 26.1 -> 23.4), slower at 12287 columns (186 -> 192 us, 239 -> 263 with
+  // residual and GeLU); the dropout epilogue stays on the class kernel (its
+  // shift form 25-47% slower), and so do bf16 rows (32768 x 4095 + GeLU:
+  // 144.1 us in the class kernel, 161.6 in the shift kernel with y one
+  // element off)
+  const bool shift_f32 = ES == 4 && EPI != kEpiReluDrop && (cols + V - 1) / V <= 2048;
+  if (congruent && !shift_f32) {
     // Rows whose windows lie inside the tensors: [r_lo, r_hi).  With the row
     // pitch pb (bytes), a row starting fewer than 16 - (x mod 16) bytes past an
     // unaligned start, or ending fewer than (end mod 16) bytes before an
