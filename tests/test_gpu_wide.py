@@ -32,7 +32,9 @@ def mbp():
 def test_ln_wide(mbp, name, cols, residual, act):
     w, d, act = _ln_case(name, 3, cols, residual, act)
     chk = check_bf16 if w.dtype == "bf16" else check_f32
-    chk(to_host(_ln_run(mbp, d, act)), _ln_ref(d, act), f"{w.dtype} 3x{cols} residual={residual} act={act}")
+    y = _ln_run(mbp, d, act)
+    chk(to_host(y), _ln_ref(d, act), f"{w.dtype} 3x{cols} residual={residual} act={act}")
+    assert torch.equal(y, _ln_run(mbp, d, act)), "not deterministic"
 
 
 @pytest.mark.parametrize("name", ["ln_8192x4096_f32", "addln_gelu_16384x8192_bf16"])
@@ -76,8 +78,10 @@ def test_ln_relu_dropout_wide(mbp, name, cols, p):
 def test_softmax_wide(mbp, fmt, dtype, cols):
     rng = np.random.default_rng([29, cols])
     xh, xf = _stored(rng, (3, cols), dtype, 4.0)
-    y = mbp.fused_softmax(xh.cuda())
+    x = xh.cuda()
+    y = mbp.fused_softmax(x)
     _softmax_gate(y, oracle.softmax(xf), fmt, f"softmax {fmt} 3x{cols}", xf)
+    assert torch.equal(y, mbp.fused_softmax(x)), "not deterministic"
 
 
 @pytest.mark.parametrize("fmt,dtype", DT2D, ids=[d[0] for d in DT2D])
