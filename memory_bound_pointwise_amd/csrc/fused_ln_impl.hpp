@@ -1272,7 +1272,13 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   }
   const int i = pick_shape((cols + V - 1) / V);
   if (i < 0) return hipErrorInvalidValue;
-  const int lanes = kShapes[i].lanes;
+  // fp32 LayerNorm rows of 2049-4096 vectors: 512-lane groups of 6 or 8
+  // vectors a lane instead of 1024 x 3 / 1024 x 4 (8192 rows of 10000, 12287,
+  // 12288, 16384 columns: 4-6% faster); not with a residual (12288 + GeLU:
+  // 1.7% slower) and not measured with the other epilogues
+  constexpr bool kAlt = ES == 4 && !RES && EPI == kEpiNone;
+  const bool w512 = kAlt && i >= 10;
+  const int lanes = w512 ? 512 : kShapes[i].lanes;
   const int block = block_for(lanes);
   const int rpb = block / lanes;
   const int64_t groups = (rows + rpb - 1) / rpb;
@@ -1281,7 +1287,7 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   Drop drop = drop_in;
   void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &ldx, &ldr, &ldy, &eps, &drop};
   if (aligned) {
-    const void* k = shape_kernel<VecSel<IO, RES, EPI>::template K>(i);
+    const void* k = shape_kernel_alt<VecSel<IO, RES, EPI>::template K, kAlt>(i, w512);
     // two row groups per block, when there are thousands: fp32 rows
     // (measured at 8192 x 4096: 46.2 us against 47.5 for one; 4 or 8 per
     // block no better) and the dropout epilogue, whose per-block set-up is
@@ -1347,13 +1353,13 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
     const int64_t per_block = (rpb == 1 && (ES == 4 || EPI == kEpiReluDrop)) ? 2 * kClassGroups : kClassGroups;
     int64_t nblk = (cgroups + per_block - 1) / per_block;
     if (nblk > kMaxGrid / 128) nblk = kMaxGrid / 128;
-    const void* k = shape_kernel<ClassSel<IO, RES, EPI>::template K>(i);
+    const void* k = shape_kernel_alt<ClassSel<IO, RES, EPI>::template K, kAlt>(i, w512);
     void* cargs[] = {&x,   &res,    &gamma, &beta, &y,    &rows, &icols, &ldx,
                      &eps, &period, &line,  &r_lo, &r_hi, (void*)&edge_blocks, &drop};
     return hipLaunchKernel(k, dim3((unsigned)(edge_blocks + period * nblk)), dim3(block), cargs, 0, s);
   }
   // kShiftGroups row groups per block amortise the per-block gamma/beta set-up
-  const void* k = shape_kernel<ShiftSel<IO, RES, EPI>::template K>(i);
+  const void* k = shape_kernel_alt<ShiftSel<IO, RES, EPI>::template K, kAlt>(i, w512);
   const int sgrid = (int)((groups + kShiftGroups - 1) / kShiftGroups);
   return hipLaunchKernel(k, dim3(sgrid), dim3(block), args, 0, s);
 }

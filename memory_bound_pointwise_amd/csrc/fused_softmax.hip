@@ -441,6 +441,13 @@ hipError_t launch_softmax_io(const void* x, int64_t ldx, void* y, int64_t ldy, i
     // window that reaches outside: the first ceil((16 - x mod 16) / pitch)
     // and the last ceil((end mod 16) / pitch) rows (x and y end alike modulo
     // 16; the smaller pitch counts).
+    // fp32 rows of 2049-4096 vectors: 512-lane groups of 6 or 8 vectors a
+    // lane instead of 1024 x 3 / 1024 x 4 (8192 rows of 12287: 2816 ->
+    // 2239 us; on 16-byte boundaries, which the vector kernel takes, they
+    // measured 1.5-8.5% slower and are not used there)
+    constexpr bool kAlt = ES == 4;
+    const bool w512 = kAlt && shape >= 10;
+    const int wblock = w512 ? 512 : block, wrpb = w512 ? 1 : rpb;
     const int64_t pmin = px < py ? px : py;
     const int64_t mb = (int64_t)(ax & 15);
     const int64_t me = (int64_t)((ax + (uintptr_t)(ES * ((rows - 1) * ldx + cols))) & 15);
@@ -449,14 +456,14 @@ hipError_t launch_softmax_io(const void* x, int64_t ldx, void* y, int64_t ldy, i
     if (r_lo > rows) r_lo = rows;
     if (r_hi < r_lo) r_hi = r_lo;
     const int64_t n_edge = r_lo + (rows - r_hi);
-    const int64_t main_blocks = (r_hi - r_lo + rpb - 1) / rpb;
-    const int64_t edge_blocks = (n_edge + rpb - 1) / rpb;
+    const int64_t main_blocks = (r_hi - r_lo + wrpb - 1) / wrpb;
+    const int64_t edge_blocks = (n_edge + wrpb - 1) / wrpb;
     if (main_blocks + edge_blocks > (1 << 30)) return hipErrorInvalidValue;  // one block per row group
     int line = line_ok ? 128 : 16;
     int eb = (int)edge_blocks;
-    const void* k = shape_kernel<SoftmaxWinSel<IO>::template K>(shape);
+    const void* k = shape_kernel_alt<SoftmaxWinSel<IO>::template K, kAlt>(shape, w512);
     void* args[] = {&xe, &ye, &rows, &icols, &ldx, &ldy, &line, &r_lo, &r_hi, &eb};
-    return hipLaunchKernel(k, dim3((unsigned)(main_blocks + edge_blocks)), dim3(block), args, 0, s);
+    return hipLaunchKernel(k, dim3((unsigned)(main_blocks + edge_blocks)), dim3(wblock), args, 0, s);
   }
   const void* k = vec ? shape_kernel<SoftmaxSel<IO, true>::template K>(shape)
                       : shape_kernel<SoftmaxSel<IO, false>::template K>(shape);

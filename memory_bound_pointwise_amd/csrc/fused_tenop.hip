@@ -146,6 +146,8 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
       if (lane + k * LANES < nvec) sum += part;
     }
     // gamma and beta widened while the reduction's exchanges are in flight
+    // (one vector a lane; with more, the wide copies would cost registers)
+    constexpr bool kEarly = VPL * VW <= 4;
     double gd[VPL][VW], bd[VPL][VW];
 #pragma unroll
     for (int k = 0; k < VPL; ++k)
@@ -153,8 +155,10 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
       for (int e = 0; e < VW; ++e) {
         gd[k][e] = (double)g[k][e];
         bd[k][e] = (double)be[k][e];
-        opaque(gd[k][e]);
-        opaque(bd[k][e]);
+        if constexpr (kEarly) {
+          opaque(gd[k][e]);
+          opaque(bd[k][e]);
+        }
       }
     const double m = group_sum<LANES, BLOCK>(sum, red[parity]) * inv_cols;
 
@@ -351,7 +355,14 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
   const bool vector8_ok = sizeof(E) == 2 && (cols % 8) == 0 && aligned16(x) && aligned16(y) &&
                           aligned16(bias) && aligned16(gamma) && aligned16(beta) && ldx % 8 == 0 &&
                           ldy % 8 == 0;
-  if (cols > kRegCols) {  // rows wider than the register-resident layouts
+  // fp32 rows of 4-element accesses past 3072 vectors take the two-pass
+  // kernel too: 1024 x 4 held s for 16 elements a lane in binary64 within the
+  // 128 registers of 1024-thread blocks (1024 x 16384: 110.2 against 43.4 us)
+  const bool wide_f32 = sizeof(E) == 4 && vector_ok && (cols + 3) / 4 > 3072;
+  // so do element-path rows past 12288 columns, whose 1024 x 16 elements a
+  // lane spill (68-76 bytes a lane)
+  const bool wide_elem = !vector_ok && !vector8_ok && cols > 12288;
+  if (cols > kRegCols || wide_f32 || wide_elem) {  // rows wider than the register-resident layouts
     const int wgrid = (int)(rows < 4096 ? rows : 4096);
     hipLaunchKernelGGL(tenop_wide_kernel<IO>, dim3(wgrid), dim3(1024), 0, s, static_cast<const E*>(x), ldx,
                        static_cast<const E*>(bias), static_cast<const E*>(gamma), static_cast<const E*>(beta),
@@ -377,6 +388,12 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
     // 1024 x 1024: 3.67 us against 3.80 for 64 lanes x 4; 8192 x 1024: 14.1
     // against 14.6)
     const int nvec = (int)((cols + 3) / 4);
+    // rows of 2049-3072 vectors: 512 lanes x 6 rather than 1024 x 3
+    // (1024 x 12288: 31.9 -> 26.8 us)
+    if (vector_ok && nvec > 2048) {
+      lanes = 512;
+      k = reinterpret_cast<const void*>(&tenop_kernel<IO, 512, 6, 4>);
+    }
     if (vector_ok && nvec <= 256) {
       lanes = nvec <= 16 ? 16 : nvec <= 32 ? 32 : nvec <= 64 ? 64 : nvec <= 128 ? 128 : 256;
       k = lanes == 16   ? reinterpret_cast<const void*>(&tenop_kernel<IO, 16, 1, 4>)

@@ -106,6 +106,23 @@ const void* shape_kernel(int i) {
   }
 }
 
+// The 512-lane alternatives of the two 1024-lane layouts (index 10: 1024 x 3
+// -> 512 x 6; 11: 1024 x 4 -> 512 x 8), for the kernels whose fp32 rows of
+// 2049-4096 vectors measured faster in them (the caller says which).
+template <template <int, int> class K>
+const void* shape_kernel_512(int i) {
+  return i == 10 ? K<512, 6>::ptr() : K<512, 8>::ptr();
+}
+// Layout i, or its 512-lane alternative where `alt` (instantiated only when
+// the caller's kernel family can take it: ALT).
+template <template <int, int> class K, bool ALT>
+const void* shape_kernel_alt(int i, bool alt) {
+  if constexpr (ALT) {
+    if (alt) return shape_kernel_512<K>(i);
+  }
+  return shape_kernel<K>(i);
+}
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace rows

@@ -157,7 +157,7 @@ def _ln_ref(d, act, rows=None, mode=oracle.EXACT):
                                      eps=1e-5, act=code, mode=mode)
 
 
-F32_COLS = [1, 3, 4, 5, 64, 255, 256, 257, 1000, 1024, 4095, 4096, 8192, 16384]
+F32_COLS = [1, 3, 4, 5, 64, 255, 256, 257, 1000, 1024, 4095, 4096, 8192, 10001, 12288, 16383, 16384]
 BF16_COLS = [1, 7, 8, 9, 33, 255, 256, 257, 768, 1023, 1024, 4095, 4096, 8192, 12288, 16384]
 
 
@@ -653,7 +653,8 @@ def test_chain_2d_in_place(mbp):
 # 8-element kernel (1024, 512, 4096, 4000, 16384, 12288 with pads that keep the
 # boundaries); 1020 takes the 4-element one; 1001 and 515 the element one.
 TENOP_2D = [(64, 1024, 0, 0), (33, 1001, 0, 0), (40, 512, 8, 16), (21, 515, 5, 3), (1, 4096, 0, 0),
-            (9, 4000, 0, 8), (12, 1020, 4, 4), (3, 16384, 0, 8), (5, 12288, 8, 0), (17, 24, 0, 0)]
+            (9, 4000, 0, 8), (12, 1020, 4, 4), (3, 16384, 0, 8), (5, 12288, 8, 0), (17, 24, 0, 0),
+            (4, 13001, 3, 1), (3, 14000, 5, 0), (6, 10000, 0, 4)]
 
 
 @pytest.mark.parametrize("fmt,dtype", DT2D, ids=[d[0] for d in DT2D])
@@ -859,7 +860,8 @@ def test_softmax_masks_in_place_and_misaligned(mbp, fmt, dtype):
 
 
 @pytest.mark.parametrize("fmt,dtype", DT2D, ids=[d[0] for d in DT2D])
-@pytest.mark.parametrize("cols,rows", [(4095, 70), (4088, 20), (1000, 40), (769, 70), (33, 90), (16383, 5)])
+@pytest.mark.parametrize("cols,rows", [(4095, 70), (4088, 20), (1000, 40), (769, 70), (33, 90), (16383, 5),
+                                       (12287, 9)])
 @pytest.mark.parametrize("offs", [(0, 0), (4, 4), (20, 20), (124, 124), (4, 20), (12, 124), (0, 16)])
 def test_softmax_windows(mbp, fmt, dtype, cols, rows, offs):
     """x and y starting offs[0] and offs[1] bytes past a 128-byte line.  Equal
