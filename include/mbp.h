@@ -49,9 +49,10 @@ extern "C" {
 #define MBP_ABI_VERSION 7
 
 /* Largest row length (cols) the row kernels accept.  Rows of up to 16384
- * columns live in the registers of one lane group (read once, written once);
- * wider rows take one 1024-lane block each and two or three passes over the
- * row, the later ones rereading it from the caches. */
+ * columns, and bf16 / fp16 LayerNorm and softmax rows of up to 32768, live in
+ * the registers of one lane group (read once, written once); other wider rows
+ * take one 1024-lane block each and two or three passes over the row, the
+ * later ones rereading it from the caches. */
 #define MBP_MAX_COLS 32768
 
 typedef enum {
@@ -130,7 +131,7 @@ mbp_status fused_row_mean_epilogue(const float* x, const float* bias, const floa
  * normalisation are computed in binary64.  dtype MBP_BF16: all five are bf16;
  * arithmetic is fp32, the output is rounded to nearest even.  The statistics are
  * two-pass over the row (mean first, then the centred sum of squares), held in
- * registers up to 16384 columns.  GeLU uses the identity 0.5 (1 + tanh z) = 1 / (1 + exp(-2 z)).
+ * registers up to 16384 columns (bf16: up to MBP_MAX_COLS).  GeLU uses the identity 0.5 (1 + tanh z) = 1 / (1 + exp(-2 z)).
  * x, residual: [rows, cols]; gamma, beta: [cols]; y: [rows, cols]; y == x or
  * y == residual is allowed.  eps: finite, >= 0.  1 <= cols <= MBP_MAX_COLS.
  */
@@ -163,8 +164,8 @@ mbp_status fused_layernorm_relu_dropout(mbp_dtype dtype, const void* x, const vo
  *   m_i = max_j x[i,j];  l_i = sum_j exp(x[i,j] - m_i);  y[i,j] = exp(x[i,j] - m_i) / l_i
  * ([P1] section 4.2: normalised by the row maximum, with the running
  * max / sum statistics; [P3] section 4.2 lists softmax as the "Reduce +
- * Element-wise" fusion pattern).  One launch; up to 16384 columns the row is
- * read once and written once.  x, y: device [rows, cols], dense, in `dtype` (MBP_F32,
+ * Element-wise" fusion pattern).  One launch; up to 16384 columns (bf16 and
+ * fp16: up to MBP_MAX_COLS) the row is read once and written once.  x, y: device [rows, cols], dense, in `dtype` (MBP_F32,
  * MBP_BF16 or MBP_F16); y == x is allowed.  cols <= MBP_MAX_COLS.
  * Arithmetic in fp32 with one rounding to `dtype` at the store; -inf entries
  * (masks) give exactly 0, a row of -inf only gives NaN (0/0), a NaN makes its

@@ -158,7 +158,7 @@ __device__ __forceinline__ void halves_at(const u32x4& w0, const u32x4& w1, int 
 
 // ------------------------------------------------------------ wide rows
 
-// Rows of more than kRegCols columns: one 1024-lane block per row, three
+// fp32 rows of more than kRegCols columns: one 1024-lane block per row, three
 // passes over it -- the sum, the squared deviations about the mean, the
 // output -- the second and third rereading x (and the residual) from the
 // caches.  Column c is lane c mod 1024's; any width, alignment and row
@@ -1262,22 +1262,31 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   const bool aligned = aligned16(x) && aligned16(y) && (!res || aligned16(res)) && aligned16(gamma) &&
                        aligned16(beta) && cols % V == 0 && (ES * ldx) % 16 == 0 && (ES * ldy) % 16 == 0 &&
                        (!res || (ES * ldr) % 16 == 0);
-  if (cols > kRegCols) {  // rows wider than the register-resident layouts
-    const int wgrid = (int)(rows < 4096 ? rows : 4096);
-    int wcols = (int)cols;
-    Drop wdrop = drop_in;
-    void* wargs[] = {&x, &res, &gamma, &beta, &y, &rows, &wcols, &ldx, &ldr, &ldy, &eps, &wdrop};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&ln_wide_kernel<IO, RES, EPI>), dim3(wgrid),
-                           dim3(1024), wargs, 0, s);
+  // fp32 rows past kRegCols columns take the multi-pass kernel; 16-bit rows
+  // (at most 4096 vectors of 8 at the 32768-column maximum) all stay in
+  // registers (512-lane layouts, below)
+  if constexpr (ES == 4) {
+    if (cols > kRegCols) {
+      const int wgrid = (int)(rows < 4096 ? rows : 4096);
+      int wcols = (int)cols;
+      Drop wdrop = drop_in;
+      void* wargs[] = {&x, &res, &gamma, &beta, &y, &rows, &wcols, &ldx, &ldr, &ldy, &eps, &wdrop};
+      return hipLaunchKernel(reinterpret_cast<const void*>(&ln_wide_kernel<IO, RES, EPI>), dim3(wgrid),
+                             dim3(1024), wargs, 0, s);
+    }
   }
   const int i = pick_shape((cols + V - 1) / V);
   if (i < 0) return hipErrorInvalidValue;
-  // fp32 LayerNorm rows of 2049-4096 vectors: 512-lane groups of 6 or 8
-  // vectors a lane instead of 1024 x 3 / 1024 x 4 (8192 rows of 10000, 12287,
-  // 12288, 16384 columns: 4-6% faster); not with a residual (12288 + GeLU:
-  // 1.7% slower) and not measured with the other epilogues
-  constexpr bool kAlt = ES == 4 && !RES && EPI == kEpiNone;
+  // Rows of 2049-4096 vectors: 512-lane groups of 6 or 8 vectors a lane
+  // instead of 1024 x 3 / 1024 x 4, for plain fp32 LayerNorm (8192 rows of
+  // 10000, 12287, 12288, 16384 columns: 4-6% faster; not with a residual:
+  // 12288 + GeLU 1.7% slower; not measured with the other epilogues) and for
+  // every 16-bit form (16385-32768 columns, where the multi-pass kernel
+  // took 1.4-3.8 times as long: 16384 x 24576 + residual + GeLU 786.5 ->
+  // 499.0 us, LayerNorm -> ReLU -> dropout 1367.3 -> 361.0 us)
+  constexpr bool kAlt = (ES == 4 && !RES && EPI == kEpiNone) || ES == 2;
   const bool w512 = kAlt && i >= 10;
+  constexpr int kLast = ES == 2 ? 9 : 11;  // 16-bit rows never take the 1024-lane layouts
   const int lanes = w512 ? 512 : kShapes[i].lanes;
   const int block = block_for(lanes);
   const int rpb = block / lanes;
@@ -1287,7 +1296,7 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   Drop drop = drop_in;
   void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &ldx, &ldr, &ldy, &eps, &drop};
   if (aligned) {
-    const void* k = shape_kernel_alt<VecSel<IO, RES, EPI>::template K, kAlt>(i, w512);
+    const void* k = shape_kernel_alt<VecSel<IO, RES, EPI>::template K, kAlt, true, kLast>(i, w512);
     // two row groups per block, when there are thousands: fp32 rows
     // (measured at 8192 x 4096: 46.2 us against 47.5 for one; 4 or 8 per
     // block no better) and the dropout epilogue, whose per-block set-up is
@@ -1314,7 +1323,12 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   // 144.1 us in the class kernel, 161.6 in the shift kernel with y one
   // element off)
   const bool shift_f32 = ES == 4 && EPI != kEpiReluDrop && (cols + V - 1) / V <= 2048;
-  if (congruent && !shift_f32) {
+  // 16-bit dropout rows of 3073-4096 vectors: the class kernel would need more
+  // than the 256 registers of 512-thread blocks (140 bytes a lane of spill;
+  // measured 797 us against 861 for the shift kernel on 16384 x 32767), so
+  // they take the spill-free shift kernel
+  const bool shift_drop8 = ES == 2 && EPI == kEpiReluDrop && i == 11;
+  if (congruent && !shift_f32 && !shift_drop8) {
     // Rows whose windows lie inside the tensors: [r_lo, r_hi).  With the row
     // pitch pb (bytes), a row starting fewer than 16 - (x mod 16) bytes past an
     // unaligned start, or ending fewer than (end mod 16) bytes before an
@@ -1353,13 +1367,14 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
     const int64_t per_block = (rpb == 1 && (ES == 4 || EPI == kEpiReluDrop)) ? 2 * kClassGroups : kClassGroups;
     int64_t nblk = (cgroups + per_block - 1) / per_block;
     if (nblk > kMaxGrid / 128) nblk = kMaxGrid / 128;
-    const void* k = shape_kernel_alt<ClassSel<IO, RES, EPI>::template K, kAlt>(i, w512);
+    const void* k =
+        shape_kernel_alt<ClassSel<IO, RES, EPI>::template K, kAlt, !(ES == 2 && EPI == kEpiReluDrop), kLast>(i, w512);
     void* cargs[] = {&x,   &res,    &gamma, &beta, &y,    &rows, &icols, &ldx,
                      &eps, &period, &line,  &r_lo, &r_hi, (void*)&edge_blocks, &drop};
     return hipLaunchKernel(k, dim3((unsigned)(edge_blocks + period * nblk)), dim3(block), cargs, 0, s);
   }
   // kShiftGroups row groups per block amortise the per-block gamma/beta set-up
-  const void* k = shape_kernel_alt<ShiftSel<IO, RES, EPI>::template K, kAlt>(i, w512);
+  const void* k = shape_kernel_alt<ShiftSel<IO, RES, EPI>::template K, kAlt, true, kLast>(i, w512);
   const int sgrid = (int)((groups + kShiftGroups - 1) / kShiftGroups);
   return hipLaunchKernel(k, dim3(sgrid), dim3(block), args, 0, s);
 }

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(block_for(LANES)) void softmax_kernel(const typenam
   }
 }
 
-// Rows of more than kRegCols columns: one 1024-lane block per row, three
+// fp32 rows of more than kRegCols columns: one 1024-lane block per row, three
 // passes -- the row maximum M, then L = sum of exp(x - M), then the output
 // exp(x - M) / L -- the later two rereading x from the caches; any width,
 // alignment and row strides.  -inf entries give exactly 0, a row of -inf
@@ -396,8 +396,8 @@ struct SoftmaxSel {
   template <int L, int V>
   struct K {
     static const void* ptr() {
-      return VEC ? reinterpret_cast<const void*>(&softmax_kernel<IO, L, V, IO::kVec>)
-                 : reinterpret_cast<const void*>(&softmax_kernel<IO, L, IO::kVec * V, 1>);
+      if constexpr (VEC) return reinterpret_cast<const void*>(&softmax_kernel<IO, L, V, IO::kVec>);
+      else return reinterpret_cast<const void*>(&softmax_kernel<IO, L, IO::kVec * V, 1>);
     }
   };
 };
@@ -410,16 +410,26 @@ hipError_t launch_softmax_io(const void* x, int64_t ldx, void* y, int64_t ldy, i
   constexpr int64_t ES = (int64_t)sizeof(E);
   if (rows == 1) ldx = ldy = cols;  // one row: its stride is never used
   const int64_t nvec = (cols + V - 1) / V;
-  if (cols > kRegCols) {  // rows wider than the register-resident layouts
-    const int wgrid = (int)(rows < 4096 ? rows : 4096);
-    hipLaunchKernelGGL(softmax_wide_kernel<IO>, dim3(wgrid), dim3(1024), 0, s, static_cast<const E*>(x),
-                       static_cast<E*>(y), rows, (int)cols, ldx, ldy);
-    return hipGetLastError();
+  // fp32 rows past kRegCols columns take the multi-pass kernel; 16-bit rows
+  // (at most 4096 vectors of 8 at the 32768-column maximum) all stay in
+  // registers (512-lane layouts, below: 16384 rows of 24576 bf16 606.1 ->
+  // 259.9 us, 32768 columns 815.1 -> 376.9 us)
+  if constexpr (ES == 4) {
+    if (cols > kRegCols) {
+      const int wgrid = (int)(rows < 4096 ? rows : 4096);
+      hipLaunchKernelGGL(softmax_wide_kernel<IO>, dim3(wgrid), dim3(1024), 0, s, static_cast<const E*>(x),
+                         static_cast<E*>(y), rows, (int)cols, ldx, ldy);
+      return hipGetLastError();
+    }
   }
   const int shape = pick_shape(nvec);
   if (shape < 0) return hipErrorInvalidValue;
-  const int block = block_for(kShapes[shape].lanes);
-  const int rpb = block / kShapes[shape].lanes;
+  // 16-bit rows of 2049-4096 vectors: 512 x 6 / 512 x 8 (the 1024-lane
+  // layouts are not instantiated for them)
+  constexpr bool kAlt16 = ES == 2;
+  const bool a16 = kAlt16 && shape >= 10;
+  const int block = a16 ? 512 : block_for(kShapes[shape].lanes);
+  const int rpb = a16 ? 1 : block / kShapes[shape].lanes;
   const E* xe = static_cast<const E*>(x);
   E* ye = static_cast<E*>(y);
   int icols = (int)cols;
@@ -441,12 +451,11 @@ hipError_t launch_softmax_io(const void* x, int64_t ldx, void* y, int64_t ldy, i
     // window that reaches outside: the first ceil((16 - x mod 16) / pitch)
     // and the last ceil((end mod 16) / pitch) rows (x and y end alike modulo
     // 16; the smaller pitch counts).
-    // fp32 rows of 2049-4096 vectors: 512-lane groups of 6 or 8 vectors a
-    // lane instead of 1024 x 3 / 1024 x 4 (8192 rows of 12287: 2816 ->
-    // 2239 us; on 16-byte boundaries, which the vector kernel takes, they
-    // measured 1.5-8.5% slower and are not used there)
-    constexpr bool kAlt = ES == 4;
-    const bool w512 = kAlt && shape >= 10;
+    // Rows of 2049-4096 vectors: 512-lane groups of 6 or 8 vectors a lane
+    // instead of 1024 x 3 / 1024 x 4 (fp32, 8192 rows of 12287: 2816 ->
+    // 2239 us; fp32 rows on 16-byte boundaries, which the vector kernel
+    // takes, measured 1.5-8.5% slower in them and keep the 1024-lane ones)
+    const bool w512 = shape >= 10;
     const int wblock = w512 ? 512 : block, wrpb = w512 ? 1 : rpb;
     const int64_t pmin = px < py ? px : py;
     const int64_t mb = (int64_t)(ax & 15);
@@ -461,12 +470,12 @@ hipError_t launch_softmax_io(const void* x, int64_t ldx, void* y, int64_t ldy, i
     if (main_blocks + edge_blocks > (1 << 30)) return hipErrorInvalidValue;  // one block per row group
     int line = line_ok ? 128 : 16;
     int eb = (int)edge_blocks;
-    const void* k = shape_kernel_alt<SoftmaxWinSel<IO>::template K, kAlt>(shape, w512);
+    const void* k = shape_kernel_alt<SoftmaxWinSel<IO>::template K, true, true, 9>(shape, w512);
     void* args[] = {&xe, &ye, &rows, &icols, &ldx, &ldy, &line, &r_lo, &r_hi, &eb};
     return hipLaunchKernel(k, dim3((unsigned)(main_blocks + edge_blocks)), dim3(wblock), args, 0, s);
   }
-  const void* k = vec ? shape_kernel<SoftmaxSel<IO, true>::template K>(shape)
-                      : shape_kernel<SoftmaxSel<IO, false>::template K>(shape);
+  const void* k = vec ? shape_kernel_alt<SoftmaxSel<IO, true>::template K, kAlt16, true, kAlt16 ? 9 : 11>(shape, a16)
+                      : shape_kernel_alt<SoftmaxSel<IO, false>::template K, kAlt16, true, kAlt16 ? 9 : 11>(shape, a16);
   const int64_t groups = (rows + rpb - 1) / rpb;
   const int grid = (int)(groups < (1 << 30) ? groups : (1 << 30));
   if (groups > grid) return hipErrorInvalidValue;  // one block per row group

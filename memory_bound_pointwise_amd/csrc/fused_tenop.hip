@@ -335,8 +335,8 @@ struct TenopSel {
   template <int L, int V>
   struct K {
     static const void* ptr() {
-      return VEC ? reinterpret_cast<const void*>(&tenop_kernel<IO, L, V, 4>)
-                 : reinterpret_cast<const void*>(&tenop_kernel<IO, L, 4 * V, 1>);
+      if constexpr (VEC) return reinterpret_cast<const void*>(&tenop_kernel<IO, L, V, 4>);
+      else return reinterpret_cast<const void*>(&tenop_kernel<IO, L, 4 * V, 1>);
     }
   };
 };
@@ -371,8 +371,10 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
   }
   const int shape = vector8_ok ? pick_shape(cols / 8) : pick_shape((cols + 3) / 4);
   if (shape < 0) return hipErrorInvalidValue;
+  // the element path never takes 1024 x 4 (its rows past 12288 columns took
+  // the two-pass kernel above)
   const void* k = vector_ok ? shape_kernel<TenopSel<IO, true>::template K>(shape)
-                            : shape_kernel<TenopSel<IO, false>::template K>(shape);
+                            : shape_kernel<TenopSel<IO, false>::template K, 10>(shape);
   int lanes = kShapes[shape].lanes;
   if constexpr (sizeof(E) == 2) {
     if (vector8_ok) k = shape_kernel<Tenop8Sel<IO>::template K>(shape);

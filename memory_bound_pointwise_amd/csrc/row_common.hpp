@@ -66,9 +66,12 @@ __device__ __forceinline__ float mean_cols(float s, int n) {
 }
 __device__ __forceinline__ double mean_cols(double s, int n) { return s / (double)n; }
 
-// Rows of more than kRegCols columns are not held in registers: they take
-// the three-pass row kernels (one 1024-lane block per row, the later passes
-// rereading the row from the caches), which hold nothing per element.
+// fp32 rows of more than kRegCols columns are not held in registers: they
+// take the multi-pass row kernels (one 1024-lane block per row, the later
+// passes rereading the row from the caches), which hold nothing per element.
+// 16-bit LayerNorm and softmax rows stay in registers up to the 32768-column
+// maximum (4096 vectors: 512 x 8); the 10-op graph's 16-bit rows past
+// kRegCols take its multi-pass kernel.
 constexpr int64_t kRegCols = 16384;
 
 // (LANES, VPL) layouts.  The first layout whose LANES * VPL vectors cover the
@@ -87,8 +90,10 @@ inline int pick_shape(int64_t nvec) {
   return -1;
 }
 
-// Kernel pointer of layout i: K<LANES, VPL>::ptr().
-template <template <int, int> class K>
+// Kernel pointer of layout i: K<LANES, VPL>::ptr().  LAST: the last layout
+// the caller's family can be asked for (later ones are not instantiated; a
+// larger i gives nullptr, which the callers never pass on).
+template <template <int, int> class K, int LAST = 11>
 const void* shape_kernel(int i) {
   switch (i) {
     case 0: return K<16, 2>::ptr();
@@ -101,26 +106,33 @@ const void* shape_kernel(int i) {
     case 7: return K<256, 4>::ptr();
     case 8: return K<512, 3>::ptr();
     case 9: return K<512, 4>::ptr();
-    case 10: return K<1024, 3>::ptr();
-    default: return K<1024, 4>::ptr();
+    case 10:
+      if constexpr (LAST >= 10) return K<1024, 3>::ptr();
+      else return nullptr;
+    default:
+      if constexpr (LAST >= 11) return K<1024, 4>::ptr();
+      else return nullptr;
   }
 }
 
 // The 512-lane alternatives of the two 1024-lane layouts (index 10: 1024 x 3
 // -> 512 x 6; 11: 1024 x 4 -> 512 x 8), for the kernels whose fp32 rows of
 // 2049-4096 vectors measured faster in them (the caller says which).
-template <template <int, int> class K>
+// EIGHT false: the family has no 512 x 8 instance (the caller never asks for
+// index 11 there).
+template <template <int, int> class K, bool EIGHT = true>
 const void* shape_kernel_512(int i) {
-  return i == 10 ? K<512, 6>::ptr() : K<512, 8>::ptr();
+  if constexpr (EIGHT) return i == 10 ? K<512, 6>::ptr() : K<512, 8>::ptr();
+  else return K<512, 6>::ptr();
 }
 // Layout i, or its 512-lane alternative where `alt` (instantiated only when
 // the caller's kernel family can take it: ALT).
-template <template <int, int> class K, bool ALT>
+template <template <int, int> class K, bool ALT, bool EIGHT = true, int LAST = 11>
 const void* shape_kernel_alt(int i, bool alt) {
   if constexpr (ALT) {
-    if (alt) return shape_kernel_512<K>(i);
+    if (alt) return shape_kernel_512<K, EIGHT>(i);
   }
-  return shape_kernel<K>(i);
+  return shape_kernel<K, LAST>(i);
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
