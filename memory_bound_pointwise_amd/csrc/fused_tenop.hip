@@ -180,6 +180,57 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
   }
 }
 
+// fp32 rows of at most 256 vectors (4-element accesses): one vector a lane,
+// one row group per block and no loop over row groups, every load issued up
+// front -- bias first (its widening overlaps the wait for the row), then the
+// row, then gamma and beta, which are needed only after the reduction.
+// Measured at 1024 x 1024 (graph-replayed calls, inputs out of the caches)
+// against tenop_kernel<F32IO, 256, 1, 4>, whose grid-stride loop holds the
+// parameters in storage form across rows: 3.41 -> 3.25 us; giving each block
+// 2, 4 or 8 rows with all their loads issued first: 3.57, 3.80, 5.06 us;
+// 128 x 2, 64 x 4 and 32 x 8 lanes x vectors: slower still.
+template <int LANES>
+__global__ __launch_bounds__(block_for(LANES)) void tenop1_kernel(
+    const float* x, int64_t ldx, const float* __restrict__ bias, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float* y, int64_t ldy, int64_t rows, int cols, double alpha, double c,
+    double inv_cols) {
+  constexpr int BLOCK = block_for(LANES);
+  constexpr int RPB = BLOCK / LANES;
+  __shared__ double red[BLOCK / 64];
+  const int lane = threadIdx.x % LANES;
+  const int nvec = cols / 4;
+  const int vi = min(lane, nvec - 1);  // lanes past the row reread its last vector
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LANES;
+  const int64_t rowc = row < rows ? row : rows - 1;  // rows past the end reread the last row
+  float bi[4], g[4], be[4], xv[4];
+  load4<F32IO>(bias + 4 * vi, bi);
+  load4_nt<F32IO>(x + rowc * ldx + 4 * vi, xv);
+  load4<F32IO>(gamma + 4 * vi, g);
+  load4<F32IO>(beta + 4 * vi, be);
+  double bd[4], gd[4], ed[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bd[e] = bi[e];
+    gd[e] = g[e];
+    ed[e] = be[e];
+  }
+  double s[4], part = 0.0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const double t = __builtin_fma((double)xv[e], alpha, bd[e]);
+    const double a = (t < 0.0) ? 0.0 : t;  // relu; NaN passes through
+    s[e] = __builtin_fma(a, a, a * c);
+    part += s[e];
+  }
+  const double m = group_sum<LANES, BLOCK>(lane < nvec ? part : 0.0, red) * inv_cols;
+  if (row < rows && lane < nvec) {
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = narrow_bits<F32IO>(__builtin_fma(s[e] - m, gd[e], ed[e]));
+    store4_nt<F32IO>(y + row * ldy + 4 * lane, o);
+  }
+}
+
 // s = relu(x * alpha + bias) * (relu(...) + c) as the 10-op kernels form it
 __device__ __forceinline__ double tenop_s(float xv, float bv, double alpha, double c) {
   const double t = __builtin_fma((double)xv, alpha, (double)bv);
@@ -398,11 +449,20 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
     }
     if (vector_ok && nvec <= 256) {
       lanes = nvec <= 16 ? 16 : nvec <= 32 ? 32 : nvec <= 64 ? 64 : nvec <= 128 ? 128 : 256;
-      k = lanes == 16   ? reinterpret_cast<const void*>(&tenop_kernel<IO, 16, 1, 4>)
-          : lanes == 32 ? reinterpret_cast<const void*>(&tenop_kernel<IO, 32, 1, 4>)
-          : lanes == 64 ? reinterpret_cast<const void*>(&tenop_kernel<IO, 64, 1, 4>)
-          : lanes == 128 ? reinterpret_cast<const void*>(&tenop_kernel<IO, 128, 1, 4>)
-                         : reinterpret_cast<const void*>(&tenop_kernel<IO, 256, 1, 4>);
+      const int64_t g1 = (rows + 256 / lanes - 1) / (256 / lanes);
+      if (g1 < (1 << 30)) {  // one block per row group, no loop
+        k = lanes == 16    ? reinterpret_cast<const void*>(&tenop1_kernel<16>)
+            : lanes == 32  ? reinterpret_cast<const void*>(&tenop1_kernel<32>)
+            : lanes == 64  ? reinterpret_cast<const void*>(&tenop1_kernel<64>)
+            : lanes == 128 ? reinterpret_cast<const void*>(&tenop1_kernel<128>)
+                           : reinterpret_cast<const void*>(&tenop1_kernel<256>);
+      } else {
+        k = lanes == 16    ? reinterpret_cast<const void*>(&tenop_kernel<IO, 16, 1, 4>)
+            : lanes == 32  ? reinterpret_cast<const void*>(&tenop_kernel<IO, 32, 1, 4>)
+            : lanes == 64  ? reinterpret_cast<const void*>(&tenop_kernel<IO, 64, 1, 4>)
+            : lanes == 128 ? reinterpret_cast<const void*>(&tenop_kernel<IO, 128, 1, 4>)
+                           : reinterpret_cast<const void*>(&tenop_kernel<IO, 256, 1, 4>);
+      }
     }
   }
   const int block = block_for(lanes);
