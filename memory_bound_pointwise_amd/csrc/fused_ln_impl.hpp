@@ -262,7 +262,37 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
   }
 
   const int64_t groups = (rows + RPB - 1) / RPB;
+  // The loads of a row group: a group past the last row reads the last row
+  // (and stores nothing); a slot past the row's last vector reads that vector
+  // and is left out of the sums.  Every load is in bounds and none needs a
+  // branch or a zero fill.
+  auto issue_loads = [&](int64_t gi, u32x4* xo, u32x4* ro) {
+    const int64_t r = gi * RPB + sub;
+    const int64_t lr = r < rows ? r : rows - 1;
+    const typename IO::elem* xr = x + lr * ldx;
+    const typename IO::elem* rr = RES ? res + lr * ldr : nullptr;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int vi = min(lane + k * LANES, nvec - 1);
+      xo[k] = stream_vec<IO>(xr, vi);
+      if constexpr (RES) ro[k] = stream_vec<IO>(rr, vi);
+    }
+  };
+  // 16-bit rows in groups of up to 256 lanes: the first row group's loads
+  // are issued before the wait for gamma/beta, and each next group's before
+  // the current one is computed.  fp32 rows issue a group's loads at the top
+  // of its iteration: holding a second fp32 row cost an occupancy step
+  // (8192 x 8192 fp32 + residual + GeLU: 104 -> 136 registers, 135 -> 164 us);
+  // so did 512-lane 16-bit groups (16384 x 12288 + GeLU: 193.3 -> 199.1 us).
+  constexpr bool kAhead = sizeof(typename IO::elem) == 2 && LANES <= 256;
+  u32x4 xv[VPL], rv[VPL];
+  if constexpr (kAhead) {
+    if ((int64_t)blockIdx.x < groups) issue_loads(blockIdx.x, xv, rv);
+  }
   for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    u32x4 xn[VPL], rn[VPL];
+    const bool more = kAhead && grp + gridDim.x < groups;
+    if (more) issue_loads(grp + gridDim.x, xn, rn);
     if constexpr (kPacked) {
 #pragma unroll
       for (int k = 0; k < VPL; ++k) {
@@ -283,22 +313,8 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
     }
     const int64_t row = grp * RPB + sub;
     const bool live = row < rows;
-    // A group past the last row reads the last row (and stores nothing); a slot
-    // past the row's last vector reads that vector and is left out of the
-    // sums.  Every load is in bounds and none needs a branch or a zero fill.
-    const int64_t lrow = live ? row : rows - 1;
-    const typename IO::elem* xr = x + lrow * ldx;
-    const typename IO::elem* rr = RES ? res + lrow * ldr : nullptr;
     typename IO::elem* yr = y + row * ldy;
-
-    // issue every load of the row first
-    u32x4 xv[VPL], rv[VPL];
-#pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-      const int vi = min(lane + k * LANES, nvec - 1);
-      xv[k] = stream_vec<IO>(xr, vi);
-      if constexpr (RES) rv[k] = stream_vec<IO>(rr, vi);
-    }
+    if constexpr (!kAhead) issue_loads(grp, xv, rv);
     Val v[VPL][V];
     Acc sum = 0;
 #pragma unroll
@@ -345,6 +361,13 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
       if constexpr (EPI == kEpiReluDrop)  // rows start on multiples of V: one aligned group
         relu_dropout<V, true>(o, (uint64_t)row * (uint64_t)cols + (uint64_t)(vi * V), drop);
       store_nt(reinterpret_cast<u32x4*>(yr) + vi, pack_vec<IO>(o));
+    }
+    if (more) {
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) {
+        xv[k] = xn[k];
+        if constexpr (RES) rv[k] = rn[k];
+      }
     }
   }
 }
@@ -1299,12 +1322,16 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
     const void* k = shape_kernel_alt<VecSel<IO, RES, EPI>::template K, kAlt, true, kLast>(i, w512);
     // two row groups per block, when there are thousands: fp32 rows
     // (measured at 8192 x 4096: 46.2 us against 47.5 for one; 4 or 8 per
-    // block no better) and the dropout epilogue, whose per-block set-up is
-    // then paid once for two rows (16384 x 8192 bf16: 96.8 -> 91.9 us; 4 or 8
-    // per block no better; 512 x 2 and 1024 x 1 layouts 23% and 33% slower);
-    // the other bf16 rows gain nothing
+    // block no better) and 16-bit rows in 256-lane groups other than the
+    // dropout epilogue, whose second group's loads are then issued while the
+    // first is computed (16384 x 8192 + residual + GeLU: 134.7 -> 130.7 us,
+    // plain LayerNorm 96.7 -> 90.0; one group a block: 132.5 and 91.5).
+    // The dropout epilogue and the other 16-bit layouts take one (dropout
+    // 16384 x 8192: 92.5 us for two groups a block without the early loads,
+    // 91.3 for one with them, 92.4 for two with them; 32768 x 4096 + GeLU:
+    // 128.0, 125.9 with them, 128.8 for two)
     int vgrid = grid;
-    if ((sizeof(typename IO::elem) == 4 || EPI == kEpiReluDrop) && groups >= 4096) vgrid = (int)((groups + 1) / 2);
+    if (groups >= 4096 && (ES == 4 || (lanes == 256 && EPI != kEpiReluDrop))) vgrid = (int)((groups + 1) / 2);
     return hipLaunchKernel(k, dim3(vgrid), dim3(block), args, 0, s);
   }
   const uintptr_t ax = reinterpret_cast<uintptr_t>(x);
