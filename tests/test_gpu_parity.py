@@ -388,6 +388,18 @@ def test_ln_f32_two_groups_per_block(mbp):
     check_f32(to_host(y)[rows], _ln_ref(d, act, rows), "fp32 LN 4097 x 4096, two groups per block")
 
 
+@pytest.mark.parametrize("cols,residual,act", [(8192, True, "gelu_tanh"), (6144, True, "gelu_tanh"),
+                                              (8192, False, "none"), (7000, False, "gelu_tanh")])
+def test_ln_bf16_loads_ahead(mbp, cols, residual, act):
+    """16-bit rows in 256-lane groups run two row groups per block when there
+    are thousands, the second group's loads issued while the first is
+    computed; an odd count leaves the last block one group.  Every element of
+    the output is checked."""
+    w, d, act = _ln_case("addln_gelu_16384x8192_bf16", 4097, cols, residual, act)
+    y = to_host(_ln_run(mbp, d, act))
+    check_bf16(y, _ln_ref(d, act), f"bf16 4097 x {cols} residual={residual} act={act}, loads ahead")
+
+
 # ------------------------------------------------------------------ row strides of the row kernels
 
 # (rows, cols, x (pad, offset), residual (pad, offset) or None, y (pad, offset) or "x")
