@@ -1311,9 +1311,9 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   const bool w512 = kAlt && i >= 10;
   constexpr int kLast = ES == 2 ? 9 : 11;  // 16-bit rows never take the 1024-lane layouts
   const int lanes = w512 ? 512 : kShapes[i].lanes;
-  const int block = block_for(lanes);
-  const int rpb = block / lanes;
-  const int64_t groups = (rows + rpb - 1) / rpb;
+  const int block_v = block_for(lanes);
+  const int rpb_v = block_v / lanes;
+  const int64_t groups = (rows + rpb_v - 1) / rpb_v;
   const int grid = (int)(groups < kMaxGrid ? groups : kMaxGrid);  // one block per row group
   int icols = (int)cols;
   Drop drop = drop_in;
@@ -1332,7 +1332,7 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
     // 128.0, 125.9 with them, 128.8 for two)
     int vgrid = grid;
     if (groups >= 4096 && (ES == 4 || (lanes == 256 && EPI != kEpiReluDrop))) vgrid = (int)((groups + 1) / 2);
-    return hipLaunchKernel(k, dim3(vgrid), dim3(block), args, 0, s);
+    return hipLaunchKernel(k, dim3(vgrid), dim3(block_v), args, 0, s);
   }
   const uintptr_t ax = reinterpret_cast<uintptr_t>(x);
   // x, residual and y agree modulo 16 bytes in every row: congruent bases and
@@ -1356,6 +1356,15 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   // they take the spill-free shift kernel
   const bool shift_drop8 = ES == 2 && EPI == kEpiReluDrop && i == 11;
   if (congruent && !shift_f32 && !shift_drop8) {
+    // 16-bit rows of 385-512 vectors without dropout: 256 lanes x 2 rather
+    // than the table's 128 x 4, one row group a block (32768 x 4095 + residual
+    // + GeLU: 145.4 -> 143.3 us, 74 registers against 117 and no scalar
+    // spills; with eight row groups a block 149.7, 512 x 1 143.5 / 149.2;
+    // 32768 x 3501: 129.5 -> 128.2).  Shorter rows keep 128 x 4 (32768 x 2101:
+    // 95.7 against 100.9 us, the second vector of most lanes unused)
+    const bool c256 = ES == 2 && EPI != kEpiReluDrop && i == 5 && (cols + V - 1) / V > 384;
+    const int rpb = c256 ? 1 : rpb_v;
+    const int block = c256 ? 256 : block_v;
     // Rows whose windows lie inside the tensors: [r_lo, r_hi).  With the row
     // pitch pb (bytes), a row starting fewer than 16 - (x mod 16) bytes past an
     // unaligned start, or ending fewer than (end mod 16) bytes before an
@@ -1395,7 +1404,8 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
     int64_t nblk = (cgroups + per_block - 1) / per_block;
     if (nblk > kMaxGrid / 128) nblk = kMaxGrid / 128;
     const void* k =
-        shape_kernel_alt<ClassSel<IO, RES, EPI>::template K, kAlt, !(ES == 2 && EPI == kEpiReluDrop), kLast>(i, w512);
+        c256 ? reinterpret_cast<const void*>(&ln_class_kernel<IO, 256, 2, RES, EPI>)
+             : shape_kernel_alt<ClassSel<IO, RES, EPI>::template K, kAlt, !(ES == 2 && EPI == kEpiReluDrop), kLast>(i, w512);
     void* cargs[] = {&x,   &res,    &gamma, &beta, &y,    &rows, &icols, &ldx,
                      &eps, &period, &line,  &r_lo, &r_hi, (void*)&edge_blocks, &drop};
     return hipLaunchKernel(k, dim3((unsigned)(edge_blocks + period * nblk)), dim3(block), cargs, 0, s);
@@ -1403,7 +1413,7 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   // kShiftGroups row groups per block amortise the per-block gamma/beta set-up
   const void* k = shape_kernel_alt<ShiftSel<IO, RES, EPI>::template K, kAlt, true, kLast>(i, w512);
   const int sgrid = (int)((groups + kShiftGroups - 1) / kShiftGroups);
-  return hipLaunchKernel(k, dim3(sgrid), dim3(block), args, 0, s);
+  return hipLaunchKernel(k, dim3(sgrid), dim3(block_v), args, 0, s);
 }
 
 // act: kEpiNone, kEpiGelu, kEpiReluDrop (no residual; `drop` describes it).
