@@ -116,6 +116,33 @@ def test_tenop_in_place_and_misaligned(mbp):
     check_f32(to_host(y), ref, "misaligned x (scalar path)")
 
 
+@pytest.mark.parametrize("cols", [1024, 1000, 64, 4096])
+def test_tenop_special_values(mbp, cols):
+    """NaN and infinities in x: a NaN makes its whole row NaN (relu passes it
+    on, the row sum carries it); +inf gives inf in s and in the row sum, so
+    its element is inf - inf = NaN and the others -inf * gamma + beta; -inf
+    is cut by the relu.  Positions of NaN and of each signed infinity must
+    match the oracle, the finite elements the fp32 gate."""
+    w = W.scaled(W.BY_NAME["tenop_1024x1024_f32"], rows=6)
+    d = W.generate(w, cols=cols)
+    x = d["x"].copy()
+    x[0, 3] = np.nan
+    x[1, cols // 2] = np.inf
+    x[2, 0] = -np.inf
+    x[3, cols - 1] = -np.inf
+    x[3, 1] = np.nan
+    g = d["gamma"].copy()
+    g[5 % cols] = 0.0  # 0 * inf = NaN in row 1
+    y = to_host(mbp.fused_row_mean_epilogue(to_dev(x), to_dev(d["bias"]), to_dev(g), to_dev(d["beta"])))
+    ref = oracle.row_mean_epilogue(x, d["bias"], g, d["beta"])
+    assert np.array_equal(np.isnan(y), np.isnan(ref)), "NaN positions"
+    assert np.array_equal(np.isposinf(y), np.isposinf(ref)) and np.array_equal(np.isneginf(y), np.isneginf(ref)), \
+        "infinity positions"
+    fin = np.isfinite(ref)
+    check_f32(y[fin], ref[fin], f"10-op special values, {cols} columns")
+    assert np.isnan(y[0]).all() and np.isnan(y[1, cols // 2]) and np.isfinite(y[2]).all()
+
+
 def test_tenop_full_workload(mbp):
     w = W.BY_NAME["tenop_1024x1024_f32"]
     d = W.generate(w)
