@@ -1356,15 +1356,21 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   // they take the spill-free shift kernel
   const bool shift_drop8 = ES == 2 && EPI == kEpiReluDrop && i == 11;
   if (congruent && !shift_f32 && !shift_drop8) {
-    // 16-bit rows of 385-512 vectors without dropout: 256 lanes x 2 rather
-    // than the table's 128 x 4, one row group a block (32768 x 4095 + residual
-    // + GeLU: 145.4 -> 143.3 us, 74 registers against 117 and no scalar
-    // spills; with eight row groups a block 149.7, 512 x 1 143.5 / 149.2;
-    // 32768 x 3501: 129.5 -> 128.2).  Shorter rows keep 128 x 4 (32768 x 2101:
-    // 95.7 against 100.9 us, the second vector of most lanes unused)
-    const bool c256 = ES == 2 && EPI != kEpiReluDrop && i == 5 && (cols + V - 1) / V > 384;
-    const int rpb = c256 ? 1 : rpb_v;
-    const int block = c256 ? 256 : block_v;
+    // 16-bit rows without dropout in two vectors a lane, one row group a
+    // block: 385-512 vectors in 256 lanes rather than the table's 128 x 4
+    // (32768 x 4095 + residual + GeLU: 145.4 -> 143.3 us, 74 registers
+    // against 117 and no scalar spills; with eight row groups a block 149.7,
+    // 512 x 1 143.5 / 149.2; 32768 x 3501: 129.5 -> 128.2), 769-1024 vectors
+    // in 512 lanes rather than 256 x 4, eight row groups a block (16384 x 8191
+    // + residual + GeLU: 146.2 -> 141.7 us, without the residual 108.9 ->
+    // 102.7, 16384 x 6999: 130.1 -> 128.0; four groups a block 144.8, twelve
+    // or sixteen 152).  Shorter rows keep the table's layout (32768 x 2101 in
+    // 256 x 2: 95.7 against 100.9 us, the second vector of most lanes unused)
+    const int nv2 = (int)((cols + V - 1) / V);
+    const bool c256 = ES == 2 && EPI != kEpiReluDrop && i == 5 && nv2 > 384;
+    const bool c512 = ES == 2 && EPI != kEpiReluDrop && i == 7 && nv2 > 768;
+    const int rpb = (c256 || c512) ? 1 : rpb_v;
+    const int block = c256 ? 256 : c512 ? 512 : block_v;
     // Rows whose windows lie inside the tensors: [r_lo, r_hi).  With the row
     // pitch pb (bytes), a row starting fewer than 16 - (x mod 16) bytes past an
     // unaligned start, or ending fewer than (end mod 16) bytes before an
@@ -1400,11 +1406,13 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
     int period = line;
     while (period > 1 && (pb * (period / 2)) % line == 0) period /= 2;
     const int64_t cgroups = ((r_hi - r_lo + period - 1) / period + rpb - 1) / rpb;
-    const int64_t per_block = (rpb == 1 && (ES == 4 || EPI == kEpiReluDrop)) ? 2 * kClassGroups : kClassGroups;
+    const int64_t per_block =
+        (c512 || (rpb == 1 && (ES == 4 || EPI == kEpiReluDrop))) ? 2 * kClassGroups : kClassGroups;
     int64_t nblk = (cgroups + per_block - 1) / per_block;
     if (nblk > kMaxGrid / 128) nblk = kMaxGrid / 128;
     const void* k =
-        c256 ? reinterpret_cast<const void*>(&ln_class_kernel<IO, 256, 2, RES, EPI>)
+        c512   ? reinterpret_cast<const void*>(&ln_class_kernel<IO, 512, 2, RES, EPI>)
+        : c256 ? reinterpret_cast<const void*>(&ln_class_kernel<IO, 256, 2, RES, EPI>)
              : shape_kernel_alt<ClassSel<IO, RES, EPI>::template K, kAlt, !(ES == 2 && EPI == kEpiReluDrop), kLast>(i, w512);
     void* cargs[] = {&x,   &res,    &gamma, &beta, &y,    &rows, &icols, &ldx,
                      &eps, &period, &line,  &r_lo, &r_hi, (void*)&edge_blocks, &drop};

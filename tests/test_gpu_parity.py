@@ -227,6 +227,10 @@ def test_ln_misaligned_and_in_place(mbp, dtype_name):
     ("addln_gelu_16384x8192_bf16", 768, 3, 9), ("addln_gelu_16384x8192_bf16", 8192, 7, 9),
     ("addln_gelu_16384x8192_bf16", 3, 5, 40), ("addln_gelu_16384x8192_bf16", 1, 7, 21),
     ("addln_gelu_16384x8192_bf16", 13, 2, 300), ("addln_gelu_16384x8192_bf16", 12290, 1, 5),
+    # 512-lane class layout with eight row groups a block (several per class)
+    ("addln_gelu_16384x8192_bf16", 8191, 1, 600), ("addln_gelu_16384x8192_bf16", 6145, 0, 530),
+    # 256-lane class layout, several row groups a block
+    ("addln_gelu_16384x8192_bf16", 3501, 3, 300),
     ("ln_8192x4096_f32", 4093, 1, 9), ("ln_8192x4096_f32", 1024, 2, 9), ("ln_8192x4096_f32", 5, 3, 40),
     ("ln_8192x4096_f32", 6, 0, 17)])
 def test_ln_common_misalignment(mbp, dtype_name, cols, shift, rows):
