@@ -652,20 +652,43 @@ __global__ __launch_bounds__(block_for(LANES)) __attribute__((amdgpu_waves_per_e
         b = partial_vec<IO>(beta, V * vi, cols);
       }
     };
+    // every gamma / beta vector is read from global memory once: the raw
+    // vectors go to the ring first, each slot takes its predecessor from
+    // there, and the funnelled vectors replace them
     u32x4 tg[kIt], tb[kIt];
 #pragma unroll
     for (int i = 0; i < kIt; ++i) {
       const int jc = min((int)threadIdx.x + i * BLOCK, nvec - 1);
-      const int jp = jc == 0 ? nvec - 1 : jc - 1;
-      u32x4 gc, bc, ga = {{0u, 0u, 0u, 0u}}, ba = {{0u, 0u, 0u, 0u}};
-      fetch(jc, gc, bc);
-      if (sb != 0) fetch(jp, ga, ba);
-      switch (sb == 0 ? -1 : q) {
-        case -1: tg[i] = gc; tb[i] = bc; break;
-        case 0: tg[i] = funnel<ES, 0>(ga, gc.w, bb); tb[i] = funnel<ES, 0>(ba, bc.w, bb); break;
-        case 1: tg[i] = funnel<ES, 1>(ga, gc.w, bb); tb[i] = funnel<ES, 1>(ba, bc.w, bb); break;
-        case 2: tg[i] = funnel<ES, 2>(ga, gc.w, bb); tb[i] = funnel<ES, 2>(ba, bc.w, bb); break;
-        default: tg[i] = funnel<ES, 3>(ga, gc.w, bb); tb[i] = funnel<ES, 3>(ba, bc.w, bb); break;
+      fetch(jc, tg[i], tb[i]);
+    }
+    if (sb != 0) {
+#pragma unroll
+      for (int i = 0; i < kIt; ++i) {
+        const int v = (int)threadIdx.x + i * BLOCK;
+        if (v < nvec) {
+          ringg[v] = tg[i];
+          ringb[v] = tb[i];
+        }
+      }
+      lds_barrier();
+      u32x4 ga[kIt], ba[kIt];
+#pragma unroll
+      for (int i = 0; i < kIt; ++i) {
+        const int jc = min((int)threadIdx.x + i * BLOCK, nvec - 1);
+        const int jp = jc == 0 ? nvec - 1 : jc - 1;
+        ga[i] = ringg[jp];
+        ba[i] = ringb[jp];
+      }
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < kIt; ++i) {
+        const u32x4 gc = tg[i], bc = tb[i];
+        switch (q) {
+          case 0: tg[i] = funnel<ES, 0>(ga[i], gc.w, bb); tb[i] = funnel<ES, 0>(ba[i], bc.w, bb); break;
+          case 1: tg[i] = funnel<ES, 1>(ga[i], gc.w, bb); tb[i] = funnel<ES, 1>(ba[i], bc.w, bb); break;
+          case 2: tg[i] = funnel<ES, 2>(ga[i], gc.w, bb); tb[i] = funnel<ES, 2>(ba[i], bc.w, bb); break;
+          default: tg[i] = funnel<ES, 3>(ga[i], gc.w, bb); tb[i] = funnel<ES, 3>(ba[i], bc.w, bb); break;
+        }
       }
     }
 #pragma unroll
