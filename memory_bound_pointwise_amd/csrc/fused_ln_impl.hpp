@@ -280,11 +280,14 @@ __global__ __launch_bounds__(block_for(LANES)) void ln_vec_kernel(
   };
   // 16-bit rows in groups of up to 256 lanes: the first row group's loads
   // are issued before the wait for gamma/beta, and each next group's before
-  // the current one is computed.  fp32 rows issue a group's loads at the top
-  // of its iteration: holding a second fp32 row cost an occupancy step
+  // the current one is computed; so do plain fp32 LayerNorm rows in 256 x 4,
+  // which the host runs as a persistent loop (below: 100 -> 114 registers,
+  // still four waves per SIMD).  Other fp32 rows issue a group's loads at the
+  // top of its iteration: holding a second fp32 row cost an occupancy step
   // (8192 x 8192 fp32 + residual + GeLU: 104 -> 136 registers, 135 -> 164 us);
   // so did 512-lane 16-bit groups (16384 x 12288 + GeLU: 193.3 -> 199.1 us).
-  constexpr bool kAhead = sizeof(typename IO::elem) == 2 && LANES <= 256;
+  constexpr bool kAhead = (sizeof(typename IO::elem) == 2 && LANES <= 256) ||
+                          (sizeof(typename IO::elem) == 4 && !RES && EPI == kEpiNone && LANES == 256 && VPL == 4);
   u32x4 xv[VPL], rv[VPL];
   if constexpr (kAhead) {
     if ((int64_t)blockIdx.x < groups) issue_loads(blockIdx.x, xv, rv);
@@ -1355,6 +1358,18 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
     // 128.0, 125.9 with them, 128.8 for two)
     int vgrid = grid;
     if (groups >= 4096 && (ES == 4 || (lanes == 256 && EPI != kEpiReluDrop))) vgrid = (int)((groups + 1) / 2);
+    // plain fp32 LayerNorm in 256 x 4 (3073-4096 columns): a persistent loop
+    // of two blocks per compute unit, each loading gamma/beta (32 KB) once
+    // for its many rows and issuing the next row's loads ahead (same process,
+    // us: 8192 x 4096 45.8 -> 45.0, 16384 x 4096 88.8 -> 87.9, 12000 x 4096
+    // 66.0 -> 64.7, 4096 x 4096 25.0 -> 24.8; three blocks per unit 45.1, four
+    // 47.1; the same for 16-bit rows was slower, 2-18%)
+    if constexpr (ES == 4 && !RES && EPI == kEpiNone) {
+      if (i == 7 && !w512) {
+        const int64_t pg = 2 * (int64_t)compute_units();
+        if (pg > 0) vgrid = (int)(groups < pg ? groups : pg);
+      }
+    }
     return hipLaunchKernel(k, dim3(vgrid), dim3(block_v), args, 0, s);
   }
   const uintptr_t ax = reinterpret_cast<uintptr_t>(x);

@@ -96,4 +96,8 @@ hipError_t launch_row_var(int dtype, const void* a, const float* mean, float* va
 // in bytes.  Allocates nothing.
 hipError_t static_scratch(void** ptr, size_t* bytes);
 
+// Compute units of the current GPU (looked up once per GPU and kept); 0 when
+// the runtime does not say.
+int compute_units();
+
 }  // namespace mbp

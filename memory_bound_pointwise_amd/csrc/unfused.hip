@@ -34,6 +34,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::atomic<int> g_cu_count[kMaxDevices];
 std::mutex g_scratch_mu;
 
 constexpr int kBlock = 256;
@@ -297,6 +298,17 @@ int64_t stat_grid(int64_t rows, int64_t cols, int es) {
 }
 
 }  // namespace
+
+int compute_units() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 hipError_t static_scratch(void** ptr, size_t* bytes) {
   *ptr = nullptr;
