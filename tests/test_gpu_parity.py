@@ -419,6 +419,17 @@ def test_ln_f32_two_groups_per_block(mbp):
     check_f32(to_host(y)[rows], _ln_ref(d, act, rows), "fp32 LN 4097 x 4096, two groups per block")
 
 
+@pytest.mark.parametrize("rows,cols", [(1031, 3500), (517, 4096), (3, 4096), (2049, 3073)])
+def test_ln_f32_persistent_loop(mbp, rows, cols):
+    """Plain fp32 LayerNorm rows of 3073-4096 columns run as a loop of two
+    blocks per compute unit over the rows, each block issuing its next row's
+    loads ahead: row counts that leave the blocks uneven shares.  Every output
+    element is checked."""
+    w, d, act = _ln_case("ln_8192x4096_f32", rows, cols, residual=False, act="none")
+    y = to_host(_ln_run(mbp, d, act))
+    check_f32(y, _ln_ref(d, act), f"fp32 LN {rows} x {cols}, persistent loop")
+
+
 @pytest.mark.parametrize("cols,residual,act", [(8192, True, "gelu_tanh"), (6144, True, "gelu_tanh"),
                                               (8192, False, "none"), (7000, False, "gelu_tanh")])
 def test_ln_bf16_loads_ahead(mbp, cols, residual, act):
