@@ -452,6 +452,8 @@ LN_STRIDED = [
     (37, 4096, (3, 5), (3, 5), (3, 5)),           # the same, bases off 16 bytes (sliced columns)
     (37, 4096, (3, 0), (5, 0), (0, 0)),           # different pitches: lane-shift kernel
     (40, 4095, (1, 0), (1, 0), "x"),              # in place on a padded buffer
+    (520, 8192, (3, 0), (3, 0), "x"),             # 512 x 2 class layout, in place, several groups a block
+    (300, 3600, (5, 2), (5, 2), (5, 2)),          # 256 x 2 class layout, bases off 16 bytes
     (41, 768, (8, 2), None, (9, 1)),              # narrow rows, sub-wave groups
     (9, 12288, (16, 0), (7, 3), (16, 0)),
     (5, 16384, (2, 1), (2, 1), (2, 1)),           # the widest rows, per-class windows
