@@ -368,6 +368,73 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop8_kernel(
   }
 }
 
+// 16-bit rows of 65-128 vectors: a wave per row (64 lanes x 2 vectors), 16
+// rows a 1024-thread block.  bias, gamma and beta are widened to binary64
+// once per block into LDS (24 KB) instead of twice per use in every wave --
+// the kernel is bound by its vector instructions, and the widenings were six
+// of its ~30 a element: 8192 x 1024 fp16 10.42 -> 9.40 us, bf16 10.26 ->
+// 9.54, 32768 x 1024 fp16 33.7 -> 31.9 (4 rows a block: 11.2; 8: 9.6).  The
+// arithmetic and the reduction order are tenop8_kernel's, so are the results.
+template <class IO>
+__global__ __launch_bounds__(1024) void tenop8_wave_kernel(
+    const typename IO::elem* x, int64_t ldx, const typename IO::elem* __restrict__ bias,
+    const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
+    typename IO::elem* y, int64_t ldy, int64_t rows, int cols, double alpha, double c, double inv_cols) {
+  constexpr int LANES = 64, VPL = 2, RPB = 16, BLOCK = LANES * RPB;
+  static_assert(sizeof(typename IO::elem) == 2, "16-bit storage only");
+  __shared__ double pw[3][8 * LANES * VPL];  // bias, gamma, beta of the row's columns
+  const int lane = threadIdx.x % LANES;
+  const int nvec = cols / 8;  // 65 .. 128 (the host checks)
+  for (int v = threadIdx.x; v < nvec; v += BLOCK) {
+    const u32x4 b = reinterpret_cast<const u32x4*>(bias)[v];
+    const u32x4 g = reinterpret_cast<const u32x4*>(gamma)[v];
+    const u32x4 e = reinterpret_cast<const u32x4*>(beta)[v];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      pw[0][8 * v + k] = (double)IO::get(b, k);
+      pw[1][8 * v + k] = (double)IO::get(g, k);
+      pw[2][8 * v + k] = (double)IO::get(e, k);
+    }
+  }
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LANES;
+  const bool live = row < rows;
+  // past the last row: reread the last row, store nothing; slots past the
+  // row's end reread its last vector and stay out of the sum
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + (live ? row : rows - 1) * ldx);
+  u32x4 xv[VPL];
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) xv[k] = load_nt(xr + min(lane + k * LANES, nvec - 1));
+  __syncthreads();  // the widened parameters are in LDS
+  double sk[VPL][8];
+  double sum = 0.0;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int vi = min(lane + k * LANES, nvec - 1);
+    double part = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double t = __builtin_fma((double)IO::get(xv[k], e), alpha, pw[0][8 * vi + e]);
+      const double a = (t < 0.0) ? 0.0 : t;  // relu; NaN passes through
+      sk[k][e] = __builtin_fma(a, a, a * c);
+      part += sk[k][e];
+    }
+    if (lane + k * LANES < nvec) sum += part;
+  }
+  const double m = wave_reduce<LANES>(sum, SumOp()) * inv_cols;
+  if (!live) return;
+  u32x4* yr = reinterpret_cast<u32x4*>(y + row * ldy);
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int vi = lane + k * LANES;
+    if (vi >= nvec) continue;
+    uint32_t o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      o[e] = narrow_bits<IO>(__builtin_fma(sk[k][e] - m, pw[1][8 * vi + e], pw[2][8 * vi + e]));
+    store_nt(yr + vi, u32x4{{o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16)}});
+  }
+}
+
 // s is held in registers (measured 10% faster than computing it twice at
 // 8192 x 1024 fp16) except in 1024-lane groups of 4 vectors, whose 1024-thread
 // blocks are limited to 128 registers a lane.
@@ -431,8 +498,19 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
     if (vector8_ok) k = shape_kernel<Tenop8Sel<IO>::template K>(shape);
     // rows of 65-128 vectors: 64 lanes x 2 rather than the table's 32 x 4
     // (8192 x 1024 fp16, row stride 1056: 10.26 against 10.57 us; 128 x 1:
-    // 10.63)
+    // 10.63), 16 rows a block with the parameters widened once (above)
     if (vector8_ok && cols / 8 > 64 && cols / 8 <= 128) {
+      const int64_t g16 = (rows + 15) / 16;
+      if (g16 < (1 << 30)) {
+        int icols8 = (int)cols;
+        const E *xe = static_cast<const E*>(x), *bie = static_cast<const E*>(bias);
+        const E *ge = static_cast<const E*>(gamma), *bee = static_cast<const E*>(beta);
+        E* ye = static_cast<E*>(y);
+        double inv8 = 1.0 / (double)cols;
+        void* args8[] = {&xe, &ldx, &bie, &ge, &bee, &ye, &ldy, &rows, &icols8, &alpha, &c, &inv8};
+        return hipLaunchKernel(reinterpret_cast<const void*>(&tenop8_wave_kernel<IO>), dim3((unsigned)g16),
+                               dim3(1024), args8, 0, s);
+      }
       lanes = 64;
       k = reinterpret_cast<const void*>(&tenop8_kernel<IO, 64, 2, true>);
     }
