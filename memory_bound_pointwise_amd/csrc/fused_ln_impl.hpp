@@ -1283,11 +1283,16 @@ struct VecSel {
     static const void* ptr() { return reinterpret_cast<const void*>(&ln_vec_kernel<IO, L, P, RES, EPI>); }
   };
 };
+// fp32 rows of up to 2048 vectors take the shift kernel unless the epilogue
+// is dropout (launch_flags), so those class layouts are not instantiated
 template <class IO, bool RES, int EPI>
 struct ClassSel {
   template <int L, int P>
   struct K {
-    static const void* ptr() { return reinterpret_cast<const void*>(&ln_class_kernel<IO, L, P, RES, EPI>); }
+    static const void* ptr() {
+      if constexpr (sizeof(typename IO::elem) == 4 && EPI != kEpiReluDrop && L * P <= 2048) return nullptr;
+      else return reinterpret_cast<const void*>(&ln_class_kernel<IO, L, P, RES, EPI>);
+    }
   };
 };
 template <class IO, bool RES, int EPI>
@@ -1335,7 +1340,8 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   // 499.0 us, LayerNorm -> ReLU -> dropout 1367.3 -> 361.0 us)
   constexpr bool kAlt = (ES == 4 && !RES && EPI == kEpiNone) || ES == 2;
   const bool w512 = kAlt && i >= 10;
-  constexpr int kLast = ES == 2 ? 9 : 11;  // 16-bit rows never take the 1024-lane layouts
+  // the families with the 512-lane alternatives never take the 1024-lane layouts
+  constexpr int kLast = kAlt ? 9 : 11;
   const int lanes = w512 ? 512 : kShapes[i].lanes;
   const int block_v = block_for(lanes);
   const int rpb_v = block_v / lanes;

@@ -270,13 +270,11 @@ __global__ __launch_bounds__(1024) void tenop_wide_kernel(
 }
 
 // 16-bit storage on 16-byte boundaries: 8 elements per access (one 16-byte
-// load or store per vector).  The row and the parameters stay in storage form.
-// KEEP: s is held in binary64 registers from the row sum to the epilogue (two
-// registers per element); otherwise s is computed twice -- once for the row
-// sum, once for the epilogue -- so that a lane holding 32 elements fits in the
-// registers the 4-element form needs for 16.  Both evaluations are the same
-// binary64 operations, so they give the same s.
-template <class IO, int LANES, int VPL, bool KEEP>
+// load or store per vector).  The row and the parameters stay in storage form;
+// s is held in binary64 registers from the row sum to the epilogue (two
+// registers per element; measured 10% faster than computing it twice at
+// 8192 x 1024 fp16).
+template <class IO, int LANES, int VPL>
 __global__ __launch_bounds__(block_for(LANES)) void tenop8_kernel(
     const typename IO::elem* x, int64_t ldx, const typename IO::elem* __restrict__ bias,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
@@ -314,7 +312,7 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop8_kernel(
 #pragma unroll
     for (int k = 0; k < VPL; ++k) opaque(pb[k]);
 
-    double sk[KEEP ? VPL : 1][8];
+    double sk[VPL][8];
     double sum = 0.0;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
@@ -324,22 +322,13 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop8_kernel(
         const double t = __builtin_fma((double)IO::get(xv[k], e), alpha, (double)IO::get(pb[k], e));
         const double a = (t < 0.0) ? 0.0 : t;  // relu; NaN passes through
         const double sv = __builtin_fma(a, a, a * c);
-        if constexpr (KEEP) sk[k][e] = sv;
+        sk[k][e] = sv;
         part += sv;
       }
       if (lane + k * LANES < nvec) sum += part;
     }
     const double m = group_sum<LANES, BLOCK>(sum, red[parity]) * inv_cols;
 
-    if constexpr (!KEEP) {
-      // new values as far as the compiler knows: s is evaluated again below,
-      // not kept from the loop above
-#pragma unroll
-      for (int k = 0; k < VPL; ++k) {
-        opaque(xv[k]);
-        opaque(pb[k]);
-      }
-    }
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       opaque(pg[k]);
@@ -352,15 +341,7 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop8_kernel(
       uint32_t o[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        double sv;
-        if constexpr (KEEP) {
-          sv = sk[k][e];
-        } else {
-          const double t = __builtin_fma((double)IO::get(xv[k], e), alpha, (double)IO::get(pb[k], e));
-          const double a = (t < 0.0) ? 0.0 : t;
-          sv = __builtin_fma(a, a, a * c);
-        }
-        o[e] = narrow_bits<IO>(__builtin_fma(sv - m, (double)IO::get(pg[k], e), (double)IO::get(pe[k], e)));
+        o[e] = narrow_bits<IO>(__builtin_fma(sk[k][e] - m, (double)IO::get(pg[k], e), (double)IO::get(pe[k], e)));
       }
       store_nt(yr + vi, u32x4{{o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16),
                                o[6] | (o[7] << 16)}});
@@ -373,7 +354,11 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop8_kernel(
 // once per block into LDS (24 KB) instead of twice per use in every wave --
 // the kernel is bound by its vector instructions, and the widenings were six
 // of its ~30 a element: 8192 x 1024 fp16 10.42 -> 9.40 us, bf16 10.26 ->
-// 9.54, 32768 x 1024 fp16 33.7 -> 31.9 (4 rows a block: 11.2; 8: 9.6).  The
+// 9.54, 32768 x 1024 fp16 33.7 -> 31.9 (4 rows a block: 11.2; 8: 9.6).  With
+// each vector's eight values side by side, a wave's 16-byte reads were 64
+// bytes apart and stalled on LDS bank conflicts (2.65 M conflict cycles a
+// launch at 8192 x 1024); pairs interleaved by vector are read conflict-free:
+// 9.71 -> 8.85 us (bf16 9.73 -> 8.72, 8192 x 600 fp16 8.83 -> 8.52).  The
 // arithmetic and the reduction order are tenop8_kernel's, so are the results.
 template <class IO>
 __global__ __launch_bounds__(1024) void tenop8_wave_kernel(
@@ -382,7 +367,12 @@ __global__ __launch_bounds__(1024) void tenop8_wave_kernel(
     typename IO::elem* y, int64_t ldy, int64_t rows, int cols, double alpha, double c, double inv_cols) {
   constexpr int LANES = 64, VPL = 2, RPB = 16, BLOCK = LANES * RPB;
   static_assert(sizeof(typename IO::elem) == 2, "16-bit storage only");
-  __shared__ double pw[3][8 * LANES * VPL];  // bias, gamma, beta of the row's columns
+  // bias, gamma, beta of the row's columns; element e of vector v at
+  // pidx(v, e): pairs of elements interleaved by vector, so that the lanes of
+  // a wave read consecutive 16-byte pairs
+  constexpr int NV = LANES * VPL;
+  __shared__ double pw[3][8 * NV];
+  auto pidx = [](int v, int e) { return ((e >> 1) * NV + v) * 2 + (e & 1); };
   const int lane = threadIdx.x % LANES;
   const int nvec = cols / 8;  // 65 .. 128 (the host checks)
   for (int v = threadIdx.x; v < nvec; v += BLOCK) {
@@ -391,9 +381,9 @@ __global__ __launch_bounds__(1024) void tenop8_wave_kernel(
     const u32x4 e = reinterpret_cast<const u32x4*>(beta)[v];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      pw[0][8 * v + k] = (double)IO::get(b, k);
-      pw[1][8 * v + k] = (double)IO::get(g, k);
-      pw[2][8 * v + k] = (double)IO::get(e, k);
+      pw[0][pidx(v, k)] = (double)IO::get(b, k);
+      pw[1][pidx(v, k)] = (double)IO::get(g, k);
+      pw[2][pidx(v, k)] = (double)IO::get(e, k);
     }
   }
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LANES;
@@ -413,7 +403,7 @@ __global__ __launch_bounds__(1024) void tenop8_wave_kernel(
     double part = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double t = __builtin_fma((double)IO::get(xv[k], e), alpha, pw[0][8 * vi + e]);
+      const double t = __builtin_fma((double)IO::get(xv[k], e), alpha, pw[0][pidx(vi, e)]);
       const double a = (t < 0.0) ? 0.0 : t;  // relu; NaN passes through
       sk[k][e] = __builtin_fma(a, a, a * c);
       part += sk[k][e];
@@ -430,30 +420,36 @@ __global__ __launch_bounds__(1024) void tenop8_wave_kernel(
     uint32_t o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      o[e] = narrow_bits<IO>(__builtin_fma(sk[k][e] - m, pw[1][8 * vi + e], pw[2][8 * vi + e]));
+      o[e] = narrow_bits<IO>(__builtin_fma(sk[k][e] - m, pw[1][pidx(vi, e)], pw[2][pidx(vi, e)]));
     store_nt(yr + vi, u32x4{{o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16)}});
   }
 }
 
-// s is held in registers (measured 10% faster than computing it twice at
-// 8192 x 1024 fp16) except in 1024-lane groups of 4 vectors, whose 1024-thread
-// blocks are limited to 128 registers a lane.
+// Rows of 65-128 vectors (32 x 3, 32 x 4) take tenop8_wave_kernel and rows
+// past 16384 columns the two-pass kernel, so those layouts are not
+// instantiated here.
 template <class IO>
 struct Tenop8Sel {
   template <int L, int V>
   struct K {
-    static const void* ptr() { return reinterpret_cast<const void*>(&tenop8_kernel<IO, L, V, !(L == 1024 && V >= 4)>); }
+    static const void* ptr() {
+      if constexpr ((L == 32 && V >= 3) || L == 1024) return nullptr;
+      else return reinterpret_cast<const void*>(&tenop8_kernel<IO, L, V>);
+    }
   };
 };
 
 // Kernel of layout (L, V) of the row tables: V groups of 4 elements per lane,
-// or, on the element path, the same elements one at a time.
+// or, on the element path, the same elements one at a time.  fp32 rows of
+// 4-element accesses take tenop1_kernel up to 256 vectors, 512 x 6 past 2048
+// and the two-pass kernel past 3072, so those layouts are not instantiated.
 template <class IO, bool VEC>
 struct TenopSel {
   template <int L, int V>
   struct K {
     static const void* ptr() {
-      if constexpr (VEC) return reinterpret_cast<const void*>(&tenop_kernel<IO, L, V, 4>);
+      if constexpr (VEC && sizeof(typename IO::elem) == 4 && (L * V <= 256 || L == 1024)) return nullptr;
+      else if constexpr (VEC) return reinterpret_cast<const void*>(&tenop_kernel<IO, L, V, 4>);
       else return reinterpret_cast<const void*>(&tenop_kernel<IO, L, 4 * V, 1>);
     }
   };
@@ -501,7 +497,10 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
     // 10.63), 16 rows a block with the parameters widened once (above)
     if (vector8_ok && cols / 8 > 64 && cols / 8 <= 128) {
       const int64_t g16 = (rows + 15) / 16;
-      if (g16 < (1 << 30)) {
+      // one block per 16 rows, no loop: past 2^30 blocks (2^34 rows) the
+      // launch would exceed what one dispatch can address
+      if (g16 >= (1 << 30)) return hipErrorInvalidValue;
+      {
         int icols8 = (int)cols;
         const E *xe = static_cast<const E*>(x), *bie = static_cast<const E*>(bias);
         const E *ge = static_cast<const E*>(gamma), *bee = static_cast<const E*>(beta);
@@ -511,8 +510,6 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
         return hipLaunchKernel(reinterpret_cast<const void*>(&tenop8_wave_kernel<IO>), dim3((unsigned)g16),
                                dim3(1024), args8, 0, s);
       }
-      lanes = 64;
-      k = reinterpret_cast<const void*>(&tenop8_kernel<IO, 64, 2, true>);
     }
   } else {
     // fp32 rows of at most 256 vectors: one vector per lane (measured at
@@ -527,22 +524,18 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
     }
     if (vector_ok && nvec <= 256) {
       lanes = nvec <= 16 ? 16 : nvec <= 32 ? 32 : nvec <= 64 ? 64 : nvec <= 128 ? 128 : 256;
+      // one block per row group, no loop (past 2^30 blocks, at least 2^34
+      // rows, the launch would exceed what one dispatch can address)
       const int64_t g1 = (rows + 256 / lanes - 1) / (256 / lanes);
-      if (g1 < (1 << 30)) {  // one block per row group, no loop
-        k = lanes == 16    ? reinterpret_cast<const void*>(&tenop1_kernel<16>)
-            : lanes == 32  ? reinterpret_cast<const void*>(&tenop1_kernel<32>)
-            : lanes == 64  ? reinterpret_cast<const void*>(&tenop1_kernel<64>)
-            : lanes == 128 ? reinterpret_cast<const void*>(&tenop1_kernel<128>)
-                           : reinterpret_cast<const void*>(&tenop1_kernel<256>);
-      } else {
-        k = lanes == 16    ? reinterpret_cast<const void*>(&tenop_kernel<IO, 16, 1, 4>)
-            : lanes == 32  ? reinterpret_cast<const void*>(&tenop_kernel<IO, 32, 1, 4>)
-            : lanes == 64  ? reinterpret_cast<const void*>(&tenop_kernel<IO, 64, 1, 4>)
-            : lanes == 128 ? reinterpret_cast<const void*>(&tenop_kernel<IO, 128, 1, 4>)
-                           : reinterpret_cast<const void*>(&tenop_kernel<IO, 256, 1, 4>);
-      }
+      if (g1 >= (1 << 30)) return hipErrorInvalidValue;
+      k = lanes == 16    ? reinterpret_cast<const void*>(&tenop1_kernel<16>)
+          : lanes == 32  ? reinterpret_cast<const void*>(&tenop1_kernel<32>)
+          : lanes == 64  ? reinterpret_cast<const void*>(&tenop1_kernel<64>)
+          : lanes == 128 ? reinterpret_cast<const void*>(&tenop1_kernel<128>)
+                         : reinterpret_cast<const void*>(&tenop1_kernel<256>);
     }
   }
+  if (!k) return hipErrorInvalidValue;  // no layout instantiated for this case (not reached)
   const int block = block_for(lanes);
   const int rpb = block / lanes;
   const int64_t groups = (rows + rpb - 1) / rpb;

@@ -260,21 +260,39 @@ __global__ __launch_bounds__(kBlock) void row_stat_kernel(const typename IO::ele
   }
 }
 
+// Only the (type, op, access width) forms a caller can reach are
+// instantiated: the bf16 calls never multiply, scale or take the 10-op
+// groups (the unfused chain and 10-op graph are fp32), and relu and exp only
+// ever read and write the 256-byte aligned workspace, so never one element
+// at a time.
 template <class IO, int VW>
 const void* ew_ptr(int op) {
+  constexpr bool kBf16 = sizeof(typename IO::elem) == 2;
   switch (op) {
     case EW_ADD: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_ADD, VW>);
     case EW_SUB: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_SUB, VW>);
-    case EW_MUL: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_MUL, VW>);
-    case EW_RELU: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_RELU, VW>);
-    case EW_MULS: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_MULS, VW>);
+    case EW_MUL:
+      if constexpr (!kBf16) return reinterpret_cast<const void*>(&ew_kernel<IO, EW_MUL, VW>);
+      return nullptr;
+    case EW_RELU:
+      if constexpr (VW != 1) return reinterpret_cast<const void*>(&ew_kernel<IO, EW_RELU, VW>);
+      return nullptr;
+    case EW_MULS:
+      if constexpr (!kBf16) return reinterpret_cast<const void*>(&ew_kernel<IO, EW_MULS, VW>);
+      return nullptr;
     case EW_DIVSD: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_DIVSD, VW>);
     case EW_MULADD: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_MULADD, VW>);
     case EW_GELU: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_GELU, VW>);
     case EW_DROPOUT: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_DROPOUT, VW>);
-    case EW_PROLOGUE: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_PROLOGUE, VW>);
-    case EW_CENTER_AFFINE: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_CENTER_AFFINE, VW>);
-    case EW_EXP: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_EXP, VW>);
+    case EW_PROLOGUE:
+      if constexpr (!kBf16) return reinterpret_cast<const void*>(&ew_kernel<IO, EW_PROLOGUE, VW>);
+      return nullptr;
+    case EW_CENTER_AFFINE:
+      if constexpr (!kBf16) return reinterpret_cast<const void*>(&ew_kernel<IO, EW_CENTER_AFFINE, VW>);
+      return nullptr;
+    case EW_EXP:
+      if constexpr (VW != 1) return reinterpret_cast<const void*>(&ew_kernel<IO, EW_EXP, VW>);
+      return nullptr;
     case EW_DIV: return reinterpret_cast<const void*>(&ew_kernel<IO, EW_DIV, VW>);
     default: return nullptr;
   }

@@ -302,3 +302,22 @@ def test_binding_rejects_cpu_tensors(mbp):
     x = torch.zeros(8)
     with pytest.raises(ValueError):
         mbp.fused_pointwise_chain(x, x, x)
+
+
+def test_kernel_coverage_lists_the_kernels(tmp_path):
+    """tests/kernel_coverage.py: the library's kernel stubs are found, and a
+    kernel trace's names (with their argument lists) match them."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import kernel_coverage as kc
+    inst = kc.instantiated()
+    assert "mbp::ln::ln_vec_kernel<mbp::BF16IO, 256, 4, true, 1>" in inst
+    assert "mbp::chain_kernel<1>" in inst
+    assert not any("shape_kernel" in n for n in inst)
+    stats = tmp_path / "k.csv"
+    stats.write_text('"Name","Calls"\n'
+                     '"void mbp::(anonymous namespace)::chain_kernel<1>(float const*, float const*, float const*, '
+                     'float*, long, long, long, double)",3\n'
+                     '"__amd_rocclr_copyBuffer",2\n')
+    assert kc.dispatched(str(stats)) == {"mbp::chain_kernel<1>"}
+    assert kc.main(["kernel_coverage.py", str(stats)]) == 1
