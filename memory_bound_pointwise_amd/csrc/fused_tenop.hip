@@ -166,10 +166,11 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop_kernel(
     for (int k = 0; k < VPL; ++k) {
       const int vi = lane + k * LANES;
       if (!(live && vi < nvec)) continue;
-      uint32_t o[VW];
+      double yv[VW];
 #pragma unroll
-      for (int e = 0; e < VW; ++e)
-        o[e] = narrow_bits<IO>(__builtin_fma(s[k][e] - m, gd[k][e], bd[k][e]));
+      for (int e = 0; e < VW; ++e) yv[e] = __builtin_fma(s[k][e] - m, gd[k][e], bd[k][e]);
+      uint32_t o[VW];
+      narrow_n<IO, VW>(yv, o);
       if constexpr (VW == 1) {
         if constexpr (sizeof(E) == 4) yr[vi] = __uint_as_float(o[0]);
         else yr[vi] = (uint16_t)o[0];
@@ -338,11 +339,11 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop8_kernel(
     for (int k = 0; k < VPL; ++k) {
       const int vi = lane + k * LANES;
       if (!(live && vi < nvec)) continue;
-      uint32_t o[8];
+      double yv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        o[e] = narrow_bits<IO>(__builtin_fma(sk[k][e] - m, (double)IO::get(pg[k], e), (double)IO::get(pe[k], e)));
-      }
+      for (int e = 0; e < 8; ++e) yv[e] = __builtin_fma(sk[k][e] - m, (double)IO::get(pg[k], e), (double)IO::get(pe[k], e));
+      uint32_t o[8];
+      narrow_n<IO, 8>(yv, o);
       store_nt(yr + vi, u32x4{{o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16),
                                o[6] | (o[7] << 16)}});
     }
@@ -417,10 +418,11 @@ __global__ __launch_bounds__(1024) void tenop8_wave_kernel(
   for (int k = 0; k < VPL; ++k) {
     const int vi = lane + k * LANES;
     if (vi >= nvec) continue;
-    uint32_t o[8];
+    double yv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      o[e] = narrow_bits<IO>(__builtin_fma(sk[k][e] - m, pw[1][pidx(vi, e)], pw[2][pidx(vi, e)]));
+    for (int e = 0; e < 8; ++e) yv[e] = __builtin_fma(sk[k][e] - m, pw[1][pidx(vi, e)], pw[2][pidx(vi, e)]);
+    uint32_t o[8];
+    narrow_n<IO, 8>(yv, o);
     store_nt(yr + vi, u32x4{{o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16)}});
   }
 }

@@ -117,6 +117,43 @@ __device__ __forceinline__ uint32_t narrow_bits(double d) {
   else return f32_to_f16(round_odd_f32(d));
 }
 
+// N binary64 values -> their stored bits, each rounded once to nearest even,
+// as narrow_bits gives them.  For the 16-bit types: rounding to nearest
+// binary32 first and then to 16 bits gives the same result unless the binary32
+// value is itself a halfway point of the 16-bit format -- every such halfway
+// point is a binary32 value and both roundings are monotone, so a value that
+// does not land on one stays on its side of every halfway point.  Halfway
+// points have the bits below the 16-bit significand equal to 100...0 (bf16:
+// the low 16 bits, at every exponent; binary16: the low 13 bits in its normal
+// range, including the boundary to infinity, 65520); binary16's subnormal
+// range, whose halfway points sit at other positions, is sent the same way.
+// Those values -- about one in 8192 -- take round_odd_f32, once per N values
+// when any lane has one.
+template <class IO, int N>
+__device__ __forceinline__ void narrow_n(const double* d, uint32_t* o) {
+  if constexpr (sizeof(typename IO::elem) == 4) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) o[e] = __float_as_uint((float)d[e]);
+  } else {
+    constexpr bool kBf16 = __is_same(IO, BF16IO);
+    float r[N];
+    bool tie = false;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      r[e] = (float)d[e];
+      const uint32_t u = __float_as_uint(r[e]);
+      if constexpr (kBf16) tie |= (u & 0xffffu) == 0x8000u;
+      else tie |= ((u & 0x1fffu) == 0x1000u) | (__builtin_fabsf(r[e]) < 0x1p-14f);
+    }
+    if (__builtin_expect(tie, 0)) {
+#pragma unroll
+      for (int e = 0; e < N; ++e) r[e] = round_odd_f32(d[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < N; ++e) o[e] = kBf16 ? f32_to_bf16(r[e]) : f32_to_f16(r[e]);
+  }
+}
+
 // tanh-approximated GeLU, 0.5 u (1 + tanh(k0 (u + k1 u^3))) with k0 = 0.7978845608,
 // k1 = 0.044715 ("算子融合与 Kernel 优化", section 2.3), evaluated through the exact
 // identity 0.5 (1 + tanh z) = 1 / (1 + exp(-2 z)) and exp(w) = exp2(w log2 e):

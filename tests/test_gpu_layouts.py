@@ -148,6 +148,23 @@ def _place_dev(t, off, fill=0.0):
 TENOP_PATHS = {"vec8": (8, 0), "vec4": (4, 4), "elem": (4, 1)}
 
 
+def _rounded_once(y, exact, fmt, what):
+    """16-bit outputs must be the exact value rounded once to nearest even,
+    bit for bit, wherever that rounding is stable under a relative change of
+    2^-40 (binary64 arithmetic in another order moves the result far less; a
+    double rounding through binary32 would be off by one ulp near halfway
+    points, which the 1-ulp gate alone lets through)."""
+    got = bits16(y)
+    want = oracle.round_bits(exact, fmt)
+    lo = oracle.round_bits(exact * (1 - 2.0 ** -40), fmt)
+    hi = oracle.round_bits(exact * (1 + 2.0 ** -40), fmt)
+    stable = (lo == hi) & ~np.isnan(exact)
+    bad = np.argwhere(stable & (got != want))
+    assert bad.size == 0, (f"{what}: {len(bad)} outputs not rounded once, first at {tuple(bad[0])}: "
+                           f"got {got[tuple(bad[0])]:#06x} want {want[tuple(bad[0])]:#06x}")
+    return int(stable.size - stable.sum())
+
+
 def _tenop_cols(fmt, path):
     w, _ = TENOP_PATHS[path]
     out, lo = [], 0
@@ -160,11 +177,12 @@ def _tenop_cols(fmt, path):
     return sorted({c for c in out if c <= 16384} | {12289, 16385, 20000})
 
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("path", list(TENOP_PATHS))
+# fp32 rows have no 8-element path
+TENOP_CASES = [(f, p) for f in ("f32", "bf16", "f16") for p in TENOP_PATHS if not (f == "f32" and p == "vec8")]
+
+
+@pytest.mark.parametrize("fmt,path", TENOP_CASES)
 def test_tenop_every_layout(mbp, fmt, path):
-    if fmt == "f32" and path == "vec8":
-        pytest.skip("fp32 rows have no 8-element path")
     dtype = DT[fmt]
     _, off = TENOP_PATHS[path]
     if fmt == "f32" and path == "vec4":
@@ -181,6 +199,8 @@ def test_tenop_every_layout(mbp, fmt, path):
         mbp.fused_row_mean_epilogue_2d(x, *(v[0].cuda() for v in vecs), alpha=1.1, c=0.1, out=y)
         exact = oracle.row_mean_epilogue(xf, *(v[1] for v in vecs), 1.1, 0.1)
         _gate_2d(y, exact, fmt, what, row_kernel=True)
+        if fmt != "f32":
+            _rounded_once(y, exact, fmt, what)
         assert _untouched(yb, off, y.numel()), f"{what}: wrote outside y"
 
 
@@ -276,3 +296,18 @@ def test_unfused_dropout_and_softmax_paths(mbp, fmt, offs):
             dd = np.abs(ordered(to_host(ys)) - ordered(want.astype(np.float32)))
             assert dd.max(initial=0) <= 4, f"{what}: max {dd.max()} ulp"
         assert _untouched(ysb, offs[1], ys.numel()), f"{what}: wrote outside y"
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+@pytest.mark.parametrize("cols,off", [(4096, 0), (4092, 4), (4095, 1)])
+def test_chain_2d_rounded_once(mbp, fmt, cols, off):
+    """The 16-bit chain on random inputs, every output the exact value rounded
+    once (16-byte, 4-element and single-element paths)."""
+    dtype = DT[fmt]
+    rows = 64
+    rng = np.random.default_rng([83, cols, off])
+    ops = [_stored(rng, (rows, cols), dtype) for _ in range(3)]
+    devs = [_place_dev(o[0], off)[0] for o in ops]
+    y = mbp.fused_pointwise_chain_2d(*devs, 0.5)
+    exact = oracle.pointwise_chain(*(o[1] for o in ops), 0.5)
+    _rounded_once(y, exact, fmt, f"chain 2d {fmt} {rows}x{cols} at +{off}")
