@@ -1346,7 +1346,10 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   const int block_v = block_for(lanes);
   const int rpb_v = block_v / lanes;
   const int64_t groups = (rows + rpb_v - 1) / rpb_v;
-  const int grid = (int)(groups < kMaxGrid ? groups : kMaxGrid);  // one block per row group
+  // one block per row group, within what a dispatch can address (the row
+  // kernels loop over the rest)
+  const int64_t gmax = dispatch_blocks(block_v) < kMaxGrid ? dispatch_blocks(block_v) : kMaxGrid;
+  const int grid = (int)(groups < gmax ? groups : gmax);
   int icols = (int)cols;
   Drop drop = drop_in;
   void* args[] = {&x, &res, &gamma, &beta, &y, &rows, &icols, &ldx, &ldr, &ldy, &eps, &drop};
@@ -1362,8 +1365,8 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
     // 16384 x 8192: 92.5 us for two groups a block without the early loads,
     // 91.3 for one with them, 92.4 for two with them; 32768 x 4096 + GeLU:
     // 128.0, 125.9 with them, 128.8 for two)
-    int vgrid = grid;
-    if (groups >= 4096 && (ES == 4 || (lanes == 256 && EPI != kEpiReluDrop))) vgrid = (int)((groups + 1) / 2);
+    int64_t vgrid = grid;
+    if (groups >= 4096 && (ES == 4 || (lanes == 256 && EPI != kEpiReluDrop))) vgrid = (groups + 1) / 2;
     // plain fp32 LayerNorm in 256 x 4 (3073-4096 columns): a persistent loop
     // of two blocks per compute unit, each loading gamma/beta (32 KB) once
     // for its many rows and issuing the next row's loads ahead (same process,
@@ -1373,10 +1376,11 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
     if constexpr (ES == 4 && !RES && EPI == kEpiNone) {
       if (i == 7 && !w512) {
         const int64_t pg = 2 * (int64_t)compute_units();
-        if (pg > 0) vgrid = (int)(groups < pg ? groups : pg);
+        if (pg > 0) vgrid = groups < pg ? groups : pg;
       }
     }
-    return hipLaunchKernel(k, dim3(vgrid), dim3(block_v), args, 0, s);
+    if (vgrid > grid) vgrid = grid;
+    return hipLaunchKernel(k, dim3((unsigned)vgrid), dim3(block_v), args, 0, s);
   }
   const uintptr_t ax = reinterpret_cast<uintptr_t>(x);
   // x, residual and y agree modulo 16 bytes in every row: congruent bases and
@@ -1454,6 +1458,10 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
         (c512 || (rpb == 1 && (ES == 4 || EPI == kEpiReluDrop))) ? 2 * kClassGroups : kClassGroups;
     int64_t nblk = (cgroups + per_block - 1) / per_block;
     if (nblk > kMaxGrid / 128) nblk = kMaxGrid / 128;
+    // the blocks of a class loop over its row groups; keep the launch within
+    // what a dispatch can address
+    const int64_t nmax = (dispatch_blocks(block) - edge_blocks) / period;
+    if (nblk > nmax) nblk = nmax;
     const void* k =
         c512   ? reinterpret_cast<const void*>(&ln_class_kernel<IO, 512, 2, RES, EPI>)
         : c256 ? reinterpret_cast<const void*>(&ln_class_kernel<IO, 256, 2, RES, EPI>)
@@ -1464,7 +1472,8 @@ hipError_t launch_flags(const void* x, int64_t ldx, const void* res, int64_t ldr
   }
   // kShiftGroups row groups per block amortise the per-block gamma/beta set-up
   const void* k = shape_kernel_alt<ShiftSel<IO, RES, EPI>::template K, kAlt, true, kLast>(i, w512);
-  const int sgrid = (int)((groups + kShiftGroups - 1) / kShiftGroups);
+  const int64_t sg = (groups + kShiftGroups - 1) / kShiftGroups;
+  const int sgrid = (int)(sg < grid ? sg : grid);  // the shift kernel loops over the rest
   return hipLaunchKernel(k, dim3(sgrid), dim3(block_v), args, 0, s);
 }
 

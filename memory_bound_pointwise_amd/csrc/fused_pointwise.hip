@@ -18,7 +18,7 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kChainUnroll = 1;
-constexpr int64_t kMaxGrid = 1 << 30;
+constexpr int64_t kMaxGrid = dispatch_blocks(kBlock);  // every kernel here loops over its items
 
 __device__ __forceinline__ float chain_op(float x, float b1, float b2, double scale) {
   const double t = (double)x + (double)b1;

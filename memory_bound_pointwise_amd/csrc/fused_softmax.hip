@@ -408,6 +408,18 @@ hipError_t launch_softmax_io(const void* x, int64_t ldx, void* y, int64_t ldy, i
   typedef typename IO::elem E;
   constexpr int V = IO::kVec;
   constexpr int64_t ES = (int64_t)sizeof(E);
+  // softmax_kernel and softmax_win_kernel take one block per row group and no
+  // loop: rows past what one dispatch can address go in chunks (rows are
+  // independent; a stride of 0 keeps its one row)
+  if (rows > kRowsPerDispatch) {
+    for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerDispatch) {
+      const int64_t n = rows - r0 < kRowsPerDispatch ? rows - r0 : kRowsPerDispatch;
+      const hipError_t e = launch_softmax_io<IO>(static_cast<const E*>(x) + r0 * ldx, ldx,
+                                                 static_cast<E*>(y) + r0 * ldy, ldy, n, cols, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (rows == 1) ldx = ldy = cols;  // one row: its stride is never used
   const int64_t nvec = (cols + V - 1) / V;
   // fp32 rows past kRegCols columns take the multi-pass kernel; 16-bit rows
@@ -467,7 +479,8 @@ hipError_t launch_softmax_io(const void* x, int64_t ldx, void* y, int64_t ldy, i
     const int64_t n_edge = r_lo + (rows - r_hi);
     const int64_t main_blocks = (r_hi - r_lo + wrpb - 1) / wrpb;
     const int64_t edge_blocks = (n_edge + wrpb - 1) / wrpb;
-    if (main_blocks + edge_blocks > (1 << 30)) return hipErrorInvalidValue;  // one block per row group
+    // one block per row group (at most kRowsPerDispatch rows here)
+    if (main_blocks + edge_blocks > dispatch_blocks(wblock)) return hipErrorInvalidValue;
     int line = line_ok ? 128 : 16;
     int eb = (int)edge_blocks;
     const void* k = shape_kernel_alt<SoftmaxWinSel<IO>::template K, true, true, 9>(shape, w512);
@@ -477,8 +490,8 @@ hipError_t launch_softmax_io(const void* x, int64_t ldx, void* y, int64_t ldy, i
   const void* k = vec ? shape_kernel_alt<SoftmaxSel<IO, true>::template K, kAlt16, true, kAlt16 ? 9 : 11>(shape, a16)
                       : shape_kernel_alt<SoftmaxSel<IO, false>::template K, kAlt16, true, kAlt16 ? 9 : 11>(shape, a16);
   const int64_t groups = (rows + rpb - 1) / rpb;
-  const int grid = (int)(groups < (1 << 30) ? groups : (1 << 30));
-  if (groups > grid) return hipErrorInvalidValue;  // one block per row group
+  const int grid = (int)(groups < dispatch_blocks(block) ? groups : dispatch_blocks(block));
+  if (groups > grid) return hipErrorInvalidValue;  // one block per row group (at most kRowsPerDispatch rows here)
   void* args[] = {&xe, &ye, &rows, &icols, &ldx, &ldy};
   return hipLaunchKernel(k, dim3(grid), dim3(block), args, 0, s);
 }

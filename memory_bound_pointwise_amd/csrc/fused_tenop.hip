@@ -462,6 +462,18 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
                         void* y, int64_t ldy, int64_t rows, int64_t cols, double alpha, double c,
                         hipStream_t s) {
   typedef typename IO::elem E;
+  // tenop1_kernel and tenop8_wave_kernel take one block per row group and no
+  // loop: rows past what one dispatch can address go in chunks (rows are
+  // independent; a stride of 0 keeps its one row)
+  if (rows > kRowsPerDispatch) {
+    for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerDispatch) {
+      const int64_t n = rows - r0 < kRowsPerDispatch ? rows - r0 : kRowsPerDispatch;
+      const hipError_t e = launch_tenop<IO>(static_cast<const E*>(x) + r0 * ldx, ldx, bias, gamma, beta,
+                                            static_cast<E*>(y) + r0 * ldy, ldy, n, cols, alpha, c, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   // 4-element accesses: every row start on a 4-element boundary
   constexpr uintptr_t A4 = 4 * sizeof(E);
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) % A4) == 0; };
@@ -499,9 +511,8 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
     // 10.63), 16 rows a block with the parameters widened once (above)
     if (vector8_ok && cols / 8 > 64 && cols / 8 <= 128) {
       const int64_t g16 = (rows + 15) / 16;
-      // one block per 16 rows, no loop: past 2^30 blocks (2^34 rows) the
-      // launch would exceed what one dispatch can address
-      if (g16 >= (1 << 30)) return hipErrorInvalidValue;
+      // one block per 16 rows, no loop (at most kRowsPerDispatch rows here)
+      if (g16 > dispatch_blocks(1024)) return hipErrorInvalidValue;
       {
         int icols8 = (int)cols;
         const E *xe = static_cast<const E*>(x), *bie = static_cast<const E*>(bias);
@@ -526,10 +537,9 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
     }
     if (vector_ok && nvec <= 256) {
       lanes = nvec <= 16 ? 16 : nvec <= 32 ? 32 : nvec <= 64 ? 64 : nvec <= 128 ? 128 : 256;
-      // one block per row group, no loop (past 2^30 blocks, at least 2^34
-      // rows, the launch would exceed what one dispatch can address)
+      // one block per row group, no loop (at most kRowsPerDispatch rows here)
       const int64_t g1 = (rows + 256 / lanes - 1) / (256 / lanes);
-      if (g1 >= (1 << 30)) return hipErrorInvalidValue;
+      if (g1 > dispatch_blocks(256)) return hipErrorInvalidValue;
       k = lanes == 16    ? reinterpret_cast<const void*>(&tenop1_kernel<16>)
           : lanes == 32  ? reinterpret_cast<const void*>(&tenop1_kernel<32>)
           : lanes == 64  ? reinterpret_cast<const void*>(&tenop1_kernel<64>)
@@ -541,7 +551,8 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
   const int block = block_for(lanes);
   const int rpb = block / lanes;
   const int64_t groups = (rows + rpb - 1) / rpb;
-  const int grid = (int)(groups < (1 << 30) ? groups : (1 << 30));  // one block per row group
+  // one block per row group (tenop_kernel and tenop8_kernel loop over the rest)
+  const int grid = (int)(groups < dispatch_blocks(block) ? groups : dispatch_blocks(block));
   int icols = (int)cols;
   const E *xe = static_cast<const E*>(x), *bie = static_cast<const E*>(bias);
   const E *ge = static_cast<const E*>(gamma), *bee = static_cast<const E*>(beta);

@@ -22,6 +22,15 @@ struct Drop {
 // epilogues of the LayerNorm kernels
 constexpr int kEpiNone = 0, kEpiGelu = 1, kEpiReluDrop = 2;
 
+// A dispatch addresses at most 2^32 - 1 work-items along x, so a launch of
+// `block`-thread blocks takes at most this many blocks.  Kernels that loop
+// over their work cap their grids at it; kernels with one block per row group
+// and no loop are launched on row chunks of at most kRowsPerDispatch rows
+// (2^21 rows make at most 2^21 row groups: with the few edge blocks of the
+// window kernels, under 2^22 blocks of up to 1024 threads).
+constexpr int64_t dispatch_blocks(int block) { return (int64_t)0xFFFFFFFFu / block; }
+constexpr int64_t kRowsPerDispatch = int64_t(1) << 21;
+
 hipError_t launch_chain(const float* x, const float* b1, const float* b2, float* y, int64_t n,
                         double scale, hipStream_t s);
 // dtype: 0 fp32, 1 bf16, 2 fp16; row strides in elements (0: broadcast row)

@@ -38,7 +38,7 @@ std::atomic<int> g_cu_count[kMaxDevices];
 std::mutex g_scratch_mu;
 
 constexpr int kBlock = 256;
-constexpr int64_t kMaxGrid = 1 << 30;
+constexpr int64_t kMaxGrid = dispatch_blocks(kBlock);  // every kernel here loops over its items
 
 template <int OP>
 __device__ __forceinline__ float ew_apply(float a, float b, float c, float d, float scalar,

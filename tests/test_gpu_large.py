@@ -92,3 +92,86 @@ def test_tenop_f32_past_2_31(mbp):
     ti = torch.from_numpy(rs).cuda()
     ref = oracle.row_mean_epilogue(x[ti].cpu().numpy(), *(t.cpu().numpy() for t in (bias, gamma, beta)))
     check_f32(to_host(y[ti]), ref, f"10-op {rows}x{cols} fp32, rows around element 2^31")
+
+
+# ------------------------------------------------------------------ more row groups than one dispatch holds
+#
+# A dispatch addresses at most 2^32 - 1 work-items, 2^24 - 1 blocks of 256
+# threads; the narrowest layouts hold 16 rows a block, so 2^28 + 37 rows need
+# more blocks than that.  Kernels that loop over row groups run on a capped
+# grid; those with one block per row group are launched on chunks of 2^21 rows.
+
+MANY = (1 << 28) + 37
+CHUNK = 1 << 21
+
+
+def _rows_many(rows):
+    """first and last rows, both sides of every 2^21-row chunk boundary in the
+    first few and the last, around 16 x (2^24 - 1) rows (a full 256-thread
+    dispatch of 16-row groups), and a seeded random sample"""
+    near = [0, 1, 2, rows - 3, rows - 2, rows - 1, 16 * ((1 << 24) - 1) - 1, 16 * ((1 << 24) - 1),
+            16 * ((1 << 24) - 1) + 1]
+    for k in (1, 2, 3, rows // CHUNK - 1, rows // CHUNK):
+        near += [k * CHUNK - 1, k * CHUNK, k * CHUNK + 1]
+    sample = np.random.default_rng(41).integers(0, rows, 2000)
+    return np.unique(np.clip(np.array(near + list(sample)), 0, rows - 1))
+
+
+@pytest.mark.parametrize("cols", [8, 7])
+def test_layernorm_bf16_many_rows(mbp, cols):
+    """8: 16-byte accesses (16 rows a block, a capped grid); 7: rows off
+    16-byte boundaries (the window-class kernel, its class blocks capped)"""
+    rows = MANY
+    x, r = _randn((rows, cols), torch.bfloat16, 51), _randn((rows, cols), torch.bfloat16, 52)
+    g = (1 + 0.1 * _randn((cols,), torch.float32, 53)).to(torch.bfloat16)
+    b = (0.1 * _randn((cols,), torch.float32, 54)).to(torch.bfloat16)
+    y = torch.full_like(x, 3.0)
+    mbp.fused_add_layernorm_gelu(x, r, g, b, eps=1e-5, act="gelu_tanh", out=y)
+    ti = torch.from_numpy(_rows_many(rows)).cuda()
+    ref = oracle.add_layernorm_gelu(_host16(x[ti]), _host16(r[ti]), _host16(g), _host16(b), eps=1e-5,
+                                    act=oracle.ACT_GELU_TANH)
+    check_bf16(to_host(y[ti]), ref, f"residual+LN+GeLU {rows}x{cols} bf16, sampled rows")
+    assert not (y == 3.0).all(dim=1).any().item(), "a row was not written"
+
+
+@pytest.mark.parametrize("cols", [4, 5])
+def test_softmax_f32_many_rows(mbp, cols):
+    """4: 16-byte accesses; 5: rows off 16-byte boundaries (windows); both in
+    2^21-row chunks"""
+    rows = MANY
+    x = _randn((rows, cols), torch.float32, 61, std=3.0)
+    y = torch.full_like(x, 3.0)
+    mbp.fused_softmax(x, out=y)
+    ti = torch.from_numpy(_rows_many(rows)).cuda()
+    from parity_util import check_softmax_f32
+    xs = x[ti].cpu().numpy()
+    check_softmax_f32(to_host(y[ti]), oracle.softmax(xs), xs, f"softmax {rows}x{cols} fp32, sampled rows")
+    assert not (y == 3.0).all(dim=1).any().item(), "a row was not written"
+
+
+def test_tenop_f32_many_rows(mbp):
+    """one 16-lane group a row, 16 rows a block, no loop: 2^21-row chunks"""
+    rows, cols = MANY, 4
+    x = _randn((rows, cols), torch.float32, 71)
+    bias, gamma, beta = (_randn((cols,), torch.float32, s) for s in (72, 73, 74))
+    y = torch.full_like(x, 3.0)
+    mbp.fused_row_mean_epilogue(x, bias, gamma, beta, out=y)
+    ti = torch.from_numpy(_rows_many(rows)).cuda()
+    ref = oracle.row_mean_epilogue(x[ti].cpu().numpy(), *(t.cpu().numpy() for t in (bias, gamma, beta)))
+    check_f32(to_host(y[ti]), ref, f"10-op {rows}x{cols} fp32, sampled rows")
+    assert not (y == 3.0).all(dim=1).any().item(), "a row was not written"
+
+
+def test_tenop_f16_wave_many_rows(mbp):
+    """the wave-per-row kernel (rows of 65-128 vectors) on more rows than one
+    chunk: 2^21-row chunks of 16-row blocks"""
+    rows, cols = 2 * CHUNK + 21, 520
+    x = _randn((rows, cols), torch.float16, 81)
+    bias, gamma, beta = (_randn((cols,), torch.float16, s) for s in (82, 83, 84))
+    y = mbp.fused_row_mean_epilogue_2d(x, bias, gamma, beta, 1.1, 0.1)
+    rs = _rows_many(rows)
+    ti = torch.from_numpy(rs).cuda()
+    ref = oracle.row_mean_epilogue(x[ti].float().cpu().numpy(), *(t.float().cpu().numpy() for t in (bias, gamma, beta)),
+                                   1.1, 0.1)
+    from parity_util import check_ulp16
+    check_ulp16(bits16(y[ti]), ref, "f16", f"10-op {rows}x{cols} fp16, sampled rows")
