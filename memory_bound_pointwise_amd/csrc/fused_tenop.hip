@@ -350,8 +350,14 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop8_kernel(
   }
 }
 
-// 16-bit rows of 65-128 vectors: a wave per row (64 lanes x 2 vectors), 16
-// rows a 1024-thread block.  bias, gamma and beta are widened to binary64
+// 16-bit rows of 65-512 vectors: a wave per row (64 lanes x VPL vectors: 2
+// up to 128 vectors, 4 up to 256, 8 up to 512), RPB rows a block (16; 8 for
+// 8 vectors, whose 512-thread blocks leave 256 registers a lane: 164-168
+// used, LDS 96 KB).  Measured (same process, inputs out of the caches, us)
+// against tenop8_kernel's table layouts: 4 vectors 8192 x 2048 fp16 18.02 ->
+// 16.09, 8192 x 1536 bf16 15.24 -> 13.25, 4096 x 1032 fp16 8.70 -> 7.49; 8
+// vectors 4096 x 2056 fp16 15.38 -> 14.20, 4096 x 4096 bf16 18.12 -> 17.59.
+// bias, gamma and beta are widened to binary64
 // once per block into LDS (24 KB) instead of twice per use in every wave --
 // the kernel is bound by its vector instructions, and the widenings were six
 // of its ~30 a element: 8192 x 1024 fp16 10.42 -> 9.40 us, bf16 10.26 ->
@@ -361,12 +367,12 @@ __global__ __launch_bounds__(block_for(LANES)) void tenop8_kernel(
 // launch at 8192 x 1024); pairs interleaved by vector are read conflict-free:
 // 9.71 -> 8.85 us (bf16 9.73 -> 8.72, 8192 x 600 fp16 8.83 -> 8.52).  The
 // arithmetic and the reduction order are tenop8_kernel's, so are the results.
-template <class IO>
-__global__ __launch_bounds__(1024) void tenop8_wave_kernel(
+template <class IO, int VPL, int RPB = 16>
+__global__ __launch_bounds__(64 * RPB) void tenop8_wave_kernel(
     const typename IO::elem* x, int64_t ldx, const typename IO::elem* __restrict__ bias,
     const typename IO::elem* __restrict__ gamma, const typename IO::elem* __restrict__ beta,
     typename IO::elem* y, int64_t ldy, int64_t rows, int cols, double alpha, double c, double inv_cols) {
-  constexpr int LANES = 64, VPL = 2, RPB = 16, BLOCK = LANES * RPB;
+  constexpr int LANES = 64, BLOCK = LANES * RPB;
   static_assert(sizeof(typename IO::elem) == 2, "16-bit storage only");
   // bias, gamma, beta of the row's columns; element e of vector v at
   // pidx(v, e): pairs of elements interleaved by vector, so that the lanes of
@@ -375,7 +381,7 @@ __global__ __launch_bounds__(1024) void tenop8_wave_kernel(
   __shared__ double pw[3][8 * NV];
   auto pidx = [](int v, int e) { return ((e >> 1) * NV + v) * 2 + (e & 1); };
   const int lane = threadIdx.x % LANES;
-  const int nvec = cols / 8;  // 65 .. 128 (the host checks)
+  const int nvec = cols / 8;  // (LANES VPL / 2, LANES VPL] (the host checks)
   for (int v = threadIdx.x; v < nvec; v += BLOCK) {
     const u32x4 b = reinterpret_cast<const u32x4*>(bias)[v];
     const u32x4 g = reinterpret_cast<const u32x4*>(gamma)[v];
@@ -427,15 +433,15 @@ __global__ __launch_bounds__(1024) void tenop8_wave_kernel(
   }
 }
 
-// Rows of 65-128 vectors (32 x 3, 32 x 4) take tenop8_wave_kernel and rows
-// past 16384 columns the two-pass kernel, so those layouts are not
+// Rows of 65-512 vectors (32 x 3 up to 128 x 4) take tenop8_wave_kernel and
+// rows past 16384 columns the two-pass kernel, so those layouts are not
 // instantiated here.
 template <class IO>
 struct Tenop8Sel {
   template <int L, int V>
   struct K {
     static const void* ptr() {
-      if constexpr ((L == 32 && V >= 3) || L == 1024) return nullptr;
+      if constexpr ((L == 32 && V >= 3) || (L == 64 && V == 4) || (L == 128 && V == 4) || L == 1024) return nullptr;
       else return reinterpret_cast<const void*>(&tenop8_kernel<IO, L, V>);
     }
   };
@@ -506,13 +512,16 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
   int lanes = kShapes[shape].lanes;
   if constexpr (sizeof(E) == 2) {
     if (vector8_ok) k = shape_kernel<Tenop8Sel<IO>::template K>(shape);
-    // rows of 65-128 vectors: 64 lanes x 2 rather than the table's 32 x 4
-    // (8192 x 1024 fp16, row stride 1056: 10.26 against 10.57 us; 128 x 1:
-    // 10.63), 16 rows a block with the parameters widened once (above)
-    if (vector8_ok && cols / 8 > 64 && cols / 8 <= 128) {
-      const int64_t g16 = (rows + 15) / 16;
+    // rows of 65-512 vectors: a wave per row with the parameters widened
+    // once per block (above; rows of 65-128 vectors: 64 lanes x 2 rather than
+    // the table's 32 x 4, 8192 x 1024 fp16 in rows of 1056: 10.26 against
+    // 10.57 us; 128 x 1: 10.63)
+    if (vector8_ok && cols / 8 > 64 && cols / 8 <= 512) {
+      const bool w8 = cols / 8 > 256;
+      const int rpbw = w8 ? 8 : 16;
+      const int64_t g16 = (rows + rpbw - 1) / rpbw;
       // one block per 16 rows, no loop (at most kRowsPerDispatch rows here)
-      if (g16 > dispatch_blocks(1024)) return hipErrorInvalidValue;
+      if (g16 > dispatch_blocks(64 * rpbw)) return hipErrorInvalidValue;
       {
         int icols8 = (int)cols;
         const E *xe = static_cast<const E*>(x), *bie = static_cast<const E*>(bias);
@@ -520,8 +529,10 @@ hipError_t launch_tenop(const void* x, int64_t ldx, const void* bias, const void
         E* ye = static_cast<E*>(y);
         double inv8 = 1.0 / (double)cols;
         void* args8[] = {&xe, &ldx, &bie, &ge, &bee, &ye, &ldy, &rows, &icols8, &alpha, &c, &inv8};
-        return hipLaunchKernel(reinterpret_cast<const void*>(&tenop8_wave_kernel<IO>), dim3((unsigned)g16),
-                               dim3(1024), args8, 0, s);
+        const void* kw = cols / 8 <= 128 ? reinterpret_cast<const void*>(&tenop8_wave_kernel<IO, 2>)
+                         : !w8            ? reinterpret_cast<const void*>(&tenop8_wave_kernel<IO, 4>)
+                                          : reinterpret_cast<const void*>(&tenop8_wave_kernel<IO, 8, 8>);
+        return hipLaunchKernel(kw, dim3((unsigned)g16), dim3(64 * rpbw), args8, 0, s);
       }
     }
   } else {
