@@ -713,6 +713,34 @@ TENOP_2D = [(64, 1024, 0, 0), (33, 1001, 0, 0), (40, 512, 8, 16), (21, 515, 5, 3
             (4, 13001, 3, 1), (3, 14000, 5, 0), (6, 10000, 0, 4)]
 
 
+# The looping 10-op kernels run on a few blocks per compute unit (two for
+# fp32, four for 16-bit), each taking many row groups in turn (its LDS
+# reduction buffers alternating): row counts that give every block several
+# groups and the last ones uneven shares, on each looping path -- fp32 with
+# 4-element accesses and one element at a time, 16-bit with 8-element (rows
+# up to 64 and past 512 vectors), 4-element and single-element accesses.
+TENOP_LOOP = [("f32", 4099, 2048, 0), ("f32", 4101, 1001, 1), ("bf16", 4097, 4104, 0), ("f16", 40003, 256, 0),
+              ("f16", 6001, 1028, 4), ("bf16", 8003, 1001, 1)]
+
+
+@pytest.mark.parametrize("fmt,rows,cols,off", TENOP_LOOP)
+def test_tenop_persistent_loop(mbp, fmt, rows, cols, off):
+    dtype = dict(DT2D)[fmt]
+    rng = np.random.default_rng([89, rows, cols])
+    xh, xf = _stored(rng, (rows, cols), dtype)
+    vecs = [_stored(rng, (cols,), dtype) for _ in range(3)]
+    buf = torch.zeros(rows * cols + 8, dtype=dtype, device="cuda")
+    x = buf[off:off + rows * cols].view(rows, cols)
+    x.copy_(xh.cuda())
+    ybuf = torch.full((rows * cols + 8,), 3.0, dtype=dtype, device="cuda")
+    y = ybuf[off:off + rows * cols].view(rows, cols)
+    mbp.fused_row_mean_epilogue_2d(x, *(v[0].cuda() for v in vecs), alpha=1.1, c=0.1, out=y)
+    exact = oracle.row_mean_epilogue(xf, *(v[1] for v in vecs), 1.1, 0.1)
+    _gate_2d(y, exact, fmt, f"10-op {fmt} {rows}x{cols} at +{off}, persistent loop", row_kernel=True)
+    rest = torch.cat([ybuf[:off], ybuf[off + rows * cols:]]).float()
+    assert (rest == 3.0).all(), "wrote outside y"
+
+
 @pytest.mark.parametrize("fmt,dtype", DT2D, ids=[d[0] for d in DT2D])
 @pytest.mark.parametrize("rows,cols,xpad,ypad", TENOP_2D)
 def test_tenop_2d(mbp, fmt, dtype, rows, cols, xpad, ypad):
